@@ -1,0 +1,151 @@
+"""CPU oracle for the fixed-order row softmax -- TEST INFRASTRUCTURE ONLY.
+
+This package wraps ``libjas_oracle.so`` (built from ``jas_oracle.c`` by
+``oracle/build.py``) with numpy arrays.  It is the reference the HIP library is
+checked against.  Only the tests, ``__graft_entry__.smoke()`` and the CPU
+baseline leg of ``bench.py`` may import it; the HIP library and its Python
+binding never do.
+
+Arrays: bf16 tensors travel as ``numpy.uint16`` bit patterns, fp32 tensors as
+``numpy.float32``.  All functions follow the pages cited in ``jas_oracle.c``:
+RL-Kernel PR #453 (fixed-order online softmax, fixed-order backward), ROCm
+TransformerEngine PR #678 (softmax sink), RL-Kernel PR #240 (fixed power-of-two
+reduction tree, fully masked rows).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libjas_oracle.so")
+_lib = None
+
+F32, BF16 = 0, 1
+_I64 = ctypes.c_int64
+_VP = ctypes.c_void_p
+
+
+def default_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _b
+            _b.build()
+        L = ctypes.CDLL(_LIB_PATH)
+        L.jas_oracle_fwd.restype = ctypes.c_int
+        L.jas_oracle_fwd.argtypes = [ctypes.c_int, _I64, _I64, _I64, _I64, _I64, _VP, _VP,
+                                     _I64, _I64, _I64, _VP, _VP, _VP, ctypes.c_int]
+        L.jas_oracle_bwd.restype = ctypes.c_int
+        L.jas_oracle_bwd.argtypes = [ctypes.c_int, _I64, _I64, _I64, _I64, _I64, _VP, _VP, _VP,
+                                     _VP, _VP, ctypes.c_int]
+        L.jas_oracle_dsink.restype = ctypes.c_int
+        L.jas_oracle_dsink.argtypes = [_I64, _I64, _I64, _VP, _VP]
+        L.jas_oracle_exp.restype = ctypes.c_float
+        L.jas_oracle_exp.argtypes = [ctypes.c_float]
+        L.jas_oracle_log2e.restype = ctypes.c_float
+        L.jas_oracle_log2e.argtypes = []
+        L.jas_oracle_bf16.restype = ctypes.c_uint16
+        L.jas_oracle_bf16.argtypes = [ctypes.c_float]
+        L.jas_oracle_tree_sum256.restype = ctypes.c_float
+        L.jas_oracle_tree_sum256.argtypes = [_VP]
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError(f"scores must be float32 or uint16 (bf16 bits), got {a.dtype}")
+
+
+def fwd(scores, B, H, Sq, N, ld=None, mask=None, mask_strides=(0, 0, 0), sink=None,
+        threads=None):
+    """Forward pass.  ``scores`` is a C-contiguous array holding B*H*Sq rows of
+    stride ``ld`` (default N).  Returns ``(P, p_sink)``; ``P`` has the layout
+    and dtype of ``scores`` (row padding past N is left zero) and ``p_sink`` is
+    float32 [B*H*Sq] or None when no sink is given."""
+    scores = np.ascontiguousarray(scores)
+    ld = N if ld is None else ld
+    rows = B * H * Sq
+    if scores.size < (rows - 1) * ld + N if rows else 0:
+        raise ValueError("scores too small for the shape")
+    P = np.zeros_like(scores)
+    if mask is not None:
+        mask = np.ascontiguousarray(mask, dtype=np.float32)
+    if sink is not None:
+        sink = np.ascontiguousarray(sink, dtype=np.float32)
+        if sink.size < H:
+            raise ValueError("sink needs one value per head")
+    ps = np.zeros(rows, np.float32) if sink is not None else None
+    msb, msh, msq = mask_strides
+    rc = lib().jas_oracle_fwd(_dtype_code(scores), B, H, Sq, N, ld, _ptr(scores), _ptr(mask),
+                              msb, msh, msq, _ptr(sink), _ptr(P), _ptr(ps),
+                              threads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"jas_oracle_fwd failed: {rc}")
+    return P, ps
+
+
+def bwd(P, dP, B, H, Sq, N, ld=None, p_sink=None, threads=None):
+    """Backward pass on stored probabilities.  Returns ``(dS, v)`` where ``v``
+    is the float32 per-row d_sink share (None without ``p_sink``)."""
+    P = np.ascontiguousarray(P)
+    dP = np.ascontiguousarray(dP)
+    if P.dtype != dP.dtype or P.shape != dP.shape:
+        raise ValueError("P and dP must share dtype and shape")
+    ld = N if ld is None else ld
+    rows = B * H * Sq
+    dS = np.zeros_like(P)
+    v = None
+    if p_sink is not None:
+        p_sink = np.ascontiguousarray(p_sink, dtype=np.float32)
+        v = np.zeros(rows, np.float32)
+    rc = lib().jas_oracle_bwd(_dtype_code(P), B, H, Sq, N, ld, _ptr(P), _ptr(dP), _ptr(p_sink),
+                              _ptr(dS), _ptr(v), threads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"jas_oracle_bwd failed: {rc}")
+    return dS, v
+
+
+def dsink(v, B, H, Sq):
+    """Per-head d_sink from per-row shares ``v`` (float32 [B*H*Sq])."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.zeros(H, np.float32)
+    rc = lib().jas_oracle_dsink(B, H, Sq, _ptr(v), _ptr(out))
+    if rc != 0:
+        raise RuntimeError(f"jas_oracle_dsink failed: {rc}")
+    return out
+
+
+def exp_(y: float) -> np.float32:
+    return np.float32(lib().jas_oracle_exp(float(np.float32(y))))
+
+
+def log2e() -> np.float32:
+    return np.float32(lib().jas_oracle_log2e())
+
+
+def bf16_rne(x: float) -> int:
+    return int(lib().jas_oracle_bf16(float(np.float32(x))))
+
+
+def tree_sum256(v) -> np.float32:
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    if v.size != 256:
+        raise ValueError("tree_sum256 takes exactly 256 values")
+    return np.float32(lib().jas_oracle_tree_sum256(_ptr(v)))
