@@ -1,0 +1,223 @@
+"""Python binding of libjas.so: fixed-order, batch-invariant row softmax on
+MI355X (gfx950).
+
+The C ABI (include/jas.h) is the product; this module only marshals
+arguments.  ``jas_fwd`` / ``jas_bwd`` / ``jas_fwd_ex`` / ``jas_bwd_ex`` /
+``jas_bwd_workspace_bytes`` / ``jas_status_str`` / ``jas_contract`` call the C
+functions of the same names with raw pointers.  ``fwd`` and ``bwd`` take torch
+tensors: torch provides device memory and the current stream, every step of
+the computation runs in the library's HIP kernels.  There is no fallback: if
+``libjas.so`` is missing the first call raises.
+"""
+import ctypes
+import os
+
+__all__ = [
+    "JAS_DTYPE_F32", "JAS_DTYPE_BF16", "JAS_FLAG_MASK", "JAS_FLAG_SINK", "JAS_MAX_KEYS",
+    "STATUS", "JasError", "jas_desc_t", "jas_launch_t", "lib", "jas_fwd", "jas_fwd_ex",
+    "jas_bwd", "jas_bwd_ex", "jas_bwd_workspace_bytes", "jas_status_str", "jas_contract",
+    "make_desc", "fwd", "bwd", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libjas.so")
+
+JAS_DTYPE_F32, JAS_DTYPE_BF16 = 0, 1
+JAS_FLAG_MASK, JAS_FLAG_SINK = 1, 2
+JAS_MAX_KEYS = 16384
+STATUS = {
+    0: "JAS_OK", 1: "JAS_ERR_NULL_POINTER", 2: "JAS_ERR_BAD_SHAPE", 3: "JAS_ERR_BAD_DTYPE",
+    4: "JAS_ERR_BAD_FLAGS", 5: "JAS_ERR_ALIASING", 6: "JAS_ERR_WORKSPACE",
+    7: "JAS_ERR_UNSUPPORTED", 8: "JAS_ERR_HIP", 9: "JAS_ERR_ALIGNMENT",
+}
+
+
+class jas_desc_t(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("heads", ctypes.c_int64), ("q_rows", ctypes.c_int64),
+        ("keys", ctypes.c_int64), ("ld", ctypes.c_int64), ("dtype", ctypes.c_int32),
+        ("flags", ctypes.c_uint32), ("mask_stride_b", ctypes.c_int64),
+        ("mask_stride_h", ctypes.c_int64), ("mask_stride_q", ctypes.c_int64),
+    ]
+
+
+class jas_launch_t(ctypes.Structure):
+    _fields_ = [
+        ("waves_per_row", ctypes.c_int32), ("chunks_per_lane", ctypes.c_int32),
+        ("rows_per_block", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
+    ]
+
+
+class JasError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({jas_status_str(status)})")
+
+
+_lib = None
+_VP = ctypes.c_void_p
+_DP = ctypes.POINTER(jas_desc_t)
+_LP = ctypes.POINTER(jas_launch_t)
+
+
+def lib():
+    """Load libjas.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        L.jas_fwd.restype = ctypes.c_int
+        L.jas_fwd.argtypes = [_DP, _VP, _VP, _VP, _VP, _VP, _VP]
+        L.jas_fwd_ex.restype = ctypes.c_int
+        L.jas_fwd_ex.argtypes = [_DP, _VP, _VP, _VP, _VP, _VP, _LP, _VP]
+        L.jas_bwd.restype = ctypes.c_int
+        L.jas_bwd.argtypes = [_DP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]
+        L.jas_bwd_ex.restype = ctypes.c_int
+        L.jas_bwd_ex.argtypes = [_DP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _LP, _VP]
+        L.jas_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.jas_bwd_workspace_bytes.argtypes = [_DP]
+        L.jas_status_str.restype = ctypes.c_char_p
+        L.jas_status_str.argtypes = [ctypes.c_int]
+        L.jas_contract.restype = ctypes.c_char_p
+        L.jas_contract.argtypes = []
+        _lib = L
+    return _lib
+
+
+# ---- the C entry points, one to one -------------------------------------
+
+def jas_fwd(desc, scores, mask, sink, probs, p_sink, stream):
+    return lib().jas_fwd(ctypes.byref(desc), scores, mask, sink, probs, p_sink, stream)
+
+
+def jas_fwd_ex(desc, scores, mask, sink, probs, p_sink, launch, stream):
+    lp = ctypes.byref(launch) if launch is not None else None
+    return lib().jas_fwd_ex(ctypes.byref(desc), scores, mask, sink, probs, p_sink, lp, stream)
+
+
+def jas_bwd(desc, probs, dprobs, p_sink, dscores, d_sink, workspace, workspace_bytes, stream):
+    return lib().jas_bwd(ctypes.byref(desc), probs, dprobs, p_sink, dscores, d_sink, workspace,
+                         workspace_bytes, stream)
+
+
+def jas_bwd_ex(desc, probs, dprobs, p_sink, dscores, d_sink, workspace, workspace_bytes, launch,
+               stream):
+    lp = ctypes.byref(launch) if launch is not None else None
+    return lib().jas_bwd_ex(ctypes.byref(desc), probs, dprobs, p_sink, dscores, d_sink, workspace,
+                            workspace_bytes, lp, stream)
+
+
+def jas_bwd_workspace_bytes(desc):
+    return int(lib().jas_bwd_workspace_bytes(ctypes.byref(desc)))
+
+
+def jas_status_str(status):
+    return lib().jas_status_str(int(status)).decode()
+
+
+def jas_contract():
+    return lib().jas_contract().decode()
+
+
+# ---- torch-tensor marshalling -------------------------------------------
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def make_desc(shape, dtype_code, flags=0, ld=None, mask_strides=(0, 0, 0)):
+    B, H, S, N = (int(v) for v in shape)
+    d = jas_desc_t()
+    d.batch, d.heads, d.q_rows, d.keys = B, H, S, N
+    d.ld = N if ld is None else int(ld)
+    d.dtype = dtype_code
+    d.flags = flags
+    d.mask_stride_b, d.mask_stride_h, d.mask_stride_q = (int(v) for v in mask_strides)
+    return d
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return JAS_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return JAS_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _launch(launch):
+    if launch is None:
+        return None
+    if isinstance(launch, jas_launch_t):
+        return launch
+    L = jas_launch_t()
+    L.waves_per_row, L.chunks_per_lane, L.rows_per_block, L.max_blocks = (
+        int(v) for v in (tuple(launch) + (0, 0, 0, 0))[:4])
+    return L
+
+
+def _shape4(t):
+    if t.dim() != 4:
+        raise ValueError("tensors are [batch, heads, q_rows, keys]")
+    if t.stride(3) != 1 or t.stride(2) < t.shape[3] or t.stride(1) != t.shape[2] * t.stride(2) \
+            or t.stride(0) != t.shape[1] * t.stride(1):
+        raise ValueError("rows must be contiguous with one row stride (ld)")
+    return t.shape, t.stride(2)
+
+
+def fwd(scores, mask=None, mask_strides=None, sink=None, out=None, p_sink=None, launch=None):
+    """Forward on device tensors.  ``scores`` [B,H,Sq,N] bf16/fp32 (rows may
+    have a stride ld >= N); ``mask`` fp32 addressed with ``mask_strides``
+    (b, h, q) in elements (default: a contiguous [B,H,Sq,N] tensor broadcast
+    by its own zero strides); ``sink`` fp32 [H].  Returns (probs, p_sink)."""
+    import torch
+    shape, ld = _shape4(scores)
+    flags = 0
+    if mask is not None:
+        flags |= JAS_FLAG_MASK
+        if mask_strides is None:
+            m4 = mask.expand(shape[0], shape[1], shape[2], shape[3])
+            if m4.stride(3) != 1:
+                raise ValueError("mask keys must be contiguous")
+            mask_strides = (m4.stride(0), m4.stride(1), m4.stride(2))
+    if sink is not None:
+        flags |= JAS_FLAG_SINK
+    d = make_desc(shape, _dtype_code(scores), flags, ld, mask_strides or (0, 0, 0))
+    if out is None:
+        out = torch.empty_like(scores)
+    if sink is not None and p_sink is None:
+        p_sink = torch.empty(shape[0] * shape[1] * shape[2], dtype=torch.float32,
+                             device=scores.device)
+    st = jas_fwd_ex(d, _ptr(scores), _ptr(mask), _ptr(sink), _ptr(out),
+                    _ptr(p_sink) if sink is not None else None, _launch(launch), _stream())
+    if st != 0:
+        raise JasError(st, "jas_fwd")
+    return out, (p_sink if sink is not None else None)
+
+
+def bwd(probs, dprobs, p_sink=None, out=None, d_sink=None, workspace=None, launch=None):
+    """Backward on device tensors.  Returns (dscores, d_sink or None)."""
+    import torch
+    shape, ld = _shape4(probs)
+    flags = JAS_FLAG_SINK if p_sink is not None else 0
+    d = make_desc(shape, _dtype_code(probs), flags, ld)
+    if out is None:
+        out = torch.empty_like(probs)
+    ws_bytes = jas_bwd_workspace_bytes(d)
+    if p_sink is not None:
+        if d_sink is None:
+            d_sink = torch.empty(shape[1], dtype=torch.float32, device=probs.device)
+        if workspace is None:
+            workspace = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device=probs.device)
+    st = jas_bwd_ex(d, _ptr(probs), _ptr(dprobs), _ptr(p_sink), _ptr(out),
+                    _ptr(d_sink) if p_sink is not None else None,
+                    _ptr(workspace) if p_sink is not None else None,
+                    workspace.numel() if workspace is not None else 0, _launch(launch), _stream())
+    if st != 0:
+        raise JasError(st, "jas_bwd")
+    return out, (d_sink if p_sink is not None else None)

@@ -1,0 +1,309 @@
+// jas_api.cpp -- the C ABI of include/jas.h: host-side validation, launch
+// geometry, dispatch.  Every check runs on the host before any HIP call; the
+// library never allocates, frees or synchronizes.
+
+#include <stdint.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "jas.h"
+#include "jas_internal.h"
+
+namespace {
+
+using jas::Geometry;
+
+struct Dims {
+  int64_t rows;     // batch*heads*q_rows
+  int64_t span;     // elements from the first row's start to the last row's end
+  int64_t esz;      // bytes per element
+  int T;            // tiles per row
+};
+
+bool mul_ok(int64_t a, int64_t b, int64_t *out) { return !__builtin_mul_overflow(a, b, out); }
+bool add_ok(int64_t a, int64_t b, int64_t *out) { return !__builtin_add_overflow(a, b, out); }
+
+jas_status_t check_desc(const jas_desc_t *d, Dims *dims) {
+  if (!d) return JAS_ERR_NULL_POINTER;
+  if (d->dtype != JAS_DTYPE_F32 && d->dtype != JAS_DTYPE_BF16) return JAS_ERR_BAD_DTYPE;
+  if (d->flags & ~(uint32_t)(JAS_FLAG_MASK | JAS_FLAG_SINK)) return JAS_ERR_BAD_FLAGS;
+  if (d->batch < 0 || d->heads < 0 || d->q_rows < 0 || d->keys < 1 || d->ld < d->keys)
+    return JAS_ERR_BAD_SHAPE;
+  if (d->mask_stride_b < 0 || d->mask_stride_h < 0 || d->mask_stride_q < 0)
+    return JAS_ERR_BAD_SHAPE;
+  int64_t bh = 0, rows = 0, span = 0, bytes = 0;
+  if (!mul_ok(d->batch, d->heads, &bh) || !mul_ok(bh, d->q_rows, &rows)) return JAS_ERR_BAD_SHAPE;
+  const int64_t esz = d->dtype == JAS_DTYPE_BF16 ? 2 : 4;
+  if (rows > 0) {
+    if (!mul_ok(rows - 1, d->ld, &span) || !add_ok(span, d->keys, &span) ||
+        !mul_ok(span, esz, &bytes))
+      return JAS_ERR_BAD_SHAPE;
+  }
+  if (d->keys > JAS_MAX_KEYS) return JAS_ERR_UNSUPPORTED;
+  dims->rows = rows;
+  dims->span = span;
+  dims->esz = esz;
+  dims->T = (int)((d->keys + jas::kTile - 1) / jas::kTile);
+  return JAS_OK;
+}
+
+// Byte range [lo, hi) of a buffer.
+struct Range {
+  uintptr_t lo, hi;
+};
+
+Range range_of(const void *p, int64_t bytes) {
+  const uintptr_t a = (uintptr_t)p;
+  return Range{a, a + (uintptr_t)(bytes > 0 ? bytes : 0)};
+}
+
+bool overlap(Range a, Range b) {
+  if (a.lo == a.hi || b.lo == b.hi) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void *p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
+
+// Bytes of the mask touched by the shape: the largest addressed element + 1.
+jas_status_t mask_bytes(const jas_desc_t *d, int64_t *bytes) {
+  int64_t off = d->keys, t = 0;
+  const int64_t dims[3] = {d->batch, d->heads, d->q_rows};
+  const int64_t strides[3] = {d->mask_stride_b, d->mask_stride_h, d->mask_stride_q};
+  for (int i = 0; i < 3; ++i) {
+    if (!mul_ok(dims[i] - 1, strides[i], &t) || !add_ok(off, t, &off)) return JAS_ERR_BAD_SHAPE;
+  }
+  if (!mul_ok(off, 4, bytes)) return JAS_ERR_BAD_SHAPE;
+  return JAS_OK;
+}
+
+// Launch geometry: the override when given (checked), else the default.
+// tiles are covered by slots of TPS tiles; a row needs ceil(T/TPS) slots,
+// spread over wpr waves holding cpl slots each.
+jas_status_t choose_geometry(int dtype, int T, int64_t rows, const jas_launch_t *ov, Geometry *g) {
+  const int tps = jas::tiles_per_slot(dtype);
+  const int nslots = (T + tps - 1) / tps;
+  int ncpl = 0;
+  const int *cpls = jas::compiled_cpls(dtype, &ncpl);
+  int wpr = ov ? ov->waves_per_row : 0;
+  int cpl = ov ? ov->chunks_per_lane : 0;
+  int rpb = ov ? ov->rows_per_block : 0;
+  const int64_t cap = ov ? ov->max_blocks : 0;
+  if (wpr < 0 || cpl < 0 || rpb < 0 || cap < 0) return JAS_ERR_UNSUPPORTED;
+  if (wpr == 0) {
+    // fewest waves per row whose register share stays within the default cap
+    for (int w : {1, 2, 4}) {
+      const int need = (nslots + w - 1) / w;
+      if (cpl ? cpl * w >= nslots : need <= jas::default_cpl_max(dtype)) {
+        wpr = w;
+        break;
+      }
+    }
+    if (wpr == 0) return JAS_ERR_UNSUPPORTED;
+  }
+  if (cpl == 0) {
+    const int need = (nslots + wpr - 1) / wpr;
+    for (int i = 0; i < ncpl; ++i)
+      if (cpls[i] >= need) {
+        cpl = cpls[i];
+        break;
+      }
+    if (cpl == 0) return JAS_ERR_UNSUPPORTED;
+  }
+  if (!jas::cpl_compiled(dtype, wpr, cpl) || (int64_t)wpr * cpl < nslots) return JAS_ERR_UNSUPPORTED;
+  if (rpb == 0) rpb = jas::kBlockWaves / wpr;
+  if (rpb < 1 || wpr * rpb > jas::kBlockWaves) return JAS_ERR_UNSUPPORTED;
+  int64_t blocks = (rows + rpb - 1) / rpb;
+  if (cap > 0 && blocks > cap) blocks = cap;
+  if (blocks > 0x7fffffff) blocks = 0x7fffffff;  // the workgroups loop over the rest
+  g->wpr = wpr;
+  g->cpl = cpl;
+  g->rpb = rpb;
+  g->blocks = blocks;
+  return JAS_OK;
+}
+
+jas_status_t fwd_impl(const jas_desc_t *d, const void *scores, const float *mask,
+                      const float *sink, void *probs, float *p_sink, const jas_launch_t *launch,
+                      void *stream) {
+  Dims dm;
+  jas_status_t st = check_desc(d, &dm);
+  if (st != JAS_OK) return st;
+  const bool has_mask = (d->flags & JAS_FLAG_MASK) != 0;
+  const bool has_sink = (d->flags & JAS_FLAG_SINK) != 0;
+  if (dm.rows == 0) {  // nothing is read or written; row pointers may be NULL
+    if ((!has_mask && mask) || (!has_sink && (sink || p_sink))) return JAS_ERR_BAD_FLAGS;
+    return JAS_OK;
+  }
+  if (!scores || !probs) return JAS_ERR_NULL_POINTER;
+  if (has_mask && !mask) return JAS_ERR_NULL_POINTER;
+  if (has_sink && (!sink || !p_sink)) return JAS_ERR_NULL_POINTER;
+  if ((!has_mask && mask) || (!has_sink && (sink || p_sink))) return JAS_ERR_BAD_FLAGS;
+  if (!aligned(scores, dm.esz) || !aligned(probs, dm.esz) || (mask && !aligned(mask, 4)) ||
+      (sink && !aligned(sink, 4)) || (p_sink && !aligned(p_sink, 4)))
+    return JAS_ERR_ALIGNMENT;
+
+  const int64_t tbytes = dm.span * dm.esz;
+  const Range rs = range_of(scores, tbytes), rp = range_of(probs, tbytes);
+  int64_t mb = 0;
+  if (has_mask && dm.rows > 0) {
+    st = mask_bytes(d, &mb);
+    if (st != JAS_OK) return st;
+  }
+  const Range rm = range_of(mask, has_mask ? mb : 0);
+  const Range rk = range_of(sink, has_sink ? d->heads * 4 : 0);
+  const Range rps = range_of(p_sink, has_sink ? dm.rows * 4 : 0);
+  if (probs != scores && overlap(rp, rs)) return JAS_ERR_ALIASING;
+  if (overlap(rp, rm) || overlap(rp, rk) || overlap(rp, rps)) return JAS_ERR_ALIASING;
+  if (overlap(rps, rs) || overlap(rps, rm) || overlap(rps, rk)) return JAS_ERR_ALIASING;
+
+  Geometry g;
+  st = choose_geometry(d->dtype, dm.T, dm.rows, launch, &g);
+  if (st != JAS_OK) return st;
+  jas::FwdArgs a;
+  a.scores = scores;
+  a.probs = probs;
+  a.mask = has_mask ? mask : nullptr;
+  a.msb = d->mask_stride_b;
+  a.msh = d->mask_stride_h;
+  a.msq = d->mask_stride_q;
+  a.sink = has_sink ? sink : nullptr;
+  a.p_sink = has_sink ? p_sink : nullptr;
+  a.s = jas::RowShape{dm.rows, d->keys, d->ld, d->heads, d->q_rows, dm.T};
+  // 16-byte path: every row is whole 16-byte chunks starting on 16-byte
+  // boundaries (and so is every mask row); otherwise element-wise access.
+  // Both paths compute the same bits.
+  const int64_t kpc = jas::keys_per_chunk(d->dtype);
+  a.vec_mask = !has_mask || (aligned(mask, 16) && d->mask_stride_b % 4 == 0 &&
+                             d->mask_stride_h % 4 == 0 && d->mask_stride_q % 4 == 0);
+  a.vec_io = aligned(scores, 16) && aligned(probs, 16) && (d->ld % kpc == 0) &&
+             (d->keys % kpc == 0) && a.vec_mask;
+  if (jas::launch_fwd(d->dtype, a, g, (hipStream_t)stream) != hipSuccess) return JAS_ERR_HIP;
+  return JAS_OK;
+}
+
+jas_status_t bwd_impl(const jas_desc_t *d, const void *probs, const void *dprobs,
+                      const float *p_sink, void *dscores, float *d_sink, void *workspace,
+                      size_t workspace_bytes, const jas_launch_t *launch, void *stream) {
+  Dims dm;
+  jas_status_t st = check_desc(d, &dm);
+  if (st != JAS_OK) return st;
+  const bool has_sink = (d->flags & JAS_FLAG_SINK) != 0;
+  if (dm.rows == 0) {  // nothing is read; only d_sink is written (+0 per head)
+    if (!has_sink && (p_sink || d_sink)) return JAS_ERR_BAD_FLAGS;
+    if (!has_sink || d->heads == 0) return JAS_OK;
+    if (!d_sink) return JAS_ERR_NULL_POINTER;
+    if (!aligned(d_sink, 4)) return JAS_ERR_ALIGNMENT;
+    jas::DsinkArgs s{nullptr, d_sink, d->batch, d->heads, d->q_rows};
+    if (jas::launch_dsink(s, (hipStream_t)stream) != hipSuccess) return JAS_ERR_HIP;
+    return JAS_OK;
+  }
+  if (!probs || !dprobs || !dscores) return JAS_ERR_NULL_POINTER;
+  if (has_sink && (!p_sink || !d_sink)) return JAS_ERR_NULL_POINTER;
+  if (!has_sink && (p_sink || d_sink)) return JAS_ERR_BAD_FLAGS;
+  if (!aligned(probs, dm.esz) || !aligned(dprobs, dm.esz) || !aligned(dscores, dm.esz) ||
+      (p_sink && !aligned(p_sink, 4)) || (d_sink && !aligned(d_sink, 4)))
+    return JAS_ERR_ALIGNMENT;
+  const size_t need = jas_bwd_workspace_bytes(d);
+  if (has_sink) {
+    if (!workspace || workspace_bytes < need) return JAS_ERR_WORKSPACE;
+    if (!aligned(workspace, 4)) return JAS_ERR_ALIGNMENT;
+  }
+
+  const int64_t tbytes = dm.span * dm.esz;
+  const Range rp = range_of(probs, tbytes), rg = range_of(dprobs, tbytes);
+  const Range rd = range_of(dscores, tbytes);
+  const Range rps = range_of(p_sink, has_sink ? dm.rows * 4 : 0);
+  const Range rds = range_of(d_sink, has_sink ? d->heads * 4 : 0);
+  const Range rw = range_of(workspace, has_sink ? (int64_t)need : 0);
+  if (dscores != probs && overlap(rd, rp)) return JAS_ERR_ALIASING;
+  if (dscores != dprobs && overlap(rd, rg)) return JAS_ERR_ALIASING;
+  if (overlap(rd, rps) || overlap(rd, rds) || overlap(rd, rw)) return JAS_ERR_ALIASING;
+  if (overlap(rds, rp) || overlap(rds, rg) || overlap(rds, rps) || overlap(rds, rw))
+    return JAS_ERR_ALIASING;
+  if (overlap(rw, rp) || overlap(rw, rg) || overlap(rw, rps)) return JAS_ERR_ALIASING;
+
+  Geometry g;
+  st = choose_geometry(d->dtype, dm.T, dm.rows, launch, &g);
+  if (st != JAS_OK) return st;
+
+  {
+    jas::BwdArgs a;
+    a.probs = probs;
+    a.dprobs = dprobs;
+    a.dscores = dscores;
+    a.p_sink = has_sink ? p_sink : nullptr;
+    a.v = has_sink ? static_cast<float *>(workspace) : nullptr;
+    a.s = jas::RowShape{dm.rows, d->keys, d->ld, d->heads, d->q_rows, dm.T};
+    const int64_t kpc = jas::keys_per_chunk(d->dtype);
+    a.vec_io = aligned(probs, 16) && aligned(dprobs, 16) && aligned(dscores, 16) &&
+               (d->ld % kpc == 0) && (d->keys % kpc == 0);
+    if (jas::launch_bwd(d->dtype, a, g, (hipStream_t)stream) != hipSuccess) return JAS_ERR_HIP;
+  }
+  if (has_sink) {
+    jas::DsinkArgs s{static_cast<const float *>(workspace), d_sink, d->batch, d->heads, d->q_rows};
+    if (jas::launch_dsink(s, (hipStream_t)stream) != hipSuccess) return JAS_ERR_HIP;
+  }
+  return JAS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+jas_status_t jas_fwd(const jas_desc_t *desc, const void *scores, const float *mask,
+                     const float *sink, void *probs, float *p_sink, void *stream) {
+  return fwd_impl(desc, scores, mask, sink, probs, p_sink, nullptr, stream);
+}
+
+jas_status_t jas_fwd_ex(const jas_desc_t *desc, const void *scores, const float *mask,
+                        const float *sink, void *probs, float *p_sink,
+                        const jas_launch_t *launch, void *stream) {
+  return fwd_impl(desc, scores, mask, sink, probs, p_sink, launch, stream);
+}
+
+size_t jas_bwd_workspace_bytes(const jas_desc_t *desc) {
+  Dims dm;
+  if (check_desc(desc, &dm) != JAS_OK) return 0;
+  if (!(desc->flags & JAS_FLAG_SINK)) return 0;
+  const size_t b = (size_t)dm.rows * 4u;
+  return (b + 255u) & ~(size_t)255u;
+}
+
+jas_status_t jas_bwd(const jas_desc_t *desc, const void *probs, const void *dprobs,
+                     const float *p_sink, void *dscores, float *d_sink, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+  return bwd_impl(desc, probs, dprobs, p_sink, dscores, d_sink, workspace, workspace_bytes,
+                  nullptr, stream);
+}
+
+jas_status_t jas_bwd_ex(const jas_desc_t *desc, const void *probs, const void *dprobs,
+                        const float *p_sink, void *dscores, float *d_sink, void *workspace,
+                        size_t workspace_bytes, const jas_launch_t *launch, void *stream) {
+  return bwd_impl(desc, probs, dprobs, p_sink, dscores, d_sink, workspace, workspace_bytes,
+                  launch, stream);
+}
+
+const char *jas_status_str(jas_status_t s) {
+  switch (s) {
+    case JAS_OK: return "ok";
+    case JAS_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case JAS_ERR_BAD_SHAPE: return "invalid shape, row stride or mask stride";
+    case JAS_ERR_BAD_DTYPE: return "unknown dtype";
+    case JAS_ERR_BAD_FLAGS: return "unknown flag, or a pointer given for a flag that is not set";
+    case JAS_ERR_ALIASING: return "an output overlaps another buffer";
+    case JAS_ERR_WORKSPACE: return "workspace missing or too small";
+    case JAS_ERR_UNSUPPORTED: return "row length or launch geometry not supported";
+    case JAS_ERR_HIP: return "the HIP runtime refused a launch";
+    case JAS_ERR_ALIGNMENT: return "a pointer is not aligned to its element size";
+  }
+  return "unknown status";
+}
+
+const char *jas_contract(void) {
+  return "jas/1 tile=256 tree=balanced-pairwise-by-key fold=left-to-right sink=merged-last "
+         "acc=fp32 exp=2^fl(y*log2e),flush<2^-126,v_exp_f32 div=ieee cvt=rne "
+         "fpcontract=off atomics=none dsink=256-row-chunks,left-fold arch=gfx950";
+}
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// Internal interface between the host validation layer (jas_api.cpp) and the
+// gfx950 kernels (jas_kernels.hip).  Not installed; the public ABI is jas.h.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace jas {
+
+constexpr int kTile = 256;         // keys per tile (fixed, never tuned)
+constexpr int kWave = 64;          // CDNA wavefront
+constexpr int kMaxKeys = 16384;
+constexpr int kMaxTiles = kMaxKeys / kTile;  // 64: one tile state per lane
+constexpr int kBlockWaves = 4;     // waves per workgroup (256 threads)
+
+struct RowShape {
+  int64_t rows;   // batch * heads * q_rows
+  int64_t N;      // keys
+  int64_t ld;     // row stride in elements
+  int64_t H, Sq;  // for decoding row -> (b, h, q)
+  int T;          // tiles per row
+};
+
+struct FwdArgs {
+  const void *scores;
+  void *probs;
+  const float *mask;  // nullptr when no mask
+  int64_t msb, msh, msq;
+  const float *sink;  // nullptr when no sink
+  float *p_sink;
+  RowShape s;
+  int vec_io;         // 16-byte path: rows (and mask rows) are whole aligned 16-byte chunks
+  int vec_mask;       // mask rows start on 16-byte boundaries (or no mask)
+};
+
+struct BwdArgs {
+  const void *probs;
+  const void *dprobs;
+  void *dscores;
+  const float *p_sink;  // nullptr when no sink
+  float *v;             // per-row d_sink share (workspace), nullptr when no sink
+  RowShape s;
+  int vec_io;         // 16-byte path: rows are whole aligned 16-byte chunks
+};
+
+struct DsinkArgs {
+  const float *v;
+  float *d_sink;
+  int64_t B, H, Sq;
+};
+
+struct Geometry {
+  int wpr;         // waves per row
+  int cpl;         // 16-byte chunks per lane (compiled size)
+  int rpb;         // rows per workgroup
+  int64_t blocks;  // grid size
+};
+
+// Keys held by one 16-byte chunk: 8 bf16 or 4 fp32.
+inline int keys_per_chunk(int dtype) { return dtype == 1 ? 8 : 4; }
+// Tiles covered by one wave-wide chunk (64 lanes x 16 bytes).
+inline int tiles_per_slot(int dtype) { return dtype == 1 ? 2 : 1; }
+
+bool cpl_compiled(int dtype, int wpr, int cpl);
+int default_cpl_max(int dtype);
+const int *compiled_cpls(int dtype, int *count);
+
+hipError_t launch_fwd(int dtype, const FwdArgs &a, const Geometry &g, hipStream_t stream);
+hipError_t launch_bwd(int dtype, const BwdArgs &a, const Geometry &g, hipStream_t stream);
+hipError_t launch_dsink(const DsinkArgs &a, hipStream_t stream);
+
+}  // namespace jas

@@ -1,0 +1,696 @@
+// jas_kernels.hip -- gfx950 kernels of the fixed-order, batch-invariant row
+// softmax (forward, backward, per-head d_sink).
+//
+// Method: RL-Kernel PR #453, "[WS1][kernels] Add fixed-order joint-attention
+// softmax for Qwen-Image", Summary (fixed-order online softmax over 256-key
+// tiles taken left to right, one fixed tree per tile for max and sum, tile
+// states merged in order, FP32 intermediates, one conversion at the write;
+// fixed-order backward delta = sum(P*dP), dS = P*(dP - delta)).  Sink: ROCm
+// TransformerEngine PR #678, Description (one learnable logit per head in the
+// denominator, d_sink per head).  Tree shape independent of launch: RL-Kernel
+// PR #240, Fixed Reduction Contract.
+//
+// Mapping to CDNA4.  A row is owned by one wavefront (or by 2 or 4
+// wavefronts of one workgroup for long rows).  The row is read as 16-byte
+// chunks: a lane's chunk is 8 consecutive bf16 keys or 4 consecutive fp32
+// keys, so a 256-key tile is 32 lanes (bf16) or 64 lanes (fp32) and one
+// wave-wide load ("slot") covers 2 or 1 tiles.  The balanced pairwise tile
+// tree is realised exactly: pairwise adds inside the lane over its
+// consecutive keys, then across lanes with DPP quad permutes (lane xor 1,
+// xor 2), row half-mirror and row mirror (groups of 8 and 16 lanes whose
+// values are already uniform within each half), and the gfx950 permlane16 /
+// permlane32 swaps for 32 and 64 lanes.  IEEE addition is commutative, so
+// every lane of a group ends with the same bits, and the tree is a function
+// of key positions only.  Tile states go through LDS to one lane per tile;
+// the merge is done as a prefix max across lanes, per-tile rescale factors in
+// parallel, then the short serial chain L = L*a_t + q_t that the left fold
+// needs.  No MFMA: there is no contraction here, the kernels are bound by HBM
+// bandwidth.  No atomics: every output element has one writer.
+//
+// Built with -ffp-contract=off (no fused multiply-add is formed from a*b+c),
+// without fast-math, FP32 denormals preserved.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "jas_internal.h"
+
+#if defined(__FAST_MATH__) || (defined(__FINITE_MATH_ONLY__) && __FINITE_MATH_ONLY__)
+#error "fast-math changes the arithmetic contract; build without it"
+#endif
+
+namespace jas {
+namespace {
+
+constexpr float kLog2e = 0x1.715476p+0f;  // binary32 nearest to log2(e)
+constexpr float kNegInf = -__builtin_inff();
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// exp_(y) = 2^fl(y*log2e) with the hardware base-2 exponential; +0 when the
+// exponent is below -126 (no subnormal e) and for y = -inf.
+__device__ __forceinline__ float exp_(float y) {
+  const float u = y * kLog2e;
+  return (u < -126.0f) ? 0.0f : __builtin_amdgcn_exp2f(u);
+}
+
+// Round two binary32 to bf16 (round to nearest-even) and pack them, low
+// half first: gfx950's v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return u2f(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return u2f(w & 0xffff0000u); }
+
+// ---------------------------------------------------------------------------
+// Cross-lane steps of the tile tree
+// ---------------------------------------------------------------------------
+
+constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141; // lane i <- 7-i within 8 lanes
+constexpr int kDppRowMirror = 0x140;     // lane i <- 15-i within 16 lanes
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return u2f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)f2u(v), CTRL, 0xF, 0xF, true));
+}
+
+// Returns (value of the even 16-lane row, value of the odd 16-lane row) of
+// the lane's 32-lane half, in every lane.
+__device__ __forceinline__ f32x2_t rows16_pair(float v) {
+  auto p = __builtin_amdgcn_permlane16_swap(f2u(v), f2u(v), false, false);
+  return f32x2_t{u2f(p[0]), u2f(p[1])};
+}
+
+// Returns (value of lanes 0-31, value of lanes 32-63) in every lane.
+__device__ __forceinline__ f32x2_t halves32_pair(float v) {
+  auto p = __builtin_amdgcn_permlane32_swap(f2u(v), f2u(v), false, false);
+  return f32x2_t{u2f(p[0]), u2f(p[1])};
+}
+
+// Sum over each aligned 32-lane group, as the top 5 levels of a balanced
+// tree whose leaves are the lanes in order.
+__device__ __forceinline__ float group32_sum(float v) {
+  v = v + dpp<kDppQuadXor1>(v);
+  v = v + dpp<kDppQuadXor2>(v);
+  v = v + dpp<kDppRowHalfMirror>(v);
+  v = v + dpp<kDppRowMirror>(v);
+  const f32x2_t p = rows16_pair(v);
+  return p[0] + p[1];
+}
+
+__device__ __forceinline__ float group64_sum(float v) {
+  v = group32_sum(v);
+  const f32x2_t p = halves32_pair(v);
+  return p[0] + p[1];
+}
+
+__device__ __forceinline__ float group32_max(float v) {
+  v = __builtin_fmaxf(v, dpp<kDppQuadXor1>(v));
+  v = __builtin_fmaxf(v, dpp<kDppQuadXor2>(v));
+  v = __builtin_fmaxf(v, dpp<kDppRowHalfMirror>(v));
+  v = __builtin_fmaxf(v, dpp<kDppRowMirror>(v));
+  const f32x2_t p = rows16_pair(v);
+  return __builtin_fmaxf(p[0], p[1]);
+}
+
+__device__ __forceinline__ float group64_max(float v) {
+  v = group32_max(v);
+  const f32x2_t p = halves32_pair(v);
+  return __builtin_fmaxf(p[0], p[1]);
+}
+
+__device__ __forceinline__ float readlane(float v, int lane) {
+  return u2f((uint32_t)__builtin_amdgcn_readlane((int)f2u(v), lane));
+}
+
+// Orders LDS traffic of one wavefront (writes by some lanes, reads by
+// others) when a row is owned by a single wave.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---------------------------------------------------------------------------
+// Element layouts
+// ---------------------------------------------------------------------------
+
+template <int DT> struct Cfg;
+template <> struct Cfg<0> {  // fp32
+  static constexpr int KPL = 4;   // keys per 16-byte chunk
+  static constexpr int LPT = 64;  // lanes per tile
+  static constexpr int TPS = 1;   // tiles per wave-wide chunk
+  static constexpr int ESZ = 4;
+};
+template <> struct Cfg<1> {  // bf16
+  static constexpr int KPL = 8;
+  static constexpr int LPT = 32;
+  static constexpr int TPS = 2;
+  static constexpr int ESZ = 2;
+};
+
+// A 16-byte chunk as 4 words.
+struct Chunk { uint32_t w[4]; };
+
+__device__ __forceinline__ Chunk load_chunk(const char *p) {
+  const uint4 v = *reinterpret_cast<const uint4 *>(p);
+  return Chunk{{v.x, v.y, v.z, v.w}};
+}
+
+__device__ __forceinline__ void store_chunk(char *p, const Chunk &c) {
+  *reinterpret_cast<uint4 *>(p) = make_uint4(c.w[0], c.w[1], c.w[2], c.w[3]);
+}
+
+// Element-by-element chunk load for unaligned rows and the tail of a row:
+// keys at or past n read as `fill` bits.
+template <int DT>
+__device__ __forceinline__ Chunk load_chunk_elems(const char *row, int64_t j0, int64_t n,
+                                                  uint32_t fill) {
+  Chunk c;
+  if constexpr (DT == 1) {
+    const uint16_t *e = reinterpret_cast<const uint16_t *>(row);
+    const uint32_t f = fill & 0xffffu;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t j = j0 + 2 * i;
+      const uint32_t lo = (j < n) ? e[j] : f;
+      const uint32_t hi = (j + 1 < n) ? e[j + 1] : f;
+      c.w[i] = lo | (hi << 16);
+    }
+  } else {
+    const uint32_t *e = reinterpret_cast<const uint32_t *>(row);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t j = j0 + i;
+      c.w[i] = (j < n) ? e[j] : fill;
+    }
+  }
+  return c;
+}
+
+template <int DT>
+__device__ __forceinline__ void store_chunk_elems(char *row, int64_t j0, int64_t n, const Chunk &c) {
+  if constexpr (DT == 1) {
+    uint16_t *e = reinterpret_cast<uint16_t *>(row);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t j = j0 + 2 * i;
+      if (j < n) e[j] = (uint16_t)(c.w[i] & 0xffffu);
+      if (j + 1 < n) e[j + 1] = (uint16_t)(c.w[i] >> 16);
+    }
+  } else {
+    uint32_t *e = reinterpret_cast<uint32_t *>(row);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t j = j0 + i;
+      if (j < n) e[j] = c.w[i];
+    }
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void unpack(const Chunk &c, float (&x)[Cfg<DT>::KPL]) {
+  if constexpr (DT == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bf16_lo(c.w[i]);
+      x[2 * i + 1] = bf16_hi(c.w[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = u2f(c.w[i]);
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ Chunk pack(const float (&x)[Cfg<DT>::KPL]) {
+  Chunk c;
+  if constexpr (DT == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c.w[i] = pack_bf16(x[2 * i], x[2 * i + 1]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c.w[i] = f2u(x[i]);
+  }
+  return c;
+}
+
+// Balanced pairwise tree over the lane's consecutive keys (the bottom
+// levels of the tile tree).
+template <int K>
+__device__ __forceinline__ float lane_tree_sum(const float (&x)[K]) {
+  if constexpr (K == 4) {
+    return (x[0] + x[1]) + (x[2] + x[3]);
+  } else {
+    return ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]));
+  }
+}
+
+template <int K>
+__device__ __forceinline__ float lane_tree_max(const float (&x)[K]) {
+  if constexpr (K == 4) {
+    return __builtin_fmaxf(__builtin_fmaxf(x[0], x[1]), __builtin_fmaxf(x[2], x[3]));
+  } else {
+    return __builtin_fmaxf(
+        __builtin_fmaxf(__builtin_fmaxf(x[0], x[1]), __builtin_fmaxf(x[2], x[3])),
+        __builtin_fmaxf(__builtin_fmaxf(x[4], x[5]), __builtin_fmaxf(x[6], x[7])));
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ float tile_sum(float v) {
+  if constexpr (Cfg<DT>::LPT == 32) return group32_sum(v);
+  else return group64_sum(v);
+}
+
+template <int DT>
+__device__ __forceinline__ float tile_max(float v) {
+  if constexpr (Cfg<DT>::LPT == 32) return group32_max(v);
+  else return group64_max(v);
+}
+
+template <int WPR>
+__device__ __forceinline__ void row_sync() {
+  if constexpr (WPR == 1) wave_sync();
+  else __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// Forward
+// ---------------------------------------------------------------------------
+
+template <int DT, int WPR, int CPL, bool VEC>
+__global__ __launch_bounds__(kWave * kBlockWaves) void fwd_kernel(const FwdArgs a) {
+  using C = Cfg<DT>;
+  constexpr int KPL = C::KPL, LPT = C::LPT, TPS = C::TPS, ESZ = C::ESZ;
+  __shared__ float lds_m[kBlockWaves][kMaxTiles];
+  __shared__ float lds_l[kBlockWaves][kMaxTiles];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int wir = wave % WPR;  // wave within the row
+  const int rib = wave / WPR;  // row within the workgroup
+  const int rpb = blockDim.x / (kWave * WPR);
+  const int T = a.s.T;
+  const int64_t N = a.s.N;
+  const int nslots = (T + TPS - 1) / TPS;
+  const int half = lane / LPT;  // tile within a slot
+  const int cil = lane % LPT;   // chunk within the tile
+  const int64_t ngroups = (a.s.rows + rpb - 1) / rpb;
+  const bool has_mask = a.mask != nullptr;
+  const bool has_sink = a.sink != nullptr;
+
+  for (int64_t grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
+    const int64_t r = grp * rpb + rib;
+    const bool active = r < a.s.rows;
+    const int64_t q = active ? r % a.s.Sq : 0;
+    const int64_t h = active ? (r / a.s.Sq) % a.s.H : 0;
+    const int64_t b = active ? r / (a.s.Sq * a.s.H) : 0;
+    const char *srow = static_cast<const char *>(a.scores) + r * a.s.ld * ESZ;
+    char *prow = static_cast<char *>(a.probs) + r * a.s.ld * ESZ;
+    const float *mrow = has_mask ? a.mask + b * a.msb + h * a.msh + q * a.msq : nullptr;
+
+    float e[CPL][KPL];
+
+    if (active) {
+#pragma unroll
+      for (int s = 0; s < CPL; ++s) {
+        const int gs = s * WPR + wir;  // slot index within the row
+        if (gs < nslots) {
+          const int t = gs * TPS + half;
+          const int64_t j0 = (int64_t)t * kTile + (int64_t)cil * KPL;
+          const bool inb = j0 < N;  // VEC: a chunk is wholly inside or wholly past the row
+          // keys past the row read as -inf (the max's identity; their e is +0)
+          constexpr uint32_t kFill = (DT == 1) ? 0xff80ff80u : 0xff800000u;
+          Chunk raw;
+          if constexpr (VEC) {
+            raw = inb ? load_chunk(srow + j0 * ESZ) : Chunk{{kFill, kFill, kFill, kFill}};
+          } else {
+            raw = load_chunk_elems<DT>(srow, j0, N, kFill);
+          }
+          float x[KPL];
+          unpack<DT>(raw, x);
+          if (has_mask) {
+            if constexpr (VEC) {
+              if (inb) {
+#pragma unroll
+                for (int k4 = 0; k4 < KPL; k4 += 4) {
+                  const float4 mv = *reinterpret_cast<const float4 *>(mrow + j0 + k4);
+                  x[k4 + 0] = x[k4 + 0] + mv.x;
+                  x[k4 + 1] = x[k4 + 1] + mv.y;
+                  x[k4 + 2] = x[k4 + 2] + mv.z;
+                  x[k4 + 3] = x[k4 + 3] + mv.w;
+                }
+              }
+            } else {
+#pragma unroll
+              for (int k = 0; k < KPL; ++k)
+                if (j0 + k < N) x[k] = x[k] + mrow[j0 + k];
+            }
+          }
+          const float m = tile_max<DT>(lane_tree_max<KPL>(x));
+          // a tile whose max is -inf has only -inf keys: subtracting 0 keeps
+          // them at -inf and every e at +0, without a -inf - -inf
+          const float msafe = (m == kNegInf) ? 0.0f : m;
+#pragma unroll
+          for (int k = 0; k < KPL; ++k) e[s][k] = exp_(x[k] - msafe);
+          const float l = tile_sum<DT>(lane_tree_sum<KPL>(e[s]));
+          if (cil == 0 && t < T) {
+            lds_m[rib][t] = m;
+            lds_l[rib][t] = l;
+          }
+        }
+      }
+    }
+    row_sync<WPR>();
+
+    if (active) {
+      // ---- merge of the tile states, lane t holds tile t ----
+      const float mt = (lane < T) ? lds_m[rib][lane] : kNegInf;
+      const float lt = (lane < T) ? lds_l[rib][lane] : 0.0f;
+      float Mi = mt;  // running max after tile `lane` (inclusive prefix max)
+#pragma unroll
+      for (int d = 1; d < kWave; d <<= 1) Mi = __builtin_fmaxf(Mi, __shfl_up(Mi, d));
+      float Me = __shfl_up(Mi, 1);  // running max before tile `lane`
+      if (lane == 0) Me = kNegInf;
+      float alpha = 0.0f, qv = 0.0f;
+      if (Mi != kNegInf) {
+        alpha = (Me == kNegInf) ? 0.0f : exp_(Me - Mi);
+        const float beta = (mt == kNegInf) ? 0.0f : exp_(mt - Mi);
+        qv = lt * beta;
+      }
+      float L = 0.0f;
+      for (int t = 0; t < T; ++t) {
+        const float La = L * readlane(alpha, t);
+        L = La + readlane(qv, t);
+      }
+      float M = readlane(Mi, T - 1);
+      float sigma = 0.0f;
+      if (has_sink) {
+        sigma = a.sink[h];  // one logit per head
+        const float Mn = __builtin_fmaxf(M, sigma);
+        if (Mn == kNegInf) {
+          M = kNegInf;
+          L = 0.0f;
+        } else {
+          const float fa = (M == kNegInf) ? 0.0f : exp_(M - Mn);
+          const float fb = (sigma == kNegInf) ? 0.0f : exp_(sigma - Mn);
+          const float La = L * fa;
+          const float lb = 1.0f * fb;
+          L = La + lb;
+          M = Mn;
+        }
+      }
+      const float invL = (L == 0.0f) ? 0.0f : 1.0f / L;
+      const float ct = (mt == kNegInf) ? 0.0f : exp_(mt - M) * invL;  // tile `lane`'s scale
+
+      // ---- rescale, convert once, write ----
+#pragma unroll
+      for (int s = 0; s < CPL; ++s) {
+        const int gs = s * WPR + wir;
+        if (gs < nslots) {
+          const int t = gs * TPS + half;
+          const int64_t j0 = (int64_t)t * kTile + (int64_t)cil * KPL;
+          float cs = readlane(ct, gs * TPS);
+          if constexpr (TPS == 2) {
+            const float c1 = readlane(ct, gs * TPS + 1);
+            cs = half ? c1 : cs;
+          }
+          float p[KPL];
+#pragma unroll
+          for (int k = 0; k < KPL; ++k) p[k] = e[s][k] * cs;
+          const Chunk out = pack<DT>(p);
+          if constexpr (VEC) {
+            if (j0 < N) store_chunk(prow + j0 * ESZ, out);
+          } else {
+            store_chunk_elems<DT>(prow, j0, N, out);
+          }
+        }
+      }
+      if (has_sink && wir == 0 && lane == 0)
+        a.p_sink[r] = (sigma == kNegInf) ? 0.0f : exp_(sigma - M) * invL;
+    }
+    if constexpr (WPR > 1) __syncthreads();  // LDS is reused by the next row group
+    else wave_sync();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Backward
+// ---------------------------------------------------------------------------
+
+template <int DT, int WPR, int CPL, bool VEC>
+__global__ __launch_bounds__(kWave * kBlockWaves) void bwd_kernel(const BwdArgs a) {
+  using C = Cfg<DT>;
+  constexpr int KPL = C::KPL, LPT = C::LPT, TPS = C::TPS, ESZ = C::ESZ;
+  __shared__ float lds_d[kBlockWaves][kMaxTiles];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int wir = wave % WPR;
+  const int rib = wave / WPR;
+  const int rpb = blockDim.x / (kWave * WPR);
+  const int T = a.s.T;
+  const int64_t N = a.s.N;
+  const int nslots = (T + TPS - 1) / TPS;
+  const int half = lane / LPT;
+  const int cil = lane % LPT;
+  const int64_t ngroups = (a.s.rows + rpb - 1) / rpb;
+  const bool has_sink = a.p_sink != nullptr;
+
+  for (int64_t grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
+    const int64_t r = grp * rpb + rib;
+    const bool active = r < a.s.rows;
+    const char *prow = static_cast<const char *>(a.probs) + r * a.s.ld * ESZ;
+    const char *grow = static_cast<const char *>(a.dprobs) + r * a.s.ld * ESZ;
+    char *drow = static_cast<char *>(a.dscores) + r * a.s.ld * ESZ;
+
+    Chunk rp[CPL], rg[CPL];
+
+    if (active) {
+#pragma unroll
+      for (int s = 0; s < CPL; ++s) {
+        const int gs = s * WPR + wir;
+        if (gs < nslots) {
+          const int t = gs * TPS + half;
+          const int64_t j0 = (int64_t)t * kTile + (int64_t)cil * KPL;
+          // keys past the row read as +0 (their product adds +0 to the tree)
+          if constexpr (VEC) {
+            const bool inb = j0 < N;
+            rp[s] = inb ? load_chunk(prow + j0 * ESZ) : Chunk{{0u, 0u, 0u, 0u}};
+            rg[s] = inb ? load_chunk(grow + j0 * ESZ) : Chunk{{0u, 0u, 0u, 0u}};
+          } else {
+            rp[s] = load_chunk_elems<DT>(prow, j0, N, 0u);
+            rg[s] = load_chunk_elems<DT>(grow, j0, N, 0u);
+          }
+          float p[KPL], g[KPL], pg[KPL];
+          unpack<DT>(rp[s], p);
+          unpack<DT>(rg[s], g);
+#pragma unroll
+          for (int k = 0; k < KPL; ++k) pg[k] = p[k] * g[k];
+          const float d = tile_sum<DT>(lane_tree_sum<KPL>(pg));
+          if (cil == 0 && t < T) lds_d[rib][t] = d;
+        }
+      }
+    }
+    row_sync<WPR>();
+
+    if (active) {
+      const float dt = (lane < T) ? lds_d[rib][lane] : 0.0f;
+      float delta = readlane(dt, 0);  // the fold starts from the first tile's sum
+      for (int t = 1; t < T; ++t) delta = delta + readlane(dt, t);
+
+#pragma unroll
+      for (int s = 0; s < CPL; ++s) {
+        const int gs = s * WPR + wir;
+        if (gs < nslots) {
+          const int t = gs * TPS + half;
+          const int64_t j0 = (int64_t)t * kTile + (int64_t)cil * KPL;
+          float p[KPL], g[KPL], ds[KPL];
+          unpack<DT>(rp[s], p);
+          unpack<DT>(rg[s], g);
+#pragma unroll
+          for (int k = 0; k < KPL; ++k) {
+            const float gd = g[k] - delta;
+            ds[k] = p[k] * gd;
+          }
+          const Chunk out = pack<DT>(ds);
+          if constexpr (VEC) {
+            if (j0 < N) store_chunk(drow + j0 * ESZ, out);
+          } else {
+            store_chunk_elems<DT>(drow, j0, N, out);
+          }
+        }
+      }
+      if (has_sink && wir == 0 && lane == 0) a.v[r] = -(a.p_sink[r] * delta);
+    }
+    if constexpr (WPR > 1) __syncthreads();
+    else wave_sync();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// d_sink: per head, 256-row chunks in (batch, query) order, balanced tree per
+// chunk, chunk sums folded left to right.  One workgroup per head, one
+// wavefront per chunk; lane l holds the chunk's rows 4l..4l+3.
+// ---------------------------------------------------------------------------
+
+constexpr int kDsinkWaves = 16;
+
+__global__ __launch_bounds__(kWave * kDsinkWaves) void dsink_kernel(const DsinkArgs a) {
+  __shared__ float part[kDsinkWaves];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int64_t h = blockIdx.x;
+  const int64_t n = a.B * a.Sq;
+  const int64_t chunks = (n + kTile - 1) / kTile;
+  float D = 0.0f;
+  for (int64_t k0 = 0; k0 < chunks; k0 += kDsinkWaves) {
+    const int64_t k = k0 + wave;
+    float cs = 0.0f;
+    if (k < chunks) {
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t idx = k * kTile + lane * 4 + i;  // position in the head's row list
+        if (idx < n) {
+          const int64_t bb = idx / a.Sq, qq = idx - bb * a.Sq;
+          v[i] = a.v[(bb * a.H + h) * a.Sq + qq];
+        } else {
+          v[i] = 0.0f;
+        }
+      }
+      cs = group64_sum((v[0] + v[1]) + (v[2] + v[3]));
+    }
+    if (lane == 0) part[wave] = cs;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int64_t m = (chunks - k0 < kDsinkWaves) ? chunks - k0 : kDsinkWaves;
+      for (int64_t i = 0; i < m; ++i) D = (k0 + i == 0) ? part[i] : D + part[i];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) a.d_sink[h] = D;
+}
+
+// ---------------------------------------------------------------------------
+// Launch tables
+// ---------------------------------------------------------------------------
+
+// chunks-per-lane sizes compiled for each dtype (register budget: the row's
+// share is kept in registers between the reduction and the write)
+constexpr int kCplF32[] = {1, 2, 3, 5, 9, 17};
+constexpr int kCplBf16[] = {1, 2, 3, 5, 9};
+
+template <int DT, int WPR, int CPL>
+hipError_t launch_fwd_t(const FwdArgs &a, const Geometry &g, hipStream_t st) {
+  const dim3 grid((unsigned)g.blocks), block(kWave * WPR * g.rpb);
+  if (a.vec_io)
+    hipLaunchKernelGGL((fwd_kernel<DT, WPR, CPL, true>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((fwd_kernel<DT, WPR, CPL, false>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+template <int DT, int WPR, int CPL>
+hipError_t launch_bwd_t(const BwdArgs &a, const Geometry &g, hipStream_t st) {
+  const dim3 grid((unsigned)g.blocks), block(kWave * WPR * g.rpb);
+  if (a.vec_io)
+    hipLaunchKernelGGL((bwd_kernel<DT, WPR, CPL, true>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((bwd_kernel<DT, WPR, CPL, false>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+#define JAS_CPL_CASES(FN, DT, WPR, ARGS)                     \
+  switch (g.cpl) {                                           \
+    case 1: return FN<DT, WPR, 1> ARGS;                      \
+    case 2: return FN<DT, WPR, 2> ARGS;                      \
+    case 3: return FN<DT, WPR, 3> ARGS;                      \
+    case 5: return FN<DT, WPR, 5> ARGS;                      \
+    case 9: return FN<DT, WPR, 9> ARGS;                      \
+    default: break;                                          \
+  }
+
+template <int DT, int WPR>
+hipError_t fwd_wpr(const FwdArgs &a, const Geometry &g, hipStream_t st) {
+  JAS_CPL_CASES(launch_fwd_t, DT, WPR, (a, g, st))
+  if constexpr (DT == 0) {
+    if (g.cpl == 17) return launch_fwd_t<DT, WPR, 17>(a, g, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int DT, int WPR>
+hipError_t bwd_wpr(const BwdArgs &a, const Geometry &g, hipStream_t st) {
+  JAS_CPL_CASES(launch_bwd_t, DT, WPR, (a, g, st))
+  if constexpr (DT == 0) {
+    if (g.cpl == 17) return launch_bwd_t<DT, WPR, 17>(a, g, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int DT>
+hipError_t fwd_dt(const FwdArgs &a, const Geometry &g, hipStream_t st) {
+  switch (g.wpr) {
+    case 1: return fwd_wpr<DT, 1>(a, g, st);
+    case 2: return fwd_wpr<DT, 2>(a, g, st);
+    case 4: return fwd_wpr<DT, 4>(a, g, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int DT>
+hipError_t bwd_dt(const BwdArgs &a, const Geometry &g, hipStream_t st) {
+  switch (g.wpr) {
+    case 1: return bwd_wpr<DT, 1>(a, g, st);
+    case 2: return bwd_wpr<DT, 2>(a, g, st);
+    case 4: return bwd_wpr<DT, 4>(a, g, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+const int *compiled_cpls(int dtype, int *count) {
+  if (dtype == 1) {
+    *count = (int)(sizeof(kCplBf16) / sizeof(int));
+    return kCplBf16;
+  }
+  *count = (int)(sizeof(kCplF32) / sizeof(int));
+  return kCplF32;
+}
+
+bool cpl_compiled(int dtype, int wpr, int cpl) {
+  if (wpr != 1 && wpr != 2 && wpr != 4) return false;
+  int n = 0;
+  const int *c = compiled_cpls(dtype, &n);
+  for (int i = 0; i < n; ++i)
+    if (c[i] == cpl) return true;
+  return false;
+}
+
+int default_cpl_max(int dtype) { return dtype == 1 ? 9 : 17; }
+
+hipError_t launch_fwd(int dtype, const FwdArgs &a, const Geometry &g, hipStream_t st) {
+  return dtype == 1 ? fwd_dt<1>(a, g, st) : fwd_dt<0>(a, g, st);
+}
+
+hipError_t launch_bwd(int dtype, const BwdArgs &a, const Geometry &g, hipStream_t st) {
+  return dtype == 1 ? bwd_dt<1>(a, g, st) : bwd_dt<0>(a, g, st);
+}
+
+hipError_t launch_dsink(const DsinkArgs &a, hipStream_t st) {
+  hipLaunchKernelGGL(dsink_kernel, dim3((unsigned)a.H), dim3(kWave * kDsinkWaves), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace jas

@@ -1,0 +1,190 @@
+/*
+ * jas.h -- fixed-order, batch-invariant row softmax for AMD Instinct MI355X
+ * (gfx950): forward, backward, optional per-head sink.
+ *
+ * What the library computes (the pages it follows):
+ *   - RL-Kernel PR #453, "[WS1][kernels] Add fixed-order joint-attention
+ *     softmax for Qwen-Image", Summary: the softmax that sits between the
+ *     QK GEMM and the AV GEMM of joint attention, taken along the key
+ *     dimension of each row of scores; each row is split into fixed
+ *     256-key tiles processed left to right, each tile reduces its max and
+ *     its sum of exponentials with one fixed tree, the per-tile states are
+ *     merged in tile order, all intermediates are FP32 and the only rounding
+ *     to the tensor dtype happens at the write.  Backward: delta is the same
+ *     fixed-order sum of P*dP, then dScores = P*(dP - delta).
+ *   - ROCm TransformerEngine PR #678, "Add softmax sink (learnable
+ *     off-by-one) support for the ROCm/CK fused attention backend", title and
+ *     Description: an optional learnable logit per head adds one term to the
+ *     softmax denominator; backward produces its gradient d_sink per head.
+ *     The sink buffer holds one value per head and is indexed by head only.
+ *   - RL-Kernel PR #240, "Batch-invariant attention (standard softmax --
+ *     cuda version)", Fixed Reduction Contract and Path Status: the reduction
+ *     tree's shape depends on nothing but the tile (not on batch size, row
+ *     position, launch geometry or grid), and fully masked rows are handled.
+ *
+ * Exact arithmetic of one row of N keys, T = ceil(N/256) tiles (every
+ * operation binary32, round to nearest-even, no fused multiply-add):
+ *   x_j   = float(s_j) (+ mask_j, one rounding, when JAS_FLAG_MASK)
+ *   m_t   = max over tile t (positions past N count as -inf)
+ *   e_j   = exp_(x_j - m_t), exp_(y) = 2^fl(y*log2e), 0 when that exponent
+ *           is below -126 (or y is -inf); 0 in a tile whose max is -inf
+ *   l_t   = balanced pairwise tree sum of the tile's 256 e values in key
+ *           order (positions past N count as 0)
+ *   (M,L) = (-inf,0) merged with (m_t,l_t) for t = 0..T-1 in order, then
+ *           with (sigma_h, 1) when JAS_FLAG_SINK; merging (m,l) into (M,L):
+ *           Mn = max(M,m), L = fl(L*exp_(M-Mn)) + fl(l*exp_(m-Mn)), a -inf
+ *           side contributes 0, and an all -inf state stays (-inf, 0)
+ *   invL  = 1/L (0 when L is 0)
+ *   P_j   = round_to_dtype(e_j * fl(exp_(m_t - M) * invL))
+ *   p_sink= fl(exp_(sigma_h - M) * invL)      (0 when sigma_h is -inf)
+ * Backward on the stored P:
+ *   d_t   = balanced tree sum of fl(P_j*dP_j) over tile t; delta = d_0, then
+ *           delta = fl(delta + d_t) for t = 1..T-1
+ *   dS_j  = round_to_dtype(P_j * fl(dP_j - delta))
+ *   d_sink[h] = the rows of head h in (batch, query) order, in chunks of 256
+ *           rows (the last padded with +0), each chunk summed with the same
+ *           balanced tree over -fl(p_sink_r*delta_r), chunk sums added left
+ *           to right from the first; d_sink is overwritten, never accumulated.
+ * The exponential is the hardware base-2 exponential; everything else is
+ * exact IEEE arithmetic, so results do not depend on batch size, a row's
+ * position, launch geometry or grid size.
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are device pointers owned by the caller.  The library
+ *     never allocates, frees or synchronizes; all work is enqueued on
+ *     `stream` (a hipStream_t; NULL is the null stream) and the call returns
+ *     without waiting for it.
+ *   - Validation is done entirely on the host before any HIP call; on any
+ *     error nothing is enqueued and the status says why.  JAS_ERR_HIP means
+ *     the HIP runtime refused a launch (hipGetLastError is read after each
+ *     launch); for jas_bwd with a sink the row kernel may then already be
+ *     enqueued while the d_sink reduction is not.
+ *   - Rows: rows = batch*heads*q_rows, row r = (b*heads + h)*q_rows + q,
+ *     row r starts at element r*ld of scores / probs / dprobs / dscores.
+ *   - An empty call (rows == 0) reads nothing; its row tensors (scores,
+ *     probs, dprobs, dscores, mask, sink, p_sink, workspace) may be NULL.
+ *     jas_bwd with JAS_FLAG_SINK still writes d_sink[h] = +0 for every head.
+ *   - Element pointers must be aligned to their element size; any further
+ *     alignment only selects the faster 16-byte load path (same results).
+ *   - The library is stateless: concurrent calls on different streams are
+ *     fine.
+ */
+#ifndef JAS_H_
+#define JAS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Largest supported row length (keys per row). */
+#define JAS_MAX_KEYS 16384
+
+/* Element type of scores, probs, dprobs and dscores.  mask, sink, p_sink,
+   d_sink and the workspace are always binary32. */
+typedef enum { JAS_DTYPE_F32 = 0, JAS_DTYPE_BF16 = 1 } jas_dtype_t;
+
+/* Flags: the only predicates for "has a mask" and "has a sink". */
+enum { JAS_FLAG_MASK = 1u << 0, JAS_FLAG_SINK = 1u << 1 };
+
+typedef enum {
+  JAS_OK = 0,
+  JAS_ERR_NULL_POINTER = 1, /* desc, a tensor, or the operand of a set flag is NULL */
+  JAS_ERR_BAD_SHAPE = 2,    /* negative dim, keys < 1, ld < keys, negative mask stride, size overflow */
+  JAS_ERR_BAD_DTYPE = 3,    /* dtype is not a jas_dtype_t */
+  JAS_ERR_BAD_FLAGS = 4,    /* unknown flag bit, or a pointer given for a flag that is not set */
+  JAS_ERR_ALIASING = 5,     /* an output overlaps another buffer (beyond the allowed in-place pairs) */
+  JAS_ERR_WORKSPACE = 6,    /* workspace NULL or smaller than jas_bwd_workspace_bytes */
+  JAS_ERR_UNSUPPORTED = 7,  /* keys > JAS_MAX_KEYS, or a launch override that cannot hold the row */
+  JAS_ERR_HIP = 8,          /* the HIP runtime refused a launch */
+  JAS_ERR_ALIGNMENT = 9     /* a pointer is not aligned to its element size */
+} jas_status_t;
+
+/* Problem description, shared by forward and backward. */
+typedef struct {
+  int64_t batch, heads, q_rows, keys; /* >= 0, keys >= 1; a zero batch/heads/q_rows is an empty call */
+  int64_t ld;                         /* elements between consecutive rows, ld >= keys */
+  int32_t dtype;                      /* jas_dtype_t */
+  uint32_t flags;                     /* JAS_FLAG_* */
+  int64_t mask_stride_b;              /* mask element (b,h,q,k) is at     */
+  int64_t mask_stride_h;              /*   mask[b*msb + h*msh + q*msq + k] */
+  int64_t mask_stride_q;              /* strides >= 0; 0 broadcasts        */
+} jas_desc_t;
+
+/* Launch geometry override (for invariance tests and tuning).  Every valid
+ * geometry gives bit-identical results.  Zero fields take the library
+ * default.  waves_per_row in {1,2,4}: wavefronts sharing one row;
+ * chunks_per_lane: 16-byte chunks of the row each lane keeps in registers
+ * (one of the compiled sizes; waves_per_row*chunks_per_lane chunks of 64
+ * lanes must cover the row); rows_per_block: rows per workgroup, with
+ * waves_per_row*rows_per_block <= 4; max_blocks: grid size cap (the
+ * workgroups then loop over the rows). */
+typedef struct {
+  int32_t waves_per_row;
+  int32_t chunks_per_lane;
+  int32_t rows_per_block;
+  int32_t max_blocks;
+} jas_launch_t;
+
+/* Forward.
+ *   scores [rows, ld] (dtype)  read.   probs [rows, ld] (dtype) written,
+ *   keys columns per row; probs == scores (in place) is allowed, any other
+ *   overlap of probs with an input is JAS_ERR_ALIASING.
+ *   mask   binary32, required iff JAS_FLAG_MASK (see jas_desc_t strides).
+ *   sink   binary32 [heads], required iff JAS_FLAG_SINK.
+ *   p_sink binary32 [rows] written, required iff JAS_FLAG_SINK; the sink's
+ *          own probability, which jas_bwd reads.
+ * (Definition: RL-Kernel PR #453, Summary, fixed-order online softmax;
+ *  sink: TransformerEngine PR #678, Description.) */
+jas_status_t jas_fwd(const jas_desc_t *desc, const void *scores, const float *mask,
+                     const float *sink, void *probs, float *p_sink, void *stream);
+
+/* jas_fwd with an explicit launch geometry (NULL = default). */
+jas_status_t jas_fwd_ex(const jas_desc_t *desc, const void *scores, const float *mask,
+                        const float *sink, void *probs, float *p_sink,
+                        const jas_launch_t *launch, void *stream);
+
+/* Bytes of device workspace jas_bwd needs: 4*rows rounded up to 256 when
+ * JAS_FLAG_SINK is set, else 0.  Depends on the shape and flags only (never
+ * on pointers).  Returns 0 for a NULL or invalid desc. */
+size_t jas_bwd_workspace_bytes(const jas_desc_t *desc);
+
+/* Backward on the stored probabilities.
+ *   probs, dprobs [rows, ld] (dtype) read.  dscores [rows, ld] written;
+ *   dscores may equal probs or dprobs (in place), any other overlap is
+ *   JAS_ERR_ALIASING.  JAS_FLAG_MASK and the mask strides are ignored:
+ *   masked keys already have P = 0.
+ *   p_sink  binary32 [rows] read, required iff JAS_FLAG_SINK.
+ *   d_sink  binary32 [heads] written (overwritten, not accumulated),
+ *           required iff JAS_FLAG_SINK.
+ *   workspace, workspace_bytes: device scratch of at least
+ *           jas_bwd_workspace_bytes(desc) bytes (binary32 aligned), used
+ *           only with a sink; its contents on entry do not matter.
+ * (Definition: RL-Kernel PR #453, Summary, fixed-order backward; d_sink:
+ *  TransformerEngine PR #678, reduced here in a fixed order without
+ *  atomics.) */
+jas_status_t jas_bwd(const jas_desc_t *desc, const void *probs, const void *dprobs,
+                     const float *p_sink, void *dscores, float *d_sink, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
+/* jas_bwd with an explicit launch geometry (NULL = default). */
+jas_status_t jas_bwd_ex(const jas_desc_t *desc, const void *probs, const void *dprobs,
+                        const float *p_sink, void *dscores, float *d_sink, void *workspace,
+                        size_t workspace_bytes, const jas_launch_t *launch, void *stream);
+
+/* Static text for a status code. */
+const char *jas_status_str(jas_status_t status);
+
+/* Static fingerprint of the arithmetic contract: tile size, tree, merge
+ * order, accumulator precision, exponential, rounding, target
+ * (RL-Kernel PR #453, Summary: the trace records reduction order,
+ * accumulator precision and a kernel fingerprint). */
+const char *jas_contract(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JAS_H_ */

@@ -1,0 +1,136 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function declared in include/jas.h, and rejects bad arguments with the
+documented status before any HIP call (nothing here reaches a launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import deterministic_attention_softmax_amd as jas
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# fake, never dereferenced device addresses (validation fails before any use)
+A = 0x10000000
+B_ = 0x20000000
+C = 0x30000000
+D = 0x40000000
+E = 0x50000000
+W = 0x60000000
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "jas.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(jas_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert {"jas_fwd", "jas_bwd", "jas_fwd_ex", "jas_bwd_ex", "jas_bwd_workspace_bytes",
+            "jas_status_str", "jas_contract"} <= set(names)
+    L = ctypes.CDLL(jas.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_contract_and_status_strings():
+    c = jas.jas_contract()
+    assert "tile=256" in c and "gfx950" in c and "atomics=none" in c
+    for code in range(10):
+        assert jas.jas_status_str(code) and jas.jas_status_str(code) != "unknown status"
+    assert jas.jas_status_str(99) == "unknown status"
+
+
+def desc(B=1, H=2, S=3, N=300, dtype=jas.JAS_DTYPE_BF16, flags=0, ld=None, ms=(0, 0, 0)):
+    return jas.make_desc((B, H, S, N), dtype, flags, ld, ms)
+
+
+def fwd(d, scores=A, mask=None, sink=None, probs=B_, p_sink=None, launch=None):
+    return jas.jas_fwd_ex(d, scores, mask, sink, probs, p_sink, launch, None)
+
+
+def bwd(d, probs=A, dprobs=B_, p_sink=None, dscores=C, d_sink=None, ws=None, ws_bytes=0):
+    return jas.jas_bwd(d, probs, dprobs, p_sink, dscores, d_sink, ws, ws_bytes, None)
+
+
+def test_null_desc_and_pointers():
+    L = jas.lib()
+    assert L.jas_fwd(None, A, None, None, B_, None, None) == 1
+    assert L.jas_bwd(None, A, B_, None, C, None, None, 0, None) == 1
+    assert fwd(desc(), scores=None) == 1
+    assert fwd(desc(), probs=None) == 1
+    assert bwd(desc(), probs=None) == 1
+    assert bwd(desc(), dprobs=None) == 1
+    assert bwd(desc(), dscores=None) == 1
+
+
+def test_flag_pointer_predicates():
+    # flag set, pointer missing -> NULL_POINTER; pointer given, flag unset -> BAD_FLAGS
+    assert fwd(desc(flags=jas.JAS_FLAG_MASK)) == 1
+    assert fwd(desc(flags=jas.JAS_FLAG_SINK), sink=C) == 1            # p_sink missing
+    assert fwd(desc(flags=jas.JAS_FLAG_SINK), p_sink=D) == 1          # sink missing
+    assert fwd(desc(), mask=C) == 4
+    assert fwd(desc(), sink=C) == 4
+    assert fwd(desc(), p_sink=D) == 4
+    assert fwd(desc(flags=1 << 5)) == 4
+    assert bwd(desc(flags=jas.JAS_FLAG_SINK), p_sink=D) == 1          # d_sink missing
+    assert bwd(desc(), p_sink=D) == 4
+    assert bwd(desc(), d_sink=E) == 4
+
+
+def test_shapes_and_dtype():
+    assert fwd(desc(N=0)) == 2
+    assert fwd(desc(B=-1)) == 2
+    assert fwd(desc(ld=299)) == 2
+    assert fwd(desc(ms=(-1, 0, 0), flags=jas.JAS_FLAG_MASK), mask=C) == 2
+    assert fwd(desc(N=jas.JAS_MAX_KEYS + 1)) == 7
+    assert fwd(desc(dtype=7)) == 3
+    # rows * ld overflowing int64
+    assert fwd(desc(B=1 << 40, H=1 << 20, S=1 << 10, N=8)) == 2
+
+
+def test_alignment():
+    assert fwd(desc(), scores=A + 1) == 9
+    assert fwd(desc(dtype=jas.JAS_DTYPE_F32), probs=B_ + 2) == 9
+    assert fwd(desc(flags=jas.JAS_FLAG_MASK), mask=C + 2) == 9
+    assert bwd(desc(), dscores=C + 1) == 9
+
+
+def test_aliasing():
+    # Every call here must fail validation: a call that passed would launch a
+    # kernel on these fake addresses.
+    d = desc(B=1, H=1, S=4, N=300)               # 4 rows x 600 bytes
+    assert fwd(d, scores=A, probs=A + 600) == 5  # partial overlap
+    assert fwd(d, scores=A, probs=A - 600) == 5
+    dm = desc(B=1, H=1, S=4, N=300, flags=jas.JAS_FLAG_MASK, ms=(0, 0, 300))
+    assert fwd(dm, mask=B_ + 4) == 5             # mask inside probs
+    ds = desc(B=1, H=1, S=4, N=300, flags=jas.JAS_FLAG_SINK)
+    assert fwd(ds, sink=C, p_sink=B_ + 8) == 5   # p_sink inside probs
+    assert bwd(d, probs=A, dprobs=B_, dscores=A + 2) == 5
+    dsb = desc(B=1, H=1, S=4, N=300, flags=jas.JAS_FLAG_SINK)
+    ws = jas.jas_bwd_workspace_bytes(dsb)
+    assert bwd(dsb, p_sink=D, d_sink=E, ws=D, ws_bytes=ws) == 5
+
+
+def test_workspace():
+    d = desc(B=2, H=3, S=5, flags=jas.JAS_FLAG_SINK)
+    need = jas.jas_bwd_workspace_bytes(d)
+    assert need == 256 and need >= 2 * 3 * 5 * 4
+    assert jas.jas_bwd_workspace_bytes(desc(B=2, H=3, S=5)) == 0
+    d2 = desc(B=1, H=1, S=1000, flags=jas.JAS_FLAG_SINK)
+    assert jas.jas_bwd_workspace_bytes(d2) == 4096
+    assert bwd(d, p_sink=D, d_sink=E, ws=None, ws_bytes=need) == 6
+    assert bwd(d, p_sink=D, d_sink=E, ws=W, ws_bytes=need - 4) == 6
+    # the size depends on shape and flags only
+    L = jas.lib()
+    assert L.jas_bwd_workspace_bytes(None) == 0
+
+
+def test_launch_override_validation():
+    d = desc(B=1, H=1, S=4, N=4352)  # 17 tiles -> 9 bf16 slots
+    bad = [(3, 0, 0, 0), (1, 4, 0, 0), (1, 5, 0, 0), (2, 9, 3, 0), (-1, 0, 0, 0)]
+    for L in bad:
+        lt = jas._launch(L)
+        assert fwd(d, launch=lt) == 7, L
