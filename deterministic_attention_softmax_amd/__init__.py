@@ -170,6 +170,21 @@ def _shape4(t):
     return t.shape, t.stride(2)
 
 
+def _empty_rows_like(t, ld):
+    """A tensor shaped like ``t`` whose rows have the same stride ``ld``."""
+    import torch
+    B, H, S, N = t.shape
+    if ld == N:
+        return torch.empty((B, H, S, N), dtype=t.dtype, device=t.device)
+    flat = torch.empty(max(0, B * H * S * ld), dtype=t.dtype, device=t.device)
+    return flat.view(B, H, S, ld)[..., :N]
+
+
+def _check_out(out, like):
+    if out.shape != like.shape or out.stride() != like.stride() or out.dtype != like.dtype:
+        raise ValueError("the output must have the input's shape, dtype and row stride")
+
+
 def fwd(scores, mask=None, mask_strides=None, sink=None, out=None, p_sink=None, launch=None):
     """Forward on device tensors.  ``scores`` [B,H,Sq,N] bf16/fp32 (rows may
     have a stride ld >= N); ``mask`` fp32 addressed with ``mask_strides``
@@ -189,7 +204,8 @@ def fwd(scores, mask=None, mask_strides=None, sink=None, out=None, p_sink=None, 
         flags |= JAS_FLAG_SINK
     d = make_desc(shape, _dtype_code(scores), flags, ld, mask_strides or (0, 0, 0))
     if out is None:
-        out = torch.empty_like(scores)
+        out = _empty_rows_like(scores, ld)
+    _check_out(out, scores)
     if sink is not None and p_sink is None:
         p_sink = torch.empty(shape[0] * shape[1] * shape[2], dtype=torch.float32,
                              device=scores.device)
@@ -206,8 +222,10 @@ def bwd(probs, dprobs, p_sink=None, out=None, d_sink=None, workspace=None, launc
     shape, ld = _shape4(probs)
     flags = JAS_FLAG_SINK if p_sink is not None else 0
     d = make_desc(shape, _dtype_code(probs), flags, ld)
+    _check_out(dprobs, probs)
     if out is None:
-        out = torch.empty_like(probs)
+        out = _empty_rows_like(probs, ld)
+    _check_out(out, probs)
     ws_bytes = jas_bwd_workspace_bytes(d)
     if p_sink is not None:
         if d_sink is None:

@@ -51,12 +51,12 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
 
-// exp_(y) = 2^fl(y*log2e) with the hardware base-2 exponential; +0 when the
-// exponent is below -126 (no subnormal e) and for y = -inf.
-__device__ __forceinline__ float exp_(float y) {
-  const float u = y * kLog2e;
-  return (u < -126.0f) ? 0.0f : __builtin_amdgcn_exp2f(u);
-}
+// exp_(y) = 2^fl(y*log2e) with the hardware base-2 exponential, for y <= 0
+// or -inf.  The contract flushes results below 2^-126 to +0; v_exp_f32 does
+// exactly that on gfx950 (every binary32 exponent from -0 down to -inf was
+// checked: +0 below -126, a normal number from -126 up, within 1 ulp of the
+// correctly rounded 2^u), so no select is needed.
+__device__ __forceinline__ float exp_(float y) { return __builtin_amdgcn_exp2f(y * kLog2e); }
 
 // Round two binary32 to bf16 (round to nearest-even) and pack them, low
 // half first: gfx950's v_cvt_pk_bf16_f32.
@@ -112,19 +112,23 @@ __device__ __forceinline__ float group64_sum(float v) {
   return p[0] + p[1];
 }
 
+// max with -0 < +0 and NaN propagation (gfx950 v_maximum3_f32); max is
+// exact, so the tree shape cannot change its value.
+__device__ __forceinline__ float fmax2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ __forceinline__ float group32_max(float v) {
-  v = __builtin_fmaxf(v, dpp<kDppQuadXor1>(v));
-  v = __builtin_fmaxf(v, dpp<kDppQuadXor2>(v));
-  v = __builtin_fmaxf(v, dpp<kDppRowHalfMirror>(v));
-  v = __builtin_fmaxf(v, dpp<kDppRowMirror>(v));
+  v = fmax2(v, dpp<kDppQuadXor1>(v));
+  v = fmax2(v, dpp<kDppQuadXor2>(v));
+  v = fmax2(v, dpp<kDppRowHalfMirror>(v));
+  v = fmax2(v, dpp<kDppRowMirror>(v));
   const f32x2_t p = rows16_pair(v);
-  return __builtin_fmaxf(p[0], p[1]);
+  return fmax2(p[0], p[1]);
 }
 
 __device__ __forceinline__ float group64_max(float v) {
   v = group32_max(v);
   const f32x2_t p = halves32_pair(v);
-  return __builtin_fmaxf(p[0], p[1]);
+  return fmax2(p[0], p[1]);
 }
 
 __device__ __forceinline__ float readlane(float v, int lane) {
@@ -172,15 +176,14 @@ __device__ __forceinline__ void store_chunk(char *p, const Chunk &c) {
 // Element-by-element chunk load for unaligned rows and the tail of a row:
 // keys at or past n read as `fill` bits.
 template <int DT>
-__device__ __forceinline__ Chunk load_chunk_elems(const char *row, int64_t j0, int64_t n,
-                                                  uint32_t fill) {
+__device__ __forceinline__ Chunk load_chunk_elems(const char *row, int j0, int n, uint32_t fill) {
   Chunk c;
   if constexpr (DT == 1) {
     const uint16_t *e = reinterpret_cast<const uint16_t *>(row);
     const uint32_t f = fill & 0xffffu;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t j = j0 + 2 * i;
+      const int j = j0 + 2 * i;
       const uint32_t lo = (j < n) ? e[j] : f;
       const uint32_t hi = (j + 1 < n) ? e[j + 1] : f;
       c.w[i] = lo | (hi << 16);
@@ -189,7 +192,7 @@ __device__ __forceinline__ Chunk load_chunk_elems(const char *row, int64_t j0, i
     const uint32_t *e = reinterpret_cast<const uint32_t *>(row);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t j = j0 + i;
+      const int j = j0 + i;
       c.w[i] = (j < n) ? e[j] : fill;
     }
   }
@@ -197,12 +200,12 @@ __device__ __forceinline__ Chunk load_chunk_elems(const char *row, int64_t j0, i
 }
 
 template <int DT>
-__device__ __forceinline__ void store_chunk_elems(char *row, int64_t j0, int64_t n, const Chunk &c) {
+__device__ __forceinline__ void store_chunk_elems(char *row, int j0, int n, const Chunk &c) {
   if constexpr (DT == 1) {
     uint16_t *e = reinterpret_cast<uint16_t *>(row);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t j = j0 + 2 * i;
+      const int j = j0 + 2 * i;
       if (j < n) e[j] = (uint16_t)(c.w[i] & 0xffffu);
       if (j + 1 < n) e[j + 1] = (uint16_t)(c.w[i] >> 16);
     }
@@ -210,7 +213,7 @@ __device__ __forceinline__ void store_chunk_elems(char *row, int64_t j0, int64_t
     uint32_t *e = reinterpret_cast<uint32_t *>(row);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t j = j0 + i;
+      const int j = j0 + i;
       if (j < n) e[j] = c.w[i];
     }
   }
@@ -257,11 +260,10 @@ __device__ __forceinline__ float lane_tree_sum(const float (&x)[K]) {
 template <int K>
 __device__ __forceinline__ float lane_tree_max(const float (&x)[K]) {
   if constexpr (K == 4) {
-    return __builtin_fmaxf(__builtin_fmaxf(x[0], x[1]), __builtin_fmaxf(x[2], x[3]));
+    return fmax2(fmax2(fmax2(x[0], x[1]), x[2]), x[3]);
   } else {
-    return __builtin_fmaxf(
-        __builtin_fmaxf(__builtin_fmaxf(x[0], x[1]), __builtin_fmaxf(x[2], x[3])),
-        __builtin_fmaxf(__builtin_fmaxf(x[4], x[5]), __builtin_fmaxf(x[6], x[7])));
+    return fmax2(fmax2(fmax2(fmax2(x[0], x[1]), x[2]), fmax2(fmax2(x[3], x[4]), x[5])),
+                 fmax2(x[6], x[7]));
   }
 }
 
@@ -284,101 +286,164 @@ __device__ __forceinline__ void row_sync() {
 }
 
 // ---------------------------------------------------------------------------
-// Forward
+// Row kernels: common indexing
+//
+// Row r is owned by WPR waves of one workgroup; wave `wir` holds the slots
+// gs = s*WPR + wir (s < CPL), slot gs covering tiles gs*TPS .. gs*TPS+TPS-1.
+// A lane's chunk starts at key gs*TPS*256 + loff with loff = half*256 +
+// cil*KPL.  The wave index is made wave-uniform (readfirstlane) so row
+// pointers live in scalar registers and every load is base + 32-bit lane
+// offset.  VEC: rows are whole 16-byte chunks on 16-byte boundaries, so a
+// chunk is wholly inside or wholly past the row; loads of a slot that
+// reaches past the row are clamped to the row's last chunk and the lanes
+// past the row are overwritten afterwards.  !VEC: element-wise access.
 // ---------------------------------------------------------------------------
 
-template <int DT, int WPR, int CPL, bool VEC>
+template <int DT, int WPR>
+struct RowIdx {
+  using C = Cfg<DT>;
+  int lane, wir, rib, rpb, loff, half, cil;
+  __device__ __forceinline__ RowIdx() {
+    lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    wir = wave % WPR;
+    rib = wave / WPR;
+    rpb = blockDim.x / (kWave * WPR);
+    half = lane / C::LPT;
+    cil = lane % C::LPT;
+    loff = half * kTile + cil * C::KPL;
+  }
+};
+
+template <int ESZ>
+__device__ __forceinline__ Chunk load_at(const char *base, int j) {
+  return load_chunk(base + (uint32_t)(j * ESZ));
+}
+
+template <int ESZ>
+__device__ __forceinline__ void store_at(char *base, int j, const Chunk &c) {
+  store_chunk(base + (uint32_t)(j * ESZ), c);
+}
+
+// ---------------------------------------------------------------------------
+// Forward
+//
+// Phase 1 issues every score load of the row before any of it is used, so
+// the row's bytes are in flight together; phase 2 reduces each tile (the
+// mask row, shared by the rows of a batch and L2-resident, is read one slot
+// ahead); the tile states meet in LDS; the merge runs in every wave of the
+// row; phase 3 rescales, converts once and stores.
+// ---------------------------------------------------------------------------
+
+template <int DT, int WPR, int CPL, bool VEC, bool MASK>
 __global__ __launch_bounds__(kWave * kBlockWaves) void fwd_kernel(const FwdArgs a) {
   using C = Cfg<DT>;
-  constexpr int KPL = C::KPL, LPT = C::LPT, TPS = C::TPS, ESZ = C::ESZ;
+  constexpr int KPL = C::KPL, TPS = C::TPS, ESZ = C::ESZ;
+  // keys past the row read as -inf (the max's identity; their e is +0)
+  constexpr uint32_t kFill = (DT == 1) ? 0xff80ff80u : 0xff800000u;
   __shared__ float lds_m[kBlockWaves][kMaxTiles];
   __shared__ float lds_l[kBlockWaves][kMaxTiles];
 
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int wir = wave % WPR;  // wave within the row
-  const int rib = wave / WPR;  // row within the workgroup
-  const int rpb = blockDim.x / (kWave * WPR);
+  const RowIdx<DT, WPR> ix;
+  const int lane = ix.lane;
   const int T = a.s.T;
-  const int64_t N = a.s.N;
+  const int N = (int)a.s.N;
   const int nslots = (T + TPS - 1) / TPS;
-  const int half = lane / LPT;  // tile within a slot
-  const int cil = lane % LPT;   // chunk within the tile
-  const int64_t ngroups = (a.s.rows + rpb - 1) / rpb;
-  const bool has_mask = a.mask != nullptr;
+  const int64_t ngroups = (a.s.rows + ix.rpb - 1) / ix.rpb;
   const bool has_sink = a.sink != nullptr;
 
   for (int64_t grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
-    const int64_t r = grp * rpb + rib;
+    const int64_t r = grp * ix.rpb + ix.rib;
     const bool active = r < a.s.rows;
-    const int64_t q = active ? r % a.s.Sq : 0;
-    const int64_t h = active ? (r / a.s.Sq) % a.s.H : 0;
-    const int64_t b = active ? r / (a.s.Sq * a.s.H) : 0;
-    const char *srow = static_cast<const char *>(a.scores) + r * a.s.ld * ESZ;
+    // a workgroup's spare rows read the last row (valid memory) and write nothing
+    const int64_t rr = active ? r : a.s.rows - 1;
+    const char *srow = static_cast<const char *>(a.scores) + rr * a.s.ld * ESZ;
     char *prow = static_cast<char *>(a.probs) + r * a.s.ld * ESZ;
-    const float *mrow = has_mask ? a.mask + b * a.msb + h * a.msh + q * a.msq : nullptr;
+    const float *mrow = nullptr;
+    int64_t h = 0;
+    if (MASK || has_sink) {
+      const int64_t q = rr % a.s.Sq;
+      const int64_t bh = rr / a.s.Sq;
+      h = bh % a.s.H;
+      if constexpr (MASK) mrow = a.mask + (bh / a.s.H) * a.msb + h * a.msh + q * a.msq;
+    }
 
+    // ---- phase 1: issue every score load of the row, straight-line.  VEC:
+    // a slot's lanes past the row (or a slot past the row) read the row's
+    // last chunk, and phase 2 replaces what they read. ----
+    Chunk raw[CPL];
+#pragma unroll
+    for (int s = 0; s < CPL; ++s) {
+      const int j0 = (s * WPR + ix.wir) * TPS * kTile + ix.loff;
+      if constexpr (VEC) raw[s] = load_at<ESZ>(srow, min(j0, N - KPL));
+      else raw[s] = load_chunk_elems<DT>(srow, j0, N, kFill);
+    }
+
+    // ---- phase 2: per tile max, exponentials, sum ----
     float e[CPL][KPL];
-
-    if (active) {
+    float4 mv[2][KPL / 4];  // mask of the current and the next slot
+    auto load_mask = [&](int s, float4 (&dst)[KPL / 4]) {
+      const int j = min((s * WPR + ix.wir) * TPS * kTile + ix.loff, N - KPL);
 #pragma unroll
-      for (int s = 0; s < CPL; ++s) {
-        const int gs = s * WPR + wir;  // slot index within the row
-        if (gs < nslots) {
-          const int t = gs * TPS + half;
-          const int64_t j0 = (int64_t)t * kTile + (int64_t)cil * KPL;
-          const bool inb = j0 < N;  // VEC: a chunk is wholly inside or wholly past the row
-          // keys past the row read as -inf (the max's identity; their e is +0)
-          constexpr uint32_t kFill = (DT == 1) ? 0xff80ff80u : 0xff800000u;
-          Chunk raw;
-          if constexpr (VEC) {
-            raw = inb ? load_chunk(srow + j0 * ESZ) : Chunk{{kFill, kFill, kFill, kFill}};
-          } else {
-            raw = load_chunk_elems<DT>(srow, j0, N, kFill);
+      for (int k4 = 0; k4 < KPL / 4; ++k4)
+        dst[k4] = *reinterpret_cast<const float4 *>(mrow + j + 4 * k4);
+    };
+    if constexpr (MASK && VEC) load_mask(0, mv[0]);
+#pragma unroll
+    for (int s = 0; s < CPL; ++s) {
+      const int gs = s * WPR + ix.wir;
+      const int sb = gs * TPS * kTile;
+      const int t = gs * TPS + ix.half;
+      const int j0 = sb + ix.loff;
+      if constexpr (MASK && VEC) {
+        if (s + 1 < CPL) load_mask(s + 1, mv[(s + 1) & 1]);
+      }
+      float x[KPL];
+      unpack<DT>(raw[s], x);
+      if constexpr (MASK) {
+        if constexpr (VEC) {
+          const float4 (&m4)[KPL / 4] = mv[s & 1];
+#pragma unroll
+          for (int k4 = 0; k4 < KPL / 4; ++k4) {
+            x[4 * k4 + 0] = x[4 * k4 + 0] + m4[k4].x;
+            x[4 * k4 + 1] = x[4 * k4 + 1] + m4[k4].y;
+            x[4 * k4 + 2] = x[4 * k4 + 2] + m4[k4].z;
+            x[4 * k4 + 3] = x[4 * k4 + 3] + m4[k4].w;
           }
-          float x[KPL];
-          unpack<DT>(raw, x);
-          if (has_mask) {
-            if constexpr (VEC) {
-              if (inb) {
+        } else {
 #pragma unroll
-                for (int k4 = 0; k4 < KPL; k4 += 4) {
-                  const float4 mv = *reinterpret_cast<const float4 *>(mrow + j0 + k4);
-                  x[k4 + 0] = x[k4 + 0] + mv.x;
-                  x[k4 + 1] = x[k4 + 1] + mv.y;
-                  x[k4 + 2] = x[k4 + 2] + mv.z;
-                  x[k4 + 3] = x[k4 + 3] + mv.w;
-                }
-              }
-            } else {
-#pragma unroll
-              for (int k = 0; k < KPL; ++k)
-                if (j0 + k < N) x[k] = x[k] + mrow[j0 + k];
-            }
-          }
-          const float m = tile_max<DT>(lane_tree_max<KPL>(x));
-          // a tile whose max is -inf has only -inf keys: subtracting 0 keeps
-          // them at -inf and every e at +0, without a -inf - -inf
-          const float msafe = (m == kNegInf) ? 0.0f : m;
-#pragma unroll
-          for (int k = 0; k < KPL; ++k) e[s][k] = exp_(x[k] - msafe);
-          const float l = tile_sum<DT>(lane_tree_sum<KPL>(e[s]));
-          if (cil == 0 && t < T) {
-            lds_m[rib][t] = m;
-            lds_l[rib][t] = l;
-          }
+          for (int k = 0; k < KPL; ++k)
+            if (j0 + k < N) x[k] = x[k] + mrow[j0 + k];
         }
+      }
+      if constexpr (VEC) {
+        if (sb + TPS * kTile > N) {  // a slot reaching past the row (uniform)
+          const bool inb = j0 < N;
+#pragma unroll
+          for (int k = 0; k < KPL; ++k) x[k] = inb ? x[k] : kNegInf;
+        }
+      }
+      const float m = tile_max<DT>(lane_tree_max<KPL>(x));
+      // a tile whose max is -inf has only -inf keys: subtracting 0 keeps
+      // them at -inf and every e at +0, without a -inf - -inf
+      const float msafe = (m == kNegInf) ? 0.0f : m;
+#pragma unroll
+      for (int k = 0; k < KPL; ++k) e[s][k] = exp_(x[k] - msafe);
+      const float l = tile_sum<DT>(lane_tree_sum<KPL>(e[s]));
+      if (ix.cil == 0 && t < T) {
+        lds_m[ix.rib][t] = m;
+        lds_l[ix.rib][t] = l;
       }
     }
     row_sync<WPR>();
 
     if (active) {
       // ---- merge of the tile states, lane t holds tile t ----
-      const float mt = (lane < T) ? lds_m[rib][lane] : kNegInf;
-      const float lt = (lane < T) ? lds_l[rib][lane] : 0.0f;
+      const float mt = (lane < T) ? lds_m[ix.rib][lane] : kNegInf;
+      const float lt = (lane < T) ? lds_l[ix.rib][lane] : 0.0f;
       float Mi = mt;  // running max after tile `lane` (inclusive prefix max)
 #pragma unroll
-      for (int d = 1; d < kWave; d <<= 1) Mi = __builtin_fmaxf(Mi, __shfl_up(Mi, d));
+      for (int d = 1; d < kWave; d <<= 1) Mi = fmax2(Mi, __shfl_up(Mi, d));
       float Me = __shfl_up(Mi, 1);  // running max before tile `lane`
       if (lane == 0) Me = kNegInf;
       float alpha = 0.0f, qv = 0.0f;
@@ -396,7 +461,7 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void fwd_kernel(const FwdArgs 
       float sigma = 0.0f;
       if (has_sink) {
         sigma = a.sink[h];  // one logit per head
-        const float Mn = __builtin_fmaxf(M, sigma);
+        const float Mn = fmax2(M, sigma);
         if (Mn == kNegInf) {
           M = kNegInf;
           L = 0.0f;
@@ -412,30 +477,30 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void fwd_kernel(const FwdArgs 
       const float invL = (L == 0.0f) ? 0.0f : 1.0f / L;
       const float ct = (mt == kNegInf) ? 0.0f : exp_(mt - M) * invL;  // tile `lane`'s scale
 
-      // ---- rescale, convert once, write ----
+      // ---- phase 3: rescale, convert once, write ----
 #pragma unroll
       for (int s = 0; s < CPL; ++s) {
-        const int gs = s * WPR + wir;
+        const int gs = s * WPR + ix.wir;
         if (gs < nslots) {
-          const int t = gs * TPS + half;
-          const int64_t j0 = (int64_t)t * kTile + (int64_t)cil * KPL;
+          const int sb = gs * TPS * kTile;
+          const int j0 = sb + ix.loff;
           float cs = readlane(ct, gs * TPS);
           if constexpr (TPS == 2) {
             const float c1 = readlane(ct, gs * TPS + 1);
-            cs = half ? c1 : cs;
+            cs = ix.half ? c1 : cs;
           }
           float p[KPL];
 #pragma unroll
           for (int k = 0; k < KPL; ++k) p[k] = e[s][k] * cs;
           const Chunk out = pack<DT>(p);
           if constexpr (VEC) {
-            if (j0 < N) store_chunk(prow + j0 * ESZ, out);
+            if (sb + TPS * kTile <= N || j0 < N) store_at<ESZ>(prow, j0, out);
           } else {
             store_chunk_elems<DT>(prow, j0, N, out);
           }
         }
       }
-      if (has_sink && wir == 0 && lane == 0)
+      if (has_sink && ix.wir == 0 && lane == 0)
         a.p_sink[r] = (sigma == kNegInf) ? 0.0f : exp_(sigma - M) * invL;
     }
     if constexpr (WPR > 1) __syncthreads();  // LDS is reused by the next row group
@@ -444,76 +509,84 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void fwd_kernel(const FwdArgs 
 }
 
 // ---------------------------------------------------------------------------
-// Backward
+// Backward: phase 1 loads P and dP for the whole row, phase 2 forms the tile
+// sums of P*dP, the fold runs over the tile sums in order, phase 3 writes dS.
 // ---------------------------------------------------------------------------
 
 template <int DT, int WPR, int CPL, bool VEC>
 __global__ __launch_bounds__(kWave * kBlockWaves) void bwd_kernel(const BwdArgs a) {
   using C = Cfg<DT>;
-  constexpr int KPL = C::KPL, LPT = C::LPT, TPS = C::TPS, ESZ = C::ESZ;
+  constexpr int KPL = C::KPL, TPS = C::TPS, ESZ = C::ESZ;
   __shared__ float lds_d[kBlockWaves][kMaxTiles];
 
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int wir = wave % WPR;
-  const int rib = wave / WPR;
-  const int rpb = blockDim.x / (kWave * WPR);
+  const RowIdx<DT, WPR> ix;
+  const int lane = ix.lane;
   const int T = a.s.T;
-  const int64_t N = a.s.N;
+  const int N = (int)a.s.N;
   const int nslots = (T + TPS - 1) / TPS;
-  const int half = lane / LPT;
-  const int cil = lane % LPT;
-  const int64_t ngroups = (a.s.rows + rpb - 1) / rpb;
+  const int64_t ngroups = (a.s.rows + ix.rpb - 1) / ix.rpb;
   const bool has_sink = a.p_sink != nullptr;
 
   for (int64_t grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
-    const int64_t r = grp * rpb + rib;
+    const int64_t r = grp * ix.rpb + ix.rib;
     const bool active = r < a.s.rows;
-    const char *prow = static_cast<const char *>(a.probs) + r * a.s.ld * ESZ;
-    const char *grow = static_cast<const char *>(a.dprobs) + r * a.s.ld * ESZ;
+    const int64_t rr = active ? r : a.s.rows - 1;  // spare rows read the last row
+    const char *prow = static_cast<const char *>(a.probs) + rr * a.s.ld * ESZ;
+    const char *grow = static_cast<const char *>(a.dprobs) + rr * a.s.ld * ESZ;
     char *drow = static_cast<char *>(a.dscores) + r * a.s.ld * ESZ;
 
+    // ---- phase 1: issue every load of the row, straight-line ----
     Chunk rp[CPL], rg[CPL];
+#pragma unroll
+    for (int s = 0; s < CPL; ++s) {
+      const int j0 = (s * WPR + ix.wir) * TPS * kTile + ix.loff;
+      if constexpr (VEC) {
+        rp[s] = load_at<ESZ>(prow, min(j0, N - KPL));
+        rg[s] = load_at<ESZ>(grow, min(j0, N - KPL));
+      } else {  // keys past the row read as +0
+        rp[s] = load_chunk_elems<DT>(prow, j0, N, 0u);
+        rg[s] = load_chunk_elems<DT>(grow, j0, N, 0u);
+      }
+    }
 
-    if (active) {
+    // ---- phase 2: tile sums of P*dP; keys past the row count as +0 ----
 #pragma unroll
-      for (int s = 0; s < CPL; ++s) {
-        const int gs = s * WPR + wir;
-        if (gs < nslots) {
-          const int t = gs * TPS + half;
-          const int64_t j0 = (int64_t)t * kTile + (int64_t)cil * KPL;
-          // keys past the row read as +0 (their product adds +0 to the tree)
-          if constexpr (VEC) {
-            const bool inb = j0 < N;
-            rp[s] = inb ? load_chunk(prow + j0 * ESZ) : Chunk{{0u, 0u, 0u, 0u}};
-            rg[s] = inb ? load_chunk(grow + j0 * ESZ) : Chunk{{0u, 0u, 0u, 0u}};
-          } else {
-            rp[s] = load_chunk_elems<DT>(prow, j0, N, 0u);
-            rg[s] = load_chunk_elems<DT>(grow, j0, N, 0u);
+    for (int s = 0; s < CPL; ++s) {
+      const int gs = s * WPR + ix.wir;
+      const int sb = gs * TPS * kTile;
+      const int t = gs * TPS + ix.half;
+      if constexpr (VEC) {
+        if (sb + TPS * kTile > N) {  // a slot reaching past the row (uniform)
+          const bool inb = sb + ix.loff < N;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            rp[s].w[i] = inb ? rp[s].w[i] : 0u;
+            rg[s].w[i] = inb ? rg[s].w[i] : 0u;
           }
-          float p[KPL], g[KPL], pg[KPL];
-          unpack<DT>(rp[s], p);
-          unpack<DT>(rg[s], g);
-#pragma unroll
-          for (int k = 0; k < KPL; ++k) pg[k] = p[k] * g[k];
-          const float d = tile_sum<DT>(lane_tree_sum<KPL>(pg));
-          if (cil == 0 && t < T) lds_d[rib][t] = d;
         }
       }
+      float p[KPL], g[KPL], pg[KPL];
+      unpack<DT>(rp[s], p);
+      unpack<DT>(rg[s], g);
+#pragma unroll
+      for (int k = 0; k < KPL; ++k) pg[k] = p[k] * g[k];
+      const float d = tile_sum<DT>(lane_tree_sum<KPL>(pg));
+      if (ix.cil == 0 && t < T) lds_d[ix.rib][t] = d;
     }
     row_sync<WPR>();
 
     if (active) {
-      const float dt = (lane < T) ? lds_d[rib][lane] : 0.0f;
+      const float dt = (lane < T) ? lds_d[ix.rib][lane] : 0.0f;
       float delta = readlane(dt, 0);  // the fold starts from the first tile's sum
       for (int t = 1; t < T; ++t) delta = delta + readlane(dt, t);
 
+      // ---- phase 3: dS = P * (dP - delta), convert once, write ----
 #pragma unroll
       for (int s = 0; s < CPL; ++s) {
-        const int gs = s * WPR + wir;
+        const int gs = s * WPR + ix.wir;
         if (gs < nslots) {
-          const int t = gs * TPS + half;
-          const int64_t j0 = (int64_t)t * kTile + (int64_t)cil * KPL;
+          const int sb = gs * TPS * kTile;
+          const int j0 = sb + ix.loff;
           float p[KPL], g[KPL], ds[KPL];
           unpack<DT>(rp[s], p);
           unpack<DT>(rg[s], g);
@@ -524,13 +597,13 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void bwd_kernel(const BwdArgs 
           }
           const Chunk out = pack<DT>(ds);
           if constexpr (VEC) {
-            if (j0 < N) store_chunk(drow + j0 * ESZ, out);
+            if (sb + TPS * kTile <= N || j0 < N) store_at<ESZ>(drow, j0, out);
           } else {
             store_chunk_elems<DT>(drow, j0, N, out);
           }
         }
       }
-      if (has_sink && wir == 0 && lane == 0) a.v[r] = -(a.p_sink[r] * delta);
+      if (has_sink && ix.wir == 0 && lane == 0) a.v[r] = -(a.p_sink[r] * delta);
     }
     if constexpr (WPR > 1) __syncthreads();
     else wave_sync();
@@ -593,10 +666,14 @@ constexpr int kCplBf16[] = {1, 2, 3, 5, 9};
 template <int DT, int WPR, int CPL>
 hipError_t launch_fwd_t(const FwdArgs &a, const Geometry &g, hipStream_t st) {
   const dim3 grid((unsigned)g.blocks), block(kWave * WPR * g.rpb);
-  if (a.vec_io)
-    hipLaunchKernelGGL((fwd_kernel<DT, WPR, CPL, true>), grid, block, 0, st, a);
-  else
-    hipLaunchKernelGGL((fwd_kernel<DT, WPR, CPL, false>), grid, block, 0, st, a);
+  const bool mask = a.mask != nullptr;
+  if (a.vec_io) {
+    if (mask) hipLaunchKernelGGL((fwd_kernel<DT, WPR, CPL, true, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((fwd_kernel<DT, WPR, CPL, true, false>), grid, block, 0, st, a);
+  } else {
+    if (mask) hipLaunchKernelGGL((fwd_kernel<DT, WPR, CPL, false, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((fwd_kernel<DT, WPR, CPL, false, false>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 

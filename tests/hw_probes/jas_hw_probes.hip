@@ -1,0 +1,134 @@
+// jas_hw_probes.hip -- test-only probes of gfx950 instructions the library
+// relies on.  Not part of the library; built beside the tests.
+//
+//  * exp2 sweep: every negative binary32 u (down to -inf) through v_exp_f32, against
+//    2^u evaluated in double and rounded to binary32 with results below
+//    2^-126 taken as +0 (the library's exponential contract).  Reports the
+//    largest difference in ulps and every place where the flush behaviour
+//    differs.
+//  * bf16 conversion sweep: every binary32 bit pattern through
+//    v_cvt_pk_bf16_f32 against round-to-nearest-even on the bit pattern.
+//
+// Each thread handles kPer consecutive inputs; each workgroup writes its own
+// four result words, no atomics.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+constexpr int kThreads = 256;
+constexpr int kPer = 64;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ inline float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ inline uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+__device__ inline uint32_t ord(float f) {  // monotone map of finite floats to integers
+  uint32_t u = f2u(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// out[4*block + 0] = max |ulp diff|, +1 = #u with diff != 0,
+// +2 = #u >= -126 whose result is below 2^-126, +3 = #u < -126 whose result is not +0
+__global__ void exp2_sweep(uint32_t first, uint32_t count, uint32_t *out) {
+  uint32_t mx = 0, ndiff = 0, nlow = 0, nnz = 0;
+  const uint32_t base = (blockIdx.x * kThreads + threadIdx.x) * kPer;
+  for (int i = 0; i < kPer; ++i) {
+    const uint32_t k = base + i;
+    if (k >= count) break;
+    const float u = u2f(first + k);  // negative floats: bit patterns increase toward -inf
+    const float hw = __builtin_amdgcn_exp2f(u);
+    float ref;
+    if (u < -126.0f) ref = 0.0f;
+    else ref = (float)exp2((double)u);
+    const uint32_t a = ord(hw), b = ord(ref);
+    const uint32_t d = a > b ? a - b : b - a;
+    mx = d > mx ? d : mx;
+    ndiff += d != 0;
+    if (u >= -126.0f && !(hw >= 0x1p-126f)) ++nlow;
+    if (u < -126.0f && f2u(hw) != 0u) ++nnz;
+  }
+  __shared__ uint32_t s[4][kThreads];
+  s[0][threadIdx.x] = mx; s[1][threadIdx.x] = ndiff; s[2][threadIdx.x] = nlow; s[3][threadIdx.x] = nnz;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r0 = 0, r1 = 0, r2 = 0, r3 = 0;
+    for (int t = 0; t < kThreads; ++t) {
+      r0 = s[0][t] > r0 ? s[0][t] : r0; r1 += s[1][t]; r2 += s[2][t]; r3 += s[3][t];
+    }
+    out[4 * blockIdx.x + 0] = r0; out[4 * blockIdx.x + 1] = r1;
+    out[4 * blockIdx.x + 2] = r2; out[4 * blockIdx.x + 3] = r3;
+  }
+}
+
+__device__ inline uint32_t rne_bits(uint32_t u) {
+  uint32_t lo = u >> 16, rest = u & 0xffffu;
+  if (rest > 0x8000u || (rest == 0x8000u && (lo & 1u))) lo += 1u;
+  return lo;
+}
+
+// out[2*block + 0] = #non-NaN patterns whose conversion differs from RNE,
+// +1 = #NaN patterns whose result is not a NaN
+__global__ void bf16_sweep(uint64_t first, uint64_t count, uint32_t *out) {
+  uint32_t bad = 0, badnan = 0;
+  const uint64_t base = ((uint64_t)blockIdx.x * kThreads + threadIdx.x) * kPer;
+  for (int i = 0; i < kPer; i += 2) {
+    const uint64_t k = base + i;
+    if (k >= count) break;
+    const uint32_t u0 = (uint32_t)(first + k), u1 = (uint32_t)(first + k + 1);
+    f32x2_t v = {u2f(u0), u2f(u1)};
+    const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+    const uint32_t h[2] = {w & 0xffffu, w >> 16};
+    const uint32_t in[2] = {u0, u1};
+    for (int j = 0; j < 2; ++j) {
+      const bool isnan = (in[j] & 0x7f800000u) == 0x7f800000u && (in[j] & 0x7fffffu);
+      if (isnan) badnan += !((h[j] & 0x7f80u) == 0x7f80u && (h[j] & 0x7fu));
+      else bad += h[j] != rne_bits(in[j]);
+    }
+  }
+  __shared__ uint32_t s[2][kThreads];
+  s[0][threadIdx.x] = bad; s[1][threadIdx.x] = badnan;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r0 = 0, r1 = 0;
+    for (int t = 0; t < kThreads; ++t) { r0 += s[0][t]; r1 += s[1][t]; }
+    out[2 * blockIdx.x] = r0; out[2 * blockIdx.x + 1] = r1;
+  }
+}
+
+// lane layout of the gfx950 permlane swaps: out[2*lane], out[2*lane+1]
+__global__ void permlane_layout(uint32_t *out) {
+  const uint32_t l = threadIdx.x;
+  auto p16 = __builtin_amdgcn_permlane16_swap(l, l, false, false);
+  auto p32 = __builtin_amdgcn_permlane32_swap(l, l, false, false);
+  out[4 * l + 0] = p16[0]; out[4 * l + 1] = p16[1];
+  out[4 * l + 2] = p32[0]; out[4 * l + 3] = p32[1];
+}
+}  // namespace
+
+extern "C" {
+// Sweep [first, first+count) (negative binary32 bit patterns).  out holds
+// 4 words per workgroup; returns the number of workgroups used, or -1.
+int probe_exp2_sweep(uint32_t first, uint32_t count, uint32_t *out, uint32_t out_words) {
+  const uint64_t per_block = (uint64_t)kThreads * kPer;
+  const uint64_t blocks = (count + per_block - 1) / per_block;
+  if (blocks * 4 > out_words || blocks == 0) return -1;
+  hipLaunchKernelGGL(exp2_sweep, dim3((unsigned)blocks), dim3(kThreads), 0, 0, first, count, out);
+  return hipDeviceSynchronize() == hipSuccess ? (int)blocks : -1;
+}
+
+int probe_bf16_sweep(uint64_t first, uint64_t count, uint32_t *out, uint32_t out_words) {
+  const uint64_t per_block = (uint64_t)kThreads * kPer;
+  if (count % 2) return -1;
+  const uint64_t blocks = (count + per_block - 1) / per_block;
+  if (blocks * 2 > out_words || blocks == 0) return -1;
+  hipLaunchKernelGGL(bf16_sweep, dim3((unsigned)blocks), dim3(kThreads), 0, 0, first, count, out);
+  return hipDeviceSynchronize() == hipSuccess ? (int)blocks : -1;
+}
+
+int probe_permlane_layout(uint32_t *out) {  // out: 256 words
+  hipLaunchKernelGGL(permlane_layout, dim3(1), dim3(64), 0, 0, out);
+  return hipDeviceSynchronize() == hipSuccess ? 0 : -1;
+}
+}

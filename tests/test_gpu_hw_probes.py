@@ -1,0 +1,75 @@
+"""Exhaustive probes of the gfx950 instructions the library's arithmetic
+rests on (test-only kernels in tests/hw_probes/):
+
+* v_exp_f32 over every binary32 u from -0 down to -inf: its largest error
+  against 2^u rounded to binary32, and that it returns +0 exactly where the
+  exponential contract flushes (every u below -126) and a normal number from
+  -126 up -- the kernels' exp_ relies on this instead of a select.
+* v_cvt_pk_bf16_f32 over all 2^32 bit patterns: round to nearest-even, as the
+  oracle's conversion (RL-Kernel PR #453: one dtype conversion at the write).
+* the lane layout of the permlane16/32 swaps used by the tile trees.
+"""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from tests.gpu_util import log
+
+pytestmark = pytest.mark.gpu
+LIB = os.path.join(os.path.dirname(__file__), "hw_probes", "libjas_hw_probes.so")
+
+
+def probes():
+    L = ctypes.CDLL(LIB)
+    L.probe_exp2_sweep.restype = ctypes.c_int
+    L.probe_exp2_sweep.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_uint32]
+    L.probe_bf16_sweep.restype = ctypes.c_int
+    L.probe_bf16_sweep.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint32]
+    L.probe_permlane_layout.restype = ctypes.c_int
+    L.probe_permlane_layout.argtypes = [ctypes.c_void_p]
+    return L
+
+
+def test_v_exp_f32_sweep():
+    L = probes()
+    first = 0x80000000                     # -0.0
+    last = 0xFF800000                      # -inf: every negative binary32
+    count = last - first + 1
+    words = 4 * ((count + 256 * 64 - 1) // (256 * 64))
+    out = torch.zeros(words, dtype=torch.int32, device="cuda")
+    nb = L.probe_exp2_sweep(first, count, out.data_ptr(), words)
+    assert nb > 0
+    r = out.cpu().numpy().view(np.uint32).reshape(-1, 4)
+    max_ulp, ndiff, nlow, nnz = int(r[:, 0].max()), int(r[:, 1].sum()), int(r[:, 2].sum()), int(r[:, 3].sum())
+    log(f"v_exp_f32 over {count} inputs in [-inf,0]: max {max_ulp} ulp, {ndiff} differ, "
+        f"{nlow} below 2^-126 for u >= -126, {nnz} nonzero for u < -126")
+    assert max_ulp <= 1
+    assert nlow == 0 and nnz == 0
+
+
+def test_v_cvt_pk_bf16_f32_is_rne_on_all_patterns():
+    L = probes()
+    count = 1 << 32
+    words = 2 * (count // (256 * 64))
+    out = torch.zeros(words, dtype=torch.int32, device="cuda")
+    assert L.probe_bf16_sweep(0, count, out.data_ptr(), words) > 0
+    r = out.cpu().numpy().view(np.uint32).reshape(-1, 2)
+    bad, badnan = int(r[:, 0].sum()), int(r[:, 1].sum())
+    log(f"v_cvt_pk_bf16_f32: {bad} non-NaN mismatches, {badnan} NaN results not NaN")
+    assert bad == 0 and badnan == 0
+
+
+def test_permlane_swap_layout():
+    L = probes()
+    out = torch.zeros(256, dtype=torch.int32, device="cuda")
+    assert L.probe_permlane_layout(out.data_ptr()) == 0
+    r = out.cpu().numpy().reshape(64, 4)
+    lanes = np.arange(64)
+    # every lane sees (its even 16-lane row's value, the odd row's value) of
+    # its 32-lane half, and (lower half's value, upper half's value)
+    row_even = (lanes // 32) * 32 + (lanes % 16)
+    assert np.array_equal(r[:, 0], row_even) and np.array_equal(r[:, 1], row_even + 16)
+    assert np.array_equal(r[:, 2], lanes % 32) and np.array_equal(r[:, 3], lanes % 32 + 32)

@@ -113,7 +113,8 @@ def test_elementwise_path_matches_vector_path(dt):
         gbig = torch.zeros_like(big)
         gv = gbig[off:].view(B, H, S, ld)[..., :N]
         gv.copy_(g)
-        P1, ps1 = jas.fwd(sv, sink=sink)          # out: contiguous
+        P1, ps1 = jas.fwd(sv, sink=sink)          # out: same row stride
+        assert P1.stride() == sv.stride()
         Pbig = torch.full_like(big, 7.0)
         Pv = Pbig[off:].view(B, H, S, ld)[..., :N]
         jas.fwd(sv, sink=sink, out=Pv, p_sink=torch.empty_like(ps0))
