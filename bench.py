@@ -143,6 +143,37 @@ def cpu_baseline(wl, s, mask, sink, g, target_s):
     }
 
 
+def copy_ceiling(nbytes, stream, steps=10):
+    """A plain 16-byte copy of `nbytes` (the dominant kernel's bytes: half
+    read, half written) with the test-only probe kernel, if it is built: the
+    attainable read+write bandwidth on this machine."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "tests", "hw_probes", "libjas_hw_probes.so")
+    if not os.path.exists(path):
+        return None
+    L = ctypes.CDLL(path)
+    L.probe_copy16.restype = ctypes.c_int
+    L.probe_copy16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int,
+                               ctypes.c_int, ctypes.c_void_p]
+    n16 = max(1, nbytes // 32)
+    src = torch.empty(n16 * 16, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    out = {}
+    for nt in (0, 1):
+        for _ in range(3):
+            L.probe_copy16(src.data_ptr(), dst.data_ptr(), n16, nt, 0, stream.cuda_stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            L.probe_copy16(src.data_ptr(), dst.data_ptr(), n16, nt, 0, stream.cuda_stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        out["nontemporal" if nt else "plain"] = round(2 * n16 * 16 / (ms * 1e-3) / 1e9, 1)
+    return {"unit": "GB/s", "bytes": 2 * n16 * 16, **out}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -184,6 +215,12 @@ def main():
         if ev:
             ev[2].record(stream)
 
+    # bring clocks and page mappings to steady state (untimed, before the
+    # warmup steps proper)
+    t_end = time.perf_counter() + 0.5
+    while time.perf_counter() < t_end:
+        step()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -227,6 +264,10 @@ def main():
                      "avg_launch_ms": round(float(dom[3]), 4)},
         "parity": check,
     }
+    out["copy_ceiling"] = copy_ceiling(dom[2], stream)
+    if out["copy_ceiling"]:
+        best = max(out["copy_ceiling"]["plain"], out["copy_ceiling"]["nontemporal"])
+        out["roofline"]["frac_of_copy"] = round(dom[1] / best, 4)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(wl, s, mask, sink, g, args.cpu_seconds)

@@ -91,13 +91,14 @@ jas_status_t choose_geometry(int dtype, int T, int64_t rows, const jas_launch_t 
   const int64_t cap = ov ? ov->max_blocks : 0;
   if (wpr < 0 || cpl < 0 || rpb < 0 || cap < 0) return JAS_ERR_UNSUPPORTED;
   if (wpr == 0) {
-    // fewest waves per row whose register share stays within the default cap
-    for (int w : {1, 2, 4}) {
-      const int need = (nslots + w - 1) / w;
-      if (cpl ? cpl * w >= nslots : need <= jas::default_cpl_max(dtype)) {
-        wpr = w;
-        break;
-      }
+    if (cpl) {
+      for (int w : {1, 2, 4})
+        if (cpl * w >= nslots) {
+          wpr = w;
+          break;
+        }
+    } else {
+      wpr = jas::default_wpr(dtype, nslots);
     }
     if (wpr == 0) return JAS_ERR_UNSUPPORTED;
   }
@@ -111,7 +112,10 @@ jas_status_t choose_geometry(int dtype, int T, int64_t rows, const jas_launch_t 
     if (cpl == 0) return JAS_ERR_UNSUPPORTED;
   }
   if (!jas::cpl_compiled(dtype, wpr, cpl) || (int64_t)wpr * cpl < nslots) return JAS_ERR_UNSUPPORTED;
-  if (rpb == 0) rpb = jas::kBlockWaves / wpr;
+  // one row per wavefront: 4 rows per workgroup; a row spread over several
+  // wavefronts: one row per workgroup (measured faster: its barriers then
+  // couple only the row's own waves)
+  if (rpb == 0) rpb = (wpr == 1) ? jas::kBlockWaves : 1;
   if (rpb < 1 || wpr * rpb > jas::kBlockWaves) return JAS_ERR_UNSUPPORTED;
   int64_t blocks = (rows + rpb - 1) / rpb;
   if (cap > 0 && blocks > cap) blocks = cap;

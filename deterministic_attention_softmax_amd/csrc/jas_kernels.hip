@@ -163,14 +163,19 @@ template <> struct Cfg<1> {  // bf16
 
 // A 16-byte chunk as 4 words.
 struct Chunk { uint32_t w[4]; };
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Scores, probabilities and gradients are streamed once: nontemporal
+// 16-byte loads and stores keep them from displacing reused data (the mask
+// row) in the caches.
 __device__ __forceinline__ Chunk load_chunk(const char *p) {
-  const uint4 v = *reinterpret_cast<const uint4 *>(p);
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
   return Chunk{{v.x, v.y, v.z, v.w}};
 }
 
 __device__ __forceinline__ void store_chunk(char *p, const Chunk &c) {
-  *reinterpret_cast<uint4 *>(p) = make_uint4(c.w[0], c.w[1], c.w[2], c.w[3]);
+  const u32x4 v = {c.w[0], c.w[1], c.w[2], c.w[3]};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
 }
 
 // Element-by-element chunk load for unaligned rows and the tail of a row:
@@ -755,7 +760,20 @@ bool cpl_compiled(int dtype, int wpr, int cpl) {
   return false;
 }
 
-int default_cpl_max(int dtype) { return dtype == 1 ? 9 : 17; }
+// Default waves per row for a row of `nslots` wave-wide chunks (the
+// chunks-per-lane size then is the smallest compiled one that covers the
+// row).  Measured on MI355X: a bf16 row of up to 9 slots (4,608 keys) runs
+// fastest on one wavefront, longer rows on four wavefronts of at most 5
+// slots each until 20 slots, then four of 9; fp32 rows are twice as many
+// slots for the same registers.  Any choice gives the same bits.
+int default_wpr(int dtype, int nslots) {
+  const int one = dtype == 1 ? 9 : 17;   // largest single-wave share
+  const int four = dtype == 1 ? 20 : 36; // four waves of <= 5 (bf16) / 9 (fp32) slots
+  if (nslots <= one) return 1;
+  if (nslots <= four) return 4;
+  if (nslots <= 4 * (dtype == 1 ? 9 : 17)) return 4;
+  return 0;
+}
 
 hipError_t launch_fwd(int dtype, const FwdArgs &a, const Geometry &g, hipStream_t st) {
   return dtype == 1 ? fwd_dt<1>(a, g, st) : fwd_dt<0>(a, g, st);

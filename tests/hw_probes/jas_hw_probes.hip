@@ -97,6 +97,34 @@ __global__ void bf16_sweep(uint64_t first, uint64_t count, uint32_t *out) {
   }
 }
 
+// Plain copy of n16 16-byte words: each thread moves 4 words per trip, all
+// four loads issued before the stores; grid-stride over the buffer.  A
+// bandwidth ceiling for kernels that read and write once, and a calibration
+// point for the HBM byte counters.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <bool NT>
+__global__ __launch_bounds__(256) void copy16(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst,
+                                              uint64_t n16) {
+  const uint64_t stride = (uint64_t)gridDim.x * 256 * 4;
+  for (uint64_t base = (uint64_t)blockIdx.x * 256 * 4 + threadIdx.x; base < n16; base += stride) {
+    u32x4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint64_t k = base + (uint64_t)i * 256;
+      if (k < n16) v[i] = NT ? __builtin_nontemporal_load(src + k) : src[k];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint64_t k = base + (uint64_t)i * 256;
+      if (k < n16) {
+        if (NT) __builtin_nontemporal_store(v[i], dst + k);
+        else dst[k] = v[i];
+      }
+    }
+  }
+}
+
 // lane layout of the gfx950 permlane swaps: out[2*lane], out[2*lane+1]
 __global__ void permlane_layout(uint32_t *out) {
   const uint32_t l = threadIdx.x;
@@ -125,6 +153,21 @@ int probe_bf16_sweep(uint64_t first, uint64_t count, uint32_t *out, uint32_t out
   if (blocks * 2 > out_words || blocks == 0) return -1;
   hipLaunchKernelGGL(bf16_sweep, dim3((unsigned)blocks), dim3(kThreads), 0, 0, first, count, out);
   return hipDeviceSynchronize() == hipSuccess ? (int)blocks : -1;
+}
+
+// Enqueue one copy of n16 16-byte words on `stream` (no synchronisation);
+// blocks = 0 picks 4 workgroups per CU-ish (2048).  Returns 0 or -1.
+int probe_copy16(const void *src, void *dst, uint64_t n16, int nontemporal, int blocks,
+                 void *stream) {
+  if (!src || !dst || ((uintptr_t)src | (uintptr_t)dst) % 16) return -1;
+  const unsigned g = blocks > 0 ? (unsigned)blocks : 2048u;
+  if (nontemporal)
+    hipLaunchKernelGGL(copy16<true>, dim3(g), dim3(256), 0, (hipStream_t)stream,
+                       (const u32x4 *)src, (u32x4 *)dst, n16);
+  else
+    hipLaunchKernelGGL(copy16<false>, dim3(g), dim3(256), 0, (hipStream_t)stream,
+                       (const u32x4 *)src, (u32x4 *)dst, n16);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int probe_permlane_layout(uint32_t *out) {  // out: 256 words
