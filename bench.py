@@ -11,11 +11,12 @@ per-kernel HIP-event durations, the roofline fraction of the dominant kernel
 against MI355X's 8 TB/s, and the CPU oracle timed on a bounded sample of the
 same rows on this host's cores.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3|c2|c5]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload joint4352|rows4352|causal8192]
 """
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -29,13 +30,40 @@ METRIC = "fwd+bwd softmax HBM GB/s and rows/s (bf16, 4,352 keys) vs 8 TB/s roofl
 
 WORKLOADS = {
     # name: (description, B, H, S, N, dtype, mask, sink, causal, backward)
-    "c3": ("joint image+text attention scores bf16 [1,24,4352,4352], per-batch text padding mask, fwd+bwd",
+    "joint4352": ("joint image+text attention scores bf16 [1,24,4352,4352], per-batch text padding mask, fwd+bwd",
            1, 24, 4352, 4352, "bf16", True, False, False, True),
-    "c2": ("bf16 scores 16384 rows x 4352 keys, N(0,1) with x8 outliers on 0.1%, fwd only",
+    "rows4352": ("bf16 scores 16384 rows x 4352 keys, N(0,1) with x8 outliers on 0.1%, fwd only",
            1, 1, 16384, 4352, "bf16", False, False, False, False),
-    "c5": ("causal self-attention scores bf16 [1,32,8192,8192] + per-head sink, fwd+bwd",
+    "causal8192": ("causal self-attention scores bf16 [1,32,8192,8192] + per-head sink, fwd+bwd",
            1, 32, 8192, 8192, "bf16", False, True, True, True),
 }
+
+
+KERNEL_SOURCE = os.path.join(ROOT, "deterministic_attention_softmax_amd", "csrc", "jas_kernels.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash():
+    import hashlib
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_record_path(wl):
+    return os.path.join(PROFILES, f"pmc_traffic_jas_{wl}.json")
+
+
+def load_traffic(wl, kernel):
+    """HBM bytes per launch of `kernel` ("fwd"/"bwd") from the committed PMC
+    record, or None when there is none or the kernels changed since."""
+    path = traffic_record_path(wl)
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else int(k["hbm_bytes_per_launch"])
 
 
 def parse():
@@ -43,11 +71,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="joint4352", choices=sorted(WORKLOADS))
     ap.add_argument("--no-check", action="store_true", help="skip the parity check before timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target wall time of the CPU oracle sample")
+    ap.add_argument("--json-out", metavar="PATH", help="also write the result line to PATH")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="summarise rocprofv3 output under DIR (trace/, fetch/, write/) into profiles/")
     return ap.parse_args()
 
 
@@ -60,13 +91,13 @@ def make_inputs(wl, dev):
     import synth
     _, B, H, S, N, dt, has_mask, has_sink, causal, _ = WORKLOADS[wl]
     mask = sink = g = None
-    if wl == "c3":
-        s, mask, g, _ = synth.c3_inputs(seed=3, device=dev, B=B, H=H, S=S, N=N)
+    if wl == "joint4352":
+        s, mask, g, _ = synth.joint_attention_bf16(seed=3, device=dev, B=B, H=H, S=S, N=N)
         mask = mask.view(B, 1, 1, N)
-    elif wl == "c2":
-        s = synth.c2_scores(seed=2, device=dev, rows=S, N=N)
+    elif wl == "rows4352":
+        s = synth.rows_with_outliers_bf16(seed=2, device=dev, rows=S, N=N)
     else:
-        s, sink, g = synth.c5_inputs(seed=5, device=dev, B=B, H=H, S=S)
+        s, sink, g = synth.causal_sink_bf16(seed=5, device=dev, B=B, H=H, S=S)
     return s, mask, sink, g
 
 
@@ -174,8 +205,116 @@ def copy_ceiling(nbytes, stream, steps=10):
     return {"unit": "GB/s", "bytes": 2 * n16 * 16, **out}
 
 
+def _kernel_kind(name):
+    if "fwd_kernel" in name:
+        return "fwd"
+    if "bwd_kernel" in name:
+        return "bwd"
+    if "dsink_kernel" in name:
+        return "dsink"
+    if "copy16<true>" in name:
+        return "copy_nt"
+    if "copy16<false>" in name:
+        return "copy"
+    return None
+
+
+def summarize_profiles(prof_dir, wl):
+    """Write profiles/kernel_trace_jas_<wl>.md and pmc_traffic_jas_<wl>.{md,json}
+    from rocprofv3 CSV output (see the commands recorded in them)."""
+    import csv
+    desc = WORKLOADS[wl][0]
+    os.makedirs(PROFILES, exist_ok=True)
+    trace = os.path.join(prof_dir, "trace", f"{wl}_kernel_stats.csv")
+    bench_log = os.path.join(prof_dir, "trace", "bench_line.json")
+    rows = list(csv.DictReader(open(trace)))
+    line = json.load(open(bench_log)) if os.path.exists(bench_log) else None
+    out = [f"# rocprofv3 kernel trace: jas kernels, workload {wl}", "",
+           f"Workload: {desc}.", "",
+           "Command (repository root, MI355X, ROCm 7.2):", "",
+           "```",
+           f"rocprofv3 --kernel-trace --stats --output-format csv -d {prof_dir}/trace -o {wl} -- "
+           f"python3 bench.py --workload {wl} --steps 10 --warmup 3 --no-cpu-baseline "
+           f"--json-out {prof_dir}/trace/bench_line.json",
+           "```", "",
+           "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    avg = {}
+    for r in rows:
+        kind = _kernel_kind(r["Name"])
+        if kind is None:
+            continue
+        name = re.sub(r"\([^()]*\)$", "", r["Name"]).replace("void ", "")
+        a = float(r["AverageNs"]) / 1e3
+        avg[kind] = a
+        out.append(f"| `{name}` | {r['Calls']} | {a:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                   f"{float(r['MaxNs']) / 1e3:.1f} |")
+    if line:
+        out += ["", "The same run's bench.py line (HIP events on the launch stream):", "",
+                f"- fwd average {line['fwd_ms'] * 1e3:.1f} us ({line['fwd_gbs']} GB/s)"]
+        if line.get("bwd_ms"):
+            out.append(f"- bwd average {line['bwd_ms'] * 1e3:.1f} us ({line['bwd_gbs']} GB/s)")
+        out.append(f"- fwd+bwd {line['value']} GB/s, {line['ms_per_step']} ms per step")
+    open(os.path.join(PROFILES, f"kernel_trace_jas_{wl}.md"), "w").write("\n".join(out) + "\n")
+
+    # PMC: FETCH_SIZE / WRITE_SIZE in KiB per dispatch, calibrated on the copy
+    # kernel of known size that bench.py runs in the same process
+    counters = {}
+    for cname, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+        path = os.path.join(prof_dir, sub, f"{wl}_counter_collection.csv")
+        for r in csv.DictReader(open(path)):
+            kind = _kernel_kind(r["Kernel_Name"])
+            if kind is None or r["Counter_Name"] != cname:
+                continue
+            counters.setdefault((kind, cname), []).append(float(r["Counter_Value"]) * 1024.0)
+    line_pmc = json.load(open(os.path.join(prof_dir, "fetch", "bench_line.json")))
+    copy_bytes = line_pmc["copy_ceiling"]["bytes"] / 2  # read = written = half the moved bytes
+    fac = {c: copy_bytes / np.mean(counters[("copy", c)]) for c in ("FETCH_SIZE", "WRITE_SIZE")}
+    E = WORKLOADS[wl][1] * WORKLOADS[wl][2] * WORKLOADS[wl][3] * WORKLOADS[wl][4]
+    alg = {"fwd": (2 * E, 2 * E), "bwd": (4 * E, 2 * E)}
+    rec = {"workload": wl, "kernel_source_sha256": kernel_source_hash(),
+           "calibration": {"copy_bytes_read": copy_bytes, "copy_bytes_written": copy_bytes,
+                           "fetch_factor": round(fac["FETCH_SIZE"], 4),
+                           "write_factor": round(fac["WRITE_SIZE"], 4)},
+           "kernels": {}}
+    md = [f"# rocprofv3 HBM traffic: jas kernels, workload {wl}", "",
+          f"Workload: {desc}.", "", "Commands (repository root):", "", "```"]
+    for c, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+        md.append(f"rocprofv3 --pmc {c} --output-format csv -d {prof_dir}/{sub} -o {wl} -- "
+                  f"python3 bench.py --workload {wl} --steps 2 --warmup 1 --no-cpu-baseline --no-check "
+                  f"--json-out {prof_dir}/{sub}/bench_line.json")
+    md += [f"python3 bench.py --workload {wl} --summarize-profiles {prof_dir}", "```", "",
+           "Counters are KiB per dispatch.  Each is scaled by what it reads for the 16-byte copy "
+           f"kernel of known size in the same process ({copy_bytes / 1e6:.1f} MB read and written): "
+           f"FETCH_SIZE x {fac['FETCH_SIZE']:.4f}, WRITE_SIZE x {fac['WRITE_SIZE']:.4f}.", "",
+           "| kernel | dispatches | HBM read MB | HBM written MB | algorithmic read MB | "
+           "algorithmic written MB | traffic / algorithmic |", "|---|---|---|---|---|---|---|"]
+    for kind in ("fwd", "bwd"):
+        if (kind, "FETCH_SIZE") not in counters:
+            continue
+        rd = float(np.mean(counters[(kind, "FETCH_SIZE")])) * fac["FETCH_SIZE"]
+        wr = float(np.mean(counters[(kind, "WRITE_SIZE")])) * fac["WRITE_SIZE"]
+        ar, aw = alg[kind]
+        rec["kernels"][kind] = {"hbm_read_bytes": int(rd), "hbm_write_bytes": int(wr),
+                                "hbm_bytes_per_launch": int(rd + wr),
+                                "algorithmic_bytes_per_launch": ar + aw}
+        md.append(f"| jas {kind} | {len(counters[(kind, 'FETCH_SIZE')])} | {rd / 1e6:.1f} | "
+                  f"{wr / 1e6:.1f} | {ar / 1e6:.1f} | {aw / 1e6:.1f} | {(rd + wr) / (ar + aw):.4f} |")
+    md += ["", "Algorithmic bytes: forward reads the scores and writes P (2 bytes each per "
+           "element), backward reads P and dP and writes dS; the per-row sink values (4 bytes "
+           "per row, written and read as one scattered word per row) and the mask row are not "
+           "counted there and show as the small excess.", "",
+           f"Kernel source sha256 at measurement: `{rec['kernel_source_sha256']}`; bench.py "
+           "reports these bytes as `roofline.traffic` only while the source still hashes to it."]
+    open(os.path.join(PROFILES, f"pmc_traffic_jas_{wl}.md"), "w").write("\n".join(md) + "\n")
+    json.dump(rec, open(traffic_record_path(wl), "w"), indent=1)
+    print("\n".join(out + [""] + md))
+
+
 def main():
     args = parse()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles, args.workload)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -260,8 +399,8 @@ def main():
         "bwd_gbs": round(bwd_gbs, 1) if backward else None,
         "roofline": {"bound": "hbm", "kernel": dom[0], "achieved": round(dom[1], 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom[1] / HBM_PEAK_GBS, 4),
-                     "traffic": None, "bytes_per_launch": dom[2],
-                     "avg_launch_ms": round(float(dom[3]), 4)},
+                     "traffic": load_traffic(wl, "bwd" if backward else "fwd"),
+                     "bytes_per_launch": dom[2], "avg_launch_ms": round(float(dom[3]), 4)},
         "parity": check,
     }
     out["copy_ceiling"] = copy_ceiling(dom[2], stream)
@@ -272,6 +411,9 @@ def main():
         log("timing the CPU oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(wl, s, mask, sink, g, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+    if args.json_out:
+        os.makedirs(os.path.dirname(os.path.abspath(args.json_out)), exist_ok=True)
+        json.dump(out, open(args.json_out, "w"))
 
 
 if __name__ == "__main__":

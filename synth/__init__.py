@@ -17,8 +17,8 @@ import math
 import torch
 
 __all__ = [
-    "gen", "normal", "c1_scores_grad", "c2_scores", "c3_inputs", "c4_batch",
-    "c5_inputs", "synthetic_bwd_inputs", "to_numpy_bits", "from_numpy_bits",
+    "gen", "normal", "grad_check_fp32", "rows_with_outliers_bf16", "joint_attention_bf16", "batch_sweep_fp32",
+    "causal_sink_bf16", "synthetic_bwd_inputs", "to_numpy_bits", "from_numpy_bits",
 ]
 
 
@@ -36,14 +36,14 @@ def normal(shape, std, seed, device, dtype=torch.float32):
     return z.to(dtype)
 
 
-def c1_scores_grad(seed=1, device="cpu", B=2, H=4, S=257, N=257):
+def grad_check_fp32(seed=1, device="cpu", B=2, H=4, S=257, N=257):
     """fp32 scores [B,H,S,N] ~ N(0, 3^2) and upstream gradient ~ N(0, 1)."""
     s = normal((B, H, S, N), 3.0, seed, device)
     g = normal((B, H, S, N), 1.0, seed + 1, device)
     return s, g
 
 
-def c2_scores(seed=2, device="cpu", rows=16384, N=4352, outlier_frac=0.001, outlier_mult=8.0):
+def rows_with_outliers_bf16(seed=2, device="cpu", rows=16384, N=4352, outlier_frac=0.001, outlier_mult=8.0):
     """bf16 scores [1,1,rows,N]: z ~ N(0,1) in fp32, multiplied by sqrt(128)
     then by 1/sqrt(128) (the QK scaling of a 128-wide head, done as two fp32
     roundings); exactly round(outlier_frac * E) positions, drawn without
@@ -57,7 +57,7 @@ def c2_scores(seed=2, device="cpu", rows=16384, N=4352, outlier_frac=0.001, outl
     return z.to(torch.bfloat16).view(1, 1, rows, N)
 
 
-def c3_inputs(seed=3, device="cpu", B=1, H=24, S=4352, N=4352, std=2.0, max_pad=255):
+def joint_attention_bf16(seed=3, device="cpu", B=1, H=24, S=4352, N=4352, std=2.0, max_pad=255):
     """Joint image+text attention: bf16 scores [B,H,S,N] ~ N(0, std^2); per
     batch entry a text-padding length pad_b ~ U{0..max_pad}, the additive fp32
     mask [B, N] is -inf on the last pad_b keys and 0 elsewhere (broadcast over
@@ -73,7 +73,7 @@ def c3_inputs(seed=3, device="cpu", B=1, H=24, S=4352, N=4352, std=2.0, max_pad=
     return s, mask.to(device), g, [int(p) for p in pads]
 
 
-def c4_batch(n, seed_block=40, seed=41, device="cpu", H=32, N=8449, place_seed=42):
+def batch_sweep_fp32(n, seed_block=40, seed=41, device="cpu", H=32, N=8449, place_seed=42):
     """Batch-invariance sweep: fp32 [n, H, 1, N].  A fixed block of H rows
     (scores and dP ~ N(0,1) from ``seed_block``) sits at batch index
     p ~ U{0..n-1} (drawn from ``place_seed`` and n); the other rows are drawn
@@ -88,7 +88,7 @@ def c4_batch(n, seed_block=40, seed=41, device="cpu", H=32, N=8449, place_seed=4
     return s, g, p
 
 
-def c5_inputs(seed=5, device="cpu", B=1, H=32, S=8192, N=None):
+def causal_sink_bf16(seed=5, device="cpu", B=1, H=32, S=8192, N=None):
     """Causal self-attention: bf16 scores [B,H,S,S] ~ N(0,1) with -inf where
     key > query (the causal condition key <= Skv - Sq + query with Sq = Skv),
     per-head fp32 sink logits ~ N(0,1), bf16 dP ~ N(0,1).  The -inf fill runs

@@ -28,12 +28,12 @@ def bits(t):
     return synth.to_numpy_bits(t)
 
 
-def test_config4_batch_invariance_fp32_8449():
+def test_batch_invariance_fp32_8449_keys():
     H, N = 32, 8449
     ref = None
     for n in (1, 3, 17, 64):
-        log(f"c4: fp32 [{n},{H},1,{N}] fwd+bwd")
-        s, g, p = synth.c4_batch(n, device="cpu")
+        log(f"batch sweep: fp32 [{n},{H},1,{N}] fwd+bwd")
+        s, g, p = synth.batch_sweep_fp32(n, device="cpu")
         P, _ = jas.fwd(s.to(dev()))
         dS, _ = jas.bwd(P, g.to(dev()))
         torch.cuda.synchronize()
@@ -44,12 +44,12 @@ def test_config4_batch_invariance_fp32_8449():
             # stage-isolated on the oracle's P
             s_np = bits(s[p:p + 1])
             P_o, _ = oracle.fwd(s_np, 1, H, 1, N)
-            assert_close(blk[0].reshape(P_o.shape), P_o, "c4 P")
+            assert_close(blk[0].reshape(P_o.shape), P_o, "batch sweep P")
             Pin = synth.from_numpy_bits(P_o, dev())
             dSi, _ = jas.bwd(Pin, g[p:p + 1].to(dev()))
             torch.cuda.synchronize()
             dS_o, _ = oracle.bwd(P_o, bits(g[p:p + 1]), 1, H, 1, N)
-            assert_bitexact(bits(dSi), dS_o, "c4 dS")
+            assert_bitexact(bits(dSi), dS_o, "batch sweep dS")
         else:
             assert blk[0].tobytes() == ref[0].tobytes(), f"P bytes changed at batch {n}"
             assert blk[1].tobytes() == ref[1].tobytes(), f"dS bytes changed at batch {n}"

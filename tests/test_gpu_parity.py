@@ -50,16 +50,16 @@ def run_fwd_bwd_full(s, g, mask=None, mask_strides=None, sink=None, launch=None)
     return worst
 
 
-def test_config1_fp32_257():
+def test_grad_check_fp32_2x4x257x257():
     # fp32 scores [2,4,257,257] ~ N(0, 3^2), dP ~ N(0,1); two tiles, tail of 1
-    log("c1: fp32 [2,4,257,257] fwd+bwd")
-    s, g = synth.c1_scores_grad(seed=1)
+    log("fp32 [2,4,257,257] fwd+bwd")
+    s, g = synth.grad_check_fp32(seed=1)
     run_fwd_bwd_full(s, g)
 
 
-def test_config1_bf16_257_with_mask_and_sink():
-    log("c1 bf16 variant: [2,4,257,257] with per-batch mask and sink")
-    s, g = synth.c1_scores_grad(seed=11)
+def test_bf16_2x4x257x257_with_mask_and_sink():
+    log("bf16 [2,4,257,257] with per-batch mask and sink")
+    s, g = synth.grad_check_fp32(seed=11)
     s, g = s.to(torch.bfloat16), g.to(torch.bfloat16)
     mask = torch.zeros((2, 1, 1, 257))
     mask[0, ..., 200:] = float("-inf")
@@ -79,24 +79,24 @@ def test_row_lengths(N, dt):
     run_fwd_bwd_full(s, g, sink=sink)
 
 
-def test_config2_full_forward():
+def test_rows_16384x4352_forward_all_rows():
     # bf16 [1,1,16384,4352], N(0,1) scaled by sqrt(128) then 1/sqrt(128), x8 on 0.1%
-    log("c2: bf16 16384 x 4352 forward, all rows")
-    s = synth.c2_scores(seed=2, device=dev())
+    log("bf16 16384 x 4352 forward, all rows")
+    s = synth.rows_with_outliers_bf16(seed=2, device=dev())
     P, _ = jas.fwd(s)
     torch.cuda.synchronize()
     s_np = synth.to_numpy_bits(s)
     P_o, _ = oracle.fwd(s_np, 1, 1, 16384, 4352)
-    worst = assert_close(synth.to_numpy_bits(P), P_o, "c2 P")
-    log(f"c2: max {worst} bf16 ulp")
+    worst = assert_close(synth.to_numpy_bits(P), P_o, "16384x4352 P")
+    log(f"16384 x 4352: max {worst} bf16 ulp")
 
 
-def test_config3_full_size_sampled():
+def test_joint_attention_1x24x4352x4352_sampled():
     # bf16 [1,24,4352,4352] ~ N(0, 2^2), per-batch text padding mask; full-size
     # launch, sampled rows compared with the oracle
-    log("c3: bf16 [1,24,4352,4352] mask fwd; bwd on synthetic P; sampled rows")
+    log("bf16 [1,24,4352,4352] mask fwd; bwd on synthetic P; sampled rows")
     B, H, S, N = 1, 24, 4352, 4352
-    s, mask, g, pads = synth.c3_inputs(seed=3, device=dev(), B=B, H=H, S=S, N=N)
+    s, mask, g, pads = synth.joint_attention_bf16(seed=3, device=dev(), B=B, H=H, S=S, N=N)
     P, _ = jas.fwd(s, mask=mask.view(B, 1, 1, N), mask_strides=(N, 0, 0))
     torch.cuda.synchronize()
     idx = sample_rows(B * H * S, 96, seed=30)
@@ -104,30 +104,30 @@ def test_config3_full_size_sampled():
     m_np = mask.cpu().numpy()
     b_of = idx // (H * S)
     P_o, _ = oracle_rows_fwd(s_rows, N, mask_rows=np.ascontiguousarray(m_np[b_of]))
-    assert_close(gather_rows(P, idx), P_o, "c3 P")
+    assert_close(gather_rows(P, idx), P_o, "joint P")
     del P
     # stage-isolated backward on seeded synthetic P (all rows on the GPU)
     Pin, gin, _ = synth.synthetic_bwd_inputs((B, H, S, N), torch.bfloat16, 33, dev())
     dS, _ = jas.bwd(Pin, gin)
     torch.cuda.synchronize()
     dS_o, _ = oracle_rows_bwd(gather_rows(Pin, idx), gather_rows(gin, idx), N)
-    assert_bitexact(gather_rows(dS, idx), dS_o, "c3 dS")
+    assert_bitexact(gather_rows(dS, idx), dS_o, "joint dS")
 
 
-def test_config3_batch2_full_compare():
+def test_joint_attention_batch2_all_rows():
     # the per-batch mask with B=2 (different padding per batch entry), smaller S
-    log("c3 B=2: bf16 [2,3,96,4352] mask fwd+bwd, all rows")
-    s, mask, g, pads = synth.c3_inputs(seed=34, device="cpu", B=2, H=3, S=96, N=4352)
+    log("bf16 [2,3,96,4352] per-batch mask fwd+bwd, all rows")
+    s, mask, g, pads = synth.joint_attention_bf16(seed=34, device="cpu", B=2, H=3, S=96, N=4352)
     assert pads[0] != pads[1]
     run_fwd_bwd_full(s, g, mask=mask.view(2, 1, 1, 4352), mask_strides=(4352, 0, 0))
 
 
-def test_config5_full_size_sampled():
+def test_causal_sink_1x32x8192x8192_sampled():
     # bf16 causal [1,32,8192,8192] + per-head sink, 2^31 elements (64-bit offsets)
-    log("c5: bf16 [1,32,8192,8192] causal+sink fwd; bwd+d_sink on synthetic inputs")
+    log("bf16 [1,32,8192,8192] causal+sink fwd; bwd+d_sink on synthetic inputs")
     B, H, S = 1, 32, 8192
     N = S
-    s, sink, g = synth.c5_inputs(seed=5, device=dev(), B=B, H=H, S=S)
+    s, sink, g = synth.causal_sink_bf16(seed=5, device=dev(), B=B, H=H, S=S)
     del g
     P, ps = jas.fwd(s, sink=sink)
     torch.cuda.synchronize()
@@ -137,8 +137,8 @@ def test_config5_full_size_sampled():
     s_rows = gather_rows(s, idx)
     h_of = (idx // S) % H
     P_o, ps_o = oracle_rows_fwd(s_rows, N, sigma_rows=np.ascontiguousarray(sink.cpu().numpy()[h_of]))
-    assert_close(gather_rows(P, idx), P_o, "c5 P")
-    assert_close(ps.cpu().numpy()[idx], ps_o, "c5 p_sink")
+    assert_close(gather_rows(P, idx), P_o, "causal P")
+    assert_close(ps.cpu().numpy()[idx], ps_o, "causal p_sink")
     del P, ps, s
     torch.cuda.empty_cache()
     # backward: synthetic causal P, dP, p_sink on all rows
@@ -150,7 +150,7 @@ def test_config5_full_size_sampled():
     ps_np = psin.cpu().numpy()
     dS_o, _ = oracle_rows_bwd(gather_rows(Pin, idx), gather_rows(gin, idx), N,
                               ps_rows=np.ascontiguousarray(ps_np[idx]))
-    assert_bitexact(gather_rows(dS, idx), dS_o, "c5 dS")
+    assert_bitexact(gather_rows(dS, idx), dS_o, "causal dS")
     # d_sink for two heads needs every row of those heads
     dsk_np = dsk.cpu().numpy()
     for h in (0, H - 1):
@@ -159,7 +159,7 @@ def test_config5_full_size_sampled():
         _, v_h = oracle.bwd(P_h.reshape(1, 1, S, N), g_h.reshape(1, 1, S, N), 1, 1, S, N,
                             p_sink=np.ascontiguousarray(ps_np[h * S:(h + 1) * S]))
         d_h = oracle.dsink(v_h, 1, 1, S)
-        assert_bitexact(dsk_np[h:h + 1], d_h, f"c5 d_sink[{h}]")
+        assert_bitexact(dsk_np[h:h + 1], d_h, f"causal d_sink[{h}]")
 
 
 def test_composed_chain_condition_scaled():
