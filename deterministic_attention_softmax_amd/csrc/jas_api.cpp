@@ -80,7 +80,8 @@ jas_status_t mask_bytes(const jas_desc_t *d, int64_t *bytes) {
 // Launch geometry: the override when given (checked), else the default.
 // tiles are covered by slots of TPS tiles; a row needs ceil(T/TPS) slots,
 // spread over wpr waves holding cpl slots each.
-jas_status_t choose_geometry(int dtype, int T, int64_t rows, const jas_launch_t *ov, Geometry *g) {
+jas_status_t choose_geometry(int dtype, int T, int64_t rows, bool backward, const jas_launch_t *ov,
+                             Geometry *g) {
   const int tps = jas::tiles_per_slot(dtype);
   const int nslots = (T + tps - 1) / tps;
   int ncpl = 0;
@@ -98,7 +99,7 @@ jas_status_t choose_geometry(int dtype, int T, int64_t rows, const jas_launch_t 
           break;
         }
     } else {
-      wpr = jas::default_wpr(dtype, nslots);
+      wpr = jas::default_wpr(dtype, nslots, backward);
     }
     if (wpr == 0) return JAS_ERR_UNSUPPORTED;
   }
@@ -162,7 +163,7 @@ jas_status_t fwd_impl(const jas_desc_t *d, const void *scores, const float *mask
   if (overlap(rps, rs) || overlap(rps, rm) || overlap(rps, rk)) return JAS_ERR_ALIASING;
 
   Geometry g;
-  st = choose_geometry(d->dtype, dm.T, dm.rows, launch, &g);
+  st = choose_geometry(d->dtype, dm.T, dm.rows, false, launch, &g);
   if (st != JAS_OK) return st;
   jas::FwdArgs a;
   a.scores = scores;
@@ -228,7 +229,7 @@ jas_status_t bwd_impl(const jas_desc_t *d, const void *probs, const void *dprobs
   if (overlap(rw, rp) || overlap(rw, rg) || overlap(rw, rps)) return JAS_ERR_ALIASING;
 
   Geometry g;
-  st = choose_geometry(d->dtype, dm.T, dm.rows, launch, &g);
+  st = choose_geometry(d->dtype, dm.T, dm.rows, true, launch, &g);
   if (st != JAS_OK) return st;
 
   {

@@ -63,7 +63,7 @@ inline int keys_per_chunk(int dtype) { return dtype == 1 ? 8 : 4; }
 inline int tiles_per_slot(int dtype) { return dtype == 1 ? 2 : 1; }
 
 bool cpl_compiled(int dtype, int wpr, int cpl);
-int default_wpr(int dtype, int nslots);
+int default_wpr(int dtype, int nslots, bool backward);
 const int *compiled_cpls(int dtype, int *count);
 
 hipError_t launch_fwd(int dtype, const FwdArgs &a, const Geometry &g, hipStream_t stream);

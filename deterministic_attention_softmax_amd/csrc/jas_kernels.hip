@@ -330,6 +330,32 @@ __device__ __forceinline__ void store_at(char *base, int j, const Chunk &c) {
   store_chunk(base + (uint32_t)(j * ESZ), c);
 }
 
+// A raw buffer resource over one row (gfx9 family: stride 0, 32-bit
+// records).  Loads at or past `bytes` return 0 and stores there are
+// dropped, which handles the lanes past the row and the spare rows of a
+// workgroup (bytes = 0) without clamps or branches.  The row offset of a
+// slot is wave-uniform and goes in the scalar offset; the lane's offset in
+// the slot is one VGPR shared by all slots.
+constexpr int kBufWord3 = 0x00020000;
+constexpr int kAuxNT = 2;  // nontemporal: the row is streamed once
+
+struct Buf {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ __forceinline__ Buf(const void *base, uint32_t bytes)
+      : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kBufWord3)) {}
+};
+
+template <int AUX>
+__device__ __forceinline__ Chunk bload(const Buf &b, uint32_t voff, uint32_t soff) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(b.r, (int)voff, (int)soff, AUX);
+  return Chunk{{v.x, v.y, v.z, v.w}};
+}
+
+__device__ __forceinline__ void bstore(const Buf &b, uint32_t voff, uint32_t soff, const Chunk &c) {
+  const u32x4 v = {c.w[0], c.w[1], c.w[2], c.w[3]};
+  __builtin_amdgcn_raw_buffer_store_b128(v, b.r, (int)voff, (int)soff, kAuxNT);
+}
+
 // ---------------------------------------------------------------------------
 // Forward
 //
@@ -360,10 +386,14 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void fwd_kernel(const FwdArgs 
   for (int64_t grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
     const int64_t r = grp * ix.rpb + ix.rib;
     const bool active = r < a.s.rows;
-    // a workgroup's spare rows read the last row (valid memory) and write nothing
+    // a workgroup's spare rows read the last row (element-wise path) or see
+    // an empty buffer (VEC), and write nothing
     const int64_t rr = active ? r : a.s.rows - 1;
     const char *srow = static_cast<const char *>(a.scores) + rr * a.s.ld * ESZ;
     char *prow = static_cast<char *>(a.probs) + r * a.s.ld * ESZ;
+    const uint32_t row_bytes = active ? (uint32_t)(N * ESZ) : 0u;
+    const Buf sbuf(srow, row_bytes), pbuf(prow, row_bytes);
+    const uint32_t voff = (uint32_t)(ix.loff * ESZ);
     const float *mrow = nullptr;
     int64_t h = 0;
     if (MASK || has_sink) {
@@ -372,26 +402,28 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void fwd_kernel(const FwdArgs 
       h = bh % a.s.H;
       if constexpr (MASK) mrow = a.mask + (bh / a.s.H) * a.msb + h * a.msh + q * a.msq;
     }
+    const Buf mbuf(mrow, MASK ? row_bytes * (4 / ESZ) : 0u);
 
-    // ---- phase 1: issue every score load of the row, straight-line.  VEC:
-    // a slot's lanes past the row (or a slot past the row) read the row's
-    // last chunk, and phase 2 replaces what they read. ----
+    // ---- phase 1: issue every score load of the row, straight-line (VEC:
+    // lanes past the row read 0 and are overwritten in phase 2) ----
     Chunk raw[CPL];
 #pragma unroll
     for (int s = 0; s < CPL; ++s) {
-      const int j0 = (s * WPR + ix.wir) * TPS * kTile + ix.loff;
-      if constexpr (VEC) raw[s] = load_at<ESZ>(srow, min(j0, N - KPL));
-      else raw[s] = load_chunk_elems<DT>(srow, j0, N, kFill);
+      const int sb = (s * WPR + ix.wir) * TPS * kTile;
+      if constexpr (VEC) raw[s] = bload<kAuxNT>(sbuf, voff, (uint32_t)(sb * ESZ));
+      else raw[s] = load_chunk_elems<DT>(srow, sb + ix.loff, N, kFill);
     }
 
     // ---- phase 2: per tile max, exponentials, sum ----
     float e[CPL][KPL];
     float4 mv[2][KPL / 4];  // mask of the current and the next slot
     auto load_mask = [&](int s, float4 (&dst)[KPL / 4]) {
-      const int j = min((s * WPR + ix.wir) * TPS * kTile + ix.loff, N - KPL);
+      const uint32_t sb4 = (uint32_t)((s * WPR + ix.wir) * TPS * kTile * 4);
 #pragma unroll
-      for (int k4 = 0; k4 < KPL / 4; ++k4)
-        dst[k4] = *reinterpret_cast<const float4 *>(mrow + j + 4 * k4);
+      for (int k4 = 0; k4 < KPL / 4; ++k4) {
+        const Chunk c = bload<0>(mbuf, (uint32_t)(ix.loff * 4 + 16 * k4), sb4);
+        dst[k4] = make_float4(u2f(c.w[0]), u2f(c.w[1]), u2f(c.w[2]), u2f(c.w[3]));
+      }
     };
     if constexpr (MASK && VEC) load_mask(0, mv[0]);
 #pragma unroll
@@ -498,11 +530,8 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void fwd_kernel(const FwdArgs 
 #pragma unroll
           for (int k = 0; k < KPL; ++k) p[k] = e[s][k] * cs;
           const Chunk out = pack<DT>(p);
-          if constexpr (VEC) {
-            if (sb + TPS * kTile <= N || j0 < N) store_at<ESZ>(prow, j0, out);
-          } else {
-            store_chunk_elems<DT>(prow, j0, N, out);
-          }
+          if constexpr (VEC) bstore(pbuf, voff, (uint32_t)(sb * ESZ), out);
+          else store_chunk_elems<DT>(prow, j0, N, out);
         }
       }
       if (has_sink && ix.wir == 0 && lane == 0)
@@ -535,41 +564,33 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void bwd_kernel(const BwdArgs 
   for (int64_t grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
     const int64_t r = grp * ix.rpb + ix.rib;
     const bool active = r < a.s.rows;
-    const int64_t rr = active ? r : a.s.rows - 1;  // spare rows read the last row
+    const int64_t rr = active ? r : a.s.rows - 1;  // spare rows (element-wise path)
     const char *prow = static_cast<const char *>(a.probs) + rr * a.s.ld * ESZ;
     const char *grow = static_cast<const char *>(a.dprobs) + rr * a.s.ld * ESZ;
     char *drow = static_cast<char *>(a.dscores) + r * a.s.ld * ESZ;
+    const uint32_t row_bytes = active ? (uint32_t)(N * ESZ) : 0u;
+    const Buf pbuf(prow, row_bytes), gbuf(grow, row_bytes), dbuf(drow, row_bytes);
+    const uint32_t voff = (uint32_t)(ix.loff * ESZ);
 
-    // ---- phase 1: issue every load of the row, straight-line ----
+    // ---- phase 1: issue every load of the row, straight-line; keys past
+    // the row read as +0 ----
     Chunk rp[CPL], rg[CPL];
 #pragma unroll
     for (int s = 0; s < CPL; ++s) {
-      const int j0 = (s * WPR + ix.wir) * TPS * kTile + ix.loff;
+      const int sb = (s * WPR + ix.wir) * TPS * kTile;
       if constexpr (VEC) {
-        rp[s] = load_at<ESZ>(prow, min(j0, N - KPL));
-        rg[s] = load_at<ESZ>(grow, min(j0, N - KPL));
-      } else {  // keys past the row read as +0
-        rp[s] = load_chunk_elems<DT>(prow, j0, N, 0u);
-        rg[s] = load_chunk_elems<DT>(grow, j0, N, 0u);
+        rp[s] = bload<kAuxNT>(pbuf, voff, (uint32_t)(sb * ESZ));
+        rg[s] = bload<kAuxNT>(gbuf, voff, (uint32_t)(sb * ESZ));
+      } else {
+        rp[s] = load_chunk_elems<DT>(prow, sb + ix.loff, N, 0u);
+        rg[s] = load_chunk_elems<DT>(grow, sb + ix.loff, N, 0u);
       }
     }
 
     // ---- phase 2: tile sums of P*dP; keys past the row count as +0 ----
 #pragma unroll
     for (int s = 0; s < CPL; ++s) {
-      const int gs = s * WPR + ix.wir;
-      const int sb = gs * TPS * kTile;
-      const int t = gs * TPS + ix.half;
-      if constexpr (VEC) {
-        if (sb + TPS * kTile > N) {  // a slot reaching past the row (uniform)
-          const bool inb = sb + ix.loff < N;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            rp[s].w[i] = inb ? rp[s].w[i] : 0u;
-            rg[s].w[i] = inb ? rg[s].w[i] : 0u;
-          }
-        }
-      }
+      const int t = (s * WPR + ix.wir) * TPS + ix.half;
       float p[KPL], g[KPL], pg[KPL];
       unpack<DT>(rp[s], p);
       unpack<DT>(rg[s], g);
@@ -601,11 +622,8 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void bwd_kernel(const BwdArgs 
             ds[k] = p[k] * gd;
           }
           const Chunk out = pack<DT>(ds);
-          if constexpr (VEC) {
-            if (sb + TPS * kTile <= N || j0 < N) store_at<ESZ>(drow, j0, out);
-          } else {
-            store_chunk_elems<DT>(drow, j0, N, out);
-          }
+          if constexpr (VEC) bstore(dbuf, voff, (uint32_t)(sb * ESZ), out);
+          else store_chunk_elems<DT>(drow, j0, N, out);
         }
       }
       if (has_sink && ix.wir == 0 && lane == 0) a.v[r] = -(a.p_sink[r] * delta);
@@ -762,17 +780,19 @@ bool cpl_compiled(int dtype, int wpr, int cpl) {
 
 // Default waves per row for a row of `nslots` wave-wide chunks (the
 // chunks-per-lane size then is the smallest compiled one that covers the
-// row).  Measured on MI355X: a bf16 row of up to 9 slots (4,608 keys) runs
-// fastest on one wavefront, longer rows on four wavefronts of at most 5
-// slots each until 20 slots, then four of 9; fp32 rows are twice as many
-// slots for the same registers.  Any choice gives the same bits.
-int default_wpr(int dtype, int nslots) {
-  const int one = dtype == 1 ? 9 : 17;   // largest single-wave share
-  const int four = dtype == 1 ? 20 : 36; // four waves of <= 5 (bf16) / 9 (fp32) slots
-  if (nslots <= one) return 1;
-  if (nslots <= four) return 4;
-  if (nslots <= 4 * (dtype == 1 ? 9 : 17)) return 4;
-  return 0;
+// row).  Measured on MI355X, bf16 (fp32 rows are twice as many slots for the
+// same keys and registers): the forward runs fastest with one wavefront per
+// row up to 9 slots (4,608 keys), two up to 18, four beyond; the backward,
+// which keeps two inputs in registers, with one wavefront up to 4 slots and
+// four beyond.  Any choice gives the same bits.
+int default_wpr(int dtype, int nslots, bool backward) {
+  const int u = dtype == 1 ? 1 : 2;  // slots per bf16-slot of keys
+  const int cap = 4 * (dtype == 1 ? 9 : 17);
+  if (nslots > cap) return 0;
+  if (backward) return nslots <= 4 * u ? 1 : 4;
+  if (nslots <= 9 * u) return 1;
+  if (nslots <= 18 * u) return 2;
+  return 4;
 }
 
 hipError_t launch_fwd(int dtype, const FwdArgs &a, const Geometry &g, hipStream_t st) {
