@@ -43,10 +43,11 @@ def lib():
         L = ctypes.CDLL(_LIB_PATH)
         L.jas_oracle_fwd.restype = ctypes.c_int
         L.jas_oracle_fwd.argtypes = [ctypes.c_int, _I64, _I64, _I64, _I64, _I64, _VP, _VP,
-                                     _I64, _I64, _I64, _VP, _VP, _VP, ctypes.c_int]
+                                     _I64, _I64, _I64, ctypes.c_int, _VP, _VP, _VP, _VP,
+                                     ctypes.c_int]
         L.jas_oracle_bwd.restype = ctypes.c_int
-        L.jas_oracle_bwd.argtypes = [ctypes.c_int, _I64, _I64, _I64, _I64, _I64, _VP, _VP, _VP,
-                                     _VP, _VP, ctypes.c_int]
+        L.jas_oracle_bwd.argtypes = [ctypes.c_int, _I64, _I64, _I64, _I64, _I64, _VP, _VP,
+                                     ctypes.c_int, _VP, _VP, _VP, _VP, ctypes.c_int]
         L.jas_oracle_dsink.restype = ctypes.c_int
         L.jas_oracle_dsink.argtypes = [_I64, _I64, _I64, _VP, _VP]
         L.jas_oracle_exp.restype = ctypes.c_float
@@ -73,12 +74,23 @@ def _dtype_code(a: np.ndarray) -> int:
     raise TypeError(f"scores must be float32 or uint16 (bf16 bits), got {a.dtype}")
 
 
+def _key_len(key_len, B):
+    if key_len is None:
+        return None
+    k = np.ascontiguousarray(key_len, dtype=np.int32)
+    if k.size < B:
+        raise ValueError("key_len needs one value per batch entry")
+    return k
+
+
 def fwd(scores, B, H, Sq, N, ld=None, mask=None, mask_strides=(0, 0, 0), sink=None,
-        threads=None):
+        threads=None, causal=False, key_len=None):
     """Forward pass.  ``scores`` is a C-contiguous array holding B*H*Sq rows of
-    stride ``ld`` (default N).  Returns ``(P, p_sink)``; ``P`` has the layout
-    and dtype of ``scores`` (row padding past N is left zero) and ``p_sink`` is
-    float32 [B*H*Sq] or None when no sink is given."""
+    stride ``ld`` (default N).  ``causal`` excludes keys past the causal
+    condition, ``key_len`` (int32 [B]) keys past each batch entry's length.
+    Returns ``(P, p_sink)``; ``P`` has the layout and dtype of ``scores`` (row
+    padding past N is left zero) and ``p_sink`` is float32 [B*H*Sq] or None
+    when no sink is given."""
     scores = np.ascontiguousarray(scores)
     ld = N if ld is None else ld
     rows = B * H * Sq
@@ -93,17 +105,19 @@ def fwd(scores, B, H, Sq, N, ld=None, mask=None, mask_strides=(0, 0, 0), sink=No
             raise ValueError("sink needs one value per head")
     ps = np.zeros(rows, np.float32) if sink is not None else None
     msb, msh, msq = mask_strides
+    kl = _key_len(key_len, B)
     rc = lib().jas_oracle_fwd(_dtype_code(scores), B, H, Sq, N, ld, _ptr(scores), _ptr(mask),
-                              msb, msh, msq, _ptr(sink), _ptr(P), _ptr(ps),
-                              threads or default_threads())
+                              msb, msh, msq, int(bool(causal)), _ptr(kl), _ptr(sink), _ptr(P),
+                              _ptr(ps), threads or default_threads())
     if rc != 0:
         raise RuntimeError(f"jas_oracle_fwd failed: {rc}")
     return P, ps
 
 
-def bwd(P, dP, B, H, Sq, N, ld=None, p_sink=None, threads=None):
-    """Backward pass on stored probabilities.  Returns ``(dS, v)`` where ``v``
-    is the float32 per-row d_sink share (None without ``p_sink``)."""
+def bwd(P, dP, B, H, Sq, N, ld=None, p_sink=None, threads=None, causal=False, key_len=None):
+    """Backward pass on stored probabilities (P taken as +0 on keys the
+    ``causal`` / ``key_len`` exclusion removes).  Returns ``(dS, v)`` where
+    ``v`` is the float32 per-row d_sink share (None without ``p_sink``)."""
     P = np.ascontiguousarray(P)
     dP = np.ascontiguousarray(dP)
     if P.dtype != dP.dtype or P.shape != dP.shape:
@@ -115,8 +129,10 @@ def bwd(P, dP, B, H, Sq, N, ld=None, p_sink=None, threads=None):
     if p_sink is not None:
         p_sink = np.ascontiguousarray(p_sink, dtype=np.float32)
         v = np.zeros(rows, np.float32)
-    rc = lib().jas_oracle_bwd(_dtype_code(P), B, H, Sq, N, ld, _ptr(P), _ptr(dP), _ptr(p_sink),
-                              _ptr(dS), _ptr(v), threads or default_threads())
+    kl = _key_len(key_len, B)
+    rc = lib().jas_oracle_bwd(_dtype_code(P), B, H, Sq, N, ld, _ptr(P), _ptr(dP),
+                              int(bool(causal)), _ptr(kl), _ptr(p_sink), _ptr(dS), _ptr(v),
+                              threads or default_threads())
     if rc != 0:
         raise RuntimeError(f"jas_oracle_bwd failed: {rc}")
     return dS, v

@@ -179,9 +179,11 @@ static void merge(float *M, float *L, float m, float l) {
 
 /* One row of N keys.  `s` is the row of scores (dtype dt), `a` the additive
    mask row (binary32, may be NULL), `sigma` the head's sink logit when
-   has_sink.  Writes the row of probabilities and, with a sink, the sink's
-   own probability.  Scratch buffers are supplied by the caller. */
-static void fwd_row(int dt, int64_t N, const void *s, const float *a,
+   has_sink.  Keys at or past `kend` are excluded (causal or key-length
+   exclusion): they count as a score of -inf and are not read.  Writes the
+   row of probabilities and, with a sink, the sink's own probability.
+   Scratch buffers are supplied by the caller. */
+static void fwd_row(int dt, int64_t N, int64_t kend, const void *s, const float *a,
                     int has_sink, float sigma, void *P, float *p_sink,
                     float *x, float *e, float *m, float *l) {
   const int64_t T = (N + TILE - 1) / TILE;
@@ -189,6 +191,10 @@ static void fwd_row(int dt, int64_t N, const void *s, const float *a,
 
   /* scores to binary32 (exact), then the additive mask, one rounding */
   for (int64_t j = 0; j < N; ++j) {
+    if (j >= kend) {
+      x[j] = -INFINITY;
+      continue;
+    }
     x[j] = load_elem(dt, s, j);
     if (a) x[j] = x[j] + a[j];
   }
@@ -240,9 +246,16 @@ static void fwd_row(int dt, int64_t N, const void *s, const float *a,
 
 /* One row: delta is the fixed-order sum of P*dP (same tiles and tree as the
    forward, tiles folded left to right starting from the first tile's sum),
-   then dS = P * (dP - delta) ([P1] Fixed-order backward).  With a sink the
-   row's share of d_sink, -p_sink*delta, is written to *v. */
-static void bwd_row(int dt, int64_t N, const void *P, const void *dP,
+   then dS = P * (dP - delta) ([P1] Fixed-order backward).  Keys at or past
+   `kend` are excluded keys, whose probability the forward wrote as +0: P is
+   taken as +0 there without being read (dP still is, so dS keeps its signed
+   zero).  With a sink the row's share of d_sink, -p_sink*delta, is written
+   to *v. */
+static float p_at(int dt, const void *P, int64_t j, int64_t kend) {
+  return (j < kend) ? load_elem(dt, P, j) : 0.0f;
+}
+
+static void bwd_row(int dt, int64_t N, int64_t kend, const void *P, const void *dP,
                     int has_sink, float ps, void *dS, float *v) {
   const int64_t T = (N + TILE - 1) / TILE;
   float buf[TILE];
@@ -250,17 +263,35 @@ static void bwd_row(int dt, int64_t N, const void *P, const void *dP,
   for (int64_t t = 0; t < T; ++t) {
     for (int i = 0; i < TILE; ++i) {
       int64_t j = t * TILE + i;
-      buf[i] = (j < N) ? load_elem(dt, P, j) * load_elem(dt, dP, j) : 0.0f;
+      buf[i] = (j < N) ? p_at(dt, P, j, kend) * load_elem(dt, dP, j) : 0.0f;
     }
     float d = tree_sum256(buf);
     delta = (t == 0) ? d : delta + d;
   }
   for (int64_t j = 0; j < N; ++j) {
-    float p = load_elem(dt, P, j);
+    float p = p_at(dt, P, j, kend);
     float g = load_elem(dt, dP, j);
     store_elem(dt, dS, j, p * (g - delta));
   }
   if (has_sink && v) *v = -(ps * delta);
+}
+
+/* Valid key prefix of row (b, q): all N keys, cut by the causal condition
+   key <= N - Sq + q ([P3] Prefill / Decode: key_index <= Skv - Sq +
+   query_index) and by the batch entry's valid key length (key padding,
+   [P3] Path Status), clamped to [0, N]. */
+static int64_t row_kend(int64_t N, int64_t Sq, int64_t b, int64_t q, int causal,
+                        const int32_t *key_len) {
+  int64_t kend = N;
+  if (causal) {
+    int64_t c = q + (N - Sq) + 1;
+    if (c < kend) kend = c;
+  }
+  if (key_len) {
+    int64_t k = key_len[b];
+    if (k < kend) kend = k;
+  }
+  return kend < 0 ? 0 : kend;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -275,6 +306,8 @@ typedef struct {
   const float *mask;    /* fwd only, may be NULL */
   int64_t msb, msh, msq;
   const float *sink;    /* fwd: [H] sink logits     bwd: [rows] p_sink */
+  int causal;           /* exclude keys past the causal condition */
+  const int32_t *key_len; /* [B] valid keys per batch entry, or NULL */
   void *out;            /* fwd: P           bwd: dS      */
   float *out_row;       /* fwd: p_sink[rows]  bwd: v[rows] (may be NULL) */
   int64_t r0, r1;
@@ -303,7 +336,8 @@ static void *fwd_worker(void *arg) {
     int has_sink = j->sink != NULL;
     float sigma = has_sink ? j->sink[h] : 0.0f;  /* one value per head ([P2]) */
     float *ps = has_sink ? &j->out_row[r] : NULL;
-    fwd_row(j->dt, N, srow, arow, has_sink, sigma, prow, ps, x, e, m, l);
+    int64_t kend = row_kend(N, j->Sq, b, q, j->causal, j->key_len);
+    fwd_row(j->dt, N, kend, srow, arow, has_sink, sigma, prow, ps, x, e, m, l);
   }
   free(x); free(e); free(m); free(l);
   j->status = 0;
@@ -315,13 +349,16 @@ static void *bwd_worker(void *arg) {
   ieee_env();
   const size_t es = (j->dt == DT_BF16) ? 2 : 4;
   for (int64_t r = j->r0; r < j->r1; ++r) {
+    int64_t q = r % j->Sq;
+    int64_t b = r / (j->Sq * j->H);
+    int64_t kend = row_kend(j->N, j->Sq, b, q, j->causal, j->key_len);
     const char *prow = (const char *)j->in0 + (size_t)(r * j->ld) * es;
     const char *grow = (const char *)j->in1 + (size_t)(r * j->ld) * es;
     char *drow = (char *)j->out + (size_t)(r * j->ld) * es;
     int has_sink = j->sink != NULL;
     float ps = has_sink ? j->sink[r] : 0.0f;
     float *v = (has_sink && j->out_row) ? &j->out_row[r] : NULL;
-    bwd_row(j->dt, j->N, prow, grow, has_sink, ps, drow, v);
+    bwd_row(j->dt, j->N, kend, prow, grow, has_sink, ps, drow, v);
   }
   j->status = 0;
   return NULL;
@@ -359,13 +396,15 @@ static int run_jobs(job_t *proto, int64_t rows, int threads, void *(*fn)(void *)
 /* ------------------------------------------------------------------------ */
 
 /* Forward over scores [B, H, Sq, N] (row stride ld elements).  mask: binary32,
-   element (b,h,q,k) at mask[b*msb + h*msh + q*msq + k], or NULL.  sink:
-   binary32 [H] or NULL.  probs: same layout as scores.  p_sink: binary32
-   [B*H*Sq], written when sink is given.  Returns 0 on success. */
+   element (b,h,q,k) at mask[b*msb + h*msh + q*msq + k], or NULL.  causal:
+   exclude keys past the causal condition.  key_len: int32 [B] valid keys per
+   batch entry, or NULL.  sink: binary32 [H] or NULL.  probs: same layout as
+   scores.  p_sink: binary32 [B*H*Sq], written when sink is given.  Returns 0
+   on success. */
 int jas_oracle_fwd(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t N, int64_t ld,
                    const void *scores, const float *mask, int64_t msb, int64_t msh,
-                   int64_t msq, const float *sink, void *probs, float *p_sink,
-                   int threads) {
+                   int64_t msq, int causal, const int32_t *key_len, const float *sink,
+                   void *probs, float *p_sink, int threads) {
   if ((dtype != DT_F32 && dtype != DT_BF16) || B < 0 || H < 0 || Sq < 0 || N < 1 || ld < N)
     return -2;
   if (sink && !p_sink) return -3;
@@ -376,15 +415,17 @@ int jas_oracle_fwd(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t N, int64
   j.dt = dtype; j.B = B; j.H = H; j.Sq = Sq; j.N = N; j.ld = ld;
   j.in0 = scores; j.mask = mask; j.msb = msb; j.msh = msh; j.msq = msq;
   j.sink = sink; j.out = probs; j.out_row = p_sink;
+  j.causal = causal; j.key_len = key_len;
   return run_jobs(&j, rows, threads, fwd_worker);
 }
 
-/* Backward over probs/dprobs [B, H, Sq, N] (row stride ld).  p_sink: [rows]
+/* Backward over probs/dprobs [B, H, Sq, N] (row stride ld).  causal and
+   key_len as for the forward (excluded keys: P taken as +0).  p_sink: [rows]
    or NULL.  dscores: same layout.  v: [rows] per-row d_sink share, written
    when p_sink and v are both given. */
 int jas_oracle_bwd(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t N, int64_t ld,
-                   const void *probs, const void *dprobs, const float *p_sink,
-                   void *dscores, float *v, int threads) {
+                   const void *probs, const void *dprobs, int causal, const int32_t *key_len,
+                   const float *p_sink, void *dscores, float *v, int threads) {
   if ((dtype != DT_F32 && dtype != DT_BF16) || B < 0 || H < 0 || Sq < 0 || N < 1 || ld < N)
     return -2;
   int64_t rows = B * H * Sq;
@@ -393,6 +434,7 @@ int jas_oracle_bwd(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t N, int64
   memset(&j, 0, sizeof j);
   j.dt = dtype; j.B = B; j.H = H; j.Sq = Sq; j.N = N; j.ld = ld;
   j.in0 = probs; j.in1 = dprobs; j.sink = p_sink; j.out = dscores; j.out_row = v;
+  j.causal = causal; j.key_len = key_len;
   return run_jobs(&j, rows, threads, bwd_worker);
 }
 
