@@ -11,7 +11,13 @@ per-kernel HIP-event durations, the roofline fraction of the dominant kernel
 against MI355X's 8 TB/s, and the CPU oracle timed on a bounded sample of the
 same rows on this host's cores.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload joint4352|rows4352|causal8192]
+Other workloads: joint4352_keylen (the padding as key lengths, padded keys
+not read), rows4352 (forward only), causal8192 (causal scores, -inf above the
+diagonal, read like any other key) and causal8192_skip (the same scores with
+the causal flag: nothing above the diagonal is read).  With keys excluded,
+the algorithmic bytes count the scores and P of the visible keys only.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
 import argparse
 import json
@@ -29,14 +35,34 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "fwd+bwd softmax HBM GB/s and rows/s (bf16, 4,352 keys) vs 8 TB/s roofline"
 
 WORKLOADS = {
-    # name: (description, B, H, S, N, dtype, mask, sink, causal, backward)
+    # name: (description, B, H, S, N, dtype, mask, sink, exclusion, backward); exclusion is
+    # None (every key read), "causal" (JAS_FLAG_CAUSAL) or "key_len" (JAS_FLAG_KEY_LEN)
     "joint4352": ("joint image+text attention scores bf16 [1,24,4352,4352], per-batch text padding mask, fwd+bwd",
-           1, 24, 4352, 4352, "bf16", True, False, False, True),
+           1, 24, 4352, 4352, "bf16", True, False, None, True),
+    "joint4352_keylen": ("joint image+text attention scores bf16 [1,24,4352,4352], text padding as per-batch "
+                         "key lengths (keys past them not read), fwd+bwd",
+           1, 24, 4352, 4352, "bf16", False, False, "key_len", True),
     "rows4352": ("bf16 scores 16384 rows x 4352 keys, N(0,1) with x8 outliers on 0.1%, fwd only",
-           1, 1, 16384, 4352, "bf16", False, False, False, False),
-    "causal8192": ("causal self-attention scores bf16 [1,32,8192,8192] + per-head sink, fwd+bwd",
-           1, 32, 8192, 8192, "bf16", False, True, True, True),
+           1, 1, 16384, 4352, "bf16", False, False, None, False),
+    "causal8192": ("causal self-attention scores bf16 [1,32,8192,8192] + per-head sink, -inf scores above "
+                   "the diagonal read like any other, fwd+bwd",
+           1, 32, 8192, 8192, "bf16", False, True, None, True),
+    "causal8192_skip": ("causal self-attention scores bf16 [1,32,8192,8192] + per-head sink, causal flag "
+                        "(scores and P above the diagonal not read), fwd+bwd",
+           1, 32, 8192, 8192, "bf16", False, True, "causal", True),
 }
+
+
+def row_kends(wl, key_len):
+    """Visible keys of every row (int64 [B*H*S]): the causal condition
+    key <= N - S + q and the batch entry's key length, clamped to [0, N]."""
+    _, B, H, S, N, _, _, _, excl, _ = WORKLOADS[wl]
+    k = np.full((B, H, S), N, np.int64)
+    if excl == "causal":
+        k = np.minimum(k, (np.arange(S) + (N - S) + 1)[None, None, :])
+    if excl == "key_len":
+        k = np.minimum(k, np.asarray(key_len, np.int64)[:, None, None])
+    return np.clip(k, 0, N).reshape(-1)
 
 
 KERNEL_SOURCE = os.path.join(ROOT, "deterministic_attention_softmax_amd", "csrc", "jas_kernels.hip")
@@ -89,34 +115,50 @@ def log(msg):
 def make_inputs(wl, dev):
     import torch
     import synth
-    _, B, H, S, N, dt, has_mask, has_sink, causal, _ = WORKLOADS[wl]
-    mask = sink = g = None
-    if wl == "joint4352":
-        s, mask, g, _ = synth.joint_attention_bf16(seed=3, device=dev, B=B, H=H, S=S, N=N)
+    _, B, H, S, N, dt, has_mask, has_sink, excl, _ = WORKLOADS[wl]
+    mask = sink = g = key_len = None
+    if wl.startswith("joint4352"):
+        s, mask, g, pads = synth.joint_attention_bf16(seed=3, device=dev, B=B, H=H, S=S, N=N)
         mask = mask.view(B, 1, 1, N)
+        if excl == "key_len":
+            mask = None
+            key_len = torch.tensor([N - p for p in pads], dtype=torch.int32, device=dev)
     elif wl == "rows4352":
         s = synth.rows_with_outliers_bf16(seed=2, device=dev, rows=S, N=N)
     else:
         s, sink, g = synth.causal_sink_bf16(seed=5, device=dev, B=B, H=H, S=S)
-    return s, mask, sink, g
+    return s, mask, sink, g, key_len
 
 
-def check_parity(wl, s, mask, sink, g):
+def oracle_row_mask(wl, mask, kend, idx):
+    """fp32 [k, N] additive mask for rows `idx` handed to the oracle as
+    independent rows: the workload's mask row plus -inf past the row's
+    visible keys (the oracle treats an excluded key exactly as a -inf one)."""
+    _, B, H, S, N, _, _, _, excl, _ = WORKLOADS[wl]
+    m = np.zeros((len(idx), N), np.float32)
+    if mask is not None:
+        m += mask.reshape(B, N).cpu().numpy()[idx // (H * S)]
+    if excl is not None:
+        m[np.arange(N)[None, :] >= kend[idx][:, None]] = -np.inf
+    return m
+
+
+def check_parity(wl, s, mask, sink, g, key_len):
     """Sampled rows against the oracle before timing (forward within 1 bf16
     ulp; backward stage-isolated on the oracle's P, bit-exact)."""
     import torch
     import deterministic_attention_softmax_amd as jas
     import oracle
     import synth
-    _, B, H, S, N, _, _, _, _, backward = WORKLOADS[wl]
+    _, B, H, S, N, _, _, _, excl, backward = WORKLOADS[wl]
+    causal = excl == "causal"
     rows = B * H * S
+    kend = row_kends(wl, None if key_len is None else key_len.cpu().numpy())
     idx = np.unique(np.random.default_rng(7).choice(rows, 32, replace=False))
     it = torch.as_tensor(idx, device=s.device)
-    P, ps = jas.fwd(s, mask=mask, sink=sink)
+    P, ps = jas.fwd(s, mask=mask, sink=sink, causal=causal, key_len=key_len)
     s_rows = synth.to_numpy_bits(s.reshape(-1, N).index_select(0, it))
-    m_rows = None
-    if mask is not None:
-        m_rows = np.ascontiguousarray(mask.reshape(B, N).cpu().numpy()[idx // (H * S)])
+    m_rows = oracle_row_mask(wl, mask, kend, idx) if (mask is not None or excl) else None
     sig = None if sink is None else np.ascontiguousarray(sink.cpu().numpy()[(idx // S) % H])
     k = len(idx)
     P_o, ps_o = oracle.fwd(s_rows.reshape(1, k, 1, N), 1, k, 1, N, mask=m_rows,
@@ -126,11 +168,11 @@ def check_parity(wl, s, mask, sink, g):
     assert ulp <= 1, f"forward parity: {ulp} bf16 ulp"
     if not backward:
         return {"fwd_max_ulp": ulp}
-    # backward on the oracle's P at the sampled rows
+    # backward on the oracle's P at the sampled rows (+0 past the visible keys)
     P.reshape(-1, N).index_copy_(0, it, synth.from_numpy_bits(P_o.reshape(k, N), s.device))
     if ps is not None:
         ps[it] = torch.from_numpy(ps_o).to(s.device)
-    dS, _ = jas.bwd(P, g, p_sink=ps)
+    dS, _ = jas.bwd(P, g, p_sink=ps, causal=causal, key_len=key_len)
     g_rows = synth.to_numpy_bits(g.reshape(-1, N).index_select(0, it))
     dS_o, _ = oracle.bwd(P_o, g_rows.reshape(P_o.shape), 1, k, 1, N,
                          p_sink=None if ps is None else ps_o)
@@ -139,39 +181,61 @@ def check_parity(wl, s, mask, sink, g):
     return {"fwd_max_ulp": ulp, "bwd_bitexact": True}
 
 
-def cpu_baseline(wl, s, mask, sink, g, target_s):
-    """The oracle, as it stands, on a bounded sample of the same rows."""
+def cpu_baseline(wl, s, mask, sink, g, key_len, target_s):
+    """The oracle, as it stands, on a bounded sample of the same rows: k rows
+    spread evenly over the whole tensor, each handed to the oracle as its own
+    batch entry (its mask row, and its visible length as that entry's key
+    length when keys are excluded), one oracle call per head so that each
+    call has one sink logit."""
     import oracle
     import synth
-    _, B, H, S, N, _, _, _, _, backward = WORKLOADS[wl]
+    _, B, H, S, N, _, _, _, excl, backward = WORKLOADS[wl]
     threads = oracle.default_threads()
     esz = 2
+    kend = row_kends(wl, None if key_len is None else key_len.cpu().numpy())
+    m_all = None if mask is None else mask.reshape(B, N).cpu().numpy()
+    sk_all = None if sink is None else sink.cpu().numpy()
+    s2, g2 = s.reshape(-1, N), (g.reshape(-1, N) if backward else None)
 
     def run(k):
-        rows = np.arange(k)
-        s_rows = synth.to_numpy_bits(s.reshape(-1, N)[:k])
-        m_rows = None if mask is None else np.ascontiguousarray(
-            mask.reshape(B, N).cpu().numpy()[rows // (H * S)])
-        sig = None if sink is None else np.ascontiguousarray(sink.cpu().numpy()[(rows // S) % H])
-        g_rows = synth.to_numpy_bits(g.reshape(-1, N)[:k]) if backward else None
-        t0 = time.perf_counter()
-        P, ps = oracle.fwd(s_rows.reshape(1, k, 1, N), 1, k, 1, N, mask=m_rows,
-                           mask_strides=(0, N, 0), sink=sig, threads=threads)
-        if backward:
-            oracle.bwd(P, g_rows.reshape(P.shape), 1, k, 1, N, p_sink=ps, threads=threads)
-        return time.perf_counter() - t0
+        rows = np.unique(np.linspace(0, B * H * S - 1, k).round().astype(np.int64))
+        heads = (rows // S) % H
+        t = 0.0
+        for h in np.unique(heads):
+            r = rows[heads == h]
+            n = len(r)
+            it = torch_index(r, s.device)
+            s_rows = synth.to_numpy_bits(s2.index_select(0, it))
+            g_rows = synth.to_numpy_bits(g2.index_select(0, it)) if backward else None
+            m_rows = None if m_all is None else np.ascontiguousarray(m_all[r // (H * S)])
+            sig = None if sk_all is None else sk_all[h:h + 1]
+            kl = None if excl is None else np.ascontiguousarray(kend[r].astype(np.int32))
+            t0 = time.perf_counter()
+            P, ps = oracle.fwd(s_rows.reshape(n, 1, 1, N), n, 1, 1, N, mask=m_rows,
+                               mask_strides=(N, 0, 0), sink=sig, threads=threads, key_len=kl)
+            if backward:
+                oracle.bwd(P, g_rows.reshape(P.shape), n, 1, 1, N, p_sink=ps, threads=threads,
+                           key_len=kl)
+            t += time.perf_counter() - t0
+        vis = int(kend[rows].sum())
+        nbytes = esz * (vis + len(rows) * N) + (esz * (vis + 2 * len(rows) * N) if backward else 0)
+        return t, len(rows), nbytes
 
-    k0 = min(256, B * H * S)
-    t0 = run(k0)
+    k0 = min(512, B * H * S)
+    t0, _, _ = run(k0)
     k = int(min(B * H * S, max(k0, k0 * target_s / max(t0, 1e-3))))
-    t = run(k)
-    per_elem = (5 if backward else 2) * esz
+    t, k, nbytes = run(k)
     return {
-        "value": round(k * N * per_elem / t / 1e9, 4), "unit": "GB/s",
+        "value": round(nbytes / t / 1e9, 4), "unit": "GB/s",
         "rows_per_s": round(k / t, 1), "cores": threads, "kind": "oracle",
-        "sample": f"first {k} rows of the same workload ({k * N} elements), "
-                  f"{'fwd+bwd' if backward else 'fwd'}, {t:.1f} s wall",
+        "sample": f"{k} rows spread evenly over the whole workload ({k * N} elements), "
+                  f"{'fwd+bwd' if backward else 'fwd'}, {t:.1f} s of oracle time",
     }
+
+
+def torch_index(idx, device):
+    import torch
+    return torch.as_tensor(idx, device=device)
 
 
 def copy_ceiling(nbytes, stream, steps=10):
@@ -270,7 +334,8 @@ def summarize_profiles(prof_dir, wl):
     copy_bytes = line_pmc["copy_ceiling"]["bytes"] / 2  # read = written = half the moved bytes
     fac = {c: copy_bytes / np.mean(counters[("copy", c)]) for c in ("FETCH_SIZE", "WRITE_SIZE")}
     E = WORKLOADS[wl][1] * WORKLOADS[wl][2] * WORKLOADS[wl][3] * WORKLOADS[wl][4]
-    alg = {"fwd": (2 * E, 2 * E), "bwd": (4 * E, 2 * E)}
+    V = int(line_pmc["config"].get("visible_keys", E))  # keys read of scores / P
+    alg = {"fwd": (2 * V, 2 * E), "bwd": (2 * V + 2 * E, 2 * E)}
     rec = {"workload": wl, "kernel_source_sha256": kernel_source_hash(),
            "calibration": {"copy_bytes_read": copy_bytes, "copy_bytes_written": copy_bytes,
                            "fetch_factor": round(fac["FETCH_SIZE"], 4),
@@ -300,7 +365,8 @@ def summarize_profiles(prof_dir, wl):
         md.append(f"| jas {kind} | {len(counters[(kind, 'FETCH_SIZE')])} | {rd / 1e6:.1f} | "
                   f"{wr / 1e6:.1f} | {ar / 1e6:.1f} | {aw / 1e6:.1f} | {(rd + wr) / (ar + aw):.4f} |")
     md += ["", "Algorithmic bytes: forward reads the scores and writes P (2 bytes each per "
-           "element), backward reads P and dP and writes dS; the per-row sink values (4 bytes "
+           "element), backward reads P and dP and writes dS; with keys excluded, scores and P "
+           f"count on the {V} visible keys only; the per-row sink values (4 bytes "
            "per row, written and read as one scattered word per row) and the mask row are not "
            "counted there and show as the small excess.", "",
            f"Kernel source sha256 at measurement: `{rec['kernel_source_sha256']}`; bench.py "
@@ -324,16 +390,19 @@ def main():
     jas.lib()  # fail loudly when the HIP library is missing
     dev = torch.device("cuda:0")
     wl = args.workload
-    desc, B, H, S, N, dt, has_mask, has_sink, causal, backward = WORKLOADS[wl]
+    desc, B, H, S, N, dt, has_mask, has_sink, excl, backward = WORKLOADS[wl]
+    causal = excl == "causal"
     rows, E = B * H * S, B * H * S * N
     esz = 2
     log(f"workload {wl}: {desc}")
-    s, mask, sink, g = make_inputs(wl, dev)
+    s, mask, sink, g, key_len = make_inputs(wl, dev)
     torch.cuda.synchronize()
+    # keys each row reads (scores in the forward, P in the backward)
+    V = int(row_kends(wl, None if key_len is None else key_len.cpu().numpy()).sum())
 
     check = None
     if not args.no_check:
-        check = check_parity(wl, s, mask, sink, g)
+        check = check_parity(wl, s, mask, sink, g, key_len)
         log(f"parity check: {check}")
 
     P = torch.empty_like(s)
@@ -346,11 +415,12 @@ def main():
     def step(ev=None):
         if ev:
             ev[0].record(stream)
-        jas.fwd(s, mask=mask, sink=sink, out=P, p_sink=ps)
+        jas.fwd(s, mask=mask, sink=sink, out=P, p_sink=ps, causal=causal, key_len=key_len)
         if ev:
             ev[1].record(stream)
         if backward:
-            jas.bwd(P, g, p_sink=ps, out=dS, d_sink=dsk, workspace=ws)
+            jas.bwd(P, g, p_sink=ps, out=dS, d_sink=dsk, workspace=ws, causal=causal,
+                    key_len=key_len)
         if ev:
             ev[2].record(stream)
 
@@ -374,8 +444,8 @@ def main():
     bwd_ms = np.array([b.elapsed_time(c) for _, b, c in evs]) if backward else np.zeros(1)
     step_ms = wall * 1e3 / args.steps
 
-    fwd_bytes = 2 * esz * E + (E // N * 4 if has_sink else 0)
-    bwd_bytes = 3 * esz * E + (E // N * 12 if has_sink else 0) if backward else 0
+    fwd_bytes = esz * (V + E) + (rows * 4 if has_sink else 0)
+    bwd_bytes = esz * (V + 2 * E) + (rows * 12 if has_sink else 0) if backward else 0
     total_bytes = fwd_bytes + bwd_bytes
     gbs = total_bytes / (step_ms * 1e-3) / 1e9
     fwd_gbs = fwd_bytes / (fwd_ms.mean() * 1e-3) / 1e9
@@ -392,7 +462,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt,
         "data": "synthetic",
         "config": {"workload": desc, "batch": B, "heads": H, "q_rows": S, "keys": N,
-                   "rows": rows, "mask": has_mask, "sink": has_sink, "backward": backward},
+                   "rows": rows, "mask": has_mask, "sink": has_sink, "exclusion": excl,
+                   "visible_keys": V, "backward": backward},
         "rows_per_s": round(rows / (step_ms * 1e-3), 1),
         "fwd_ms": round(float(fwd_ms.mean()), 4), "fwd_gbs": round(fwd_gbs, 1),
         "bwd_ms": round(float(bwd_ms.mean()), 4) if backward else None,
@@ -409,7 +480,7 @@ def main():
         out["roofline"]["frac_of_copy"] = round(dom[1] / best, 4)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
-        out["cpu_baseline"] = cpu_baseline(wl, s, mask, sink, g, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(wl, s, mask, sink, g, key_len, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     if args.json_out:
         os.makedirs(os.path.dirname(os.path.abspath(args.json_out)), exist_ok=True)

@@ -13,7 +13,8 @@ import ctypes
 import os
 
 __all__ = [
-    "JAS_DTYPE_F32", "JAS_DTYPE_BF16", "JAS_FLAG_MASK", "JAS_FLAG_SINK", "JAS_MAX_KEYS",
+    "JAS_DTYPE_F32", "JAS_DTYPE_BF16", "JAS_FLAG_MASK", "JAS_FLAG_SINK", "JAS_FLAG_CAUSAL",
+    "JAS_FLAG_KEY_LEN", "JAS_MAX_KEYS",
     "STATUS", "JasError", "jas_desc_t", "jas_launch_t", "lib", "jas_fwd", "jas_fwd_ex",
     "jas_bwd", "jas_bwd_ex", "jas_bwd_workspace_bytes", "jas_status_str", "jas_contract",
     "make_desc", "fwd", "bwd", "LIB_PATH",
@@ -22,7 +23,7 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libjas.so")
 
 JAS_DTYPE_F32, JAS_DTYPE_BF16 = 0, 1
-JAS_FLAG_MASK, JAS_FLAG_SINK = 1, 2
+JAS_FLAG_MASK, JAS_FLAG_SINK, JAS_FLAG_CAUSAL, JAS_FLAG_KEY_LEN = 1, 2, 4, 8
 JAS_MAX_KEYS = 16384
 STATUS = {
     0: "JAS_OK", 1: "JAS_ERR_NULL_POINTER", 2: "JAS_ERR_BAD_SHAPE", 3: "JAS_ERR_BAD_DTYPE",
@@ -67,13 +68,14 @@ def lib():
             raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
         L = ctypes.CDLL(LIB_PATH)
         L.jas_fwd.restype = ctypes.c_int
-        L.jas_fwd.argtypes = [_DP, _VP, _VP, _VP, _VP, _VP, _VP]
+        L.jas_fwd.argtypes = [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]
         L.jas_fwd_ex.restype = ctypes.c_int
-        L.jas_fwd_ex.argtypes = [_DP, _VP, _VP, _VP, _VP, _VP, _LP, _VP]
+        L.jas_fwd_ex.argtypes = [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _LP, _VP]
         L.jas_bwd.restype = ctypes.c_int
-        L.jas_bwd.argtypes = [_DP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]
+        L.jas_bwd.argtypes = [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]
         L.jas_bwd_ex.restype = ctypes.c_int
-        L.jas_bwd_ex.argtypes = [_DP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _LP, _VP]
+        L.jas_bwd_ex.argtypes = [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _LP,
+                                 _VP]
         L.jas_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.jas_bwd_workspace_bytes.argtypes = [_DP]
         L.jas_status_str.restype = ctypes.c_char_p
@@ -86,25 +88,27 @@ def lib():
 
 # ---- the C entry points, one to one -------------------------------------
 
-def jas_fwd(desc, scores, mask, sink, probs, p_sink, stream):
-    return lib().jas_fwd(ctypes.byref(desc), scores, mask, sink, probs, p_sink, stream)
+def jas_fwd(desc, scores, mask, key_len, sink, probs, p_sink, stream):
+    return lib().jas_fwd(ctypes.byref(desc), scores, mask, key_len, sink, probs, p_sink, stream)
 
 
-def jas_fwd_ex(desc, scores, mask, sink, probs, p_sink, launch, stream):
+def jas_fwd_ex(desc, scores, mask, key_len, sink, probs, p_sink, launch, stream):
     lp = ctypes.byref(launch) if launch is not None else None
-    return lib().jas_fwd_ex(ctypes.byref(desc), scores, mask, sink, probs, p_sink, lp, stream)
+    return lib().jas_fwd_ex(ctypes.byref(desc), scores, mask, key_len, sink, probs, p_sink, lp,
+                            stream)
 
 
-def jas_bwd(desc, probs, dprobs, p_sink, dscores, d_sink, workspace, workspace_bytes, stream):
-    return lib().jas_bwd(ctypes.byref(desc), probs, dprobs, p_sink, dscores, d_sink, workspace,
-                         workspace_bytes, stream)
+def jas_bwd(desc, probs, dprobs, key_len, p_sink, dscores, d_sink, workspace, workspace_bytes,
+            stream):
+    return lib().jas_bwd(ctypes.byref(desc), probs, dprobs, key_len, p_sink, dscores, d_sink,
+                         workspace, workspace_bytes, stream)
 
 
-def jas_bwd_ex(desc, probs, dprobs, p_sink, dscores, d_sink, workspace, workspace_bytes, launch,
-               stream):
+def jas_bwd_ex(desc, probs, dprobs, key_len, p_sink, dscores, d_sink, workspace, workspace_bytes,
+               launch, stream):
     lp = ctypes.byref(launch) if launch is not None else None
-    return lib().jas_bwd_ex(ctypes.byref(desc), probs, dprobs, p_sink, dscores, d_sink, workspace,
-                            workspace_bytes, lp, stream)
+    return lib().jas_bwd_ex(ctypes.byref(desc), probs, dprobs, key_len, p_sink, dscores, d_sink,
+                            workspace, workspace_bytes, lp, stream)
 
 
 def jas_bwd_workspace_bytes(desc):
@@ -162,6 +166,8 @@ def _launch(launch):
 
 
 def _shape4(t):
+    if t.device.type != "cuda":
+        raise ValueError(f"tensors must be in device memory, not on {t.device}")
     if t.dim() != 4:
         raise ValueError("tensors are [batch, heads, q_rows, keys]")
     if t.stride(3) != 1 or t.stride(2) < t.shape[3] or t.stride(1) != t.shape[2] * t.stride(2) \
@@ -181,46 +187,85 @@ def _empty_rows_like(t, ld):
 
 
 def _check_out(out, like):
+    if out.device != like.device:
+        raise ValueError("every tensor must be on the scores' device")
     if out.shape != like.shape or out.stride() != like.stride() or out.dtype != like.dtype:
         raise ValueError("the output must have the input's shape, dtype and row stride")
 
 
-def fwd(scores, mask=None, mask_strides=None, sink=None, out=None, p_sink=None, launch=None):
+def _check_vec(t, like, dtype, count, name):
+    """A side tensor (mask, sink, key lengths, per-row or per-head values,
+    workspace): on ``like``'s device, of ``dtype``, contiguous, with at least
+    ``count`` elements.  The library reads these through raw device
+    pointers, so a host tensor or a short one must never reach it."""
+    if t is None:
+        return None
+    if t.device != like.device:
+        raise ValueError(f"{name} must be on the scores' device ({like.device}), not {t.device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, not {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < count:
+        raise ValueError(f"{name} needs at least {count} elements, has {t.numel()}")
+    return t
+
+
+def fwd(scores, mask=None, mask_strides=None, sink=None, out=None, p_sink=None, launch=None,
+        causal=False, key_len=None):
     """Forward on device tensors.  ``scores`` [B,H,Sq,N] bf16/fp32 (rows may
     have a stride ld >= N); ``mask`` fp32 addressed with ``mask_strides``
     (b, h, q) in elements (default: a contiguous [B,H,Sq,N] tensor broadcast
-    by its own zero strides); ``sink`` fp32 [H].  Returns (probs, p_sink)."""
+    by its own zero strides); ``sink`` fp32 [H]; ``causal`` excludes keys past
+    the causal condition; ``key_len`` int32 [B] excludes keys past each batch
+    entry's length.  Returns (probs, p_sink)."""
     import torch
     shape, ld = _shape4(scores)
-    flags = 0
+    B, H, S, N = shape
+    rows = B * H * S
+    key_len = _check_vec(key_len, scores, torch.int32, B, "key_len")
+    flags = (JAS_FLAG_CAUSAL if causal else 0) | (JAS_FLAG_KEY_LEN if key_len is not None else 0)
     if mask is not None:
         flags |= JAS_FLAG_MASK
         if mask_strides is None:
-            m4 = mask.expand(shape[0], shape[1], shape[2], shape[3])
+            m4 = mask.expand(B, H, S, N)
             if m4.stride(3) != 1:
                 raise ValueError("mask keys must be contiguous")
             mask_strides = (m4.stride(0), m4.stride(1), m4.stride(2))
+        if any(int(st) < 0 for st in mask_strides):
+            raise ValueError("mask strides must be non-negative")
+        mask_elems = 0 if rows == 0 else \
+            sum((n - 1) * int(st) for n, st in zip(shape[:3], mask_strides)) + N
+        _check_vec(mask, scores, torch.float32, mask_elems, "mask")
     if sink is not None:
         flags |= JAS_FLAG_SINK
+        _check_vec(sink, scores, torch.float32, H, "sink")
     d = make_desc(shape, _dtype_code(scores), flags, ld, mask_strides or (0, 0, 0))
     if out is None:
         out = _empty_rows_like(scores, ld)
     _check_out(out, scores)
     if sink is not None and p_sink is None:
-        p_sink = torch.empty(shape[0] * shape[1] * shape[2], dtype=torch.float32,
-                             device=scores.device)
-    st = jas_fwd_ex(d, _ptr(scores), _ptr(mask), _ptr(sink), _ptr(out),
+        p_sink = torch.empty(rows, dtype=torch.float32, device=scores.device)
+    if sink is not None:
+        _check_vec(p_sink, scores, torch.float32, rows, "p_sink")
+    st = jas_fwd_ex(d, _ptr(scores), _ptr(mask), _ptr(key_len), _ptr(sink), _ptr(out),
                     _ptr(p_sink) if sink is not None else None, _launch(launch), _stream())
     if st != 0:
         raise JasError(st, "jas_fwd")
     return out, (p_sink if sink is not None else None)
 
 
-def bwd(probs, dprobs, p_sink=None, out=None, d_sink=None, workspace=None, launch=None):
-    """Backward on device tensors.  Returns (dscores, d_sink or None)."""
+def bwd(probs, dprobs, p_sink=None, out=None, d_sink=None, workspace=None, launch=None,
+        causal=False, key_len=None):
+    """Backward on device tensors (``causal`` / ``key_len`` as for the
+    forward: P is taken as +0 on excluded keys).  Returns (dscores, d_sink or
+    None)."""
     import torch
     shape, ld = _shape4(probs)
-    flags = JAS_FLAG_SINK if p_sink is not None else 0
+    B, H, S, N = shape
+    key_len = _check_vec(key_len, probs, torch.int32, B, "key_len")
+    flags = (JAS_FLAG_SINK if p_sink is not None else 0) | (JAS_FLAG_CAUSAL if causal else 0) | \
+        (JAS_FLAG_KEY_LEN if key_len is not None else 0)
     d = make_desc(shape, _dtype_code(probs), flags, ld)
     _check_out(dprobs, probs)
     if out is None:
@@ -228,11 +273,14 @@ def bwd(probs, dprobs, p_sink=None, out=None, d_sink=None, workspace=None, launc
     _check_out(out, probs)
     ws_bytes = jas_bwd_workspace_bytes(d)
     if p_sink is not None:
+        _check_vec(p_sink, probs, torch.float32, B * H * S, "p_sink")
         if d_sink is None:
-            d_sink = torch.empty(shape[1], dtype=torch.float32, device=probs.device)
+            d_sink = torch.empty(H, dtype=torch.float32, device=probs.device)
         if workspace is None:
             workspace = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device=probs.device)
-    st = jas_bwd_ex(d, _ptr(probs), _ptr(dprobs), _ptr(p_sink), _ptr(out),
+        _check_vec(d_sink, probs, torch.float32, H, "d_sink")
+        _check_vec(workspace, probs, torch.uint8, ws_bytes, "workspace")
+    st = jas_bwd_ex(d, _ptr(probs), _ptr(dprobs), _ptr(key_len), _ptr(p_sink), _ptr(out),
                     _ptr(d_sink) if p_sink is not None else None,
                     _ptr(workspace) if p_sink is not None else None,
                     workspace.numel() if workspace is not None else 0, _launch(launch), _stream())

@@ -27,7 +27,8 @@ bool add_ok(int64_t a, int64_t b, int64_t *out) { return !__builtin_add_overflow
 jas_status_t check_desc(const jas_desc_t *d, Dims *dims) {
   if (!d) return JAS_ERR_NULL_POINTER;
   if (d->dtype != JAS_DTYPE_F32 && d->dtype != JAS_DTYPE_BF16) return JAS_ERR_BAD_DTYPE;
-  if (d->flags & ~(uint32_t)(JAS_FLAG_MASK | JAS_FLAG_SINK)) return JAS_ERR_BAD_FLAGS;
+  if (d->flags & ~(uint32_t)(JAS_FLAG_MASK | JAS_FLAG_SINK | JAS_FLAG_CAUSAL | JAS_FLAG_KEY_LEN))
+    return JAS_ERR_BAD_FLAGS;
   if (d->batch < 0 || d->heads < 0 || d->q_rows < 0 || d->keys < 1 || d->ld < d->keys)
     return JAS_ERR_BAD_SHAPE;
   if (d->mask_stride_b < 0 || d->mask_stride_h < 0 || d->mask_stride_q < 0)
@@ -129,23 +130,24 @@ jas_status_t choose_geometry(int dtype, int T, int64_t rows, bool backward, cons
 }
 
 jas_status_t fwd_impl(const jas_desc_t *d, const void *scores, const float *mask,
-                      const float *sink, void *probs, float *p_sink, const jas_launch_t *launch,
-                      void *stream) {
+                      const int32_t *key_len, const float *sink, void *probs, float *p_sink,
+                      const jas_launch_t *launch, void *stream) {
   Dims dm;
   jas_status_t st = check_desc(d, &dm);
   if (st != JAS_OK) return st;
   const bool has_mask = (d->flags & JAS_FLAG_MASK) != 0;
   const bool has_sink = (d->flags & JAS_FLAG_SINK) != 0;
-  if (dm.rows == 0) {  // nothing is read or written; row pointers may be NULL
-    if ((!has_mask && mask) || (!has_sink && (sink || p_sink))) return JAS_ERR_BAD_FLAGS;
-    return JAS_OK;
-  }
+  const bool has_klen = (d->flags & JAS_FLAG_KEY_LEN) != 0;
+  if ((!has_mask && mask) || (!has_sink && (sink || p_sink)) || (!has_klen && key_len))
+    return JAS_ERR_BAD_FLAGS;
+  if (dm.rows == 0) return JAS_OK;  // nothing is read or written; row pointers may be NULL
   if (!scores || !probs) return JAS_ERR_NULL_POINTER;
   if (has_mask && !mask) return JAS_ERR_NULL_POINTER;
   if (has_sink && (!sink || !p_sink)) return JAS_ERR_NULL_POINTER;
-  if ((!has_mask && mask) || (!has_sink && (sink || p_sink))) return JAS_ERR_BAD_FLAGS;
+  if (has_klen && !key_len) return JAS_ERR_NULL_POINTER;
   if (!aligned(scores, dm.esz) || !aligned(probs, dm.esz) || (mask && !aligned(mask, 4)) ||
-      (sink && !aligned(sink, 4)) || (p_sink && !aligned(p_sink, 4)))
+      (sink && !aligned(sink, 4)) || (p_sink && !aligned(p_sink, 4)) ||
+      (key_len && !aligned(key_len, 4)))
     return JAS_ERR_ALIGNMENT;
 
   const int64_t tbytes = dm.span * dm.esz;
@@ -158,9 +160,12 @@ jas_status_t fwd_impl(const jas_desc_t *d, const void *scores, const float *mask
   const Range rm = range_of(mask, has_mask ? mb : 0);
   const Range rk = range_of(sink, has_sink ? d->heads * 4 : 0);
   const Range rps = range_of(p_sink, has_sink ? dm.rows * 4 : 0);
+  const Range rkl = range_of(key_len, has_klen ? d->batch * 4 : 0);
   if (probs != scores && overlap(rp, rs)) return JAS_ERR_ALIASING;
-  if (overlap(rp, rm) || overlap(rp, rk) || overlap(rp, rps)) return JAS_ERR_ALIASING;
-  if (overlap(rps, rs) || overlap(rps, rm) || overlap(rps, rk)) return JAS_ERR_ALIASING;
+  if (overlap(rp, rm) || overlap(rp, rk) || overlap(rp, rps) || overlap(rp, rkl))
+    return JAS_ERR_ALIASING;
+  if (overlap(rps, rs) || overlap(rps, rm) || overlap(rps, rk) || overlap(rps, rkl))
+    return JAS_ERR_ALIASING;
 
   Geometry g;
   st = choose_geometry(d->dtype, dm.T, dm.rows, false, launch, &g);
@@ -172,6 +177,7 @@ jas_status_t fwd_impl(const jas_desc_t *d, const void *scores, const float *mask
   a.msb = d->mask_stride_b;
   a.msh = d->mask_stride_h;
   a.msq = d->mask_stride_q;
+  a.ex = jas::Exclusion{(d->flags & JAS_FLAG_CAUSAL) ? 1 : 0, has_klen ? key_len : nullptr};
   a.sink = has_sink ? sink : nullptr;
   a.p_sink = has_sink ? p_sink : nullptr;
   a.s = jas::RowShape{dm.rows, d->keys, d->ld, d->heads, d->q_rows, dm.T};
@@ -188,12 +194,15 @@ jas_status_t fwd_impl(const jas_desc_t *d, const void *scores, const float *mask
 }
 
 jas_status_t bwd_impl(const jas_desc_t *d, const void *probs, const void *dprobs,
-                      const float *p_sink, void *dscores, float *d_sink, void *workspace,
-                      size_t workspace_bytes, const jas_launch_t *launch, void *stream) {
+                      const int32_t *key_len, const float *p_sink, void *dscores, float *d_sink,
+                      void *workspace, size_t workspace_bytes, const jas_launch_t *launch,
+                      void *stream) {
   Dims dm;
   jas_status_t st = check_desc(d, &dm);
   if (st != JAS_OK) return st;
   const bool has_sink = (d->flags & JAS_FLAG_SINK) != 0;
+  const bool has_klen = (d->flags & JAS_FLAG_KEY_LEN) != 0;
+  if (!has_klen && key_len) return JAS_ERR_BAD_FLAGS;
   if (dm.rows == 0) {  // nothing is read; only d_sink is written (+0 per head)
     if (!has_sink && (p_sink || d_sink)) return JAS_ERR_BAD_FLAGS;
     if (!has_sink || d->heads == 0) return JAS_OK;
@@ -205,9 +214,11 @@ jas_status_t bwd_impl(const jas_desc_t *d, const void *probs, const void *dprobs
   }
   if (!probs || !dprobs || !dscores) return JAS_ERR_NULL_POINTER;
   if (has_sink && (!p_sink || !d_sink)) return JAS_ERR_NULL_POINTER;
+  if (has_klen && !key_len) return JAS_ERR_NULL_POINTER;
   if (!has_sink && (p_sink || d_sink)) return JAS_ERR_BAD_FLAGS;
   if (!aligned(probs, dm.esz) || !aligned(dprobs, dm.esz) || !aligned(dscores, dm.esz) ||
-      (p_sink && !aligned(p_sink, 4)) || (d_sink && !aligned(d_sink, 4)))
+      (p_sink && !aligned(p_sink, 4)) || (d_sink && !aligned(d_sink, 4)) ||
+      (key_len && !aligned(key_len, 4)))
     return JAS_ERR_ALIGNMENT;
   const size_t need = jas_bwd_workspace_bytes(d);
   if (has_sink) {
@@ -221,12 +232,16 @@ jas_status_t bwd_impl(const jas_desc_t *d, const void *probs, const void *dprobs
   const Range rps = range_of(p_sink, has_sink ? dm.rows * 4 : 0);
   const Range rds = range_of(d_sink, has_sink ? d->heads * 4 : 0);
   const Range rw = range_of(workspace, has_sink ? (int64_t)need : 0);
+  const Range rkl = range_of(key_len, has_klen ? d->batch * 4 : 0);
   if (dscores != probs && overlap(rd, rp)) return JAS_ERR_ALIASING;
   if (dscores != dprobs && overlap(rd, rg)) return JAS_ERR_ALIASING;
-  if (overlap(rd, rps) || overlap(rd, rds) || overlap(rd, rw)) return JAS_ERR_ALIASING;
-  if (overlap(rds, rp) || overlap(rds, rg) || overlap(rds, rps) || overlap(rds, rw))
+  if (overlap(rd, rps) || overlap(rd, rds) || overlap(rd, rw) || overlap(rd, rkl))
     return JAS_ERR_ALIASING;
-  if (overlap(rw, rp) || overlap(rw, rg) || overlap(rw, rps)) return JAS_ERR_ALIASING;
+  if (overlap(rds, rp) || overlap(rds, rg) || overlap(rds, rps) || overlap(rds, rw) ||
+      overlap(rds, rkl))
+    return JAS_ERR_ALIASING;
+  if (overlap(rw, rp) || overlap(rw, rg) || overlap(rw, rps) || overlap(rw, rkl))
+    return JAS_ERR_ALIASING;
 
   Geometry g;
   st = choose_geometry(d->dtype, dm.T, dm.rows, true, launch, &g);
@@ -239,6 +254,7 @@ jas_status_t bwd_impl(const jas_desc_t *d, const void *probs, const void *dprobs
     a.dscores = dscores;
     a.p_sink = has_sink ? p_sink : nullptr;
     a.v = has_sink ? static_cast<float *>(workspace) : nullptr;
+    a.ex = jas::Exclusion{(d->flags & JAS_FLAG_CAUSAL) ? 1 : 0, has_klen ? key_len : nullptr};
     a.s = jas::RowShape{dm.rows, d->keys, d->ld, d->heads, d->q_rows, dm.T};
     const int64_t kpc = jas::keys_per_chunk(d->dtype);
     a.vec_io = aligned(probs, 16) && aligned(dprobs, 16) && aligned(dscores, 16) &&
@@ -257,14 +273,15 @@ jas_status_t bwd_impl(const jas_desc_t *d, const void *probs, const void *dprobs
 extern "C" {
 
 jas_status_t jas_fwd(const jas_desc_t *desc, const void *scores, const float *mask,
-                     const float *sink, void *probs, float *p_sink, void *stream) {
-  return fwd_impl(desc, scores, mask, sink, probs, p_sink, nullptr, stream);
+                     const int32_t *key_len, const float *sink, void *probs, float *p_sink,
+                     void *stream) {
+  return fwd_impl(desc, scores, mask, key_len, sink, probs, p_sink, nullptr, stream);
 }
 
 jas_status_t jas_fwd_ex(const jas_desc_t *desc, const void *scores, const float *mask,
-                        const float *sink, void *probs, float *p_sink,
+                        const int32_t *key_len, const float *sink, void *probs, float *p_sink,
                         const jas_launch_t *launch, void *stream) {
-  return fwd_impl(desc, scores, mask, sink, probs, p_sink, launch, stream);
+  return fwd_impl(desc, scores, mask, key_len, sink, probs, p_sink, launch, stream);
 }
 
 size_t jas_bwd_workspace_bytes(const jas_desc_t *desc) {
@@ -276,17 +293,18 @@ size_t jas_bwd_workspace_bytes(const jas_desc_t *desc) {
 }
 
 jas_status_t jas_bwd(const jas_desc_t *desc, const void *probs, const void *dprobs,
-                     const float *p_sink, void *dscores, float *d_sink, void *workspace,
-                     size_t workspace_bytes, void *stream) {
-  return bwd_impl(desc, probs, dprobs, p_sink, dscores, d_sink, workspace, workspace_bytes,
-                  nullptr, stream);
+                     const int32_t *key_len, const float *p_sink, void *dscores, float *d_sink,
+                     void *workspace, size_t workspace_bytes, void *stream) {
+  return bwd_impl(desc, probs, dprobs, key_len, p_sink, dscores, d_sink, workspace,
+                  workspace_bytes, nullptr, stream);
 }
 
 jas_status_t jas_bwd_ex(const jas_desc_t *desc, const void *probs, const void *dprobs,
-                        const float *p_sink, void *dscores, float *d_sink, void *workspace,
-                        size_t workspace_bytes, const jas_launch_t *launch, void *stream) {
-  return bwd_impl(desc, probs, dprobs, p_sink, dscores, d_sink, workspace, workspace_bytes,
-                  launch, stream);
+                        const int32_t *key_len, const float *p_sink, void *dscores,
+                        float *d_sink, void *workspace, size_t workspace_bytes,
+                        const jas_launch_t *launch, void *stream) {
+  return bwd_impl(desc, probs, dprobs, key_len, p_sink, dscores, d_sink, workspace,
+                  workspace_bytes, launch, stream);
 }
 
 const char *jas_status_str(jas_status_t s) {
@@ -307,6 +325,7 @@ const char *jas_status_str(jas_status_t s) {
 
 const char *jas_contract(void) {
   return "jas/1 tile=256 tree=balanced-pairwise-by-key fold=left-to-right sink=merged-last "
+         "exclusion=suffix(causal,key_len) "
          "acc=fp32 exp=2^fl(y*log2e),flush<2^-126,v_exp_f32 div=ieee cvt=rne "
          "fpcontract=off atomics=none dsink=256-row-chunks,left-fold arch=gfx950";
 }

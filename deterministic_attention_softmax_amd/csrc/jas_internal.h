@@ -22,11 +22,18 @@ struct RowShape {
   int T;          // tiles per row
 };
 
+// Visible key prefix of a row: causal cut and per-batch key length.
+struct Exclusion {
+  int causal;              // key <= N - Sq + q
+  const int32_t *key_len;  // [B] or nullptr
+};
+
 struct FwdArgs {
   const void *scores;
   void *probs;
   const float *mask;  // nullptr when no mask
   int64_t msb, msh, msq;
+  Exclusion ex;
   const float *sink;  // nullptr when no sink
   float *p_sink;
   RowShape s;
@@ -40,6 +47,7 @@ struct BwdArgs {
   void *dscores;
   const float *p_sink;  // nullptr when no sink
   float *v;             // per-row d_sink share (workspace), nullptr when no sink
+  Exclusion ex;
   RowShape s;
   int vec_io;         // 16-byte path: rows are whole aligned 16-byte chunks
 };

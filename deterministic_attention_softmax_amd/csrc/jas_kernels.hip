@@ -356,6 +356,25 @@ __device__ __forceinline__ void bstore(const Buf &b, uint32_t voff, uint32_t sof
   __builtin_amdgcn_raw_buffer_store_b128(v, b.r, (int)voff, (int)soff, kAuxNT);
 }
 
+// Visible key prefix of row (b, q): N keys, cut by the causal condition
+// key <= N - Sq + q and by the batch entry's key length, clamped to [0, N].
+// Wave-uniform.
+__device__ __forceinline__ int row_kend(const Exclusion &ex, int N, int64_t Sq, int64_t b,
+                                        int64_t q) {
+  int64_t k = N;
+  if (ex.causal) {
+    const int64_t c = q + ((int64_t)N - Sq) + 1;
+    k = c < k ? c : k;
+  }
+  if (ex.key_len) {
+    const int64_t l = ex.key_len[b];
+    k = l < k ? l : k;
+  }
+  // a 32-bit scalar from here on: the per-slot comparisons with it stay
+  // scalar instead of 64-bit vector compares against hoisted constants
+  return __builtin_amdgcn_readfirstlane((int)(k < 0 ? 0 : k));
+}
+
 // ---------------------------------------------------------------------------
 // Forward
 //
@@ -366,7 +385,7 @@ __device__ __forceinline__ void bstore(const Buf &b, uint32_t voff, uint32_t sof
 // row; phase 3 rescales, converts once and stores.
 // ---------------------------------------------------------------------------
 
-template <int DT, int WPR, int CPL, bool VEC, bool MASK>
+template <int DT, int WPR, int CPL, bool VEC, bool MASK, bool EXCL>
 __global__ __launch_bounds__(kWave * kBlockWaves) void fwd_kernel(const FwdArgs a) {
   using C = Cfg<DT>;
   constexpr int KPL = C::KPL, TPS = C::TPS, ESZ = C::ESZ;
@@ -391,27 +410,36 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void fwd_kernel(const FwdArgs 
     const int64_t rr = active ? r : a.s.rows - 1;
     const char *srow = static_cast<const char *>(a.scores) + rr * a.s.ld * ESZ;
     char *prow = static_cast<char *>(a.probs) + r * a.s.ld * ESZ;
-    const uint32_t row_bytes = active ? (uint32_t)(N * ESZ) : 0u;
-    const Buf sbuf(srow, row_bytes), pbuf(prow, row_bytes);
-    const uint32_t voff = (uint32_t)(ix.loff * ESZ);
     const float *mrow = nullptr;
     int64_t h = 0;
-    if (MASK || has_sink) {
+    int kend = N;  // visible keys: the rest count as -inf and are not read
+    if (MASK || has_sink || EXCL) {
       const int64_t q = rr % a.s.Sq;
       const int64_t bh = rr / a.s.Sq;
       h = bh % a.s.H;
       if constexpr (MASK) mrow = a.mask + (bh / a.s.H) * a.msb + h * a.msh + q * a.msq;
+      if constexpr (EXCL) kend = row_kend(a.ex, N, a.s.Sq, bh / a.s.H, q);
     }
-    const Buf mbuf(mrow, MASK ? row_bytes * (4 / ESZ) : 0u);
+    // scores (and mask) are read up to the chunk holding the last visible
+    // key; the probabilities are written over the whole row
+    const int kread = EXCL ? (kend + KPL - 1) / KPL * KPL : N;
+    const Buf sbuf(srow, active ? (uint32_t)(kread * ESZ) : 0u);
+    const Buf pbuf(prow, active ? (uint32_t)(N * ESZ) : 0u);
+    const Buf mbuf(mrow, (MASK && active) ? (uint32_t)(kread * 4) : 0u);
+    const uint32_t voff = (uint32_t)(ix.loff * ESZ);
+    // this lane's visible keys in the chunk of the slot starting at key sb
+    // are the first (lim - sb) of it (compared against constants, so no
+    // per-key index is kept live)
+    const int lim = kend - ix.loff;
 
     // ---- phase 1: issue every score load of the row, straight-line (VEC:
-    // lanes past the row read 0 and are overwritten in phase 2) ----
+    // lanes past the visible prefix read 0 and are overwritten in phase 2) ----
     Chunk raw[CPL];
 #pragma unroll
     for (int s = 0; s < CPL; ++s) {
       const int sb = (s * WPR + ix.wir) * TPS * kTile;
       if constexpr (VEC) raw[s] = bload<kAuxNT>(sbuf, voff, (uint32_t)(sb * ESZ));
-      else raw[s] = load_chunk_elems<DT>(srow, sb + ix.loff, N, kFill);
+      else raw[s] = load_chunk_elems<DT>(srow, sb + ix.loff, kend, kFill);
     }
 
     // ---- phase 2: per tile max, exponentials, sum ----
@@ -435,38 +463,52 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void fwd_kernel(const FwdArgs 
       if constexpr (MASK && VEC) {
         if (s + 1 < CPL) load_mask(s + 1, mv[(s + 1) & 1]);
       }
-      float x[KPL];
-      unpack<DT>(raw[s], x);
-      if constexpr (MASK) {
-        if constexpr (VEC) {
-          const float4 (&m4)[KPL / 4] = mv[s & 1];
+      float m = kNegInf, l = 0.0f;
+      bool skip = false;
+      if constexpr (EXCL) skip = sb >= kend;  // uniform
+      if (skip) {  // the whole slot is past the visible keys: not read
 #pragma unroll
-          for (int k4 = 0; k4 < KPL / 4; ++k4) {
-            x[4 * k4 + 0] = x[4 * k4 + 0] + m4[k4].x;
-            x[4 * k4 + 1] = x[4 * k4 + 1] + m4[k4].y;
-            x[4 * k4 + 2] = x[4 * k4 + 2] + m4[k4].z;
-            x[4 * k4 + 3] = x[4 * k4 + 3] + m4[k4].w;
+        for (int k = 0; k < KPL; ++k) e[s][k] = 0.0f;
+      } else {
+        float x[KPL];
+        unpack<DT>(raw[s], x);
+        if constexpr (MASK) {
+          if constexpr (VEC) {
+            const float4 (&m4)[KPL / 4] = mv[s & 1];
+#pragma unroll
+            for (int k4 = 0; k4 < KPL / 4; ++k4) {
+              x[4 * k4 + 0] = x[4 * k4 + 0] + m4[k4].x;
+              x[4 * k4 + 1] = x[4 * k4 + 1] + m4[k4].y;
+              x[4 * k4 + 2] = x[4 * k4 + 2] + m4[k4].z;
+              x[4 * k4 + 3] = x[4 * k4 + 3] + m4[k4].w;
+            }
+          } else {
+#pragma unroll
+            for (int k = 0; k < KPL; ++k)
+              if (j0 + k < kend) x[k] = x[k] + mrow[j0 + k];
           }
-        } else {
-#pragma unroll
-          for (int k = 0; k < KPL; ++k)
-            if (j0 + k < N) x[k] = x[k] + mrow[j0 + k];
         }
-      }
-      if constexpr (VEC) {
-        if (sb + TPS * kTile > N) {  // a slot reaching past the row (uniform)
-          const bool inb = j0 < N;
+        if constexpr (VEC) {
+          if (sb + TPS * kTile > kend) {  // a slot reaching past the row or the cut (uniform)
+            if constexpr (EXCL) {
+              const int nv = lim - sb;
 #pragma unroll
-          for (int k = 0; k < KPL; ++k) x[k] = inb ? x[k] : kNegInf;
+              for (int k = 0; k < KPL; ++k) x[k] = (k < nv) ? x[k] : kNegInf;
+            } else {
+              const bool inb = j0 < N;  // N is a multiple of the chunk here
+#pragma unroll
+              for (int k = 0; k < KPL; ++k) x[k] = inb ? x[k] : kNegInf;
+            }
+          }
         }
-      }
-      const float m = tile_max<DT>(lane_tree_max<KPL>(x));
-      // a tile whose max is -inf has only -inf keys: subtracting 0 keeps
-      // them at -inf and every e at +0, without a -inf - -inf
-      const float msafe = (m == kNegInf) ? 0.0f : m;
+        m = tile_max<DT>(lane_tree_max<KPL>(x));
+        // a tile whose max is -inf has only -inf keys: subtracting 0 keeps
+        // them at -inf and every e at +0, without a -inf - -inf
+        const float msafe = (m == kNegInf) ? 0.0f : m;
 #pragma unroll
-      for (int k = 0; k < KPL; ++k) e[s][k] = exp_(x[k] - msafe);
-      const float l = tile_sum<DT>(lane_tree_sum<KPL>(e[s]));
+        for (int k = 0; k < KPL; ++k) e[s][k] = exp_(x[k] - msafe);
+        l = tile_sum<DT>(lane_tree_sum<KPL>(e[s]));
+      }
       if (ix.cil == 0 && t < T) {
         lds_m[ix.rib][t] = m;
         lds_l[ix.rib][t] = l;
@@ -547,7 +589,7 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void fwd_kernel(const FwdArgs 
 // sums of P*dP, the fold runs over the tile sums in order, phase 3 writes dS.
 // ---------------------------------------------------------------------------
 
-template <int DT, int WPR, int CPL, bool VEC>
+template <int DT, int WPR, int CPL, bool VEC, bool EXCL>
 __global__ __launch_bounds__(kWave * kBlockWaves) void bwd_kernel(const BwdArgs a) {
   using C = Cfg<DT>;
   constexpr int KPL = C::KPL, TPS = C::TPS, ESZ = C::ESZ;
@@ -568,12 +610,20 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void bwd_kernel(const BwdArgs 
     const char *prow = static_cast<const char *>(a.probs) + rr * a.s.ld * ESZ;
     const char *grow = static_cast<const char *>(a.dprobs) + rr * a.s.ld * ESZ;
     char *drow = static_cast<char *>(a.dscores) + r * a.s.ld * ESZ;
+    int kend = N;  // P is taken as +0 past the visible keys and not read there
+    if constexpr (EXCL) {
+      const int64_t q = rr % a.s.Sq;
+      kend = row_kend(a.ex, N, a.s.Sq, rr / (a.s.Sq * a.s.H), q);
+    }
+    const int kread = EXCL ? (kend + KPL - 1) / KPL * KPL : N;
+    const int lim = kend - ix.loff;  // as in the forward
     const uint32_t row_bytes = active ? (uint32_t)(N * ESZ) : 0u;
-    const Buf pbuf(prow, row_bytes), gbuf(grow, row_bytes), dbuf(drow, row_bytes);
+    const Buf pbuf(prow, active ? (uint32_t)(kread * ESZ) : 0u);
+    const Buf gbuf(grow, row_bytes), dbuf(drow, row_bytes);
     const uint32_t voff = (uint32_t)(ix.loff * ESZ);
 
     // ---- phase 1: issue every load of the row, straight-line; keys past
-    // the row read as +0 ----
+    // the row (P: past the visible keys) read as +0 ----
     Chunk rp[CPL], rg[CPL];
 #pragma unroll
     for (int s = 0; s < CPL; ++s) {
@@ -582,7 +632,7 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void bwd_kernel(const BwdArgs 
         rp[s] = bload<kAuxNT>(pbuf, voff, (uint32_t)(sb * ESZ));
         rg[s] = bload<kAuxNT>(gbuf, voff, (uint32_t)(sb * ESZ));
       } else {
-        rp[s] = load_chunk_elems<DT>(prow, sb + ix.loff, N, 0u);
+        rp[s] = load_chunk_elems<DT>(prow, sb + ix.loff, kend, 0u);
         rg[s] = load_chunk_elems<DT>(grow, sb + ix.loff, N, 0u);
       }
     }
@@ -591,6 +641,19 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void bwd_kernel(const BwdArgs 
 #pragma unroll
     for (int s = 0; s < CPL; ++s) {
       const int t = (s * WPR + ix.wir) * TPS + ix.half;
+      if constexpr (VEC && EXCL) {
+        const int sb = (s * WPR + ix.wir) * TPS * kTile;
+        if (sb + TPS * kTile > kend && sb < kread) {  // the slot holding the cut (uniform)
+          const int nv = lim - sb;  // this lane's visible keys in its chunk
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {  // keys at or past kend: P = +0
+            if constexpr (DT == 1)
+              rp[s].w[i] &= (nv > 2 * i ? 0x0000ffffu : 0u) | (nv > 2 * i + 1 ? 0xffff0000u : 0u);
+            else
+              rp[s].w[i] = nv > i ? rp[s].w[i] : 0u;
+          }
+        }
+      }
       float p[KPL], g[KPL], pg[KPL];
       unpack<DT>(rp[s], p);
       unpack<DT>(rg[s], g);
@@ -686,27 +749,39 @@ __global__ __launch_bounds__(kWave * kDsinkWaves) void dsink_kernel(const DsinkA
 constexpr int kCplF32[] = {1, 2, 3, 5, 9, 17};
 constexpr int kCplBf16[] = {1, 2, 3, 5, 9};
 
+// rows with an exclusion (causal or key lengths) run their own instances,
+// so the row-level cut costs the dense rows nothing
+template <int DT, int WPR, int CPL, bool EXCL>
+void launch_fwd_e(const FwdArgs &a, const dim3 grid, const dim3 block, hipStream_t st) {
+  const bool mask = a.mask != nullptr;
+  if (a.vec_io) {
+    if (mask) hipLaunchKernelGGL((fwd_kernel<DT, WPR, CPL, true, true, EXCL>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((fwd_kernel<DT, WPR, CPL, true, false, EXCL>), grid, block, 0, st, a);
+  } else {
+    if (mask) hipLaunchKernelGGL((fwd_kernel<DT, WPR, CPL, false, true, EXCL>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((fwd_kernel<DT, WPR, CPL, false, false, EXCL>), grid, block, 0, st, a);
+  }
+}
+
 template <int DT, int WPR, int CPL>
 hipError_t launch_fwd_t(const FwdArgs &a, const Geometry &g, hipStream_t st) {
   const dim3 grid((unsigned)g.blocks), block(kWave * WPR * g.rpb);
-  const bool mask = a.mask != nullptr;
-  if (a.vec_io) {
-    if (mask) hipLaunchKernelGGL((fwd_kernel<DT, WPR, CPL, true, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((fwd_kernel<DT, WPR, CPL, true, false>), grid, block, 0, st, a);
-  } else {
-    if (mask) hipLaunchKernelGGL((fwd_kernel<DT, WPR, CPL, false, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((fwd_kernel<DT, WPR, CPL, false, false>), grid, block, 0, st, a);
-  }
+  if (a.ex.causal || a.ex.key_len) launch_fwd_e<DT, WPR, CPL, true>(a, grid, block, st);
+  else launch_fwd_e<DT, WPR, CPL, false>(a, grid, block, st);
   return hipGetLastError();
 }
 
 template <int DT, int WPR, int CPL>
 hipError_t launch_bwd_t(const BwdArgs &a, const Geometry &g, hipStream_t st) {
   const dim3 grid((unsigned)g.blocks), block(kWave * WPR * g.rpb);
-  if (a.vec_io)
-    hipLaunchKernelGGL((bwd_kernel<DT, WPR, CPL, true>), grid, block, 0, st, a);
-  else
-    hipLaunchKernelGGL((bwd_kernel<DT, WPR, CPL, false>), grid, block, 0, st, a);
+  const bool excl = a.ex.causal || a.ex.key_len;
+  if (a.vec_io) {
+    if (excl) hipLaunchKernelGGL((bwd_kernel<DT, WPR, CPL, true, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((bwd_kernel<DT, WPR, CPL, true, false>), grid, block, 0, st, a);
+  } else {
+    if (excl) hipLaunchKernelGGL((bwd_kernel<DT, WPR, CPL, false, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((bwd_kernel<DT, WPR, CPL, false, false>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 

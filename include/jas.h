@@ -24,7 +24,12 @@
  *
  * Exact arithmetic of one row of N keys, T = ceil(N/256) tiles (every
  * operation binary32, round to nearest-even, no fused multiply-add):
- *   x_j   = float(s_j) (+ mask_j, one rounding, when JAS_FLAG_MASK)
+ *   kend  = the row's visible key prefix: N, cut by JAS_FLAG_CAUSAL to
+ *           q + (N - q_rows) + 1 (a key is visible to query q when
+ *           key <= keys - q_rows + q; RL-Kernel PR #240, Prefill / Decode)
+ *           and by JAS_FLAG_KEY_LEN to key_len[b], clamped to [0, N]
+ *   x_j   = float(s_j) (+ mask_j, one rounding, when JAS_FLAG_MASK) for
+ *           j < kend; -inf for j >= kend (those scores are never read)
  *   m_t   = max over tile t (positions past N count as -inf)
  *   e_j   = exp_(x_j - m_t), exp_(y) = 2^fl(y*log2e), 0 when that exponent
  *           is below -126 (or y is -inf); 0 in a tile whose max is -inf
@@ -37,7 +42,8 @@
  *   invL  = 1/L (0 when L is 0)
  *   P_j   = round_to_dtype(e_j * fl(exp_(m_t - M) * invL))
  *   p_sink= fl(exp_(sigma_h - M) * invL)      (0 when sigma_h is -inf)
- * Backward on the stored P:
+ * Backward on the stored P (P_j taken as +0 without being read for
+ * j >= kend):
  *   d_t   = balanced tree sum of fl(P_j*dP_j) over tile t; delta = d_0, then
  *           delta = fl(delta + d_t) for t = 1..T-1
  *   dS_j  = round_to_dtype(P_j * fl(dP_j - delta))
@@ -86,8 +92,17 @@ extern "C" {
    d_sink and the workspace are always binary32. */
 typedef enum { JAS_DTYPE_F32 = 0, JAS_DTYPE_BF16 = 1 } jas_dtype_t;
 
-/* Flags: the only predicates for "has a mask" and "has a sink". */
-enum { JAS_FLAG_MASK = 1u << 0, JAS_FLAG_SINK = 1u << 1 };
+/* Flags: the only predicates for "has a mask", "has a sink", "causal" and
+ * "has per-batch key lengths".  CAUSAL and KEY_LEN exclude a suffix of each
+ * row: excluded keys behave exactly as keys whose score is -inf, and whole
+ * 256-key tiles past the visible prefix are not read (forward: scores;
+ * backward: P, which the forward wrote as +0 there). */
+enum {
+  JAS_FLAG_MASK = 1u << 0,
+  JAS_FLAG_SINK = 1u << 1,
+  JAS_FLAG_CAUSAL = 1u << 2,
+  JAS_FLAG_KEY_LEN = 1u << 3
+};
 
 typedef enum {
   JAS_OK = 0,
@@ -133,17 +148,21 @@ typedef struct {
  *   keys columns per row; probs == scores (in place) is allowed, any other
  *   overlap of probs with an input is JAS_ERR_ALIASING.
  *   mask   binary32, required iff JAS_FLAG_MASK (see jas_desc_t strides).
+ *   key_len int32 [batch] device array, required iff JAS_FLAG_KEY_LEN:
+ *          keys at or past key_len[b] are excluded (values are clamped to
+ *          [0, keys] in the kernels).
  *   sink   binary32 [heads], required iff JAS_FLAG_SINK.
  *   p_sink binary32 [rows] written, required iff JAS_FLAG_SINK; the sink's
  *          own probability, which jas_bwd reads.
  * (Definition: RL-Kernel PR #453, Summary, fixed-order online softmax;
  *  sink: TransformerEngine PR #678, Description.) */
 jas_status_t jas_fwd(const jas_desc_t *desc, const void *scores, const float *mask,
-                     const float *sink, void *probs, float *p_sink, void *stream);
+                     const int32_t *key_len, const float *sink, void *probs, float *p_sink,
+                     void *stream);
 
 /* jas_fwd with an explicit launch geometry (NULL = default). */
 jas_status_t jas_fwd_ex(const jas_desc_t *desc, const void *scores, const float *mask,
-                        const float *sink, void *probs, float *p_sink,
+                        const int32_t *key_len, const float *sink, void *probs, float *p_sink,
                         const jas_launch_t *launch, void *stream);
 
 /* Bytes of device workspace jas_bwd needs: 4*rows rounded up to 256 when
@@ -155,7 +174,9 @@ size_t jas_bwd_workspace_bytes(const jas_desc_t *desc);
  *   probs, dprobs [rows, ld] (dtype) read.  dscores [rows, ld] written;
  *   dscores may equal probs or dprobs (in place), any other overlap is
  *   JAS_ERR_ALIASING.  JAS_FLAG_MASK and the mask strides are ignored:
- *   masked keys already have P = 0.
+ *   masked keys already have P = 0.  With JAS_FLAG_CAUSAL / JAS_FLAG_KEY_LEN
+ *   (key_len as for the forward) P is not read on excluded keys and taken
+ *   as +0; dprobs is read on every key, so dS keeps its signed zeros.
  *   p_sink  binary32 [rows] read, required iff JAS_FLAG_SINK.
  *   d_sink  binary32 [heads] written (overwritten, not accumulated),
  *           required iff JAS_FLAG_SINK.
@@ -166,13 +187,14 @@ size_t jas_bwd_workspace_bytes(const jas_desc_t *desc);
  *  TransformerEngine PR #678, reduced here in a fixed order without
  *  atomics.) */
 jas_status_t jas_bwd(const jas_desc_t *desc, const void *probs, const void *dprobs,
-                     const float *p_sink, void *dscores, float *d_sink, void *workspace,
-                     size_t workspace_bytes, void *stream);
+                     const int32_t *key_len, const float *p_sink, void *dscores, float *d_sink,
+                     void *workspace, size_t workspace_bytes, void *stream);
 
 /* jas_bwd with an explicit launch geometry (NULL = default). */
 jas_status_t jas_bwd_ex(const jas_desc_t *desc, const void *probs, const void *dprobs,
-                        const float *p_sink, void *dscores, float *d_sink, void *workspace,
-                        size_t workspace_bytes, const jas_launch_t *launch, void *stream);
+                        const int32_t *key_len, const float *p_sink, void *dscores,
+                        float *d_sink, void *workspace, size_t workspace_bytes,
+                        const jas_launch_t *launch, void *stream);
 
 /* Static text for a status code. */
 const char *jas_status_str(jas_status_t status);

@@ -47,18 +47,19 @@ def desc(B=1, H=2, S=3, N=300, dtype=jas.JAS_DTYPE_BF16, flags=0, ld=None, ms=(0
     return jas.make_desc((B, H, S, N), dtype, flags, ld, ms)
 
 
-def fwd(d, scores=A, mask=None, sink=None, probs=B_, p_sink=None, launch=None):
-    return jas.jas_fwd_ex(d, scores, mask, sink, probs, p_sink, launch, None)
+def fwd(d, scores=A, mask=None, sink=None, probs=B_, p_sink=None, launch=None, key_len=None):
+    return jas.jas_fwd_ex(d, scores, mask, key_len, sink, probs, p_sink, launch, None)
 
 
-def bwd(d, probs=A, dprobs=B_, p_sink=None, dscores=C, d_sink=None, ws=None, ws_bytes=0):
-    return jas.jas_bwd(d, probs, dprobs, p_sink, dscores, d_sink, ws, ws_bytes, None)
+def bwd(d, probs=A, dprobs=B_, p_sink=None, dscores=C, d_sink=None, ws=None, ws_bytes=0,
+        key_len=None):
+    return jas.jas_bwd(d, probs, dprobs, key_len, p_sink, dscores, d_sink, ws, ws_bytes, None)
 
 
 def test_null_desc_and_pointers():
     L = jas.lib()
-    assert L.jas_fwd(None, A, None, None, B_, None, None) == 1
-    assert L.jas_bwd(None, A, B_, None, C, None, None, 0, None) == 1
+    assert L.jas_fwd(None, A, None, None, None, B_, None, None) == 1
+    assert L.jas_bwd(None, A, B_, None, None, C, None, None, 0, None) == 1
     assert fwd(desc(), scores=None) == 1
     assert fwd(desc(), probs=None) == 1
     assert bwd(desc(), probs=None) == 1
@@ -78,6 +79,12 @@ def test_flag_pointer_predicates():
     assert bwd(desc(flags=jas.JAS_FLAG_SINK), p_sink=D) == 1          # d_sink missing
     assert bwd(desc(), p_sink=D) == 4
     assert bwd(desc(), d_sink=E) == 4
+    # key lengths: pointer iff JAS_FLAG_KEY_LEN
+    assert fwd(desc(flags=jas.JAS_FLAG_KEY_LEN)) == 1
+    assert fwd(desc(), key_len=W) == 4
+    assert bwd(desc(flags=jas.JAS_FLAG_KEY_LEN)) == 1
+    assert bwd(desc(), key_len=W) == 4
+    assert fwd(desc(flags=1 << 4)) == 4
 
 
 def test_shapes_and_dtype():
@@ -96,6 +103,7 @@ def test_alignment():
     assert fwd(desc(dtype=jas.JAS_DTYPE_F32), probs=B_ + 2) == 9
     assert fwd(desc(flags=jas.JAS_FLAG_MASK), mask=C + 2) == 9
     assert bwd(desc(), dscores=C + 1) == 9
+    assert fwd(desc(flags=jas.JAS_FLAG_KEY_LEN), key_len=W + 2) == 9
 
 
 def test_aliasing():
@@ -112,6 +120,9 @@ def test_aliasing():
     dsb = desc(B=1, H=1, S=4, N=300, flags=jas.JAS_FLAG_SINK)
     ws = jas.jas_bwd_workspace_bytes(dsb)
     assert bwd(dsb, p_sink=D, d_sink=E, ws=D, ws_bytes=ws) == 5
+    dk = desc(B=1, H=1, S=4, N=300, flags=jas.JAS_FLAG_KEY_LEN)
+    assert fwd(dk, key_len=B_ + 64) == 5         # key lengths inside probs
+    assert bwd(dk, key_len=C + 4) == 5           # key lengths inside dscores
 
 
 def test_workspace():
@@ -134,3 +145,14 @@ def test_launch_override_validation():
     for L in bad:
         lt = jas._launch(L)
         assert fwd(d, launch=lt) == 7, L
+
+
+def test_binding_rejects_host_tensors():
+    # the torch-level wrappers refuse tensors outside device memory before
+    # any pointer reaches the library
+    import torch
+    s = torch.zeros((1, 1, 2, 256))
+    with pytest.raises(ValueError, match="device memory"):
+        jas.fwd(s)
+    with pytest.raises(ValueError, match="device memory"):
+        jas.bwd(s, s)
