@@ -6,11 +6,11 @@ checked against.  Only the tests, ``__graft_entry__.smoke()`` and the CPU
 baseline leg of ``bench.py`` may import it; the HIP library and its Python
 binding never do.
 
-Arrays: bf16 tensors travel as ``numpy.uint16`` bit patterns, fp32 tensors as
-``numpy.float32``.  All functions follow the pages cited in ``jas_oracle.c``:
+Arrays: bf16 tensors travel as ``numpy.uint16`` bit patterns, fp16 tensors as
+``numpy.float16``, fp32 tensors as ``numpy.float32``.  All functions follow the pages cited in ``jas_oracle.c``:
 RL-Kernel PR #453 (fixed-order online softmax, fixed-order backward), ROCm
 TransformerEngine PR #678 (softmax sink), RL-Kernel PR #240 (fixed power-of-two
-reduction tree, fully masked rows).
+reduction tree, fully masked rows, the row log-sum-exp, FP16 beside BF16).
 """
 import ctypes
 import os
@@ -21,7 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libjas_oracle.so")
 _lib = None
 
-F32, BF16 = 0, 1
+F32, BF16, F16 = 0, 1, 2
 _I64 = ctypes.c_int64
 _VP = ctypes.c_void_p
 
@@ -43,7 +43,7 @@ def lib():
         L = ctypes.CDLL(_LIB_PATH)
         L.jas_oracle_fwd.restype = ctypes.c_int
         L.jas_oracle_fwd.argtypes = [ctypes.c_int, _I64, _I64, _I64, _I64, _I64, _VP, _VP,
-                                     _I64, _I64, _I64, ctypes.c_int, _VP, _VP, _VP, _VP,
+                                     _I64, _I64, _I64, ctypes.c_int, _VP, _VP, _VP, _VP, _VP,
                                      ctypes.c_int]
         L.jas_oracle_bwd.restype = ctypes.c_int
         L.jas_oracle_bwd.argtypes = [ctypes.c_int, _I64, _I64, _I64, _I64, _I64, _VP, _VP,
@@ -56,6 +56,10 @@ def lib():
         L.jas_oracle_log2e.argtypes = []
         L.jas_oracle_bf16.restype = ctypes.c_uint16
         L.jas_oracle_bf16.argtypes = [ctypes.c_float]
+        L.jas_oracle_f16_array.restype = None
+        L.jas_oracle_f16_array.argtypes = [_VP, _VP, _I64]
+        L.jas_oracle_f16_decode_array.restype = None
+        L.jas_oracle_f16_decode_array.argtypes = [_VP, _VP, _I64]
         L.jas_oracle_tree_sum256.restype = ctypes.c_float
         L.jas_oracle_tree_sum256.argtypes = [_VP]
         _lib = L
@@ -71,7 +75,9 @@ def _dtype_code(a: np.ndarray) -> int:
         return F32
     if a.dtype == np.uint16:
         return BF16
-    raise TypeError(f"scores must be float32 or uint16 (bf16 bits), got {a.dtype}")
+    if a.dtype == np.float16:
+        return F16
+    raise TypeError(f"scores must be float32, float16 or uint16 (bf16 bits), got {a.dtype}")
 
 
 def _key_len(key_len, B):
@@ -84,13 +90,14 @@ def _key_len(key_len, B):
 
 
 def fwd(scores, B, H, Sq, N, ld=None, mask=None, mask_strides=(0, 0, 0), sink=None,
-        threads=None, causal=False, key_len=None):
+        threads=None, causal=False, key_len=None, want_lse=False):
     """Forward pass.  ``scores`` is a C-contiguous array holding B*H*Sq rows of
     stride ``ld`` (default N).  ``causal`` excludes keys past the causal
     condition, ``key_len`` (int32 [B]) keys past each batch entry's length.
-    Returns ``(P, p_sink)``; ``P`` has the layout and dtype of ``scores`` (row
-    padding past N is left zero) and ``p_sink`` is float32 [B*H*Sq] or None
-    when no sink is given."""
+    Returns ``(P, p_sink)``, or ``(P, p_sink, lse)`` with ``want_lse``; ``P``
+    has the layout and dtype of ``scores`` (row padding past N is left zero),
+    ``p_sink`` is float32 [B*H*Sq] or None when no sink is given, ``lse`` the
+    float32 [B*H*Sq] row log-sum-exp."""
     scores = np.ascontiguousarray(scores)
     ld = N if ld is None else ld
     rows = B * H * Sq
@@ -104,14 +111,15 @@ def fwd(scores, B, H, Sq, N, ld=None, mask=None, mask_strides=(0, 0, 0), sink=No
         if sink.size < H:
             raise ValueError("sink needs one value per head")
     ps = np.zeros(rows, np.float32) if sink is not None else None
+    lse = np.zeros(rows, np.float32) if want_lse else None
     msb, msh, msq = mask_strides
     kl = _key_len(key_len, B)
     rc = lib().jas_oracle_fwd(_dtype_code(scores), B, H, Sq, N, ld, _ptr(scores), _ptr(mask),
                               msb, msh, msq, int(bool(causal)), _ptr(kl), _ptr(sink), _ptr(P),
-                              _ptr(ps), threads or default_threads())
+                              _ptr(ps), _ptr(lse), threads or default_threads())
     if rc != 0:
         raise RuntimeError(f"jas_oracle_fwd failed: {rc}")
-    return P, ps
+    return (P, ps, lse) if want_lse else (P, ps)
 
 
 def bwd(P, dP, B, H, Sq, N, ld=None, p_sink=None, threads=None, causal=False, key_len=None):
@@ -158,6 +166,22 @@ def log2e() -> np.float32:
 
 def bf16_rne(x: float) -> int:
     return int(lib().jas_oracle_bf16(float(np.float32(x))))
+
+
+def f16_rne(x):
+    """binary32 array -> binary16 bit patterns (uint16), the oracle's rounding."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, np.uint16)
+    lib().jas_oracle_f16_array(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def f16_decode(h):
+    """binary16 bit patterns (uint16) -> binary32, the oracle's widening."""
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    out = np.empty(h.shape, np.float32)
+    lib().jas_oracle_f16_decode_array(_ptr(h), _ptr(out), h.size)
+    return out
 
 
 def tree_sum256(v) -> np.float32:

@@ -17,8 +17,9 @@
  *        head, d_sink per head).
  *   [P3] RL-Kernel PR #240, "Batch-invariant attention (standard softmax --
  *        cuda version)", sections "Fixed Reduction Contract / Softmax and
- *        LSE" (power-of-two tree whose shape depends on nothing but the tile)
- *        and "Path Status" (fully masked rows).
+ *        LSE" (power-of-two tree whose shape depends on nothing but the tile;
+ *        the row's log-sum-exp as a second output) and "Path Status" (fully
+ *        masked rows; FP16 and BF16 dtypes).
  *
  * Arithmetic model.  Every floating-point operation below is one IEEE-754
  * binary32 operation rounded to nearest-even: the file is compiled with
@@ -54,7 +55,9 @@
 
 #define TILE 256          /* [P1] Benchmark: TILE_K = 256, fixed, never tuned */
 
-enum { DT_F32 = 0, DT_BF16 = 1 };
+enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+
+static size_t elem_size(int dt) { return dt == DT_F32 ? 4 : 2; }
 
 /* ------------------------------------------------------------------------ */
 /* Floating-point environment                                               */
@@ -98,13 +101,63 @@ static uint16_t f32_to_bf16(float x) {
   return (uint16_t)lo;
 }
 
+/* IEEE binary16 -> binary32, exact.  Fields: sign, 5 exponent bits (bias
+   15), 10 fraction bits.  Exponent 0 holds zero and the subnormals
+   (fraction * 2^-24), exponent 31 infinity and NaN. */
+static float f16_to_f32(uint16_t h) {
+  uint32_t sign = (uint32_t)(h & 0x8000u) << 16;
+  uint32_t ex = (h >> 10) & 0x1fu;
+  uint32_t fr = h & 0x3ffu;
+  if (ex == 0x1fu) return f32_from_bits(sign | 0x7f800000u | (fr << 13));
+  if (ex == 0) {
+    float v = (float)fr * 0x1p-24f;  /* exact: fr < 2^10 */
+    return sign ? -v : v;
+  }
+  return f32_from_bits(sign | ((ex + 112u) << 23) | (fr << 13));
+}
+
+/* Narrow binary32 -> binary16, round to nearest, ties to even ([P3] lists
+   FP16 beside BF16; one conversion at the final write).  A finite x is
+   first written as an integer count of its binary16 unit: 2^(e-25) for the
+   normal range (e = x's unbiased exponent + 15), 2^-24 below it; the bits
+   below that unit are the rounding remainder.  Rounding up can carry into
+   the exponent field, which is the correct next value; magnitudes from
+   65520 (half-way past the largest finite 65504, a tie that goes to the
+   even neighbour, infinity) round to infinity.  NaN stays NaN (quiet, sign
+   kept). */
+static uint16_t f32_to_f16(float x) {
+  uint32_t u = bits_from_f32(x);
+  uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+  uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return (uint16_t)(sign | 0x7e00u | ((a >> 13) & 0x3ffu));
+  if (a >= 0x477ff000u) return (uint16_t)(sign | 0x7c00u);   /* >= 65520: infinity */
+  uint32_t e = a >> 23;                  /* biased binary32 exponent */
+  uint32_t mant = (a & 0x7fffffu) | (e ? 0x800000u : 0u);
+  uint32_t shift, q, rest, half;
+  if (e >= 113) {                        /* binary16 normal range: >= 2^-14 */
+    shift = 13;
+    q = (((e - 112u) << 10) | ((a >> 13) & 0x3ffu));
+    rest = a & 0x1fffu;
+  } else {                               /* subnormal or zero: unit 2^-24 */
+    shift = 126u - e;                    /* x = mant * 2^(e-150) = (mant >> shift) units */
+    if (e == 0 || shift > 24) return sign;   /* below 2^-25: rounds to zero */
+    q = mant >> shift;
+    rest = mant & ((1u << shift) - 1u);
+  }
+  half = 1u << (shift - 1);
+  if (rest > half || (rest == half && (q & 1u))) q += 1u;
+  return (uint16_t)(sign | q);
+}
+
 static float load_elem(int dt, const void *base, int64_t idx) {
   if (dt == DT_BF16) return bf16_to_f32(((const uint16_t *)base)[idx]);
+  if (dt == DT_F16) return f16_to_f32(((const uint16_t *)base)[idx]);
   return ((const float *)base)[idx];
 }
 
 static void store_elem(int dt, void *base, int64_t idx, float v) {
   if (dt == DT_BF16) ((uint16_t *)base)[idx] = f32_to_bf16(v);
+  else if (dt == DT_F16) ((uint16_t *)base)[idx] = f32_to_f16(v);
   else ((float *)base)[idx] = v;
 }
 
@@ -181,10 +234,11 @@ static void merge(float *M, float *L, float m, float l) {
    mask row (binary32, may be NULL), `sigma` the head's sink logit when
    has_sink.  Keys at or past `kend` are excluded (causal or key-length
    exclusion): they count as a score of -inf and are not read.  Writes the
-   row of probabilities and, with a sink, the sink's own probability.
-   Scratch buffers are supplied by the caller. */
+   row of probabilities, with a sink the sink's own probability, and when
+   `lse` is given the row's log-sum-exp.  Scratch buffers are supplied by
+   the caller. */
 static void fwd_row(int dt, int64_t N, int64_t kend, const void *s, const float *a,
-                    int has_sink, float sigma, void *P, float *p_sink,
+                    int has_sink, float sigma, void *P, float *p_sink, float *lse,
                     float *x, float *e, float *m, float *l) {
   const int64_t T = (N + TILE - 1) / TILE;
   float buf[TILE];
@@ -238,6 +292,13 @@ static void fwd_row(int dt, int64_t N, int64_t kend, const void *s, const float 
   }
   if (has_sink)
     *p_sink = (sigma == -INFINITY) ? 0.0f : exp_(sigma - M) * invL;
+
+  /* the row's log-sum-exp ([P3] Softmax and LSE), from the final state:
+     the exponentials summed in L are relative to M, so
+     ln(sum exp) = M + ln(L), the sink included when there is one.  Taken
+     here as that value rounded once to binary32 (ln in double); a row with
+     nothing to sum gets -inf. */
+  if (lse) *lse = (L == 0.0f) ? -INFINITY : (float)((double)M + log((double)L));
 }
 
 /* ------------------------------------------------------------------------ */
@@ -310,6 +371,7 @@ typedef struct {
   const int32_t *key_len; /* [B] valid keys per batch entry, or NULL */
   void *out;            /* fwd: P           bwd: dS      */
   float *out_row;       /* fwd: p_sink[rows]  bwd: v[rows] (may be NULL) */
+  float *lse;           /* fwd: [rows] log-sum-exp, or NULL */
   int64_t r0, r1;
   int status;
 } job_t;
@@ -324,7 +386,7 @@ static void *fwd_worker(void *arg) {
   float *m = (float *)malloc(sizeof(float) * (size_t)T);
   float *l = (float *)malloc(sizeof(float) * (size_t)T);
   if (!x || !e || !m || !l) { j->status = -1; free(x); free(e); free(m); free(l); return NULL; }
-  const size_t es = (j->dt == DT_BF16) ? 2 : 4;
+  const size_t es = elem_size(j->dt);
   for (int64_t r = j->r0; r < j->r1; ++r) {
     /* row r = (b*H + h)*Sq + q */
     int64_t q = r % j->Sq;
@@ -337,7 +399,8 @@ static void *fwd_worker(void *arg) {
     float sigma = has_sink ? j->sink[h] : 0.0f;  /* one value per head ([P2]) */
     float *ps = has_sink ? &j->out_row[r] : NULL;
     int64_t kend = row_kend(N, j->Sq, b, q, j->causal, j->key_len);
-    fwd_row(j->dt, N, kend, srow, arow, has_sink, sigma, prow, ps, x, e, m, l);
+    fwd_row(j->dt, N, kend, srow, arow, has_sink, sigma, prow, ps, j->lse ? &j->lse[r] : NULL,
+            x, e, m, l);
   }
   free(x); free(e); free(m); free(l);
   j->status = 0;
@@ -347,7 +410,7 @@ static void *fwd_worker(void *arg) {
 static void *bwd_worker(void *arg) {
   job_t *j = (job_t *)arg;
   ieee_env();
-  const size_t es = (j->dt == DT_BF16) ? 2 : 4;
+  const size_t es = elem_size(j->dt);
   for (int64_t r = j->r0; r < j->r1; ++r) {
     int64_t q = r % j->Sq;
     int64_t b = r / (j->Sq * j->H);
@@ -399,13 +462,15 @@ static int run_jobs(job_t *proto, int64_t rows, int threads, void *(*fn)(void *)
    element (b,h,q,k) at mask[b*msb + h*msh + q*msq + k], or NULL.  causal:
    exclude keys past the causal condition.  key_len: int32 [B] valid keys per
    batch entry, or NULL.  sink: binary32 [H] or NULL.  probs: same layout as
-   scores.  p_sink: binary32 [B*H*Sq], written when sink is given.  Returns 0
-   on success. */
+   scores.  p_sink: binary32 [B*H*Sq], written when sink is given.  lse:
+   binary32 [B*H*Sq] row log-sum-exp, written when given.  Returns 0 on
+   success. */
 int jas_oracle_fwd(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t N, int64_t ld,
                    const void *scores, const float *mask, int64_t msb, int64_t msh,
                    int64_t msq, int causal, const int32_t *key_len, const float *sink,
-                   void *probs, float *p_sink, int threads) {
-  if ((dtype != DT_F32 && dtype != DT_BF16) || B < 0 || H < 0 || Sq < 0 || N < 1 || ld < N)
+                   void *probs, float *p_sink, float *lse, int threads) {
+  if ((dtype != DT_F32 && dtype != DT_BF16 && dtype != DT_F16) || B < 0 || H < 0 || Sq < 0 ||
+      N < 1 || ld < N)
     return -2;
   if (sink && !p_sink) return -3;
   int64_t rows = B * H * Sq;
@@ -414,7 +479,7 @@ int jas_oracle_fwd(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t N, int64
   memset(&j, 0, sizeof j);
   j.dt = dtype; j.B = B; j.H = H; j.Sq = Sq; j.N = N; j.ld = ld;
   j.in0 = scores; j.mask = mask; j.msb = msb; j.msh = msh; j.msq = msq;
-  j.sink = sink; j.out = probs; j.out_row = p_sink;
+  j.sink = sink; j.out = probs; j.out_row = p_sink; j.lse = lse;
   j.causal = causal; j.key_len = key_len;
   return run_jobs(&j, rows, threads, fwd_worker);
 }
@@ -426,7 +491,8 @@ int jas_oracle_fwd(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t N, int64
 int jas_oracle_bwd(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t N, int64_t ld,
                    const void *probs, const void *dprobs, int causal, const int32_t *key_len,
                    const float *p_sink, void *dscores, float *v, int threads) {
-  if ((dtype != DT_F32 && dtype != DT_BF16) || B < 0 || H < 0 || Sq < 0 || N < 1 || ld < N)
+  if ((dtype != DT_F32 && dtype != DT_BF16 && dtype != DT_F16) || B < 0 || H < 0 || Sq < 0 ||
+      N < 1 || ld < N)
     return -2;
   int64_t rows = B * H * Sq;
   if (rows == 0) return 0;
@@ -474,6 +540,12 @@ int jas_oracle_dsink(int64_t B, int64_t H, int64_t Sq, const float *v, float *d_
 float jas_oracle_exp(float y) { ieee_env(); return exp_(y); }
 float jas_oracle_log2e(void) { return log2e_f32(); }
 uint16_t jas_oracle_bf16(float x) { return f32_to_bf16(x); }
+void jas_oracle_f16_array(const float *x, uint16_t *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = f32_to_f16(x[i]);
+}
+void jas_oracle_f16_decode_array(const uint16_t *h, float *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = f16_to_f32(h[i]);
+}
 float jas_oracle_tree_sum256(const float *v) {
   float buf[TILE];
   ieee_env();
