@@ -65,14 +65,21 @@ def row_kends(wl, key_len):
     return np.clip(k, 0, N).reshape(-1)
 
 
-KERNEL_SOURCE = os.path.join(ROOT, "deterministic_attention_softmax_amd", "csrc", "jas_kernels.hip")
+CSRC = os.path.join(ROOT, "deterministic_attention_softmax_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
 def kernel_source_hash():
+    """sha256 over the kernel sources (every .h / .hip file of csrc/, in name
+    order): a traffic record is only used while it still matches."""
     import hashlib
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".h", ".hip")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
 
 
 def traffic_record_path(wl):

@@ -13,8 +13,8 @@ import ctypes
 import os
 
 __all__ = [
-    "JAS_DTYPE_F32", "JAS_DTYPE_BF16", "JAS_FLAG_MASK", "JAS_FLAG_SINK", "JAS_FLAG_CAUSAL",
-    "JAS_FLAG_KEY_LEN", "JAS_MAX_KEYS",
+    "JAS_DTYPE_F32", "JAS_DTYPE_BF16", "JAS_DTYPE_F16", "JAS_FLAG_MASK", "JAS_FLAG_SINK",
+    "JAS_FLAG_CAUSAL", "JAS_FLAG_KEY_LEN", "JAS_FLAG_LSE", "JAS_MAX_KEYS",
     "STATUS", "JasError", "jas_desc_t", "jas_launch_t", "lib", "jas_fwd", "jas_fwd_ex",
     "jas_bwd", "jas_bwd_ex", "jas_bwd_workspace_bytes", "jas_status_str", "jas_contract",
     "make_desc", "fwd", "bwd", "LIB_PATH",
@@ -22,8 +22,8 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libjas.so")
 
-JAS_DTYPE_F32, JAS_DTYPE_BF16 = 0, 1
-JAS_FLAG_MASK, JAS_FLAG_SINK, JAS_FLAG_CAUSAL, JAS_FLAG_KEY_LEN = 1, 2, 4, 8
+JAS_DTYPE_F32, JAS_DTYPE_BF16, JAS_DTYPE_F16 = 0, 1, 2
+JAS_FLAG_MASK, JAS_FLAG_SINK, JAS_FLAG_CAUSAL, JAS_FLAG_KEY_LEN, JAS_FLAG_LSE = 1, 2, 4, 8, 16
 JAS_MAX_KEYS = 16384
 STATUS = {
     0: "JAS_OK", 1: "JAS_ERR_NULL_POINTER", 2: "JAS_ERR_BAD_SHAPE", 3: "JAS_ERR_BAD_DTYPE",
@@ -68,9 +68,9 @@ def lib():
             raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
         L = ctypes.CDLL(LIB_PATH)
         L.jas_fwd.restype = ctypes.c_int
-        L.jas_fwd.argtypes = [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]
+        L.jas_fwd.argtypes = [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]
         L.jas_fwd_ex.restype = ctypes.c_int
-        L.jas_fwd_ex.argtypes = [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _LP, _VP]
+        L.jas_fwd_ex.argtypes = [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _LP, _VP]
         L.jas_bwd.restype = ctypes.c_int
         L.jas_bwd.argtypes = [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]
         L.jas_bwd_ex.restype = ctypes.c_int
@@ -88,14 +88,15 @@ def lib():
 
 # ---- the C entry points, one to one -------------------------------------
 
-def jas_fwd(desc, scores, mask, key_len, sink, probs, p_sink, stream):
-    return lib().jas_fwd(ctypes.byref(desc), scores, mask, key_len, sink, probs, p_sink, stream)
+def jas_fwd(desc, scores, mask, key_len, sink, probs, p_sink, lse, stream):
+    return lib().jas_fwd(ctypes.byref(desc), scores, mask, key_len, sink, probs, p_sink, lse,
+                         stream)
 
 
-def jas_fwd_ex(desc, scores, mask, key_len, sink, probs, p_sink, launch, stream):
+def jas_fwd_ex(desc, scores, mask, key_len, sink, probs, p_sink, lse, launch, stream):
     lp = ctypes.byref(launch) if launch is not None else None
-    return lib().jas_fwd_ex(ctypes.byref(desc), scores, mask, key_len, sink, probs, p_sink, lp,
-                            stream)
+    return lib().jas_fwd_ex(ctypes.byref(desc), scores, mask, key_len, sink, probs, p_sink, lse,
+                            lp, stream)
 
 
 def jas_bwd(desc, probs, dprobs, key_len, p_sink, dscores, d_sink, workspace, workspace_bytes,
@@ -151,6 +152,8 @@ def _dtype_code(t):
         return JAS_DTYPE_BF16
     if t.dtype == torch.float32:
         return JAS_DTYPE_F32
+    if t.dtype == torch.float16:
+        return JAS_DTYPE_F16
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
@@ -212,13 +215,14 @@ def _check_vec(t, like, dtype, count, name):
 
 
 def fwd(scores, mask=None, mask_strides=None, sink=None, out=None, p_sink=None, launch=None,
-        causal=False, key_len=None):
-    """Forward on device tensors.  ``scores`` [B,H,Sq,N] bf16/fp32 (rows may
-    have a stride ld >= N); ``mask`` fp32 addressed with ``mask_strides``
+        causal=False, key_len=None, lse=None, want_lse=False):
+    """Forward on device tensors.  ``scores`` [B,H,Sq,N] bf16/fp16/fp32 (rows
+    may have a stride ld >= N); ``mask`` fp32 addressed with ``mask_strides``
     (b, h, q) in elements (default: a contiguous [B,H,Sq,N] tensor broadcast
     by its own zero strides); ``sink`` fp32 [H]; ``causal`` excludes keys past
     the causal condition; ``key_len`` int32 [B] excludes keys past each batch
-    entry's length.  Returns (probs, p_sink)."""
+    entry's length.  Returns (probs, p_sink), or (probs, p_sink, lse) when
+    ``want_lse`` is set or an ``lse`` output (fp32 [B*H*Sq]) is given."""
     import torch
     shape, ld = _shape4(scores)
     B, H, S, N = shape
@@ -248,11 +252,19 @@ def fwd(scores, mask=None, mask_strides=None, sink=None, out=None, p_sink=None, 
         p_sink = torch.empty(rows, dtype=torch.float32, device=scores.device)
     if sink is not None:
         _check_vec(p_sink, scores, torch.float32, rows, "p_sink")
+    want_lse = want_lse or lse is not None
+    if want_lse:
+        d.flags |= JAS_FLAG_LSE
+        if lse is None:
+            lse = torch.empty(rows, dtype=torch.float32, device=scores.device)
+        _check_vec(lse, scores, torch.float32, rows, "lse")
     st = jas_fwd_ex(d, _ptr(scores), _ptr(mask), _ptr(key_len), _ptr(sink), _ptr(out),
-                    _ptr(p_sink) if sink is not None else None, _launch(launch), _stream())
+                    _ptr(p_sink) if sink is not None else None, _ptr(lse) if want_lse else None,
+                    _launch(launch), _stream())
     if st != 0:
         raise JasError(st, "jas_fwd")
-    return out, (p_sink if sink is not None else None)
+    ps = p_sink if sink is not None else None
+    return (out, ps, lse) if want_lse else (out, ps)
 
 
 def bwd(probs, dprobs, p_sink=None, out=None, d_sink=None, workspace=None, launch=None,

@@ -26,8 +26,10 @@ bool add_ok(int64_t a, int64_t b, int64_t *out) { return !__builtin_add_overflow
 
 jas_status_t check_desc(const jas_desc_t *d, Dims *dims) {
   if (!d) return JAS_ERR_NULL_POINTER;
-  if (d->dtype != JAS_DTYPE_F32 && d->dtype != JAS_DTYPE_BF16) return JAS_ERR_BAD_DTYPE;
-  if (d->flags & ~(uint32_t)(JAS_FLAG_MASK | JAS_FLAG_SINK | JAS_FLAG_CAUSAL | JAS_FLAG_KEY_LEN))
+  if (d->dtype != JAS_DTYPE_F32 && d->dtype != JAS_DTYPE_BF16 && d->dtype != JAS_DTYPE_F16)
+    return JAS_ERR_BAD_DTYPE;
+  if (d->flags & ~(uint32_t)(JAS_FLAG_MASK | JAS_FLAG_SINK | JAS_FLAG_CAUSAL | JAS_FLAG_KEY_LEN |
+                             JAS_FLAG_LSE))
     return JAS_ERR_BAD_FLAGS;
   if (d->batch < 0 || d->heads < 0 || d->q_rows < 0 || d->keys < 1 || d->ld < d->keys)
     return JAS_ERR_BAD_SHAPE;
@@ -35,7 +37,7 @@ jas_status_t check_desc(const jas_desc_t *d, Dims *dims) {
     return JAS_ERR_BAD_SHAPE;
   int64_t bh = 0, rows = 0, span = 0, bytes = 0;
   if (!mul_ok(d->batch, d->heads, &bh) || !mul_ok(bh, d->q_rows, &rows)) return JAS_ERR_BAD_SHAPE;
-  const int64_t esz = d->dtype == JAS_DTYPE_BF16 ? 2 : 4;
+  const int64_t esz = d->dtype == JAS_DTYPE_F32 ? 4 : 2;
   if (rows > 0) {
     if (!mul_ok(rows - 1, d->ld, &span) || !add_ok(span, d->keys, &span) ||
         !mul_ok(span, esz, &bytes))
@@ -131,23 +133,26 @@ jas_status_t choose_geometry(int dtype, int T, int64_t rows, bool backward, cons
 
 jas_status_t fwd_impl(const jas_desc_t *d, const void *scores, const float *mask,
                       const int32_t *key_len, const float *sink, void *probs, float *p_sink,
-                      const jas_launch_t *launch, void *stream) {
+                      float *lse, const jas_launch_t *launch, void *stream) {
   Dims dm;
   jas_status_t st = check_desc(d, &dm);
   if (st != JAS_OK) return st;
   const bool has_mask = (d->flags & JAS_FLAG_MASK) != 0;
   const bool has_sink = (d->flags & JAS_FLAG_SINK) != 0;
   const bool has_klen = (d->flags & JAS_FLAG_KEY_LEN) != 0;
-  if ((!has_mask && mask) || (!has_sink && (sink || p_sink)) || (!has_klen && key_len))
+  const bool has_lse = (d->flags & JAS_FLAG_LSE) != 0;
+  if ((!has_mask && mask) || (!has_sink && (sink || p_sink)) || (!has_klen && key_len) ||
+      (!has_lse && lse))
     return JAS_ERR_BAD_FLAGS;
   if (dm.rows == 0) return JAS_OK;  // nothing is read or written; row pointers may be NULL
   if (!scores || !probs) return JAS_ERR_NULL_POINTER;
   if (has_mask && !mask) return JAS_ERR_NULL_POINTER;
   if (has_sink && (!sink || !p_sink)) return JAS_ERR_NULL_POINTER;
   if (has_klen && !key_len) return JAS_ERR_NULL_POINTER;
+  if (has_lse && !lse) return JAS_ERR_NULL_POINTER;
   if (!aligned(scores, dm.esz) || !aligned(probs, dm.esz) || (mask && !aligned(mask, 4)) ||
       (sink && !aligned(sink, 4)) || (p_sink && !aligned(p_sink, 4)) ||
-      (key_len && !aligned(key_len, 4)))
+      (key_len && !aligned(key_len, 4)) || (lse && !aligned(lse, 4)))
     return JAS_ERR_ALIGNMENT;
 
   const int64_t tbytes = dm.span * dm.esz;
@@ -161,10 +166,15 @@ jas_status_t fwd_impl(const jas_desc_t *d, const void *scores, const float *mask
   const Range rk = range_of(sink, has_sink ? d->heads * 4 : 0);
   const Range rps = range_of(p_sink, has_sink ? dm.rows * 4 : 0);
   const Range rkl = range_of(key_len, has_klen ? d->batch * 4 : 0);
+  const Range rl = range_of(lse, has_lse ? dm.rows * 4 : 0);
   if (probs != scores && overlap(rp, rs)) return JAS_ERR_ALIASING;
-  if (overlap(rp, rm) || overlap(rp, rk) || overlap(rp, rps) || overlap(rp, rkl))
+  if (overlap(rp, rm) || overlap(rp, rk) || overlap(rp, rps) || overlap(rp, rkl) ||
+      overlap(rp, rl))
     return JAS_ERR_ALIASING;
-  if (overlap(rps, rs) || overlap(rps, rm) || overlap(rps, rk) || overlap(rps, rkl))
+  if (overlap(rps, rs) || overlap(rps, rm) || overlap(rps, rk) || overlap(rps, rkl) ||
+      overlap(rps, rl))
+    return JAS_ERR_ALIASING;
+  if (overlap(rl, rs) || overlap(rl, rm) || overlap(rl, rk) || overlap(rl, rkl))
     return JAS_ERR_ALIASING;
 
   Geometry g;
@@ -180,6 +190,7 @@ jas_status_t fwd_impl(const jas_desc_t *d, const void *scores, const float *mask
   a.ex = jas::Exclusion{(d->flags & JAS_FLAG_CAUSAL) ? 1 : 0, has_klen ? key_len : nullptr};
   a.sink = has_sink ? sink : nullptr;
   a.p_sink = has_sink ? p_sink : nullptr;
+  a.lse = has_lse ? lse : nullptr;
   a.s = jas::RowShape{dm.rows, d->keys, d->ld, d->heads, d->q_rows, dm.T};
   // 16-byte path: every row is whole 16-byte chunks starting on 16-byte
   // boundaries (and so is every mask row); otherwise element-wise access.
@@ -274,14 +285,14 @@ extern "C" {
 
 jas_status_t jas_fwd(const jas_desc_t *desc, const void *scores, const float *mask,
                      const int32_t *key_len, const float *sink, void *probs, float *p_sink,
-                     void *stream) {
-  return fwd_impl(desc, scores, mask, key_len, sink, probs, p_sink, nullptr, stream);
+                     float *lse, void *stream) {
+  return fwd_impl(desc, scores, mask, key_len, sink, probs, p_sink, lse, nullptr, stream);
 }
 
 jas_status_t jas_fwd_ex(const jas_desc_t *desc, const void *scores, const float *mask,
                         const int32_t *key_len, const float *sink, void *probs, float *p_sink,
-                        const jas_launch_t *launch, void *stream) {
-  return fwd_impl(desc, scores, mask, key_len, sink, probs, p_sink, launch, stream);
+                        float *lse, const jas_launch_t *launch, void *stream) {
+  return fwd_impl(desc, scores, mask, key_len, sink, probs, p_sink, lse, launch, stream);
 }
 
 size_t jas_bwd_workspace_bytes(const jas_desc_t *desc) {
@@ -325,8 +336,8 @@ const char *jas_status_str(jas_status_t s) {
 
 const char *jas_contract(void) {
   return "jas/1 tile=256 tree=balanced-pairwise-by-key fold=left-to-right sink=merged-last "
-         "exclusion=suffix(causal,key_len) "
-         "acc=fp32 exp=2^fl(y*log2e),flush<2^-126,v_exp_f32 div=ieee cvt=rne "
+         "exclusion=suffix(causal,key_len) lse=M+fl(log2(L)*ln2),v_log_f32 "
+         "acc=fp32 exp=2^fl(y*log2e),flush<2^-126,v_exp_f32 div=ieee cvt=rne(bf16,f16) "
          "fpcontract=off atomics=none dsink=256-row-chunks,left-fold arch=gfx950";
 }
 

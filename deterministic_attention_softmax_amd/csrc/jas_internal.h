@@ -1,5 +1,6 @@
 // Internal interface between the host validation layer (jas_api.cpp) and the
-// gfx950 kernels (jas_kernels.hip).  Not installed; the public ABI is jas.h.
+// gfx950 kernels (jas_kernels.h, instantiated per element type in
+// jas_kernels_<dtype>.hip; jas_launch.hip dispatches).  Not installed; the public ABI is jas.h.
 #pragma once
 
 #include <stdint.h>
@@ -36,6 +37,7 @@ struct FwdArgs {
   Exclusion ex;
   const float *sink;  // nullptr when no sink
   float *p_sink;
+  float *lse;         // nullptr when the row log-sum-exp is not asked for
   RowShape s;
   int vec_io;         // 16-byte path: rows (and mask rows) are whole aligned 16-byte chunks
   int vec_mask;       // mask rows start on 16-byte boundaries (or no mask)
@@ -65,14 +67,23 @@ struct Geometry {
   int64_t blocks;  // grid size
 };
 
-// Keys held by one 16-byte chunk: 8 bf16 or 4 fp32.
-inline int keys_per_chunk(int dtype) { return dtype == 1 ? 8 : 4; }
+// dtype codes: 0 fp32, 1 bf16, 2 fp16 (jas_dtype_t)
+// Keys held by one 16-byte chunk: 8 bf16 / fp16 or 4 fp32.
+inline int keys_per_chunk(int dtype) { return dtype == 0 ? 4 : 8; }
 // Tiles covered by one wave-wide chunk (64 lanes x 16 bytes).
-inline int tiles_per_slot(int dtype) { return dtype == 1 ? 2 : 1; }
+inline int tiles_per_slot(int dtype) { return dtype == 0 ? 1 : 2; }
 
 bool cpl_compiled(int dtype, int wpr, int cpl);
 int default_wpr(int dtype, int nslots, bool backward);
 const int *compiled_cpls(int dtype, int *count);
+
+// one per element type, each in its own translation unit
+hipError_t launch_fwd_f32(const FwdArgs &a, const Geometry &g, hipStream_t stream);
+hipError_t launch_bwd_f32(const BwdArgs &a, const Geometry &g, hipStream_t stream);
+hipError_t launch_fwd_bf16(const FwdArgs &a, const Geometry &g, hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdArgs &a, const Geometry &g, hipStream_t stream);
+hipError_t launch_fwd_f16(const FwdArgs &a, const Geometry &g, hipStream_t stream);
+hipError_t launch_bwd_f16(const BwdArgs &a, const Geometry &g, hipStream_t stream);
 
 hipError_t launch_fwd(int dtype, const FwdArgs &a, const Geometry &g, hipStream_t stream);
 hipError_t launch_bwd(int dtype, const BwdArgs &a, const Geometry &g, hipStream_t stream);

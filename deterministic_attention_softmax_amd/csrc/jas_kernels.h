@@ -1,5 +1,8 @@
-// jas_kernels.hip -- gfx950 kernels of the fixed-order, batch-invariant row
-// softmax (forward, backward, per-head d_sink).
+// jas_kernels.h -- gfx950 kernels of the fixed-order, batch-invariant row
+// softmax (forward and backward templates and their launch tables).  Each
+// jas_kernels_<dtype>.hip includes this file and instantiates one element
+// type, so the instances compile in parallel; jas_launch.hip holds the
+// per-head d_sink kernel and the dispatch by dtype.
 //
 // Method: RL-Kernel PR #453, "[WS1][kernels] Add fixed-order joint-attention
 // softmax for Qwen-Image", Summary (fixed-order online softmax over 256-key
@@ -12,9 +15,9 @@
 //
 // Mapping to CDNA4.  A row is owned by one wavefront (or by 2 or 4
 // wavefronts of one workgroup for long rows).  The row is read as 16-byte
-// chunks: a lane's chunk is 8 consecutive bf16 keys or 4 consecutive fp32
-// keys, so a 256-key tile is 32 lanes (bf16) or 64 lanes (fp32) and one
-// wave-wide load ("slot") covers 2 or 1 tiles.  The balanced pairwise tile
+// chunks: a lane's chunk is 8 consecutive bf16 / fp16 keys or 4 consecutive
+// fp32 keys, so a 256-key tile is 32 lanes (16-bit types) or 64 lanes (fp32)
+// and one wave-wide load ("slot") covers 2 or 1 tiles.  The balanced pairwise tile
 // tree is realised exactly: pairwise adds inside the lane over its
 // consecutive keys, then across lanes with DPP quad permutes (lane xor 1,
 // xor 2), row half-mirror and row mirror (groups of 8 and 16 lanes whose
@@ -30,6 +33,8 @@
 // Built with -ffp-contract=off (no fused multiply-add is formed from a*b+c),
 // without fast-math, FP32 denormals preserved.
 
+#pragma once
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -43,9 +48,11 @@ namespace jas {
 namespace {
 
 constexpr float kLog2e = 0x1.715476p+0f;  // binary32 nearest to log2(e)
+constexpr float kLn2 = 0x1.62e430p-1f;    // binary32 nearest to ln(2)
 constexpr float kNegInf = -__builtin_inff();
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
@@ -67,6 +74,21 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return u2f(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return u2f(w & 0xffff0000u); }
+
+// Round two binary32 to binary16 (round to nearest-even, subnormals kept,
+// overflow to infinity) and pack them, low half first.
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+
+// Two binary16 (low half first) widened to binary32, exactly.
+__device__ __forceinline__ f32x2_t unpack_f16(uint32_t w) {
+  return __builtin_convertvector(__builtin_bit_cast(f16x2_t, w), f32x2_t);
+}
+
+// ln(L) for the row log-sum-exp: the hardware base-2 logarithm times ln 2.
+__device__ __forceinline__ float ln_(float L) { return __builtin_amdgcn_logf(L) * kLn2; }
 
 // ---------------------------------------------------------------------------
 // Cross-lane steps of the tile tree
@@ -160,6 +182,12 @@ template <> struct Cfg<1> {  // bf16
   static constexpr int TPS = 2;
   static constexpr int ESZ = 2;
 };
+template <> struct Cfg<2> : Cfg<1> {};  // fp16: the bf16 layout
+
+// Bits of -inf, twice for the 16-bit types (the fill of keys past a row).
+template <int DT> constexpr uint32_t kNegInfBits = 0xff800000u;
+template <> constexpr uint32_t kNegInfBits<1> = 0xff80ff80u;
+template <> constexpr uint32_t kNegInfBits<2> = 0xfc00fc00u;
 
 // A 16-byte chunk as 4 words.
 struct Chunk { uint32_t w[4]; };
@@ -183,7 +211,7 @@ __device__ __forceinline__ void store_chunk(char *p, const Chunk &c) {
 template <int DT>
 __device__ __forceinline__ Chunk load_chunk_elems(const char *row, int j0, int n, uint32_t fill) {
   Chunk c;
-  if constexpr (DT == 1) {
+  if constexpr (DT != 0) {
     const uint16_t *e = reinterpret_cast<const uint16_t *>(row);
     const uint32_t f = fill & 0xffffu;
 #pragma unroll
@@ -206,7 +234,7 @@ __device__ __forceinline__ Chunk load_chunk_elems(const char *row, int j0, int n
 
 template <int DT>
 __device__ __forceinline__ void store_chunk_elems(char *row, int j0, int n, const Chunk &c) {
-  if constexpr (DT == 1) {
+  if constexpr (DT != 0) {
     uint16_t *e = reinterpret_cast<uint16_t *>(row);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -232,6 +260,13 @@ __device__ __forceinline__ void unpack(const Chunk &c, float (&x)[Cfg<DT>::KPL])
       x[2 * i] = bf16_lo(c.w[i]);
       x[2 * i + 1] = bf16_hi(c.w[i]);
     }
+  } else if constexpr (DT == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x2_t v = unpack_f16(c.w[i]);
+      x[2 * i] = v[0];
+      x[2 * i + 1] = v[1];
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = u2f(c.w[i]);
@@ -244,6 +279,9 @@ __device__ __forceinline__ Chunk pack(const float (&x)[Cfg<DT>::KPL]) {
   if constexpr (DT == 1) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) c.w[i] = pack_bf16(x[2 * i], x[2 * i + 1]);
+  } else if constexpr (DT == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c.w[i] = pack_f16(x[2 * i], x[2 * i + 1]);
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) c.w[i] = f2u(x[i]);
@@ -390,7 +428,7 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void fwd_kernel(const FwdArgs 
   using C = Cfg<DT>;
   constexpr int KPL = C::KPL, TPS = C::TPS, ESZ = C::ESZ;
   // keys past the row read as -inf (the max's identity; their e is +0)
-  constexpr uint32_t kFill = (DT == 1) ? 0xff80ff80u : 0xff800000u;
+  constexpr uint32_t kFill = kNegInfBits<DT>;
   __shared__ float lds_m[kBlockWaves][kMaxTiles];
   __shared__ float lds_l[kBlockWaves][kMaxTiles];
 
@@ -578,6 +616,8 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void fwd_kernel(const FwdArgs 
       }
       if (has_sink && ix.wir == 0 && lane == 0)
         a.p_sink[r] = (sigma == kNegInf) ? 0.0f : exp_(sigma - M) * invL;
+      if (a.lse && ix.wir == 0 && lane == 0)
+        a.lse[r] = (L == 0.0f) ? kNegInf : M + ln_(L);
     }
     if constexpr (WPR > 1) __syncthreads();  // LDS is reused by the next row group
     else wave_sync();
@@ -647,7 +687,7 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void bwd_kernel(const BwdArgs 
           const int nv = lim - sb;  // this lane's visible keys in its chunk
 #pragma unroll
           for (int i = 0; i < 4; ++i) {  // keys at or past kend: P = +0
-            if constexpr (DT == 1)
+            if constexpr (DT != 0)  // two 16-bit keys per word, low half first
               rp[s].w[i] &= (nv > 2 * i ? 0x0000ffffu : 0u) | (nv > 2 * i + 1 ? 0xffff0000u : 0u);
             else
               rp[s].w[i] = nv > i ? rp[s].w[i] : 0u;
@@ -697,55 +737,12 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void bwd_kernel(const BwdArgs 
 }
 
 // ---------------------------------------------------------------------------
-// d_sink: per head, 256-row chunks in (batch, query) order, balanced tree per
-// chunk, chunk sums folded left to right.  One workgroup per head, one
-// wavefront per chunk; lane l holds the chunk's rows 4l..4l+3.
-// ---------------------------------------------------------------------------
-
-constexpr int kDsinkWaves = 16;
-
-__global__ __launch_bounds__(kWave * kDsinkWaves) void dsink_kernel(const DsinkArgs a) {
-  __shared__ float part[kDsinkWaves];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int64_t h = blockIdx.x;
-  const int64_t n = a.B * a.Sq;
-  const int64_t chunks = (n + kTile - 1) / kTile;
-  float D = 0.0f;
-  for (int64_t k0 = 0; k0 < chunks; k0 += kDsinkWaves) {
-    const int64_t k = k0 + wave;
-    float cs = 0.0f;
-    if (k < chunks) {
-      float v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t idx = k * kTile + lane * 4 + i;  // position in the head's row list
-        if (idx < n) {
-          const int64_t bb = idx / a.Sq, qq = idx - bb * a.Sq;
-          v[i] = a.v[(bb * a.H + h) * a.Sq + qq];
-        } else {
-          v[i] = 0.0f;
-        }
-      }
-      cs = group64_sum((v[0] + v[1]) + (v[2] + v[3]));
-    }
-    if (lane == 0) part[wave] = cs;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const int64_t m = (chunks - k0 < kDsinkWaves) ? chunks - k0 : kDsinkWaves;
-      for (int64_t i = 0; i < m; ++i) D = (k0 + i == 0) ? part[i] : D + part[i];
-    }
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) a.d_sink[h] = D;
-}
-
-// ---------------------------------------------------------------------------
 // Launch tables
 // ---------------------------------------------------------------------------
 
 // chunks-per-lane sizes compiled for each dtype (register budget: the row's
-// share is kept in registers between the reduction and the write)
+// share is kept in registers between the reduction and the write); the
+// 16-bit types share one list
 constexpr int kCplF32[] = {1, 2, 3, 5, 9, 17};
 constexpr int kCplBf16[] = {1, 2, 3, 5, 9};
 
@@ -834,53 +831,4 @@ hipError_t bwd_dt(const BwdArgs &a, const Geometry &g, hipStream_t st) {
 }
 
 }  // namespace
-
-const int *compiled_cpls(int dtype, int *count) {
-  if (dtype == 1) {
-    *count = (int)(sizeof(kCplBf16) / sizeof(int));
-    return kCplBf16;
-  }
-  *count = (int)(sizeof(kCplF32) / sizeof(int));
-  return kCplF32;
-}
-
-bool cpl_compiled(int dtype, int wpr, int cpl) {
-  if (wpr != 1 && wpr != 2 && wpr != 4) return false;
-  int n = 0;
-  const int *c = compiled_cpls(dtype, &n);
-  for (int i = 0; i < n; ++i)
-    if (c[i] == cpl) return true;
-  return false;
-}
-
-// Default waves per row for a row of `nslots` wave-wide chunks (the
-// chunks-per-lane size then is the smallest compiled one that covers the
-// row).  Measured on MI355X, bf16 (fp32 rows are twice as many slots for the
-// same keys and registers): the forward runs fastest with one wavefront per
-// row up to 9 slots (4,608 keys), two up to 18, four beyond; the backward,
-// which keeps two inputs in registers, with one wavefront up to 4 slots and
-// four beyond.  Any choice gives the same bits.
-int default_wpr(int dtype, int nslots, bool backward) {
-  const int u = dtype == 1 ? 1 : 2;  // slots per bf16-slot of keys
-  const int cap = 4 * (dtype == 1 ? 9 : 17);
-  if (nslots > cap) return 0;
-  if (backward) return nslots <= 4 * u ? 1 : 4;
-  if (nslots <= 9 * u) return 1;
-  if (nslots <= 18 * u) return 2;
-  return 4;
-}
-
-hipError_t launch_fwd(int dtype, const FwdArgs &a, const Geometry &g, hipStream_t st) {
-  return dtype == 1 ? fwd_dt<1>(a, g, st) : fwd_dt<0>(a, g, st);
-}
-
-hipError_t launch_bwd(int dtype, const BwdArgs &a, const Geometry &g, hipStream_t st) {
-  return dtype == 1 ? bwd_dt<1>(a, g, st) : bwd_dt<0>(a, g, st);
-}
-
-hipError_t launch_dsink(const DsinkArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL(dsink_kernel, dim3((unsigned)a.H), dim3(kWave * kDsinkWaves), 0, st, a);
-  return hipGetLastError();
-}
-
 }  // namespace jas

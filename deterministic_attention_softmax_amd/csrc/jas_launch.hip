@@ -1,0 +1,116 @@
+// jas_launch.hip -- the per-head d_sink kernel, the compiled launch
+// geometries and the dispatch of the row kernels by element type.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "jas_kernels.h"
+
+namespace jas {
+namespace {
+
+// ---------------------------------------------------------------------------
+// d_sink: per head, 256-row chunks in (batch, query) order, balanced tree per
+// chunk, chunk sums folded left to right.  One workgroup per head, one
+// wavefront per chunk; lane l holds the chunk's rows 4l..4l+3.
+// ---------------------------------------------------------------------------
+
+constexpr int kDsinkWaves = 16;
+
+__global__ __launch_bounds__(kWave * kDsinkWaves) void dsink_kernel(const DsinkArgs a) {
+  __shared__ float part[kDsinkWaves];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int64_t h = blockIdx.x;
+  const int64_t n = a.B * a.Sq;
+  const int64_t chunks = (n + kTile - 1) / kTile;
+  float D = 0.0f;
+  for (int64_t k0 = 0; k0 < chunks; k0 += kDsinkWaves) {
+    const int64_t k = k0 + wave;
+    float cs = 0.0f;
+    if (k < chunks) {
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t idx = k * kTile + lane * 4 + i;  // position in the head's row list
+        if (idx < n) {
+          const int64_t bb = idx / a.Sq, qq = idx - bb * a.Sq;
+          v[i] = a.v[(bb * a.H + h) * a.Sq + qq];
+        } else {
+          v[i] = 0.0f;
+        }
+      }
+      cs = group64_sum((v[0] + v[1]) + (v[2] + v[3]));
+    }
+    if (lane == 0) part[wave] = cs;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int64_t m = (chunks - k0 < kDsinkWaves) ? chunks - k0 : kDsinkWaves;
+      for (int64_t i = 0; i < m; ++i) D = (k0 + i == 0) ? part[i] : D + part[i];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) a.d_sink[h] = D;
+}
+
+}  // namespace
+
+const int *compiled_cpls(int dtype, int *count) {
+  if (dtype != 0) {  // 16-bit types
+    *count = (int)(sizeof(kCplBf16) / sizeof(int));
+    return kCplBf16;
+  }
+  *count = (int)(sizeof(kCplF32) / sizeof(int));
+  return kCplF32;
+}
+
+bool cpl_compiled(int dtype, int wpr, int cpl) {
+  if (wpr != 1 && wpr != 2 && wpr != 4) return false;
+  int n = 0;
+  const int *c = compiled_cpls(dtype, &n);
+  for (int i = 0; i < n; ++i)
+    if (c[i] == cpl) return true;
+  return false;
+}
+
+// Default waves per row for a row of `nslots` wave-wide chunks (the
+// chunks-per-lane size then is the smallest compiled one that covers the
+// row).  Measured on MI355X, bf16 (fp16 is laid out the same; fp32 rows are
+// twice as many slots for the same keys and registers): the forward runs fastest with one wavefront per
+// row up to 9 slots (4,608 keys), two up to 18, four beyond; the backward,
+// which keeps two inputs in registers, with one wavefront up to 4 slots and
+// four beyond.  Any choice gives the same bits.
+int default_wpr(int dtype, int nslots, bool backward) {
+  const int u = dtype == 0 ? 2 : 1;  // slots per 16-bit-type slot of keys
+  const int cap = 4 * (dtype == 0 ? 17 : 9);
+  if (nslots > cap) return 0;
+  if (backward) return nslots <= 4 * u ? 1 : 4;
+  if (nslots <= 9 * u) return 1;
+  if (nslots <= 18 * u) return 2;
+  return 4;
+}
+
+hipError_t launch_fwd(int dtype, const FwdArgs &a, const Geometry &g, hipStream_t st) {
+  switch (dtype) {
+    case 0: return launch_fwd_f32(a, g, st);
+    case 1: return launch_fwd_bf16(a, g, st);
+    case 2: return launch_fwd_f16(a, g, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_bwd(int dtype, const BwdArgs &a, const Geometry &g, hipStream_t st) {
+  switch (dtype) {
+    case 0: return launch_bwd_f32(a, g, st);
+    case 1: return launch_bwd_bf16(a, g, st);
+    case 2: return launch_bwd_f16(a, g, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_dsink(const DsinkArgs &a, hipStream_t st) {
+  hipLaunchKernelGGL(dsink_kernel, dim3((unsigned)a.H), dim3(kWave * kDsinkWaves), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace jas

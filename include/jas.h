@@ -20,7 +20,9 @@
  *   - RL-Kernel PR #240, "Batch-invariant attention (standard softmax --
  *     cuda version)", Fixed Reduction Contract and Path Status: the reduction
  *     tree's shape depends on nothing but the tile (not on batch size, row
- *     position, launch geometry or grid), and fully masked rows are handled.
+ *     position, launch geometry or grid), fully masked rows are handled, the
+ *     row's log-sum-exp is a second output, and FP16 is a dtype beside
+ *     BF16.
  *
  * Exact arithmetic of one row of N keys, T = ceil(N/256) tiles (every
  * operation binary32, round to nearest-even, no fused multiply-add):
@@ -42,6 +44,9 @@
  *   invL  = 1/L (0 when L is 0)
  *   P_j   = round_to_dtype(e_j * fl(exp_(m_t - M) * invL))
  *   p_sink= fl(exp_(sigma_h - M) * invL)      (0 when sigma_h is -inf)
+ *   lse   = fl(M + fl(log2_(L) * ln2)) with the hardware base-2 logarithm
+ *           and ln2 the binary32 nearest to ln 2; -inf when L is 0.  Within
+ *           4e-6 * max(1, |lse|) of M + ln(L) rounded once.
  * Backward on the stored P (P_j taken as +0 without being read for
  * j >= kend):
  *   d_t   = balanced tree sum of fl(P_j*dP_j) over tile t; delta = d_0, then
@@ -51,8 +56,10 @@
  *           rows (the last padded with +0), each chunk summed with the same
  *           balanced tree over -fl(p_sink_r*delta_r), chunk sums added left
  *           to right from the first; d_sink is overwritten, never accumulated.
- * The exponential is the hardware base-2 exponential; everything else is
- * exact IEEE arithmetic, so results do not depend on batch size, a row's
+ * round_to_dtype is round to nearest-even into bf16 or binary16 (subnormals
+ * kept, overflow to infinity), the identity for binary32.  The exponential
+ * is the hardware base-2 exponential; everything else is exact IEEE
+ * arithmetic, so results do not depend on batch size, a row's
  * position, launch geometry or grid size.
  *
  * Conventions for every entry point:
@@ -68,7 +75,8 @@
  *   - Rows: rows = batch*heads*q_rows, row r = (b*heads + h)*q_rows + q,
  *     row r starts at element r*ld of scores / probs / dprobs / dscores.
  *   - An empty call (rows == 0) reads nothing; its row tensors (scores,
- *     probs, dprobs, dscores, mask, sink, p_sink, workspace) may be NULL.
+ *     probs, dprobs, dscores, mask, sink, p_sink, lse, workspace) may be
+ *     NULL.
  *     jas_bwd with JAS_FLAG_SINK still writes d_sink[h] = +0 for every head.
  *   - Element pointers must be aligned to their element size; any further
  *     alignment only selects the faster 16-byte load path (same results).
@@ -89,19 +97,21 @@ extern "C" {
 #define JAS_MAX_KEYS 16384
 
 /* Element type of scores, probs, dprobs and dscores.  mask, sink, p_sink,
-   d_sink and the workspace are always binary32. */
-typedef enum { JAS_DTYPE_F32 = 0, JAS_DTYPE_BF16 = 1 } jas_dtype_t;
+   lse, d_sink and the workspace are always binary32. */
+typedef enum { JAS_DTYPE_F32 = 0, JAS_DTYPE_BF16 = 1, JAS_DTYPE_F16 = 2 } jas_dtype_t;
 
-/* Flags: the only predicates for "has a mask", "has a sink", "causal" and
- * "has per-batch key lengths".  CAUSAL and KEY_LEN exclude a suffix of each
- * row: excluded keys behave exactly as keys whose score is -inf, and whole
- * 256-key tiles past the visible prefix are not read (forward: scores;
- * backward: P, which the forward wrote as +0 there). */
+/* Flags: the only predicates for "has a mask", "has a sink", "causal",
+ * "has per-batch key lengths" and "writes the row log-sum-exp".  CAUSAL and
+ * KEY_LEN exclude a suffix of each row: excluded keys behave exactly as keys
+ * whose score is -inf, and whole 256-key tiles past the visible prefix are
+ * not read (forward: scores; backward: P, which the forward wrote as +0
+ * there).  LSE applies to the forward only (the backward ignores it). */
 enum {
   JAS_FLAG_MASK = 1u << 0,
   JAS_FLAG_SINK = 1u << 1,
   JAS_FLAG_CAUSAL = 1u << 2,
-  JAS_FLAG_KEY_LEN = 1u << 3
+  JAS_FLAG_KEY_LEN = 1u << 3,
+  JAS_FLAG_LSE = 1u << 4
 };
 
 typedef enum {
@@ -154,16 +164,20 @@ typedef struct {
  *   sink   binary32 [heads], required iff JAS_FLAG_SINK.
  *   p_sink binary32 [rows] written, required iff JAS_FLAG_SINK; the sink's
  *          own probability, which jas_bwd reads.
+ *   lse    binary32 [rows] written, required iff JAS_FLAG_LSE: the row's
+ *          log-sum-exp (the sink's term included), -inf for a row with
+ *          nothing to sum.
  * (Definition: RL-Kernel PR #453, Summary, fixed-order online softmax;
- *  sink: TransformerEngine PR #678, Description.) */
+ *  sink: TransformerEngine PR #678, Description; lse: RL-Kernel PR #240,
+ *  Fixed Reduction Contract, Softmax and LSE.) */
 jas_status_t jas_fwd(const jas_desc_t *desc, const void *scores, const float *mask,
                      const int32_t *key_len, const float *sink, void *probs, float *p_sink,
-                     void *stream);
+                     float *lse, void *stream);
 
 /* jas_fwd with an explicit launch geometry (NULL = default). */
 jas_status_t jas_fwd_ex(const jas_desc_t *desc, const void *scores, const float *mask,
                         const int32_t *key_len, const float *sink, void *probs, float *p_sink,
-                        const jas_launch_t *launch, void *stream);
+                        float *lse, const jas_launch_t *launch, void *stream);
 
 /* Bytes of device workspace jas_bwd needs: 4*rows rounded up to 256 when
  * JAS_FLAG_SINK is set, else 0.  Depends on the shape and flags only (never
@@ -172,6 +186,7 @@ size_t jas_bwd_workspace_bytes(const jas_desc_t *desc);
 
 /* Backward on the stored probabilities.
  *   probs, dprobs [rows, ld] (dtype) read.  dscores [rows, ld] written;
+ *   JAS_FLAG_LSE is ignored here;
  *   dscores may equal probs or dprobs (in place), any other overlap is
  *   JAS_ERR_ALIASING.  JAS_FLAG_MASK and the mask strides are ignored:
  *   masked keys already have P = 0.  With JAS_FLAG_CAUSAL / JAS_FLAG_KEY_LEN

@@ -127,11 +127,12 @@ def synthetic_bwd_inputs(shape, dtype, seed, device, with_sink=False, zero_upper
 
 
 def to_numpy_bits(t: torch.Tensor):
-    """Host numpy view of a tensor's bytes: bf16 as uint16, fp32 as float32."""
+    """Host numpy view of a tensor's bytes: bf16 as uint16, fp16 as float16,
+    fp32 as float32."""
     t = t.detach().contiguous().cpu()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view("uint16")
-    if t.dtype == torch.float32:
+    if t.dtype in (torch.float32, torch.float16):
         return t.numpy()
     raise TypeError(f"unsupported dtype {t.dtype}")
 
@@ -141,6 +142,6 @@ def from_numpy_bits(a, device="cpu"):
     import numpy as np
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view("int16").copy()).view(torch.bfloat16).to(device)
-    if a.dtype == np.float32:
+    if a.dtype in (np.float32, np.float16):
         return torch.from_numpy(a.copy()).to(device)
     raise TypeError(f"unsupported dtype {a.dtype}")

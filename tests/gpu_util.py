@@ -1,7 +1,8 @@
 """Helpers for the GPU parity tests: comparisons at the stated tolerance and
-row sampling.  Tolerances (the acceptance bar for this softmax): bf16 results
-within 1 bf16 ulp of the oracle (+0 and -0 equal), fp32 results within
-4e-6 relative (absolute floor 1e-38 for subnormal results); stage-isolated
+row sampling.  Tolerances (the acceptance bar for this softmax): bf16 and
+fp16 results within 1 ulp of their type of the oracle (+0 and -0 equal),
+fp32 results within 4e-6 relative (absolute floor 1e-38 for subnormal
+results); the row log-sum-exp within 4e-6 * max(1, |lse|); stage-isolated
 backward results bit-exact."""
 import numpy as np
 import torch
@@ -23,8 +24,10 @@ def log(msg):
 
 
 def assert_close(got, want, what=""):
-    """got/want: numpy bit views (uint16 bf16 or float32)."""
+    """got/want: numpy bit views (uint16 bf16, float16 or float32)."""
     assert got.shape == want.shape and got.dtype == want.dtype, what
+    if got.dtype == np.float16:  # sign-magnitude 16 bits: the bf16 ordering applies
+        got, want = got.view(np.uint16), want.view(np.uint16)
     if got.dtype == np.uint16:
         d = bf16_ulp_distance(got, want)
         bad = np.count_nonzero(d > 1)
@@ -39,10 +42,30 @@ def assert_close(got, want, what=""):
 
 def assert_bitexact(got, want, what=""):
     assert got.shape == want.shape, what
-    g = got.view(np.uint16 if got.dtype == np.uint16 else np.uint32)
-    w = want.view(np.uint16 if want.dtype == np.uint16 else np.uint32)
+    g = got.view(np.uint16 if got.itemsize == 2 else np.uint32)
+    w = want.view(np.uint16 if want.itemsize == 2 else np.uint32)
     bad = np.count_nonzero(g != w)
     assert bad == 0, f"{what}: {bad} values not bit-identical"
+
+
+LSE_TOL = 4e-6
+
+
+def assert_lse_close(got, want, what="lse"):
+    """Row log-sum-exp: -inf exactly where the oracle has -inf, elsewhere
+    within 4e-6 * max(1, |lse|) (the hardware logarithm and the GPU's
+    exponentials inside L against the oracle's)."""
+    got = np.asarray(got, np.float32)
+    want = np.asarray(want, np.float32)
+    assert got.shape == want.shape, what
+    ninf = np.isneginf(want)
+    assert np.array_equal(np.isneginf(got), ninf), f"{what}: -inf rows differ"
+    g, w = got[~ninf].astype(np.float64), want[~ninf].astype(np.float64)
+    err = np.abs(g - w)
+    lim = LSE_TOL * np.maximum(1.0, np.abs(w))
+    bad = np.count_nonzero(~(err <= lim))
+    assert bad == 0, f"{what}: {bad} values outside tolerance (worst {np.max(err / lim):.3g}x)"
+    return float(np.max(err / lim)) if err.size else 0.0
 
 
 def sample_rows(rows, k, seed):

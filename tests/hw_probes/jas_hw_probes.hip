@@ -8,6 +8,11 @@
 //    differs.
 //  * bf16 conversion sweep: every binary32 bit pattern through
 //    v_cvt_pk_bf16_f32 against round-to-nearest-even on the bit pattern.
+//  * fp16 conversion sweep: every binary32 bit pattern through the packed
+//    binary32 -> binary16 conversion against round-to-nearest-even
+//    (subnormals kept, overflow to infinity).
+//  * log2 sweep: every binary32 in [1, 32768] (the range of a row's sum L)
+//    through v_log_f32 against log2 in double rounded to binary32.
 //
 // Each thread handles kPer consecutive inputs; each workgroup writes its own
 // four result words, no atomics.
@@ -19,6 +24,7 @@ constexpr int kThreads = 256;
 constexpr int kPer = 64;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ inline float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
@@ -97,6 +103,77 @@ __global__ void bf16_sweep(uint64_t first, uint64_t count, uint32_t *out) {
   }
 }
 
+// binary32 bits -> binary16 bits, round to nearest-even (not for NaN): the
+// magnitude counted in binary16 units, 2^-24 below 2^-14 and 2^(E-10) above
+// (E the unbiased exponent), the dropped bits deciding the rounding.
+__device__ inline uint32_t f16_rne_ref(uint32_t u) {
+  const uint32_t sign = (u >> 16) & 0x8000u, a = u & 0x7fffffffu;
+  if (a >= 0x477ff000u) return sign | 0x7c00u;  // from 65520 up: infinity
+  const uint32_t e = a >> 23;
+  if (e < 102) return sign;                       // below 2^-25
+  const uint32_t m = (a & 0x7fffffu) | 0x800000u;
+  const uint32_t sh = (e >= 113) ? 13u : 126u - e;
+  uint32_t q = m >> sh;
+  const uint32_t rest = m & ((1u << sh) - 1u), half = 1u << (sh - 1u);
+  if (rest > half || (rest == half && (q & 1u))) ++q;
+  return (e >= 113) ? (sign | (((e - 113u) << 10) + q)) : (sign | q);
+}
+
+// out[2*block + 0] = #non-NaN patterns whose conversion differs from RNE,
+// +1 = #NaN patterns whose result is not a NaN
+__global__ void f16_sweep(uint64_t first, uint64_t count, uint32_t *out) {
+  uint32_t bad = 0, badnan = 0;
+  const uint64_t base = ((uint64_t)blockIdx.x * kThreads + threadIdx.x) * kPer;
+  for (int i = 0; i < kPer; i += 2) {
+    const uint64_t k = base + i;
+    if (k >= count) break;
+    const uint32_t u0 = (uint32_t)(first + k), u1 = (uint32_t)(first + k + 1);
+    f32x2_t v = {u2f(u0), u2f(u1)};
+    const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+    const uint32_t h[2] = {w & 0xffffu, w >> 16};
+    const uint32_t in[2] = {u0, u1};
+    for (int j = 0; j < 2; ++j) {
+      const bool isnan = (in[j] & 0x7f800000u) == 0x7f800000u && (in[j] & 0x7fffffu);
+      if (isnan) badnan += !((h[j] & 0x7c00u) == 0x7c00u && (h[j] & 0x3ffu));
+      else bad += h[j] != f16_rne_ref(in[j]);
+    }
+  }
+  __shared__ uint32_t s[2][kThreads];
+  s[0][threadIdx.x] = bad; s[1][threadIdx.x] = badnan;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r0 = 0, r1 = 0;
+    for (int t = 0; t < kThreads; ++t) { r0 += s[0][t]; r1 += s[1][t]; }
+    out[2 * blockIdx.x] = r0; out[2 * blockIdx.x + 1] = r1;
+  }
+}
+
+// out[2*block + 0] = max |ulp diff| of v_log_f32 against log2 in double
+// rounded to binary32, +1 = #inputs that differ
+__global__ void log2_sweep(uint32_t first, uint32_t count, uint32_t *out) {
+  uint32_t mx = 0, nd = 0;
+  const uint64_t base = ((uint64_t)blockIdx.x * kThreads + threadIdx.x) * kPer;
+  for (int i = 0; i < kPer; ++i) {
+    const uint64_t k = base + i;
+    if (k >= count) break;
+    const float x = u2f((uint32_t)(first + k));
+    const float hw = __builtin_amdgcn_logf(x);
+    const float ref = (float)log2((double)x);
+    const uint32_t a = ord(hw), b = ord(ref);
+    const uint32_t d = a > b ? a - b : b - a;
+    mx = d > mx ? d : mx;
+    nd += d != 0;
+  }
+  __shared__ uint32_t s[2][kThreads];
+  s[0][threadIdx.x] = mx; s[1][threadIdx.x] = nd;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r0 = 0, r1 = 0;
+    for (int t = 0; t < kThreads; ++t) { r0 = s[0][t] > r0 ? s[0][t] : r0; r1 += s[1][t]; }
+    out[2 * blockIdx.x] = r0; out[2 * blockIdx.x + 1] = r1;
+  }
+}
+
 // Plain copy of n16 16-byte words: each thread moves 4 words per trip, all
 // four loads issued before the stores; grid-stride over the buffer.  A
 // bandwidth ceiling for kernels that read and write once, and a calibration
@@ -152,6 +229,23 @@ int probe_bf16_sweep(uint64_t first, uint64_t count, uint32_t *out, uint32_t out
   const uint64_t blocks = (count + per_block - 1) / per_block;
   if (blocks * 2 > out_words || blocks == 0) return -1;
   hipLaunchKernelGGL(bf16_sweep, dim3((unsigned)blocks), dim3(kThreads), 0, 0, first, count, out);
+  return hipDeviceSynchronize() == hipSuccess ? (int)blocks : -1;
+}
+
+int probe_f16_sweep(uint64_t first, uint64_t count, uint32_t *out, uint32_t out_words) {
+  const uint64_t per_block = (uint64_t)kThreads * kPer;
+  if (count % 2) return -1;
+  const uint64_t blocks = (count + per_block - 1) / per_block;
+  if (blocks * 2 > out_words || blocks == 0) return -1;
+  hipLaunchKernelGGL(f16_sweep, dim3((unsigned)blocks), dim3(kThreads), 0, 0, first, count, out);
+  return hipDeviceSynchronize() == hipSuccess ? (int)blocks : -1;
+}
+
+int probe_log2_sweep(uint32_t first, uint32_t count, uint32_t *out, uint32_t out_words) {
+  const uint64_t per_block = (uint64_t)kThreads * kPer;
+  const uint64_t blocks = (count + per_block - 1) / per_block;
+  if (blocks * 2 > out_words || blocks == 0) return -1;
+  hipLaunchKernelGGL(log2_sweep, dim3((unsigned)blocks), dim3(kThreads), 0, 0, first, count, out);
   return hipDeviceSynchronize() == hipSuccess ? (int)blocks : -1;
 }
 

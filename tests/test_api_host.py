@@ -47,8 +47,9 @@ def desc(B=1, H=2, S=3, N=300, dtype=jas.JAS_DTYPE_BF16, flags=0, ld=None, ms=(0
     return jas.make_desc((B, H, S, N), dtype, flags, ld, ms)
 
 
-def fwd(d, scores=A, mask=None, sink=None, probs=B_, p_sink=None, launch=None, key_len=None):
-    return jas.jas_fwd_ex(d, scores, mask, key_len, sink, probs, p_sink, launch, None)
+def fwd(d, scores=A, mask=None, sink=None, probs=B_, p_sink=None, launch=None, key_len=None,
+        lse=None):
+    return jas.jas_fwd_ex(d, scores, mask, key_len, sink, probs, p_sink, lse, launch, None)
 
 
 def bwd(d, probs=A, dprobs=B_, p_sink=None, dscores=C, d_sink=None, ws=None, ws_bytes=0,
@@ -58,7 +59,7 @@ def bwd(d, probs=A, dprobs=B_, p_sink=None, dscores=C, d_sink=None, ws=None, ws_
 
 def test_null_desc_and_pointers():
     L = jas.lib()
-    assert L.jas_fwd(None, A, None, None, None, B_, None, None) == 1
+    assert L.jas_fwd(None, A, None, None, None, B_, None, None, None) == 1
     assert L.jas_bwd(None, A, B_, None, None, C, None, None, 0, None) == 1
     assert fwd(desc(), scores=None) == 1
     assert fwd(desc(), probs=None) == 1
@@ -84,7 +85,10 @@ def test_flag_pointer_predicates():
     assert fwd(desc(), key_len=W) == 4
     assert bwd(desc(flags=jas.JAS_FLAG_KEY_LEN)) == 1
     assert bwd(desc(), key_len=W) == 4
-    assert fwd(desc(flags=1 << 4)) == 4
+    assert fwd(desc(flags=1 << 5)) == 4
+    # row log-sum-exp: pointer iff JAS_FLAG_LSE
+    assert fwd(desc(flags=jas.JAS_FLAG_LSE)) == 1
+    assert fwd(desc(), lse=W) == 4
 
 
 def test_shapes_and_dtype():
@@ -94,6 +98,8 @@ def test_shapes_and_dtype():
     assert fwd(desc(ms=(-1, 0, 0), flags=jas.JAS_FLAG_MASK), mask=C) == 2
     assert fwd(desc(N=jas.JAS_MAX_KEYS + 1)) == 7
     assert fwd(desc(dtype=7)) == 3
+    assert fwd(desc(dtype=3)) == 3
+    assert fwd(desc(dtype=jas.JAS_DTYPE_F16), scores=A + 1) == 9  # fp16 is a known dtype
     # rows * ld overflowing int64
     assert fwd(desc(B=1 << 40, H=1 << 20, S=1 << 10, N=8)) == 2
 
@@ -104,6 +110,7 @@ def test_alignment():
     assert fwd(desc(flags=jas.JAS_FLAG_MASK), mask=C + 2) == 9
     assert bwd(desc(), dscores=C + 1) == 9
     assert fwd(desc(flags=jas.JAS_FLAG_KEY_LEN), key_len=W + 2) == 9
+    assert fwd(desc(flags=jas.JAS_FLAG_LSE), lse=W + 2) == 9
 
 
 def test_aliasing():
@@ -123,6 +130,11 @@ def test_aliasing():
     dk = desc(B=1, H=1, S=4, N=300, flags=jas.JAS_FLAG_KEY_LEN)
     assert fwd(dk, key_len=B_ + 64) == 5         # key lengths inside probs
     assert bwd(dk, key_len=C + 4) == 5           # key lengths inside dscores
+    dl = desc(B=1, H=1, S=4, N=300, flags=jas.JAS_FLAG_LSE)
+    assert fwd(dl, lse=B_ + 16) == 5             # lse inside probs
+    assert fwd(dl, lse=A + 16) == 5              # lse inside scores
+    dls = desc(B=1, H=1, S=4, N=300, flags=jas.JAS_FLAG_LSE | jas.JAS_FLAG_SINK)
+    assert fwd(dls, sink=C, p_sink=D, lse=D + 8) == 5   # lse overlapping p_sink
 
 
 def test_workspace():

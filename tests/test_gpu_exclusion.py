@@ -17,8 +17,8 @@ import torch
 import deterministic_attention_softmax_amd as jas
 import oracle
 import synth
-from tests.gpu_util import (assert_bitexact, assert_close, dev, gather_rows, log,
-                            oracle_rows_bwd, oracle_rows_fwd, sample_rows)
+from tests.gpu_util import (assert_bitexact, assert_close, assert_lse_close, dev, gather_rows,
+                            log, oracle_rows_bwd, oracle_rows_fwd, sample_rows)
 from tests.test_gpu_invariance import valid_geometries
 
 pytestmark = pytest.mark.gpu
@@ -53,11 +53,13 @@ def run_case(dt, B, H, Sq, N, causal, key_len, mask=None, mask_strides=None, sin
     s_nan = fill_hidden(s, vis, float("nan")).to(dev())
     s_inf = fill_hidden(s, vis, float("-inf")).to(dev())
     # forward: exclusion on NaN-filled scores == dense on -inf scores
-    P1, ps1 = jas.fwd(s_nan, mask=md, mask_strides=mask_strides, sink=sd, causal=causal,
-                      key_len=kl, launch=launch)
-    P2, ps2 = jas.fwd(s_inf, mask=md, mask_strides=mask_strides, sink=sd, launch=launch)
+    P1, ps1, l1 = jas.fwd(s_nan, mask=md, mask_strides=mask_strides, sink=sd, causal=causal,
+                          key_len=kl, launch=launch, want_lse=True)
+    P2, ps2, l2 = jas.fwd(s_inf, mask=md, mask_strides=mask_strides, sink=sd, launch=launch,
+                          want_lse=True)
     torch.cuda.synchronize()
     assert synth.to_numpy_bits(P1).tobytes() == synth.to_numpy_bits(P2).tobytes(), "P vs dense"
+    assert l1.cpu().numpy().tobytes() == l2.cpu().numpy().tobytes(), "lse vs dense"
     if sink is not None:
         assert ps1.cpu().numpy().tobytes() == ps2.cpu().numpy().tobytes(), "p_sink vs dense"
     # backward: exclusion on NaN-filled P == dense on P (+0 there)
@@ -69,15 +71,16 @@ def run_case(dt, B, H, Sq, N, causal, key_len, mask=None, mask_strides=None, sin
     if sink is not None:
         assert d1.cpu().numpy().tobytes() == d2.cpu().numpy().tobytes(), "d_sink vs dense"
     if not check_oracle:
-        return synth.to_numpy_bits(P1), synth.to_numpy_bits(dS1)
+        return synth.to_numpy_bits(P1), synth.to_numpy_bits(dS1), l1.cpu().numpy()
     # the oracle's exclusion on the NaN-filled inputs
     kl_np = None if key_len is None else np.asarray(key_len, np.int32)
     m_np = None if mask is None else mask.cpu().numpy()
     k_np = None if sink is None else sink.cpu().numpy()
-    P_o, ps_o = oracle.fwd(synth.to_numpy_bits(s_nan), B, H, Sq, N, mask=m_np,
-                           mask_strides=mask_strides or (0, 0, 0), sink=k_np, causal=causal,
-                           key_len=kl_np)
+    P_o, ps_o, lse_o = oracle.fwd(synth.to_numpy_bits(s_nan), B, H, Sq, N, mask=m_np,
+                                  mask_strides=mask_strides or (0, 0, 0), sink=k_np,
+                                  causal=causal, key_len=kl_np, want_lse=True)
     assert_close(synth.to_numpy_bits(P1), P_o, "P")
+    assert_lse_close(l1.cpu().numpy(), lse_o)
     if sink is not None:
         assert_close(ps1.cpu().numpy(), ps_o, "p_sink")
     # stage-isolated backward: the oracle's P, NaN past the prefix, on both sides
@@ -91,12 +94,12 @@ def run_case(dt, B, H, Sq, N, causal, key_len, mask=None, mask_strides=None, sin
     assert_bitexact(synth.to_numpy_bits(dS), dS_o, "dS")
     if sink is not None:
         assert_bitexact(dsk.cpu().numpy(), oracle.dsink(v_o, B, H, Sq), "d_sink")
-    return synth.to_numpy_bits(P1), synth.to_numpy_bits(dS1)
+    return synth.to_numpy_bits(P1), synth.to_numpy_bits(dS1), l1.cpu().numpy()
 
 
 @pytest.mark.parametrize("Sq,N", [(600, 600), (64, 1000), (700, 300), (33, 4352), (5, 16384),
                                   (257, 257), (8, 8)])
-@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32, torch.float16])
 def test_causal(dt, Sq, N):
     log(f"causal: {dt} Sq={Sq} N={N}")
     sink = synth.normal((2,), 1.0, Sq + N, "cpu")
@@ -104,7 +107,7 @@ def test_causal(dt, Sq, N):
 
 
 @pytest.mark.parametrize("N", [700, 4352, 8449])
-@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32, torch.float16])
 def test_key_len(dt, N):
     # full, a cut inside a chunk, one key, none, beyond N (clamped), negative
     kl = [N, 513, 1, 0, N + 100, -3]
@@ -113,7 +116,7 @@ def test_key_len(dt, N):
     run_case(dt, len(kl), 3, 5, N, False, kl, sink=sink, seed=N)
 
 
-@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32, torch.float16])
 def test_causal_key_len_mask_sink_together(dt):
     B, H, Sq, N = 3, 2, 40, 1300
     kl = [1300, 777, 1290]
@@ -125,7 +128,7 @@ def test_causal_key_len_mask_sink_together(dt):
              seed=93)
 
 
-@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32, torch.float16])
 def test_elementwise_path(dt):
     # N not a multiple of a 16-byte chunk: the element-wise path
     log(f"exclusion, element-wise path: {dt}")
@@ -133,7 +136,8 @@ def test_elementwise_path(dt):
     run_case(dt, 2, 2, 30, 1001, True, [1001, 517], sink=sink, seed=96)
 
 
-@pytest.mark.parametrize("dt,N", [(torch.bfloat16, 4352), (torch.float32, 2000)])
+@pytest.mark.parametrize("dt,N", [(torch.bfloat16, 4352), (torch.float32, 2000),
+                                  (torch.float16, 1000)])
 def test_every_launch_geometry_with_exclusion(dt, N):
     B, H, Sq = 2, 1, 9
     kl = [N - 37, 300]
@@ -144,7 +148,7 @@ def test_every_launch_geometry_with_exclusion(dt, N):
     for L in geos:
         cur = run_case(dt, B, H, Sq, N, True, kl, sink=sink, seed=98, launch=L,
                        check_oracle=ref is None)
-        cur = (cur[0].tobytes(), cur[1].tobytes())
+        cur = (cur[0].tobytes(), cur[1].tobytes(), cur[2].tobytes())
         if ref is None:
             ref = cur
         else:

@@ -7,6 +7,10 @@ rests on (test-only kernels in tests/hw_probes/):
   -126 up -- the kernels' exp_ relies on this instead of a select.
 * v_cvt_pk_bf16_f32 over all 2^32 bit patterns: round to nearest-even, as the
   oracle's conversion (RL-Kernel PR #453: one dtype conversion at the write).
+* the packed binary32 -> binary16 conversion over all 2^32 bit patterns: round
+  to nearest-even with subnormals kept (RL-Kernel PR #240 lists FP16).
+* v_log_f32 over every binary32 in [1, 32768] (the range of a row's sum of
+  exponentials), the logarithm behind the row log-sum-exp: its largest error.
 * the lane layout of the permlane16/32 swaps used by the tile trees.
 """
 import ctypes
@@ -28,6 +32,10 @@ def probes():
     L.probe_exp2_sweep.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_uint32]
     L.probe_bf16_sweep.restype = ctypes.c_int
     L.probe_bf16_sweep.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint32]
+    L.probe_f16_sweep.restype = ctypes.c_int
+    L.probe_f16_sweep.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint32]
+    L.probe_log2_sweep.restype = ctypes.c_int
+    L.probe_log2_sweep.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_uint32]
     L.probe_permlane_layout.restype = ctypes.c_int
     L.probe_permlane_layout.argtypes = [ctypes.c_void_p]
     return L
@@ -60,6 +68,31 @@ def test_v_cvt_pk_bf16_f32_is_rne_on_all_patterns():
     bad, badnan = int(r[:, 0].sum()), int(r[:, 1].sum())
     log(f"v_cvt_pk_bf16_f32: {bad} non-NaN mismatches, {badnan} NaN results not NaN")
     assert bad == 0 and badnan == 0
+
+
+def test_f16_conversion_is_rne_on_all_patterns():
+    L = probes()
+    count = 1 << 32
+    words = 2 * (count // (256 * 64))
+    out = torch.zeros(words, dtype=torch.int32, device="cuda")
+    assert L.probe_f16_sweep(0, count, out.data_ptr(), words) > 0
+    r = out.cpu().numpy().view(np.uint32).reshape(-1, 2)
+    bad, badnan = int(r[:, 0].sum()), int(r[:, 1].sum())
+    log(f"binary32 -> binary16: {bad} non-NaN mismatches, {badnan} NaN results not NaN")
+    assert bad == 0 and badnan == 0
+
+
+def test_v_log_f32_on_row_sum_range():
+    L = probes()
+    first, last = 0x3F800000, 0x47000000   # 1.0 .. 32768.0
+    count = last - first + 1
+    words = 2 * ((count + 256 * 64 - 1) // (256 * 64))
+    out = torch.zeros(words, dtype=torch.int32, device="cuda")
+    assert L.probe_log2_sweep(first, count, out.data_ptr(), words) > 0
+    r = out.cpu().numpy().view(np.uint32).reshape(-1, 2)
+    mx, nd = int(r[:, 0].max()), int(r[:, 1].sum())
+    log(f"v_log_f32 on [1, 32768]: max {mx} ulp, {nd} of {count} differ from log2 rounded")
+    assert mx <= 2
 
 
 def test_permlane_swap_layout():

@@ -9,6 +9,7 @@ element-wise and 16-byte paths, in-place calls and run-to-run repeats, all
 compared byte for byte; plus the degenerate cases the method has.
 """
 import json
+import math
 import os
 
 import numpy as np
@@ -56,7 +57,7 @@ def test_batch_invariance_fp32_8449_keys():
 
 
 def valid_geometries(dtype, N):
-    tps = 2 if dtype == torch.bfloat16 else 1
+    tps = 1 if dtype == torch.float32 else 2
     T = (N + 255) // 256
     nslots = (T + tps - 1) // tps
     cpls = [1, 2, 3, 5, 9] + ([17] if dtype == torch.float32 else [])
@@ -72,7 +73,8 @@ def valid_geometries(dtype, N):
 
 @pytest.mark.parametrize("dt,N", [(torch.bfloat16, 4352), (torch.float32, 8449),
                                   (torch.bfloat16, 700), (torch.float32, 257),
-                                  (torch.bfloat16, 16384)])
+                                  (torch.bfloat16, 16384), (torch.float16, 4352),
+                                  (torch.float16, 700)])
 def test_every_launch_geometry_gives_identical_bytes(dt, N):
     B, H, S = 1, 3, 5
     s = synth.normal((B, H, S, N), 2.0, 200 + N, "cpu", dt).to(dev())
@@ -84,18 +86,18 @@ def test_every_launch_geometry_gives_identical_bytes(dt, N):
     log(f"geometries: {dt} N={N}: {len(geos)}")
     ref = None
     for L in geos:
-        P, ps = jas.fwd(s, mask=mask, sink=sink, launch=L)
+        P, ps, lse = jas.fwd(s, mask=mask, sink=sink, launch=L, want_lse=True)
         dS, dsk = jas.bwd(P, g, p_sink=ps, launch=L)
         torch.cuda.synchronize()
         cur = (bits(P).tobytes(), ps.cpu().numpy().tobytes(), bits(dS).tobytes(),
-               dsk.cpu().numpy().tobytes())
+               dsk.cpu().numpy().tobytes(), lse.cpu().numpy().tobytes())
         if ref is None:
             ref = cur
         else:
             assert cur == ref, f"launch {L} changed the bytes"
 
 
-@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32, torch.float16])
 def test_elementwise_path_matches_vector_path(dt):
     # a row stride with padding that breaks 16-byte alignment, and a base
     # offset by one element, take the element-wise path; bytes must not move
@@ -154,10 +156,10 @@ def test_in_place_and_repeat():
 
 
 def bits_t(t):
-    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+    return t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32)
 
 
-@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32, torch.float16])
 def test_degenerate_rows(dt):
     N = 600
     rows = 6
@@ -170,9 +172,16 @@ def test_degenerate_rows(dt):
     s[0, 0, 4, :] = 0.375
     s[0, 0, 5, :] = torch.arange(N) % 7 - 3.0
     sd = s.to(dt).to(dev())
-    P, _ = jas.fwd(sd)
-    Pn, psn = jas.fwd(sd, sink=torch.full((1,), float("-inf"), device=dev()))
+    P, _, lse = jas.fwd(sd, want_lse=True)
+    Pn, psn, lsen = jas.fwd(sd, sink=torch.full((1,), float("-inf"), device=dev()),
+                            want_lse=True)
     torch.cuda.synchronize()
+    # log-sum-exp closed forms: one finite key gives its score exactly (L = 1),
+    # nothing finite gives -inf, a uniform row c + ln N within the tolerance
+    lc = lse.cpu()
+    assert lc[1].item() == -12.25 and lc[2].item() == float("-inf")
+    assert abs(lc[0].item() - (0.375 + math.log(N))) <= 4e-6 * (0.375 + math.log(N))
+    assert torch.equal(bits_t(lse), bits_t(lsen))
     Pf = P.float().cpu()
     if dt == torch.float32:
         assert torch.all(Pf[0, 0, 0] == torch.tensor(1.0, dtype=torch.float32) / N)
@@ -181,9 +190,9 @@ def test_degenerate_rows(dt):
     # a -inf sink is the same as no sink, with p_sink = 0
     assert torch.equal(bits_t(P), bits_t(Pn)) and torch.all(psn == 0)
     # fully masked row with a sink: P = 0, p_sink = 1
-    P2, ps2 = jas.fwd(sd, sink=torch.zeros(1, device=dev()))
+    P2, ps2, lse2 = jas.fwd(sd, sink=torch.zeros(1, device=dev()), want_lse=True)
     torch.cuda.synchronize()
-    assert torch.all(P2[0, 0, 2] == 0) and ps2[2].item() == 1.0
+    assert torch.all(P2[0, 0, 2] == 0) and ps2[2].item() == 1.0 and lse2[2].item() == 0.0
     # uniform row with sink equal to the row value: P = p_sink = fl(1/(N+1))
     P3, ps3 = jas.fwd(sd, sink=torch.full((1,), 0.375, device=dev()))
     torch.cuda.synchronize()

@@ -2,7 +2,8 @@
 same seeded inputs (RL-Kernel PR #453: every GPU backend checked against the
 CPU reference of the same tile order; here the oracle in oracle/).
 
-Forward: P and p_sink within the tolerance (1 bf16 ulp, 4e-6 relative fp32);
+Forward: P and p_sink within the tolerance (1 ulp for bf16 and fp16, 4e-6
+relative fp32), the row log-sum-exp within 4e-6 * max(1, |lse|);
 the exponential is the hardware one on the GPU.  Backward, stage-isolated:
 both sides read the same P, dP, p_sink (never a GPU output), dS and d_sink are
 bit-exact.  Composed fwd->bwd chains are checked separately with a
@@ -15,8 +16,8 @@ import torch
 import deterministic_attention_softmax_amd as jas
 import oracle
 import synth
-from tests.gpu_util import (assert_bitexact, assert_close, dev, gather_rows, log,
-                            oracle_rows_bwd, oracle_rows_fwd, sample_rows)
+from tests.gpu_util import (assert_bitexact, assert_close, assert_lse_close, dev, gather_rows,
+                            log, oracle_rows_bwd, oracle_rows_fwd, sample_rows)
 from tests.ref64 import bf16_bits_to_f32
 
 pytestmark = pytest.mark.gpu
@@ -28,15 +29,17 @@ def run_fwd_bwd_full(s, g, mask=None, mask_strides=None, sink=None, launch=None)
     s_np = synth.to_numpy_bits(s)
     m_np = None if mask is None else mask.cpu().numpy()
     k_np = None if sink is None else sink.cpu().numpy()
-    P, ps = jas.fwd(s.to(dev()), mask=None if mask is None else mask.to(dev()),
-                    mask_strides=mask_strides, sink=None if sink is None else sink.to(dev()),
-                    launch=launch)
+    P, ps, lse = jas.fwd(s.to(dev()), mask=None if mask is None else mask.to(dev()),
+                         mask_strides=mask_strides, sink=None if sink is None else sink.to(dev()),
+                         launch=launch, want_lse=True)
     torch.cuda.synchronize()
-    P_o, ps_o = oracle.fwd(s_np, B, H, S, N, mask=m_np,
-                           mask_strides=mask_strides or (0, 0, 0), sink=k_np)
+    P_o, ps_o, lse_o = oracle.fwd(s_np, B, H, S, N, mask=m_np,
+                                  mask_strides=mask_strides or (0, 0, 0), sink=k_np,
+                                  want_lse=True)
     worst = assert_close(synth.to_numpy_bits(P), P_o, "P")
     if sink is not None:
         assert_close(ps.cpu().numpy(), ps_o, "p_sink")
+    assert_lse_close(lse.cpu().numpy(), lse_o)
     # backward on the oracle's P
     g_np = synth.to_numpy_bits(g)
     Pin = synth.from_numpy_bits(P_o, dev())
@@ -57,10 +60,11 @@ def test_grad_check_fp32_2x4x257x257():
     run_fwd_bwd_full(s, g)
 
 
-def test_bf16_2x4x257x257_with_mask_and_sink():
-    log("bf16 [2,4,257,257] with per-batch mask and sink")
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
+def test_16bit_2x4x257x257_with_mask_and_sink(dt):
+    log(f"{dt} [2,4,257,257] with per-batch mask and sink")
     s, g = synth.grad_check_fp32(seed=11)
-    s, g = s.to(torch.bfloat16), g.to(torch.bfloat16)
+    s, g = s.to(dt), g.to(dt)
     mask = torch.zeros((2, 1, 1, 257))
     mask[0, ..., 200:] = float("-inf")
     mask[1, ..., 256:] = float("-inf")
@@ -69,7 +73,7 @@ def test_bf16_2x4x257x257_with_mask_and_sink():
 
 
 @pytest.mark.parametrize("N", [1, 7, 8, 255, 256, 257, 511, 513, 1000, 4352, 8449, 16384])
-@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16, torch.float16])
 def test_row_lengths(N, dt):
     rows = 24 if N <= 4352 else 6
     log(f"row lengths: {dt} N={N} rows={rows}")
@@ -187,3 +191,28 @@ def test_composed_chain_condition_scaled():
     assert np.all(np.abs(got - want) <= lim)
     vscale = np.abs(ps_o.astype(np.float64) * delta[:, 0]).reshape(B, H, S).sum(axis=(0, 2))
     assert np.all(np.abs(dsk.cpu().numpy() - d_o) <= tol * vscale + 1e-30)
+
+
+def test_fp16_joint_attention_1x24x4352x4352_sampled():
+    # the joint attention workload in fp16: full-size launch, sampled rows,
+    # P, the row log-sum-exp, and the stage-isolated backward
+    log("fp16 [1,24,4352,4352] mask fwd + lse; bwd on synthetic P; sampled rows")
+    B, H, S, N = 1, 24, 4352, 4352
+    s, mask, _, _ = synth.joint_attention_bf16(seed=3, device=dev(), B=B, H=H, S=S, N=N)
+    s = s.to(torch.float16)
+    P, _, lse = jas.fwd(s, mask=mask.view(B, 1, 1, N), mask_strides=(N, 0, 0), want_lse=True)
+    torch.cuda.synchronize()
+    idx = sample_rows(B * H * S, 96, seed=31)
+    m_np = mask.cpu().numpy()
+    k = len(idx)
+    P_o, _, lse_o = oracle.fwd(gather_rows(s, idx).reshape(1, k, 1, N), 1, k, 1, N,
+                               mask=np.ascontiguousarray(m_np[idx // (H * S)]),
+                               mask_strides=(0, N, 0), want_lse=True)
+    assert_close(gather_rows(P, idx), P_o.reshape(k, N), "fp16 joint P")
+    assert_lse_close(lse.cpu().numpy()[idx], lse_o, "fp16 joint lse")
+    del P, s
+    Pin, gin, _ = synth.synthetic_bwd_inputs((B, H, S, N), torch.float16, 34, dev())
+    dS, _ = jas.bwd(Pin, gin)
+    torch.cuda.synchronize()
+    dS_o, _ = oracle_rows_bwd(gather_rows(Pin, idx), gather_rows(gin, idx), N)
+    assert_bitexact(gather_rows(dS, idx), dS_o, "fp16 joint dS")
