@@ -13,8 +13,9 @@ same rows on this host's cores.
 
 Other workloads: joint4352_keylen (the padding as key lengths, padded keys
 not read), rows4352 (forward only), causal8192 (causal scores, -inf above the
-diagonal, read like any other key) and causal8192_skip (the same scores with
-the causal flag: nothing above the diagonal is read).  With keys excluded,
+diagonal, read like any other key), causal8192_skip (the same scores with
+the causal flag: nothing above the diagonal is read) and long65536 (rows of
+65,536 keys through the streaming kernels).  With keys excluded,
 the algorithmic bytes count the scores and P of the visible keys only.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
@@ -50,6 +51,9 @@ WORKLOADS = {
     "causal8192_skip": ("causal self-attention scores bf16 [1,32,8192,8192] + per-head sink, causal flag "
                         "(scores and P above the diagonal not read), fwd+bwd",
            1, 32, 8192, 8192, "bf16", False, True, "causal", True),
+    "long65536": ("long-context rows bf16 [1,16,512,65536] (512 queries at the end of 65,536 keys), "
+                  "causal flag, streaming kernels, fwd+bwd",
+           1, 16, 512, 65536, "bf16", False, False, "causal", True),
 }
 
 
@@ -132,6 +136,8 @@ def make_inputs(wl, dev):
             key_len = torch.tensor([N - p for p in pads], dtype=torch.int32, device=dev)
     elif wl == "rows4352":
         s = synth.rows_with_outliers_bf16(seed=2, device=dev, rows=S, N=N)
+    elif wl == "long65536":
+        s, g = synth.long_context_bf16(seed=7, device=dev, B=B, H=H, S=S, N=N)
     else:
         s, sink, g = synth.causal_sink_bf16(seed=5, device=dev, B=B, H=H, S=S)
     return s, mask, sink, g, key_len

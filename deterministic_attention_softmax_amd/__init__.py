@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libjas.so")
 
 JAS_DTYPE_F32, JAS_DTYPE_BF16, JAS_DTYPE_F16 = 0, 1, 2
 JAS_FLAG_MASK, JAS_FLAG_SINK, JAS_FLAG_CAUSAL, JAS_FLAG_KEY_LEN, JAS_FLAG_LSE = 1, 2, 4, 8, 16
-JAS_MAX_KEYS = 16384
+JAS_MAX_KEYS = 262144
 STATUS = {
     0: "JAS_OK", 1: "JAS_ERR_NULL_POINTER", 2: "JAS_ERR_BAD_SHAPE", 3: "JAS_ERR_BAD_DTYPE",
     4: "JAS_ERR_BAD_FLAGS", 5: "JAS_ERR_ALIASING", 6: "JAS_ERR_WORKSPACE",
@@ -45,6 +45,7 @@ class jas_launch_t(ctypes.Structure):
     _fields_ = [
         ("waves_per_row", ctypes.c_int32), ("chunks_per_lane", ctypes.c_int32),
         ("rows_per_block", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
+        ("streaming", ctypes.c_int32),
     ]
 
 
@@ -163,8 +164,8 @@ def _launch(launch):
     if isinstance(launch, jas_launch_t):
         return launch
     L = jas_launch_t()
-    L.waves_per_row, L.chunks_per_lane, L.rows_per_block, L.max_blocks = (
-        int(v) for v in (tuple(launch) + (0, 0, 0, 0))[:4])
+    (L.waves_per_row, L.chunks_per_lane, L.rows_per_block, L.max_blocks,
+     L.streaming) = (int(v) for v in (tuple(launch) + (0, 0, 0, 0, 0))[:5])
     return L
 
 

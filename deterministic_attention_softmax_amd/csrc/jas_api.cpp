@@ -10,6 +10,8 @@
 #include "jas.h"
 #include "jas_internal.h"
 
+static_assert(JAS_MAX_KEYS == jas::kMaxStreamKeys, "the public row limit is the streaming kernels'");
+
 namespace {
 
 using jas::Geometry;
@@ -94,6 +96,23 @@ jas_status_t choose_geometry(int dtype, int T, int64_t rows, bool backward, cons
   int rpb = ov ? ov->rows_per_block : 0;
   const int64_t cap = ov ? ov->max_blocks : 0;
   if (wpr < 0 || cpl < 0 || rpb < 0 || cap < 0) return JAS_ERR_UNSUPPORTED;
+  if (ov && ov->streaming != 0 && ov->streaming != 1) return JAS_ERR_UNSUPPORTED;
+  g->stream = 0;
+  if (T > jas::kMaxTiles || (ov && ov->streaming)) {
+    // streaming: 4 waves and one row per workgroup, the row in segments
+    if ((wpr != 0 && wpr != jas::kBlockWaves) || rpb > 1) return JAS_ERR_UNSUPPORTED;
+    if (cpl == 0) cpl = jas::default_stream_cpl(dtype);
+    if (!jas::stream_cpl_compiled(dtype, cpl)) return JAS_ERR_UNSUPPORTED;
+    int64_t blocks = rows;
+    if (cap > 0 && blocks > cap) blocks = cap;
+    if (blocks > 0x7fffffff) blocks = 0x7fffffff;
+    g->wpr = jas::kBlockWaves;
+    g->cpl = cpl;
+    g->rpb = 1;
+    g->blocks = blocks;
+    g->stream = 1;
+    return JAS_OK;
+  }
   if (wpr == 0) {
     if (cpl) {
       for (int w : {1, 2, 4})

@@ -11,8 +11,9 @@ namespace jas {
 
 constexpr int kTile = 256;         // keys per tile (fixed, never tuned)
 constexpr int kWave = 64;          // CDNA wavefront
-constexpr int kMaxKeys = 16384;
+constexpr int kMaxKeys = 16384;              // longest row of the one-pass kernels
 constexpr int kMaxTiles = kMaxKeys / kTile;  // 64: one tile state per lane
+constexpr int kMaxStreamKeys = 262144;       // longest row of the streaming kernels
 constexpr int kBlockWaves = 4;     // waves per workgroup (256 threads)
 
 struct RowShape {
@@ -62,9 +63,10 @@ struct DsinkArgs {
 
 struct Geometry {
   int wpr;         // waves per row
-  int cpl;         // 16-byte chunks per lane (compiled size)
+  int cpl;         // 16-byte chunks per lane (compiled size); streaming: per segment
   int rpb;         // rows per workgroup
   int64_t blocks;  // grid size
+  int stream;      // 1: the streaming kernels (4 waves per row, rows in segments)
 };
 
 // dtype codes: 0 fp32, 1 bf16, 2 fp16 (jas_dtype_t)
@@ -76,6 +78,8 @@ inline int tiles_per_slot(int dtype) { return dtype == 0 ? 1 : 2; }
 bool cpl_compiled(int dtype, int wpr, int cpl);
 int default_wpr(int dtype, int nslots, bool backward);
 const int *compiled_cpls(int dtype, int *count);
+bool stream_cpl_compiled(int dtype, int cpl);
+int default_stream_cpl(int dtype);
 
 // one per element type, each in its own translation unit
 hipError_t launch_fwd_f32(const FwdArgs &a, const Geometry &g, hipStream_t stream);

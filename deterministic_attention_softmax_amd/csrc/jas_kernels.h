@@ -737,14 +737,384 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void bwd_kernel(const BwdArgs 
 }
 
 // ---------------------------------------------------------------------------
+// Streaming kernels, for rows longer than one pass keeps in registers (and
+// for any row when asked for).  A row belongs to one workgroup of 4 waves
+// and is cut into segments of 4 x CPL slots.  Pass 1 reduces each segment's
+// tiles exactly as the one-pass kernels do and keeps every tile state in
+// LDS; wave 0 then folds the states in tile order, 64 tiles at a time with
+// the running state carried from block to block (the same left fold);
+// pass 2 writes the outputs segment by segment, last segment first: that
+// one is still in registers, the others are read again and their
+// exponentials recomputed from the saved tile maxima -- the same operations
+// on the same inputs, so every output has the one-pass kernels' bits.
+// ---------------------------------------------------------------------------
+
+template <int DT, int CPL, bool VEC, bool MASK, bool EXCL>
+__global__ __launch_bounds__(kWave * kBlockWaves) void fwd_stream_kernel(const FwdArgs a) {
+  using C = Cfg<DT>;
+  constexpr int WPR = kBlockWaves;
+  constexpr int KPL = C::KPL, TPS = C::TPS, ESZ = C::ESZ;
+  constexpr uint32_t kFill = kNegInfBits<DT>;
+  constexpr int SPS = WPR * CPL;  // slots per segment
+  extern __shared__ float smem[];
+  const int T = a.s.T;
+  float *lds_m = smem;            // [T] tile maxima
+  float *lds_l = smem + T;        // [T] tile sums
+  float *lds_row = smem + 2 * T;  // the row's M and invL
+
+  const RowIdx<DT, WPR> ix;
+  const int lane = ix.lane;
+  const int N = (int)a.s.N;
+  const int nslots = (T + TPS - 1) / TPS;
+  const int nseg = (nslots + SPS - 1) / SPS;
+  const bool has_sink = a.sink != nullptr;
+
+  for (int64_t r = blockIdx.x; r < a.s.rows; r += gridDim.x) {
+    const char *srow = static_cast<const char *>(a.scores) + r * a.s.ld * ESZ;
+    char *prow = static_cast<char *>(a.probs) + r * a.s.ld * ESZ;
+    const float *mrow = nullptr;
+    int64_t h = 0;
+    int kend = N;
+    if (MASK || has_sink || EXCL) {
+      const int64_t q = r % a.s.Sq;
+      const int64_t bh = r / a.s.Sq;
+      h = bh % a.s.H;
+      if constexpr (MASK) mrow = a.mask + (bh / a.s.H) * a.msb + h * a.msh + q * a.msq;
+      if constexpr (EXCL) kend = row_kend(a.ex, N, a.s.Sq, bh / a.s.H, q);
+    }
+    const int kread = EXCL ? (kend + KPL - 1) / KPL * KPL : N;
+    const Buf sbuf(srow, (uint32_t)(kread * ESZ));
+    const Buf pbuf(prow, (uint32_t)(N * ESZ));
+    const Buf mbuf(mrow, MASK ? (uint32_t)(kread * 4) : 0u);
+    const uint32_t voff = (uint32_t)(ix.loff * ESZ);
+    const int lim = kend - ix.loff;
+
+    Chunk raw[CPL];
+    float e[CPL][KPL];
+    auto load_segment = [&](int g) {
+#pragma unroll
+      for (int s = 0; s < CPL; ++s) {
+        const int sb = (g * SPS + s * WPR + ix.wir) * TPS * kTile;
+        if constexpr (VEC) raw[s] = bload<kAuxNT>(sbuf, voff, (uint32_t)(sb * ESZ));
+        else raw[s] = load_chunk_elems<DT>(srow, sb + ix.loff, kend, kFill);
+      }
+    };
+    // the slot's keys as binary32 with the mask added and every key past
+    // the row or the cut at -inf; false when the whole slot is past them
+    auto slot_x = [&](int g, int s, float (&x)[KPL]) -> bool {
+      const int sb = (g * SPS + s * WPR + ix.wir) * TPS * kTile;
+      if (sb >= kend) return false;  // uniform
+      const int j0 = sb + ix.loff;
+      unpack<DT>(raw[s], x);
+      if constexpr (MASK) {
+        if constexpr (VEC) {
+#pragma unroll
+          for (int k4 = 0; k4 < KPL / 4; ++k4) {
+            const Chunk c = bload<0>(mbuf, (uint32_t)(ix.loff * 4 + 16 * k4), (uint32_t)(sb * 4));
+            x[4 * k4 + 0] = x[4 * k4 + 0] + u2f(c.w[0]);
+            x[4 * k4 + 1] = x[4 * k4 + 1] + u2f(c.w[1]);
+            x[4 * k4 + 2] = x[4 * k4 + 2] + u2f(c.w[2]);
+            x[4 * k4 + 3] = x[4 * k4 + 3] + u2f(c.w[3]);
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < KPL; ++k)
+            if (j0 + k < kend) x[k] = x[k] + mrow[j0 + k];
+        }
+      }
+      if constexpr (VEC) {
+        if (sb + TPS * kTile > kend) {  // the slot reaching past the row or the cut (uniform)
+          const int nv = lim - sb;
+#pragma unroll
+          for (int k = 0; k < KPL; ++k) x[k] = (k < nv) ? x[k] : kNegInf;
+        }
+      }
+      return true;
+    };
+
+    // segments wholly past the cut hold only -inf keys: nothing to load
+    const int nseg_read = EXCL ? (kend + SPS * TPS * kTile - 1) / (SPS * TPS * kTile) : nseg;
+
+    // ---- pass 1: tile states of every segment into LDS ----
+    for (int g = 0; g < nseg; ++g) {
+      if (g < nseg_read) load_segment(g);
+#pragma unroll
+      for (int s = 0; s < CPL; ++s) {
+        const int t = (g * SPS + s * WPR + ix.wir) * TPS + ix.half;
+        float x[KPL];
+        float m = kNegInf, l = 0.0f;
+        if (slot_x(g, s, x)) {
+          m = tile_max<DT>(lane_tree_max<KPL>(x));
+          const float msafe = (m == kNegInf) ? 0.0f : m;
+#pragma unroll
+          for (int k = 0; k < KPL; ++k) e[s][k] = exp_(x[k] - msafe);
+          l = tile_sum<DT>(lane_tree_sum<KPL>(e[s]));
+        } else {
+#pragma unroll
+          for (int k = 0; k < KPL; ++k) e[s][k] = 0.0f;
+        }
+        if (ix.cil == 0 && t < T) {
+          lds_m[t] = m;
+          lds_l[t] = l;
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- the fold, in tile order, 64 tiles per step (wave 0) ----
+    if (ix.wir == 0) {
+      float Mc = kNegInf, Lc = 0.0f;  // the state after the tiles folded so far
+      for (int b0 = 0; b0 < T; b0 += kWave) {
+        const int t = b0 + lane;
+        const float mt = (t < T) ? lds_m[t] : kNegInf;
+        const float lt = (t < T) ? lds_l[t] : 0.0f;
+        float Mi = mt;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) Mi = fmax2(Mi, __shfl_up(Mi, d));
+        Mi = fmax2(Mi, Mc);               // running max after tile t
+        float Me = __shfl_up(Mi, 1);      // running max before tile t
+        if (lane == 0) Me = Mc;
+        float alpha = 0.0f, qv = 0.0f;
+        if (Mi != kNegInf) {
+          alpha = (Me == kNegInf) ? 0.0f : exp_(Me - Mi);
+          const float beta = (mt == kNegInf) ? 0.0f : exp_(mt - Mi);
+          qv = lt * beta;
+        }
+        const int nt = (T - b0 < kWave) ? T - b0 : kWave;
+        float L = Lc;
+        for (int i = 0; i < nt; ++i) {
+          const float La = L * readlane(alpha, i);
+          L = La + readlane(qv, i);
+        }
+        Lc = L;
+        Mc = readlane(Mi, nt - 1);
+      }
+      float M = Mc, L = Lc;
+      float sigma = 0.0f;
+      if (has_sink) {
+        sigma = a.sink[h];
+        const float Mn = fmax2(M, sigma);
+        if (Mn == kNegInf) {
+          M = kNegInf;
+          L = 0.0f;
+        } else {
+          const float fa = (M == kNegInf) ? 0.0f : exp_(M - Mn);
+          const float fb = (sigma == kNegInf) ? 0.0f : exp_(sigma - Mn);
+          const float La = L * fa;
+          const float lb = 1.0f * fb;
+          L = La + lb;
+          M = Mn;
+        }
+      }
+      const float invL = (L == 0.0f) ? 0.0f : 1.0f / L;
+      if (lane == 0) {
+        lds_row[0] = M;
+        lds_row[1] = invL;
+        if (has_sink) a.p_sink[r] = (sigma == kNegInf) ? 0.0f : exp_(sigma - M) * invL;
+        if (a.lse) a.lse[r] = (L == 0.0f) ? kNegInf : M + ln_(L);
+      }
+    }
+    __syncthreads();
+    const float M = lds_row[0], invL = lds_row[1];
+
+    // ---- pass 2: rescale, convert once, write; last segment first ----
+    for (int g = nseg - 1; g >= 0; --g) {
+      const bool again = g != nseg - 1;
+      if (again && g < nseg_read) load_segment(g);
+#pragma unroll
+      for (int s = 0; s < CPL; ++s) {
+        const int gs = g * SPS + s * WPR + ix.wir;
+        if (gs < nslots) {
+          const int sb = gs * TPS * kTile;
+          const int t = gs * TPS + ix.half;
+          const float mt = lds_m[t < T ? t : T - 1];
+          if (again) {
+            float x[KPL];
+            if (slot_x(g, s, x)) {
+              const float msafe = (mt == kNegInf) ? 0.0f : mt;
+#pragma unroll
+              for (int k = 0; k < KPL; ++k) e[s][k] = exp_(x[k] - msafe);
+            } else {
+#pragma unroll
+              for (int k = 0; k < KPL; ++k) e[s][k] = 0.0f;
+            }
+          }
+          const float cs = (mt == kNegInf) ? 0.0f : exp_(mt - M) * invL;
+          float p[KPL];
+#pragma unroll
+          for (int k = 0; k < KPL; ++k) p[k] = e[s][k] * cs;
+          const Chunk out = pack<DT>(p);
+          if constexpr (VEC) bstore(pbuf, voff, (uint32_t)(sb * ESZ), out);
+          else store_chunk_elems<DT>(prow, sb + ix.loff, N, out);
+        }
+      }
+    }
+    __syncthreads();  // LDS is reused by the next row
+  }
+}
+
+template <int DT, int CPL, bool VEC, bool EXCL>
+__global__ __launch_bounds__(kWave * kBlockWaves) void bwd_stream_kernel(const BwdArgs a) {
+  using C = Cfg<DT>;
+  constexpr int WPR = kBlockWaves;
+  constexpr int KPL = C::KPL, TPS = C::TPS, ESZ = C::ESZ;
+  constexpr int SPS = WPR * CPL;
+  extern __shared__ float smem[];
+  const int T = a.s.T;
+  float *lds_d = smem;            // [T] tile sums of P*dP
+  float *lds_row = smem + T;      // delta
+
+  const RowIdx<DT, WPR> ix;
+  const int lane = ix.lane;
+  const int N = (int)a.s.N;
+  const int nslots = (T + TPS - 1) / TPS;
+  const int nseg = (nslots + SPS - 1) / SPS;
+  const bool has_sink = a.p_sink != nullptr;
+
+  for (int64_t r = blockIdx.x; r < a.s.rows; r += gridDim.x) {
+    const char *prow = static_cast<const char *>(a.probs) + r * a.s.ld * ESZ;
+    const char *grow = static_cast<const char *>(a.dprobs) + r * a.s.ld * ESZ;
+    char *drow = static_cast<char *>(a.dscores) + r * a.s.ld * ESZ;
+    int kend = N;
+    if constexpr (EXCL) kend = row_kend(a.ex, N, a.s.Sq, r / (a.s.Sq * a.s.H), r % a.s.Sq);
+    const int kread = EXCL ? (kend + KPL - 1) / KPL * KPL : N;
+    const Buf pbuf(prow, (uint32_t)(kread * ESZ));
+    const Buf gbuf(grow, (uint32_t)(N * ESZ)), dbuf(drow, (uint32_t)(N * ESZ));
+    const uint32_t voff = (uint32_t)(ix.loff * ESZ);
+    const int lim = kend - ix.loff;
+
+    Chunk rp[CPL], rg[CPL];
+    auto load_segment = [&](int g) {
+#pragma unroll
+      for (int s = 0; s < CPL; ++s) {
+        const int sb = (g * SPS + s * WPR + ix.wir) * TPS * kTile;
+        if constexpr (VEC) {
+          rp[s] = bload<kAuxNT>(pbuf, voff, (uint32_t)(sb * ESZ));
+          rg[s] = bload<kAuxNT>(gbuf, voff, (uint32_t)(sb * ESZ));
+          if constexpr (EXCL) {
+            if (sb + TPS * kTile > kend && sb < kread) {  // the slot holding the cut (uniform)
+              const int nv = lim - sb;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {  // keys at or past kend: P = +0
+                if constexpr (DT != 0)
+                  rp[s].w[i] &= (nv > 2 * i ? 0x0000ffffu : 0u) | (nv > 2 * i + 1 ? 0xffff0000u : 0u);
+                else
+                  rp[s].w[i] = nv > i ? rp[s].w[i] : 0u;
+              }
+            }
+          }
+        } else {
+          rp[s] = load_chunk_elems<DT>(prow, sb + ix.loff, kend, 0u);
+          rg[s] = load_chunk_elems<DT>(grow, sb + ix.loff, N, 0u);
+        }
+      }
+    };
+
+    // ---- pass 1: tile sums of P*dP into LDS ----
+    for (int g = 0; g < nseg; ++g) {
+      load_segment(g);
+#pragma unroll
+      for (int s = 0; s < CPL; ++s) {
+        const int t = (g * SPS + s * WPR + ix.wir) * TPS + ix.half;
+        float p[KPL], gv[KPL], pg[KPL];
+        unpack<DT>(rp[s], p);
+        unpack<DT>(rg[s], gv);
+#pragma unroll
+        for (int k = 0; k < KPL; ++k) pg[k] = p[k] * gv[k];
+        const float d = tile_sum<DT>(lane_tree_sum<KPL>(pg));
+        if (ix.cil == 0 && t < T) lds_d[t] = d;
+      }
+    }
+    __syncthreads();
+
+    // ---- delta: the tile sums folded left to right from the first (wave 0) ----
+    if (ix.wir == 0) {
+      float delta = 0.0f;
+      for (int b0 = 0; b0 < T; b0 += kWave) {
+        const int t = b0 + lane;
+        const float dt = (t < T) ? lds_d[t] : 0.0f;
+        const int nt = (T - b0 < kWave) ? T - b0 : kWave;
+        for (int i = 0; i < nt; ++i) delta = (b0 + i == 0) ? readlane(dt, 0) : delta + readlane(dt, i);
+      }
+      if (lane == 0) {
+        lds_row[0] = delta;
+        if (has_sink) a.v[r] = -(a.p_sink[r] * delta);
+      }
+    }
+    __syncthreads();
+    const float delta = lds_row[0];
+
+    // ---- pass 2: dS = P * (dP - delta), convert once, write; last segment first ----
+    for (int g = nseg - 1; g >= 0; --g) {
+      if (g != nseg - 1) load_segment(g);
+#pragma unroll
+      for (int s = 0; s < CPL; ++s) {
+        const int gs = g * SPS + s * WPR + ix.wir;
+        if (gs < nslots) {
+          const int sb = gs * TPS * kTile;
+          float p[KPL], gv[KPL], ds[KPL];
+          unpack<DT>(rp[s], p);
+          unpack<DT>(rg[s], gv);
+#pragma unroll
+          for (int k = 0; k < KPL; ++k) {
+            const float gd = gv[k] - delta;
+            ds[k] = p[k] * gd;
+          }
+          const Chunk out = pack<DT>(ds);
+          if constexpr (VEC) bstore(dbuf, voff, (uint32_t)(sb * ESZ), out);
+          else store_chunk_elems<DT>(drow, sb + ix.loff, N, out);
+        }
+      }
+    }
+    __syncthreads();  // LDS is reused by the next row
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Launch tables
 // ---------------------------------------------------------------------------
 
 // chunks-per-lane sizes compiled for each dtype (register budget: the row's
 // share is kept in registers between the reduction and the write); the
-// 16-bit types share one list
+// 16-bit types share one list.  The streaming kernels have their own
+// (a segment is 4 waves x CPL slots: 64 tiles at the larger size).
 constexpr int kCplF32[] = {1, 2, 3, 5, 9, 17};
 constexpr int kCplBf16[] = {1, 2, 3, 5, 9};
+constexpr int kStreamCplF32[] = {8, 16};
+constexpr int kStreamCplBf16[] = {4, 8};
+
+template <int DT, int CPL>
+hipError_t launch_fwd_stream(const FwdArgs &a, const Geometry &g, hipStream_t st) {
+  const dim3 grid((unsigned)g.blocks), block(kWave * kBlockWaves);
+  const size_t lds = (size_t)(2 * a.s.T + 2) * sizeof(float);
+  const bool mask = a.mask != nullptr, excl = a.ex.causal || a.ex.key_len;
+#define JAS_FWD_STREAM(V, MK, EX)                                                              \
+  hipLaunchKernelGGL((fwd_stream_kernel<DT, CPL, V, MK, EX>), grid, block, lds, st, a)
+  if (a.vec_io) {
+    if (excl) { if (mask) JAS_FWD_STREAM(true, true, true); else JAS_FWD_STREAM(true, false, true); }
+    else { if (mask) JAS_FWD_STREAM(true, true, false); else JAS_FWD_STREAM(true, false, false); }
+  } else {
+    if (excl) { if (mask) JAS_FWD_STREAM(false, true, true); else JAS_FWD_STREAM(false, false, true); }
+    else { if (mask) JAS_FWD_STREAM(false, true, false); else JAS_FWD_STREAM(false, false, false); }
+  }
+#undef JAS_FWD_STREAM
+  return hipGetLastError();
+}
+
+template <int DT, int CPL>
+hipError_t launch_bwd_stream(const BwdArgs &a, const Geometry &g, hipStream_t st) {
+  const dim3 grid((unsigned)g.blocks), block(kWave * kBlockWaves);
+  const size_t lds = (size_t)(a.s.T + 1) * sizeof(float);
+  const bool excl = a.ex.causal || a.ex.key_len;
+  if (a.vec_io) {
+    if (excl) hipLaunchKernelGGL((bwd_stream_kernel<DT, CPL, true, true>), grid, block, lds, st, a);
+    else hipLaunchKernelGGL((bwd_stream_kernel<DT, CPL, true, false>), grid, block, lds, st, a);
+  } else {
+    if (excl) hipLaunchKernelGGL((bwd_stream_kernel<DT, CPL, false, true>), grid, block, lds, st, a);
+    else hipLaunchKernelGGL((bwd_stream_kernel<DT, CPL, false, false>), grid, block, lds, st, a);
+  }
+  return hipGetLastError();
+}
 
 // rows with an exclusion (causal or key lengths) run their own instances,
 // so the row-level cut costs the dense rows nothing
@@ -812,6 +1182,13 @@ hipError_t bwd_wpr(const BwdArgs &a, const Geometry &g, hipStream_t st) {
 
 template <int DT>
 hipError_t fwd_dt(const FwdArgs &a, const Geometry &g, hipStream_t st) {
+  if (g.stream) {
+    constexpr int c0 = DT == 0 ? kStreamCplF32[0] : kStreamCplBf16[0];
+    constexpr int c1 = DT == 0 ? kStreamCplF32[1] : kStreamCplBf16[1];
+    if (g.cpl == c0) return launch_fwd_stream<DT, c0>(a, g, st);
+    if (g.cpl == c1) return launch_fwd_stream<DT, c1>(a, g, st);
+    return hipErrorInvalidValue;
+  }
   switch (g.wpr) {
     case 1: return fwd_wpr<DT, 1>(a, g, st);
     case 2: return fwd_wpr<DT, 2>(a, g, st);
@@ -822,6 +1199,13 @@ hipError_t fwd_dt(const FwdArgs &a, const Geometry &g, hipStream_t st) {
 
 template <int DT>
 hipError_t bwd_dt(const BwdArgs &a, const Geometry &g, hipStream_t st) {
+  if (g.stream) {
+    constexpr int c0 = DT == 0 ? kStreamCplF32[0] : kStreamCplBf16[0];
+    constexpr int c1 = DT == 0 ? kStreamCplF32[1] : kStreamCplBf16[1];
+    if (g.cpl == c0) return launch_bwd_stream<DT, c0>(a, g, st);
+    if (g.cpl == c1) return launch_bwd_stream<DT, c1>(a, g, st);
+    return hipErrorInvalidValue;
+  }
   switch (g.wpr) {
     case 1: return bwd_wpr<DT, 1>(a, g, st);
     case 2: return bwd_wpr<DT, 2>(a, g, st);

@@ -73,6 +73,15 @@ bool cpl_compiled(int dtype, int wpr, int cpl) {
   return false;
 }
 
+bool stream_cpl_compiled(int dtype, int cpl) {
+  const int *c = dtype == 0 ? kStreamCplF32 : kStreamCplBf16;
+  return cpl == c[0] || cpl == c[1];
+}
+
+// Streaming segments of 64 tiles (16,384 keys): 4 waves x 8 slots for the
+// 16-bit types, 4 x 16 for fp32.
+int default_stream_cpl(int dtype) { return dtype == 0 ? kStreamCplF32[1] : kStreamCplBf16[1]; }
+
 // Default waves per row for a row of `nslots` wave-wide chunks (the
 // chunks-per-lane size then is the smallest compiled one that covers the
 // row).  Measured on MI355X, bf16 (fp16 is laid out the same; fp32 rows are

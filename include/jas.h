@@ -93,8 +93,13 @@
 extern "C" {
 #endif
 
-/* Largest supported row length (keys per row). */
-#define JAS_MAX_KEYS 16384
+/* Largest supported row length (keys per row).  Rows of up to 16,384 keys
+ * are held in registers for one pass over HBM; longer rows are streamed
+ * (RL-Kernel PR #453, Summary: rows are processed tile by tile, left to
+ * right): the tile states of the whole row are kept on chip, and every
+ * segment but the last is read a second time to write the outputs, with the
+ * same arithmetic and so the same bits. */
+#define JAS_MAX_KEYS 262144
 
 /* Element type of scores, probs, dprobs and dscores.  mask, sink, p_sink,
    lse, d_sink and the workspace are always binary32. */
@@ -145,12 +150,16 @@ typedef struct {
  * (one of the compiled sizes; waves_per_row*chunks_per_lane chunks of 64
  * lanes must cover the row); rows_per_block: rows per workgroup, with
  * waves_per_row*rows_per_block <= 4; max_blocks: grid size cap (the
- * workgroups then loop over the rows). */
+ * workgroups then loop over the rows).  streaming = 1 runs the streaming
+ * kernels for rows of any length (they always run for rows over 16,384
+ * keys): 4 waves and 1 row per workgroup, chunks_per_lane per segment in
+ * {4, 8} for 16-bit types, {8, 16} for fp32. */
 typedef struct {
   int32_t waves_per_row;
   int32_t chunks_per_lane;
   int32_t rows_per_block;
   int32_t max_blocks;
+  int32_t streaming;
 } jas_launch_t;
 
 /* Forward.

@@ -18,7 +18,8 @@ import torch
 
 __all__ = [
     "gen", "normal", "grad_check_fp32", "rows_with_outliers_bf16", "joint_attention_bf16", "batch_sweep_fp32",
-    "causal_sink_bf16", "synthetic_bwd_inputs", "to_numpy_bits", "from_numpy_bits",
+    "causal_sink_bf16", "long_context_bf16", "synthetic_bwd_inputs", "to_numpy_bits",
+    "from_numpy_bits",
 ]
 
 
@@ -105,6 +106,15 @@ def causal_sink_bf16(seed=5, device="cpu", B=1, H=32, S=8192, N=None):
     sink = normal((H,), 1.0, seed + 2, device)
     g = normal((B, H, S, N), 1.0, seed + 1, device, torch.bfloat16)
     return s, sink, g
+
+
+def long_context_bf16(seed=7, device="cpu", B=1, H=16, S=512, N=65536, std=2.0):
+    """Long-context rows: bf16 scores [B,H,S,N] ~ N(0, std^2) and dP ~ N(0,1),
+    S queries at the end of N keys (the causal condition key <= N - S + q is
+    applied by the library's flag, not written into the scores)."""
+    s = normal((B, H, S, N), std, seed, device, torch.bfloat16)
+    g = normal((B, H, S, N), 1.0, seed + 1, device, torch.bfloat16)
+    return s, g
 
 
 def synthetic_bwd_inputs(shape, dtype, seed, device, with_sink=False, zero_upper=False):

@@ -153,10 +153,18 @@ def test_workspace():
 
 def test_launch_override_validation():
     d = desc(B=1, H=1, S=4, N=4352)  # 17 tiles -> 9 bf16 slots
-    bad = [(3, 0, 0, 0), (1, 4, 0, 0), (1, 5, 0, 0), (2, 9, 3, 0), (-1, 0, 0, 0)]
+    bad = [(3, 0, 0, 0), (1, 4, 0, 0), (1, 5, 0, 0), (2, 9, 3, 0), (-1, 0, 0, 0),
+           # streaming: 4 waves, one row per workgroup, a streaming segment size
+           (0, 3, 0, 0, 1), (2, 0, 0, 0, 1), (0, 0, 2, 0, 1), (0, 0, 0, 0, 2), (0, 9, 0, 0, 1)]
     for L in bad:
         lt = jas._launch(L)
         assert fwd(d, launch=lt) == 7, L
+    # rows over 16,384 keys always stream: one-pass geometries are refused
+    dl = desc(B=1, H=1, S=4, N=20000)
+    for L in [(1, 0, 0, 0), (4, 9, 0, 0), (0, 16, 0, 0)]:
+        assert fwd(dl, launch=jas._launch(L)) == 7, L
+    df = desc(B=1, H=1, S=4, N=20000, dtype=jas.JAS_DTYPE_F32)
+    assert fwd(df, launch=jas._launch((0, 4, 0, 0))) == 7  # 4 is a 16-bit segment size
 
 
 def test_binding_rejects_host_tensors():

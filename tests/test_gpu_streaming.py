@@ -1,0 +1,152 @@
+"""GPU: the streaming kernels, for rows longer than the one-pass kernels hold
+(more than 16,384 keys, up to 262,144).
+
+RL-Kernel PR #453, Summary: the row is processed tile by tile, left to
+right, the per-tile states merged in order; nothing in the result depends on
+how many tiles are held at once.  So the streaming kernels, forced onto rows
+the one-pass kernels also run, must give the same bytes (P, p_sink, lse, dS,
+d_sink), and on long rows they are checked against the oracle: forward to
+the usual tolerance, backward stage-isolated and bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import deterministic_attention_softmax_amd as jas
+import oracle
+import synth
+from tests.gpu_util import (assert_bitexact, assert_close, assert_lse_close, dev, gather_rows,
+                            log, oracle_rows_bwd, sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+STREAM_CPLS = {torch.float32: (8, 16), torch.bfloat16: (4, 8), torch.float16: (4, 8)}
+
+
+def run(s, g, launch=None, mask=None, mask_strides=None, sink=None, causal=False, key_len=None):
+    P, ps, lse = jas.fwd(s, mask=mask, mask_strides=mask_strides, sink=sink, causal=causal,
+                         key_len=key_len, launch=launch, want_lse=True)
+    dS, dsk = jas.bwd(P, g, p_sink=ps, causal=causal, key_len=key_len, launch=launch)
+    torch.cuda.synchronize()
+    out = [synth.to_numpy_bits(P).tobytes(), lse.cpu().numpy().tobytes(),
+           synth.to_numpy_bits(dS).tobytes()]
+    if sink is not None:
+        out += [ps.cpu().numpy().tobytes(), dsk.cpu().numpy().tobytes()]
+    return out
+
+
+@pytest.mark.parametrize("N", [1, 7, 257, 700, 4352, 8449, 16384])
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32, torch.float16])
+def test_forced_streaming_matches_one_pass(dt, N):
+    B, H, S = 2, 2, 5
+    log(f"forced streaming vs one pass: {dt} N={N}")
+    s = synth.normal((B, H, S, N), 2.0, 400 + N, "cpu", dt).to(dev())
+    g = synth.normal((B, H, S, N), 1.0, 401 + N, "cpu", dt).to(dev())
+    mask = torch.zeros((B, 1, 1, N), device=dev())
+    mask[1, ..., N - N // 3:] = float("-inf")
+    sink = synth.normal((H,), 1.0, 402 + N, "cpu").to(dev())
+    kl = torch.tensor([N, max(0, N - 300)], dtype=torch.int32, device=dev())
+    cases = [dict(), dict(mask=mask, sink=sink), dict(causal=True, sink=sink),
+             dict(key_len=kl, mask=mask)]
+    for kw in cases:
+        ref = run(s, g, **kw)
+        for cpl in STREAM_CPLS[dt]:
+            got = run(s, g, launch=(4, cpl, 1, 0, 1), **kw)
+            assert got == ref, f"streaming cpl={cpl} {sorted(kw)} changed the bytes"
+
+
+def long_case(dt, N, B=1, H=2, S=3, with_mask=False, with_sink=False, causal=False, kl=None,
+              seed=0):
+    s = synth.normal((B, H, S, N), 2.0, seed, "cpu", dt)
+    mask = None
+    if with_mask:
+        mask = torch.zeros((B, 1, 1, N))
+        mask[..., N // 2:N // 2 + 1000] = float("-inf")
+    sink = synth.normal((H,), 1.0, seed + 2, "cpu") if with_sink else None
+    key_len = None if kl is None else torch.tensor(kl, dtype=torch.int32)
+    P, ps, lse = jas.fwd(s.to(dev()), mask=None if mask is None else mask.to(dev()),
+                         mask_strides=None if mask is None else (N, 0, 0),
+                         sink=None if sink is None else sink.to(dev()), causal=causal,
+                         key_len=None if key_len is None else key_len.to(dev()), want_lse=True)
+    torch.cuda.synchronize()
+    P_o, ps_o, lse_o = oracle.fwd(synth.to_numpy_bits(s), B, H, S, N,
+                                  mask=None if mask is None else mask.numpy(),
+                                  mask_strides=(N, 0, 0), sink=None if sink is None else sink.numpy(),
+                                  causal=causal, key_len=None if kl is None else np.array(kl, np.int32),
+                                  want_lse=True)
+    assert_close(synth.to_numpy_bits(P), P_o, f"P N={N}")
+    assert_lse_close(lse.cpu().numpy(), lse_o, f"lse N={N}")
+    if with_sink:
+        assert_close(ps.cpu().numpy(), ps_o, "p_sink")
+    # stage-isolated backward on the oracle's P
+    g = synth.normal((B, H, S, N), 1.0, seed + 1, "cpu", dt)
+    Pin = synth.from_numpy_bits(P_o, dev())
+    psin = None if ps_o is None else torch.from_numpy(ps_o).to(dev())
+    dS, dsk = jas.bwd(Pin, g.to(dev()), p_sink=psin, causal=causal,
+                      key_len=None if key_len is None else key_len.to(dev()))
+    torch.cuda.synchronize()
+    dS_o, v_o = oracle.bwd(P_o, synth.to_numpy_bits(g), B, H, S, N, p_sink=ps_o, causal=causal,
+                           key_len=None if kl is None else np.array(kl, np.int32))
+    assert_bitexact(synth.to_numpy_bits(dS), dS_o, f"dS N={N}")
+    if with_sink:
+        assert_bitexact(dsk.cpu().numpy(), oracle.dsink(v_o, B, H, S), "d_sink")
+
+
+@pytest.mark.parametrize("N", [16385, 20000, 32768, 65536, 100003, 262144])
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32, torch.float16])
+def test_long_rows_against_oracle(dt, N):
+    log(f"long rows: {dt} N={N}")
+    long_case(dt, N, with_mask=N % 2 == 0, with_sink=True, seed=N % 1000)
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_long_rows_with_exclusion(dt):
+    N = 70000
+    log(f"long rows with exclusion: {dt} N={N}")
+    long_case(dt, N, B=2, H=2, S=3, causal=True, kl=[40001, N], with_sink=True, seed=77)
+    # a key length that cuts inside the first segment: the later segments
+    # are neither read nor computed, and their P is written as +0
+    long_case(dt, N, B=1, H=1, S=5, causal=True, kl=[12345], seed=79)
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_long_row_geometries_identical(dt):
+    # both segment sizes and a capped grid (workgroups looping over rows)
+    N = 50001
+    B, H, S = 1, 3, 4
+    log(f"long-row geometries: {dt} N={N}")
+    s = synth.normal((B, H, S, N), 2.0, 500, "cpu", dt).to(dev())
+    g = synth.normal((B, H, S, N), 1.0, 501, "cpu", dt).to(dev())
+    sink = synth.normal((H,), 1.0, 502, "cpu").to(dev())
+    ref = run(s, g, sink=sink, causal=True)
+    for cpl in STREAM_CPLS[dt]:
+        for cap in (0, 5):
+            assert run(s, g, launch=(0, cpl, 0, cap, 1), sink=sink, causal=True) == ref, (cpl, cap)
+
+
+def test_long_rows_full_size_sampled():
+    # long-context rows: bf16 [1,16,512,65536] (512 queries against 64K keys,
+    # 2^29 elements) with the causal condition (key <= N - Sq + q) as a flag;
+    # sampled rows against the oracle, stage-isolated backward on synthetic P
+    B, H, S, N = 1, 16, 512, 65536
+    log(f"bf16 [{B},{H},{S},{N}] causal flag, sampled rows")
+    s = synth.normal((B, H, S, N), 2.0, 600, dev(), torch.bfloat16)
+    P, _, lse = jas.fwd(s, causal=True, want_lse=True)
+    torch.cuda.synchronize()
+    idx = sample_rows(B * H * S, 24, seed=601)
+    q = idx % S
+    kend = q + (N - S) + 1
+    k = len(idx)
+    P_o, _, lse_o = oracle.fwd(gather_rows(s, idx).reshape(k, 1, 1, N), k, 1, 1, N,
+                               key_len=kend.astype(np.int32), want_lse=True)
+    assert_close(gather_rows(P, idx), P_o.reshape(k, N), "long P")
+    assert_lse_close(lse.cpu().numpy()[idx], lse_o, "long lse")
+    del P, s
+    torch.cuda.empty_cache()
+    Pin, gin, _ = synth.synthetic_bwd_inputs((B, H, S, N), torch.bfloat16, 602, dev())
+    dS, _ = jas.bwd(Pin, gin, causal=True)
+    torch.cuda.synchronize()
+    P_rows = gather_rows(Pin, idx)
+    P_rows[np.arange(N)[None, :] >= kend[:, None]] = 0
+    dS_o, _ = oracle_rows_bwd(P_rows, gather_rows(gin, idx), N)
+    assert_bitexact(gather_rows(dS, idx), dS_o, "long dS")
