@@ -283,9 +283,9 @@ def copy_ceiling(nbytes, stream, steps=10):
 
 
 def _kernel_kind(name):
-    if "fwd_kernel" in name:
+    if "fwd_kernel" in name or "fwd_stream_kernel" in name:
         return "fwd"
-    if "bwd_kernel" in name:
+    if "bwd_kernel" in name or "bwd_stream_kernel" in name:
         return "bwd"
     if "dsink_kernel" in name:
         return "dsink"
