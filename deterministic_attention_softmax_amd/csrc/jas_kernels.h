@@ -193,19 +193,6 @@ template <> constexpr uint32_t kNegInfBits<2> = 0xfc00fc00u;
 struct Chunk { uint32_t w[4]; };
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Scores, probabilities and gradients are streamed once: nontemporal
-// 16-byte loads and stores keep them from displacing reused data (the mask
-// row) in the caches.
-__device__ __forceinline__ Chunk load_chunk(const char *p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-  return Chunk{{v.x, v.y, v.z, v.w}};
-}
-
-__device__ __forceinline__ void store_chunk(char *p, const Chunk &c) {
-  const u32x4 v = {c.w[0], c.w[1], c.w[2], c.w[3]};
-  __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
-}
-
 // Element-by-element chunk load for unaligned rows and the tail of a row:
 // keys at or past n read as `fill` bits.
 template <int DT>
@@ -337,9 +324,10 @@ __device__ __forceinline__ void row_sync() {
 // cil*KPL.  The wave index is made wave-uniform (readfirstlane) so row
 // pointers live in scalar registers and every load is base + 32-bit lane
 // offset.  VEC: rows are whole 16-byte chunks on 16-byte boundaries, so a
-// chunk is wholly inside or wholly past the row; loads of a slot that
-// reaches past the row are clamped to the row's last chunk and the lanes
-// past the row are overwritten afterwards.  !VEC: element-wise access.
+// chunk is wholly inside or wholly past the row; the row is read and written
+// through a buffer resource of the row's size, so lanes past the row read 0
+// (replaced by -inf or +0 before use) and their stores are dropped.  !VEC:
+// element-wise access.
 // ---------------------------------------------------------------------------
 
 template <int DT, int WPR>
@@ -357,16 +345,6 @@ struct RowIdx {
     loff = half * kTile + cil * C::KPL;
   }
 };
-
-template <int ESZ>
-__device__ __forceinline__ Chunk load_at(const char *base, int j) {
-  return load_chunk(base + (uint32_t)(j * ESZ));
-}
-
-template <int ESZ>
-__device__ __forceinline__ void store_at(char *base, int j, const Chunk &c) {
-  store_chunk(base + (uint32_t)(j * ESZ), c);
-}
 
 // A raw buffer resource over one row (gfx9 family: stride 0, 32-bit
 // records).  Loads at or past `bytes` return 0 and stores there are

@@ -48,6 +48,11 @@ def lib():
         L.jas_oracle_bwd.restype = ctypes.c_int
         L.jas_oracle_bwd.argtypes = [ctypes.c_int, _I64, _I64, _I64, _I64, _I64, _VP, _VP,
                                      ctypes.c_int, _VP, _VP, _VP, _VP, ctypes.c_int]
+        L.jas_oracle_attn_fwd.restype = ctypes.c_int
+        L.jas_oracle_attn_fwd.argtypes = [ctypes.c_int, _I64, _I64, _I64, _I64, _I64, _I64, _VP,
+                                          _VP, _VP, ctypes.c_float, _VP, _I64, _I64, _I64,
+                                          ctypes.c_int, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                          ctypes.c_int]
         L.jas_oracle_dsink.restype = ctypes.c_int
         L.jas_oracle_dsink.argtypes = [_I64, _I64, _I64, _VP, _VP]
         L.jas_oracle_exp.restype = ctypes.c_float
@@ -144,6 +149,46 @@ def bwd(P, dP, B, H, Sq, N, ld=None, p_sink=None, threads=None, causal=False, ke
     if rc != 0:
         raise RuntimeError(f"jas_oracle_bwd failed: {rc}")
     return dS, v
+
+
+def attn_fwd(q, k, v, scale, mask=None, mask_strides=(0, 0, 0), causal=False, key_len=None,
+             sink=None, want_probs=False, want_scores=False, threads=None):
+    """Fixed-order attention forward.  q [B, H, Sq, D], k and v [B, Hkv, N, D]
+    (uint16 bf16 bits or float16), ``scale`` the binary32 score scale.
+    Returns a dict with ``out`` [B, H, Sq, D] (dtype of q), ``lse`` and
+    ``p_sink`` (float32 [B*H*Sq], p_sink None without a sink) and, when asked,
+    ``probs`` [B, H, Sq, N] (dtype of q) and ``scores`` (float32)."""
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    if q.dtype != k.dtype or q.dtype != v.dtype or k.shape != v.shape:
+        raise ValueError("q, k, v must share a dtype; k and v a shape")
+    B, H, Sq, D = q.shape
+    Bk, Hkv, N, Dk = k.shape
+    if Bk != B or Dk != D or H % Hkv:
+        raise ValueError("shapes do not match")
+    dt = _dtype_code(q)
+    if dt == F32:
+        raise TypeError("attention inputs are bf16 or fp16")
+    rows = B * H * Sq
+    out = np.zeros_like(q)
+    lse = np.zeros(rows, np.float32)
+    ps = np.zeros(rows, np.float32) if sink is not None else None
+    probs = np.zeros((B, H, Sq, N), q.dtype) if want_probs else None
+    scores = np.zeros((B, H, Sq, N), np.float32) if want_scores else None
+    if mask is not None:
+        mask = np.ascontiguousarray(mask, dtype=np.float32)
+    if sink is not None:
+        sink = np.ascontiguousarray(sink, dtype=np.float32)
+    kl = _key_len(key_len, B)
+    msb, msh, msq = mask_strides
+    rc = lib().jas_oracle_attn_fwd(dt, B, H, Hkv, Sq, N, D, _ptr(q), _ptr(k), _ptr(v),
+                                   float(np.float32(scale)), _ptr(mask), msb, msh, msq,
+                                   int(bool(causal)), _ptr(kl), _ptr(sink), _ptr(out), _ptr(lse),
+                                   _ptr(ps), _ptr(probs), _ptr(scores), threads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"jas_oracle_attn_fwd failed: {rc}")
+    return {"out": out, "lse": lse, "p_sink": ps, "probs": probs, "scores": scores}
 
 
 def dsink(v, B, H, Sq):

@@ -536,6 +536,149 @@ int jas_oracle_dsink(int64_t B, int64_t H, int64_t Sq, const float *v, float *d_
   return 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Fixed-order attention forward: QK, this softmax, PV                      */
+/* ------------------------------------------------------------------------ */
+
+/* One query row of attention ([P3] Fixed Reduction Contract: every score
+   has one writer and accumulates the head dimension in ascending order, the
+   softmax is the fixed-order one above, every output element has one writer
+   and accumulates the keys in ascending order; [P1] Summary: the softmax
+   sits between the QK GEMM and the AV GEMM and rounds once, to the tensor
+   dtype, when it writes P).
+     s_j   = fl(scale * dot_j), dot_j = sum over d = 0..D-1 of fl(q_d*k_jd),
+             added in that order
+     P_j   = the row softmax of s (mask, exclusion, sink as in fwd_row),
+             rounded to the tensor dtype
+     out_d = sum over j = 0..N-1 of fl(P_j*v_jd), added in that order, then
+             rounded to the tensor dtype
+   Optional outputs: the scores s (binary32) and P (tensor dtype). */
+typedef struct {
+  int dt;
+  int64_t B, H, Hkv, Sq, N, D;
+  const void *q, *k, *v;
+  float scale;
+  const float *mask;
+  int64_t msb, msh, msq;
+  int causal;
+  const int32_t *key_len;
+  const float *sink;
+  void *out;
+  float *lse, *p_sink;
+  void *probs;
+  float *scores;
+  int64_t r0, r1;
+  int status;
+} attn_job_t;
+
+static void *attn_worker(void *arg) {
+  attn_job_t *j = (attn_job_t *)arg;
+  ieee_env();
+  const int64_t N = j->N, D = j->D;
+  const int64_t T = (N + TILE - 1) / TILE;
+  const size_t es = elem_size(j->dt);
+  float *s = (float *)malloc(sizeof(float) * (size_t)N);
+  float *pf = (float *)malloc(sizeof(float) * (size_t)N);
+  void *P = malloc(es * (size_t)N);
+  float *x = (float *)malloc(sizeof(float) * (size_t)N);
+  float *e = (float *)malloc(sizeof(float) * (size_t)N);
+  float *m = (float *)malloc(sizeof(float) * (size_t)T);
+  float *l = (float *)malloc(sizeof(float) * (size_t)T);
+  if (!s || !pf || !P || !x || !e || !m || !l) {
+    j->status = -1;
+    free(s); free(pf); free(P); free(x); free(e); free(m); free(l);
+    return NULL;
+  }
+  const int64_t group = j->H / j->Hkv;  /* query heads per key/value head */
+  for (int64_t r = j->r0; r < j->r1; ++r) {
+    const int64_t qi = r % j->Sq;
+    const int64_t h = (r / j->Sq) % j->H;
+    const int64_t b = r / (j->Sq * j->H);
+    const int64_t hk = h / group;
+    const int64_t qoff = r * D;
+    const int64_t kvoff = (b * j->Hkv + hk) * N * D;
+    for (int64_t kj = 0; kj < N; ++kj) {
+      float dot = 0.0f;
+      for (int64_t d = 0; d < D; ++d) {
+        const float prod = load_elem(j->dt, j->q, qoff + d) * load_elem(j->dt, j->k, kvoff + kj * D + d);
+        dot = dot + prod;
+      }
+      s[kj] = j->scale * dot;
+    }
+    if (j->scores) memcpy(j->scores + r * N, s, sizeof(float) * (size_t)N);
+    const float *arow = j->mask ? j->mask + b * j->msb + h * j->msh + qi * j->msq : NULL;
+    const int has_sink = j->sink != NULL;
+    const float sigma = has_sink ? j->sink[h] : 0.0f;
+    float ps = 0.0f, ls = 0.0f;
+    const int64_t kend = row_kend(N, j->Sq, b, qi, j->causal, j->key_len);
+    /* the softmax of the binary32 scores, rounded to the tensor dtype at the write */
+    fwd_row(DT_F32, N, kend, s, arow, has_sink, sigma, pf, &ps, &ls, x, e, m, l);
+    for (int64_t kj = 0; kj < N; ++kj) store_elem(j->dt, P, kj, pf[kj]);
+    if (j->probs) memcpy((char *)j->probs + (size_t)(r * N) * es, P, es * (size_t)N);
+    if (has_sink) j->p_sink[r] = ps;
+    if (j->lse) j->lse[r] = ls;
+    for (int64_t d = 0; d < D; ++d) {
+      float acc = 0.0f;
+      for (int64_t kj = 0; kj < N; ++kj) {
+        const float prod = load_elem(j->dt, P, kj) * load_elem(j->dt, j->v, kvoff + kj * D + d);
+        acc = acc + prod;
+      }
+      store_elem(j->dt, j->out, qoff + d, acc);
+    }
+  }
+  free(s); free(pf); free(P); free(x); free(e); free(m); free(l);
+  j->status = 0;
+  return NULL;
+}
+
+/* Attention forward.  q, out [B, H, Sq, D]; k, v [B, Hkv, N, D] (H a
+   multiple of Hkv; query head h reads key/value head h / (H / Hkv)); all
+   contiguous, dtype bf16 or fp16.  mask / causal / key_len / sink as for
+   jas_oracle_fwd.  lse, p_sink: [B*H*Sq] or NULL; probs [B, H, Sq, N]
+   (dtype) and scores [B, H, Sq, N] (binary32) written when given. */
+int jas_oracle_attn_fwd(int dtype, int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t N,
+                        int64_t D, const void *q, const void *k, const void *v, float scale,
+                        const float *mask, int64_t msb, int64_t msh, int64_t msq, int causal,
+                        const int32_t *key_len, const float *sink, void *out, float *lse,
+                        float *p_sink, void *probs, float *scores, int threads) {
+  if ((dtype != DT_BF16 && dtype != DT_F16) || B < 0 || H < 1 || Hkv < 1 || H % Hkv ||
+      Sq < 0 || N < 1 || D < 1)
+    return -2;
+  if (sink && !p_sink) return -3;
+  const int64_t rows = B * H * Sq;
+  if (rows == 0) return 0;
+  if (threads < 1) threads = 1;
+  if (threads > 256) threads = 256;
+  if ((int64_t)threads > rows) threads = (int)rows;
+  attn_job_t jobs[256];
+  pthread_t tid[256];
+  int started[256];
+  int64_t per = rows / threads, extra = rows % threads, r = 0;
+  for (int i = 0; i < threads; ++i) {
+    attn_job_t *a = &jobs[i];
+    memset(a, 0, sizeof *a);
+    a->dt = dtype; a->B = B; a->H = H; a->Hkv = Hkv; a->Sq = Sq; a->N = N; a->D = D;
+    a->q = q; a->k = k; a->v = v; a->scale = scale;
+    a->mask = mask; a->msb = msb; a->msh = msh; a->msq = msq;
+    a->causal = causal; a->key_len = key_len; a->sink = sink;
+    a->out = out; a->lse = lse; a->p_sink = p_sink; a->probs = probs; a->scores = scores;
+    a->r0 = r;
+    r += per + (i < extra ? 1 : 0);
+    a->r1 = r;
+    a->status = -1;
+  }
+  for (int i = 0; i < threads; ++i)
+    started[i] = (i > 0) && pthread_create(&tid[i], NULL, attn_worker, &jobs[i]) == 0;
+  attn_worker(&jobs[0]);
+  for (int i = 1; i < threads; ++i) {
+    if (started[i]) pthread_join(tid[i], NULL);
+    else attn_worker(&jobs[i]);
+  }
+  for (int i = 0; i < threads; ++i)
+    if (jobs[i].status != 0) return -1;
+  return 0;
+}
+
 /* Small pieces exported for the pin tests. */
 float jas_oracle_exp(float y) { ieee_env(); return exp_(y); }
 float jas_oracle_log2e(void) { return log2e_f32(); }
