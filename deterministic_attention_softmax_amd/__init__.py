@@ -14,16 +14,20 @@ import os
 
 __all__ = [
     "JAS_DTYPE_F32", "JAS_DTYPE_BF16", "JAS_DTYPE_F16", "JAS_FLAG_MASK", "JAS_FLAG_SINK",
-    "JAS_FLAG_CAUSAL", "JAS_FLAG_KEY_LEN", "JAS_FLAG_LSE", "JAS_MAX_KEYS",
-    "STATUS", "JasError", "jas_desc_t", "jas_launch_t", "lib", "jas_fwd", "jas_fwd_ex",
-    "jas_bwd", "jas_bwd_ex", "jas_bwd_workspace_bytes", "jas_status_str", "jas_contract",
-    "make_desc", "fwd", "bwd", "LIB_PATH",
+    "JAS_FLAG_CAUSAL", "JAS_FLAG_KEY_LEN", "JAS_FLAG_LSE", "JAS_FLAG_PROBS", "JAS_FLAG_SCORES",
+    "JAS_MAX_KEYS", "JAS_ATTN_MAX_KEYS",
+    "STATUS", "JasError", "jas_desc_t", "jas_launch_t", "jas_attn_desc_t", "lib", "jas_fwd",
+    "jas_fwd_ex", "jas_bwd", "jas_bwd_ex", "jas_bwd_workspace_bytes", "jas_attn_fwd",
+    "jas_attn_workspace_bytes", "jas_status_str", "jas_contract", "make_desc",
+    "make_attn_desc", "fwd", "bwd", "attn_fwd", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libjas.so")
 
 JAS_DTYPE_F32, JAS_DTYPE_BF16, JAS_DTYPE_F16 = 0, 1, 2
 JAS_FLAG_MASK, JAS_FLAG_SINK, JAS_FLAG_CAUSAL, JAS_FLAG_KEY_LEN, JAS_FLAG_LSE = 1, 2, 4, 8, 16
+JAS_FLAG_PROBS, JAS_FLAG_SCORES = 32, 64
+JAS_ATTN_MAX_KEYS = 16384
 JAS_MAX_KEYS = 262144
 STATUS = {
     0: "JAS_OK", 1: "JAS_ERR_NULL_POINTER", 2: "JAS_ERR_BAD_SHAPE", 3: "JAS_ERR_BAD_DTYPE",
@@ -38,6 +42,16 @@ class jas_desc_t(ctypes.Structure):
         ("keys", ctypes.c_int64), ("ld", ctypes.c_int64), ("dtype", ctypes.c_int32),
         ("flags", ctypes.c_uint32), ("mask_stride_b", ctypes.c_int64),
         ("mask_stride_h", ctypes.c_int64), ("mask_stride_q", ctypes.c_int64),
+    ]
+
+
+class jas_attn_desc_t(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("heads", ctypes.c_int64), ("kv_heads", ctypes.c_int64),
+        ("q_len", ctypes.c_int64), ("kv_len", ctypes.c_int64), ("head_dim", ctypes.c_int64),
+        ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32), ("scale", ctypes.c_float),
+        ("mask_stride_b", ctypes.c_int64), ("mask_stride_h", ctypes.c_int64),
+        ("mask_stride_q", ctypes.c_int64),
     ]
 
 
@@ -83,6 +97,12 @@ def lib():
         L.jas_status_str.argtypes = [ctypes.c_int]
         L.jas_contract.restype = ctypes.c_char_p
         L.jas_contract.argtypes = []
+        _AP = ctypes.POINTER(jas_attn_desc_t)
+        L.jas_attn_workspace_bytes.restype = ctypes.c_size_t
+        L.jas_attn_workspace_bytes.argtypes = [_AP]
+        L.jas_attn_fwd.restype = ctypes.c_int
+        L.jas_attn_fwd.argtypes = [_AP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                   ctypes.c_size_t, _VP]
         _lib = L
     return _lib
 
@@ -300,3 +320,106 @@ def bwd(probs, dprobs, p_sink=None, out=None, d_sink=None, workspace=None, launc
     if st != 0:
         raise JasError(st, "jas_bwd")
     return out, (d_sink if p_sink is not None else None)
+
+
+# ---- fused attention ----------------------------------------------------------
+
+def make_attn_desc(B, H, Hkv, Sq, N, D, dtype_code, flags=0, scale=1.0, mask_strides=(0, 0, 0)):
+    d = jas_attn_desc_t()
+    d.batch, d.heads, d.kv_heads, d.q_len, d.kv_len, d.head_dim = (
+        int(v) for v in (B, H, Hkv, Sq, N, D))
+    d.dtype = dtype_code
+    d.flags = flags
+    d.scale = float(scale)
+    d.mask_stride_b, d.mask_stride_h, d.mask_stride_q = (int(v) for v in mask_strides)
+    return d
+
+
+def jas_attn_workspace_bytes(desc):
+    return int(lib().jas_attn_workspace_bytes(ctypes.byref(desc)))
+
+
+def jas_attn_fwd(desc, q, k, v, mask, key_len, sink, out, lse, p_sink, probs, scores, workspace,
+                 workspace_bytes, stream):
+    return lib().jas_attn_fwd(ctypes.byref(desc), q, k, v, mask, key_len, sink, out, lse, p_sink,
+                              probs, scores, workspace, workspace_bytes, stream)
+
+
+def _attn_tensor(t, name, like=None):
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be in device memory, not on {t.device}")
+    if t.dim() != 4 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous [batch, heads, len, head_dim] tensor")
+    if like is not None and (t.device != like.device or t.dtype != like.dtype):
+        raise ValueError(f"{name} must match q's device and dtype")
+    return t
+
+
+def attn_fwd(q, k, v, scale=None, mask=None, mask_strides=None, sink=None, causal=False,
+             key_len=None, want_lse=False, want_probs=False, want_scores=False, out=None,
+             workspace=None):
+    """Fused attention forward on device tensors: q [B, H, Sq, D], k and v
+    [B, Hkv, N, D] (bf16 or fp16, contiguous), ``scale`` (default
+    1/sqrt(D)).  Mask, sink, causal and key lengths as for :func:`fwd`.
+    Returns a dict with ``out`` and, when asked (or a sink is given),
+    ``lse``, ``p_sink``, ``probs``, ``scores``."""
+    import math
+    import torch
+    _attn_tensor(q, "q")
+    _attn_tensor(k, "k", q)
+    _attn_tensor(v, "v", q)
+    B, H, Sq, D = q.shape
+    Bk, Hkv, N, Dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or Dk != D:
+        raise ValueError("k and v must be [batch, kv_heads, kv_len, head_dim] like q")
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("attention takes bf16 or fp16")
+    rows = B * H * Sq
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    key_len = _check_vec(key_len, q, torch.int32, B, "key_len")
+    flags = (JAS_FLAG_CAUSAL if causal else 0) | (JAS_FLAG_KEY_LEN if key_len is not None else 0)
+    if mask is not None:
+        flags |= JAS_FLAG_MASK
+        if mask_strides is None:
+            m4 = mask.expand(B, H, Sq, N)
+            if m4.stride(3) != 1:
+                raise ValueError("mask keys must be contiguous")
+            mask_strides = (m4.stride(0), m4.stride(1), m4.stride(2))
+        if any(int(st) < 0 for st in mask_strides):
+            raise ValueError("mask strides must be non-negative")
+        mask_elems = 0 if rows == 0 else \
+            sum((n - 1) * int(st) for n, st in zip((B, H, Sq), mask_strides)) + N
+        _check_vec(mask, q, torch.float32, mask_elems, "mask")
+    if sink is not None:
+        flags |= JAS_FLAG_SINK
+        _check_vec(sink, q, torch.float32, H, "sink")
+    res = {"out": None, "lse": None, "p_sink": None, "probs": None, "scores": None}
+    dev = q.device
+    if want_lse:
+        flags |= JAS_FLAG_LSE
+        res["lse"] = torch.empty(rows, dtype=torch.float32, device=dev)
+    if sink is not None:
+        res["p_sink"] = torch.empty(rows, dtype=torch.float32, device=dev)
+    if want_probs:
+        flags |= JAS_FLAG_PROBS
+        res["probs"] = torch.empty((B, H, Sq, N), dtype=q.dtype, device=dev)
+    if want_scores:
+        flags |= JAS_FLAG_SCORES
+        res["scores"] = torch.empty((B, H, Sq, N), dtype=torch.float32, device=dev)
+    d = make_attn_desc(B, H, Hkv, Sq, N, D, _dtype_code(q), flags, scale, mask_strides or (0, 0, 0))
+    if out is None:
+        out = torch.empty_like(q)
+    _attn_tensor(out, "out", q)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have q's shape")
+    res["out"] = out
+    ws_bytes = jas_attn_workspace_bytes(d)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    _check_vec(workspace, q, torch.uint8, ws_bytes, "workspace")
+    st = jas_attn_fwd(d, _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(key_len), _ptr(sink),
+                      _ptr(out), _ptr(res["lse"]), _ptr(res["p_sink"]), _ptr(res["probs"]),
+                      _ptr(res["scores"]), _ptr(workspace), workspace.numel(), _stream())
+    if st != 0:
+        raise JasError(st, "jas_attn_fwd")
+    return res

@@ -15,7 +15,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libjas.so")
 SOURCES = [os.path.join(CSRC, f) for f in (
     "jas_kernels_f32.hip", "jas_kernels_bf16.hip", "jas_kernels_f16.hip", "jas_launch.hip",
-    "jas_api.cpp")]
+    "jas_attn.hip", "jas_api.cpp")]
 OBJ_DIR = os.path.join(HERE, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

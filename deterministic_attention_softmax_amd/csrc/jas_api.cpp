@@ -298,6 +298,141 @@ jas_status_t bwd_impl(const jas_desc_t *d, const void *probs, const void *dprobs
   return JAS_OK;
 }
 
+// ---- fused attention -------------------------------------------------------
+
+struct AttnDims {
+  int64_t rows;      // batch*heads*q_len
+  int64_t Np;        // keys padded to whole tiles
+  int T;
+  int64_t ws_bytes;  // V^T
+};
+
+jas_status_t check_attn_desc(const jas_attn_desc_t *d, AttnDims *dm) {
+  if (!d) return JAS_ERR_NULL_POINTER;
+  if (d->dtype != JAS_DTYPE_BF16 && d->dtype != JAS_DTYPE_F16) return JAS_ERR_BAD_DTYPE;
+  const uint32_t known = JAS_FLAG_MASK | JAS_FLAG_SINK | JAS_FLAG_CAUSAL | JAS_FLAG_KEY_LEN |
+                         JAS_FLAG_LSE | JAS_FLAG_PROBS | JAS_FLAG_SCORES;
+  if (d->flags & ~known) return JAS_ERR_BAD_FLAGS;
+  if (d->batch < 0 || d->q_len < 0 || d->heads < 1 || d->kv_heads < 1 || d->kv_len < 1 ||
+      d->heads % d->kv_heads != 0)
+    return JAS_ERR_BAD_SHAPE;
+  if (d->mask_stride_b < 0 || d->mask_stride_h < 0 || d->mask_stride_q < 0)
+    return JAS_ERR_BAD_SHAPE;
+  if (d->head_dim != 64 && d->head_dim != 128) return JAS_ERR_UNSUPPORTED;
+  if (d->kv_len > JAS_ATTN_MAX_KEYS) return JAS_ERR_UNSUPPORTED;
+  int64_t t = 0, rows = 0;
+  if (!mul_ok(d->batch, d->heads, &t) || !mul_ok(t, d->q_len, &rows)) return JAS_ERR_BAD_SHAPE;
+  // one (batch, head)'s Q, K and V^T are addressed with 32-bit byte offsets
+  int64_t qbytes = 0;
+  if (!mul_ok(d->q_len, d->head_dim * 2, &qbytes) || qbytes > 0x7fffffff) return JAS_ERR_UNSUPPORTED;
+  const int T = (int)((d->kv_len + jas::kTile - 1) / jas::kTile);
+  const int64_t Np = (int64_t)T * jas::kTile;
+  int64_t ws = 0;
+  if (!mul_ok(d->batch, d->kv_heads, &t) || !mul_ok(t, d->head_dim * Np * 2, &ws))
+    return JAS_ERR_BAD_SHAPE;
+  int64_t probe = 0;
+  if (!mul_ok(rows, d->kv_len * 4, &probe) || !mul_ok(rows, d->head_dim * 2, &probe))
+    return JAS_ERR_BAD_SHAPE;
+  // the transpose of V runs one workgroup per (key/value head, 64 keys)
+  if (!mul_ok(t, Np / 64, &probe) || probe > 0x7fffffff) return JAS_ERR_UNSUPPORTED;
+  dm->rows = rows;
+  dm->Np = Np;
+  dm->T = T;
+  dm->ws_bytes = (ws + 255) & ~(int64_t)255;
+  return JAS_OK;
+}
+
+jas_status_t attn_fwd_impl(const jas_attn_desc_t *d, const void *q, const void *k, const void *v,
+                           const float *mask, const int32_t *key_len, const float *sink,
+                           void *out, float *lse, float *p_sink, void *probs, float *scores,
+                           void *ws, size_t ws_bytes, void *stream) {
+  AttnDims dm;
+  jas_status_t st = check_attn_desc(d, &dm);
+  if (st != JAS_OK) return st;
+  const uint32_t f = d->flags;
+  const bool has_mask = f & JAS_FLAG_MASK, has_sink = f & JAS_FLAG_SINK,
+             has_klen = f & JAS_FLAG_KEY_LEN, has_lse = f & JAS_FLAG_LSE,
+             has_probs = f & JAS_FLAG_PROBS, has_scores = f & JAS_FLAG_SCORES;
+  if ((!has_mask && mask) || (!has_sink && (sink || p_sink)) || (!has_klen && key_len) ||
+      (!has_lse && lse) || (!has_probs && probs) || (!has_scores && scores))
+    return JAS_ERR_BAD_FLAGS;
+  if (dm.rows == 0) return JAS_OK;  // nothing is read or written
+  if (!q || !k || !v || !out) return JAS_ERR_NULL_POINTER;
+  if ((has_mask && !mask) || (has_sink && (!sink || !p_sink)) || (has_klen && !key_len) ||
+      (has_lse && !lse) || (has_probs && !probs) || (has_scores && !scores))
+    return JAS_ERR_NULL_POINTER;
+  if (!ws || (int64_t)ws_bytes < dm.ws_bytes) return JAS_ERR_WORKSPACE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(ws, 16) ||
+      !aligned(out, 2) || (probs && !aligned(probs, 2)) || (mask && !aligned(mask, 4)) ||
+      (sink && !aligned(sink, 4)) || (p_sink && !aligned(p_sink, 4)) ||
+      (lse && !aligned(lse, 4)) || (scores && !aligned(scores, 4)) ||
+      (key_len && !aligned(key_len, 4)))
+    return JAS_ERR_ALIGNMENT;
+
+  const int64_t D = d->head_dim;
+  const int64_t qbytes = dm.rows * D * 2;
+  const int64_t kvbytes = d->batch * d->kv_heads * d->kv_len * D * 2;
+  int64_t mb = 0;
+  if (has_mask) {
+    jas_desc_t md{};
+    md.batch = d->batch;
+    md.heads = d->heads;
+    md.q_rows = d->q_len;
+    md.keys = d->kv_len;
+    md.mask_stride_b = d->mask_stride_b;
+    md.mask_stride_h = d->mask_stride_h;
+    md.mask_stride_q = d->mask_stride_q;
+    st = mask_bytes(&md, &mb);
+    if (st != JAS_OK) return st;
+  }
+  const Range in[] = {range_of(q, qbytes), range_of(k, kvbytes), range_of(v, kvbytes),
+                      range_of(mask, mb), range_of(key_len, has_klen ? d->batch * 4 : 0),
+                      range_of(sink, has_sink ? d->heads * 4 : 0)};
+  const Range outs[] = {range_of(out, qbytes), range_of(lse, has_lse ? dm.rows * 4 : 0),
+                        range_of(p_sink, has_sink ? dm.rows * 4 : 0),
+                        range_of(probs, has_probs ? dm.rows * d->kv_len * 2 : 0),
+                        range_of(scores, has_scores ? dm.rows * d->kv_len * 4 : 0),
+                        range_of(ws, dm.ws_bytes)};
+  for (const Range &o : outs) {
+    for (const Range &i : in)
+      if (overlap(o, i)) return JAS_ERR_ALIASING;
+    for (const Range &o2 : outs)
+      if (&o2 != &o && overlap(o, o2)) return JAS_ERR_ALIASING;
+  }
+
+  jas::AttnArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.vt = ws;
+  a.out = out;
+  a.mask = has_mask ? mask : nullptr;
+  a.msb = d->mask_stride_b;
+  a.msh = d->mask_stride_h;
+  a.msq = d->mask_stride_q;
+  a.ex = jas::Exclusion{(f & JAS_FLAG_CAUSAL) ? 1 : 0, has_klen ? key_len : nullptr};
+  a.sink = has_sink ? sink : nullptr;
+  a.p_sink = has_sink ? p_sink : nullptr;
+  a.lse = has_lse ? lse : nullptr;
+  a.probs = has_probs ? probs : nullptr;
+  a.scores = has_scores ? scores : nullptr;
+  a.scale = d->scale;
+  a.B = d->batch;
+  a.H = d->heads;
+  a.Hkv = d->kv_heads;
+  a.Sq = d->q_len;
+  a.N = d->kv_len;
+  a.D = (int)D;
+  a.T = dm.T;
+  a.Np = (int)dm.Np;
+  const int64_t units = d->batch * d->heads * ((d->q_len + 15) / 16);
+  int64_t blocks = (units + 3) / 4;  // 4 waves, one 16-query unit each
+  if (blocks > 0x7fffffff) blocks = 0x7fffffff;
+  if (jas::launch_attn_fwd(d->dtype, a, blocks, (hipStream_t)stream) != hipSuccess)
+    return JAS_ERR_HIP;
+  return JAS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -335,6 +470,20 @@ jas_status_t jas_bwd_ex(const jas_desc_t *desc, const void *probs, const void *d
                         const jas_launch_t *launch, void *stream) {
   return bwd_impl(desc, probs, dprobs, key_len, p_sink, dscores, d_sink, workspace,
                   workspace_bytes, launch, stream);
+}
+
+size_t jas_attn_workspace_bytes(const jas_attn_desc_t *desc) {
+  AttnDims dm;
+  if (check_attn_desc(desc, &dm) != JAS_OK) return 0;
+  return (size_t)dm.ws_bytes;
+}
+
+jas_status_t jas_attn_fwd(const jas_attn_desc_t *desc, const void *q, const void *k,
+                          const void *v, const float *mask, const int32_t *key_len,
+                          const float *sink, void *out, float *lse, float *p_sink, void *probs,
+                          float *scores, void *workspace, size_t workspace_bytes, void *stream) {
+  return attn_fwd_impl(desc, q, k, v, mask, key_len, sink, out, lse, p_sink, probs, scores,
+                       workspace, workspace_bytes, stream);
 }
 
 const char *jas_status_str(jas_status_t s) {

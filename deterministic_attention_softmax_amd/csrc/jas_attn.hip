@@ -1,0 +1,351 @@
+// jas_attn.hip -- fixed-order fused attention forward on gfx950 MFMA: the QK
+// product, the row softmax of jas_fwd, and the PV product in one kernel.
+//
+// Method: RL-Kernel PR #453, Summary (the fixed-order softmax sits between
+// the QK GEMM and the AV GEMM; P is rounded once, to the tensor dtype) and
+// RL-Kernel PR #240, Fixed Reduction Contract (every score and every output
+// element has one writer; the head dimension and the keys are accumulated
+// in a fixed order, with no split of the key range).
+//
+// Mapping to CDNA4.  One wavefront owns 16 queries of one (batch, head).
+// Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32
+// (bf16 or fp16): A = 16 keys x 32 dims of K, B = 32 dims x 16 queries of
+// Q (kept in registers for the whole row), so lane l holds, for query
+// l%16, four consecutive keys of a 16-key block.  A 256-key tile is 8 pairs
+// of such blocks; the keys are assigned so that lane group g (= l/16) of
+// block pair j holds keys 32j + 8g .. 32j + 8g + 7 (the even block the
+// first four, the odd block the next four).  The softmax tile tree is then
+// exact: in-lane pairs and quads, the two blocks of a pair in-lane, lane
+// groups g and g^1 with permlane16_swap, groups {0,1} and {2,3} with
+// permlane32_swap, then the 8 block pairs in registers -- the balanced
+// pairwise tree over the tile's keys in order.  The same registers, rounded
+// to the tensor dtype, are the A operand of the PV product (16 queries x
+// 32 keys, lane group g holding 8 consecutive keys), so P never leaves the
+// registers; B is 32 keys x 16 dims of V, read from a transposed copy of V
+// (dims x keys, zero-padded to whole tiles) that the library writes into
+// the caller's workspace first.
+//
+// The softmax is done in two passes over the keys, so that P is exactly the
+// row softmax of the binary32 scores (the bits jas_fwd gives on them):
+// pass 1 computes every tile's (max, sum) into LDS; each lane then folds its
+// query's tile states in tile order (and the sink); pass 2 recomputes the
+// scores, forms P = e * c_t, rounds it, and accumulates P V into fp32
+// registers over the tiles in order.  The scores are recomputed rather than
+// stored: QK is computed twice, PV once.  Accumulation inside one MFMA
+// follows the hardware's fixed order; every launch computes every output
+// the same way, so results do not depend on batch, position or grid.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "jas_kernels.h"
+
+namespace jas {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kAttnWaves = 4;  // waves per workgroup, each on its own queries
+
+template <int DT>
+__device__ __forceinline__ f32x4_t mfma32(const u32x4 a, const u32x4 b, const f32x4_t c) {
+  if constexpr (DT == 1)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (DT == 1) return pack_bf16(lo, hi);
+  else return pack_f16(lo, hi);
+}
+
+__device__ __forceinline__ u32x4 bload4(const Buf &b, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(b.r, (int)voff, (int)soff, 0);
+}
+
+// Sum over the 64 lanes' groups of 16 (lane groups g = 0..3 in order) as the
+// two top levels of a balanced tree: (g0 + g1) + (g2 + g3).
+__device__ __forceinline__ float groups4_sum(float v) {
+  const f32x2_t p = rows16_pair(v);
+  v = p[0] + p[1];
+  const f32x2_t h = halves32_pair(v);
+  return h[0] + h[1];
+}
+
+__device__ __forceinline__ float groups4_max(float v) {
+  const f32x2_t p = rows16_pair(v);
+  v = fmax2(p[0], p[1]);
+  const f32x2_t h = halves32_pair(v);
+  return fmax2(h[0], h[1]);
+}
+
+template <int DT, int D>
+__global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const AttnArgs a) {
+  constexpr int ESZ = 2;
+  constexpr int DS = D / 32;  // k-steps of the QK product
+  constexpr int DB = D / 16;  // 16-dim column blocks of the output
+  __shared__ float lds_st[kAttnWaves][2][kMaxTiles * 16];  // per wave: tile max, tile sum
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  const int c16 = lane & 15;  // the lane's query (S^T column) and A/B operand row
+  const int g = lane >> 4;    // lane group: keys 8g .. 8g+7 of each 32-key step
+  const int N = (int)a.N, T = a.T, Np = a.Np;
+  const int Sq = (int)a.Sq;
+  const int64_t qblocks = (a.Sq + 15) / 16;
+  const int64_t units = a.B * a.H * qblocks;
+  float *sm = lds_st[w][0];
+  float *sl = lds_st[w][1];
+  const bool has_sink = a.sink != nullptr;
+  const bool write_all = a.probs != nullptr || a.scores != nullptr;
+
+  for (int64_t u = (int64_t)blockIdx.x * kAttnWaves + w; u < units;
+       u += (int64_t)gridDim.x * kAttnWaves) {
+    const int64_t qb = u % qblocks, bh = u / qblocks;
+    const int64_t h = bh % a.H, b = bh / a.H;
+    const int64_t hk = h / (a.H / a.Hkv);
+    const int q0 = (int)(qb * 16);
+    const int q = q0 + c16;  // this lane's query
+    const bool qvalid = q < Sq;
+    const int64_t row = bh * a.Sq + (qvalid ? q : Sq - 1);
+
+    const Buf qbuf(static_cast<const char *>(a.q) + bh * a.Sq * D * ESZ, (uint32_t)(a.Sq * D * ESZ));
+    const Buf kbuf(static_cast<const char *>(a.k) + (b * a.Hkv + hk) * a.N * D * ESZ,
+                   (uint32_t)(a.N * D * ESZ));
+    const Buf vbuf(static_cast<const char *>(a.vt) + (b * a.Hkv + hk) * (int64_t)D * Np * ESZ,
+                   (uint32_t)((int64_t)D * Np * ESZ));
+
+    // Q^T operand (B of the QK product): query q0 + c16, dims 32ds + 8g .. +7
+    u32x4 qv[DS];
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds)
+      qv[ds] = bload4(qbuf, (uint32_t)((c16 * D + 8 * g) * ESZ), (uint32_t)((q0 * D + ds * 32) * ESZ));
+
+    // visible keys of the lane's query, and of the wave's last query
+    int64_t ke = N, km = N;
+    if (a.ex.causal) {
+      const int64_t off = (int64_t)N - Sq + 1;
+      ke = (q + off < ke) ? q + off : ke;
+      const int qlast = (q0 + 15 < Sq) ? q0 + 15 : Sq - 1;
+      km = (qlast + off < km) ? qlast + off : km;
+    }
+    if (a.ex.key_len) {
+      const int64_t l = a.ex.key_len[b];
+      ke = l < ke ? l : ke;
+      km = l < km ? l : km;
+    }
+    const int kend = (int)(ke < 0 ? 0 : ke);
+    int kmax = __builtin_amdgcn_readfirstlane((int)(km < 0 ? 0 : km));
+    if (write_all) kmax = N;
+    const int tlive = (kmax + kTile - 1) / kTile;  // tiles that hold a visible key
+    const float *mrow = a.mask ? a.mask + b * a.msb + h * a.msh + (int64_t)(qvalid ? q : Sq - 1) * a.msq
+                               : nullptr;
+
+    // scores of tile t (keys t*256 + 32j + 8g + 4hb + r in acc[2j + hb][r]),
+    // scaled, masked, cut: x; the raw scaled scores stay in s when asked for
+    auto tile_scores = [&](int t, float (&x)[16][4]) {
+      f32x4_t acc[16];
+#pragma unroll
+      for (int kb = 0; kb < 16; ++kb) {
+        acc[kb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        // A row c16 of block kb = 2j + hb is key t*256 + 32j + 8(c16/4) + 4hb + c16%4
+        const int key = t * kTile + 32 * (kb >> 1) + 8 * (c16 >> 2) + 4 * (kb & 1) + (c16 & 3);
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) {
+          const u32x4 kv = bload4(kbuf, (uint32_t)((key * D + 8 * g) * ESZ), (uint32_t)(ds * 32 * ESZ));
+          acc[kb] = mfma32<DT>(kv, qv[ds], acc[kb]);
+        }
+      }
+#pragma unroll
+      for (int kb = 0; kb < 16; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = t * kTile + 32 * (kb >> 1) + 8 * g + 4 * (kb & 1) + r;
+          const float s = a.scale * acc[kb][r];
+          if (a.scores && qvalid && key < N) a.scores[row * a.N + key] = s;
+          float v = s;
+          if (mrow && key < kend) v = v + mrow[key];
+          x[kb][r] = (key < kend) ? v : kNegInf;
+        }
+      }
+    };
+
+    // ---- pass 1: tile states (max, sum) into LDS ----
+    for (int t = 0; t < T; ++t) {
+      float m = kNegInf, l = 0.0f;
+      if (t < tlive) {
+        float x[16][4];
+        tile_scores(t, x);
+        float mx = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < 16; ++kb)
+          mx = fmax2(mx, fmax2(fmax2(x[kb][0], x[kb][1]), fmax2(x[kb][2], x[kb][3])));
+        m = groups4_max(mx);
+        const float msafe = (m == kNegInf) ? 0.0f : m;
+        float pj[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {  // 8 keys of the lane group: (4 + 4), in key order
+          float e0[4], e1[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            e0[r] = exp_(x[2 * j][r] - msafe);
+            e1[r] = exp_(x[2 * j + 1][r] - msafe);
+          }
+          const float s0 = (e0[0] + e0[1]) + (e0[2] + e0[3]);
+          const float s1 = (e1[0] + e1[1]) + (e1[2] + e1[3]);
+          pj[j] = groups4_sum(s0 + s1);  // 32 keys
+        }
+        l = ((pj[0] + pj[1]) + (pj[2] + pj[3])) + ((pj[4] + pj[5]) + (pj[6] + pj[7]));
+      }
+      if (g == 0) {
+        sm[t * 16 + c16] = m;
+        sl[t * 16 + c16] = l;
+      }
+    }
+    wave_sync();
+
+    // ---- the fold of the lane's query, tile by tile in order, then the sink ----
+    float M = kNegInf, L = 0.0f;
+    for (int t = 0; t < T; ++t) {
+      const float mt = sm[t * 16 + c16], lt = sl[t * 16 + c16];
+      const float Mn = fmax2(M, mt);
+      if (Mn == kNegInf) {
+        M = kNegInf;
+        L = 0.0f;
+      } else {
+        const float fa = (M == kNegInf) ? 0.0f : exp_(M - Mn);
+        const float fb = (mt == kNegInf) ? 0.0f : exp_(mt - Mn);
+        const float La = L * fa;
+        const float lb = lt * fb;
+        L = La + lb;
+        M = Mn;
+      }
+    }
+    float sigma = 0.0f;
+    if (has_sink) {
+      sigma = a.sink[h];
+      const float Mn = fmax2(M, sigma);
+      if (Mn == kNegInf) {
+        M = kNegInf;
+        L = 0.0f;
+      } else {
+        const float fa = (M == kNegInf) ? 0.0f : exp_(M - Mn);
+        const float fb = (sigma == kNegInf) ? 0.0f : exp_(sigma - Mn);
+        const float La = L * fa;
+        const float lb = 1.0f * fb;
+        L = La + lb;
+        M = Mn;
+      }
+    }
+    const float invL = (L == 0.0f) ? 0.0f : 1.0f / L;
+    if (g == 0 && qvalid) {
+      if (has_sink) a.p_sink[row] = (sigma == kNegInf) ? 0.0f : exp_(sigma - M) * invL;
+      if (a.lse) a.lse[row] = (L == 0.0f) ? kNegInf : M + ln_(L);
+    }
+
+    // ---- pass 2: P = e * c_t rounded to the dtype, O += P V over the tiles ----
+    f32x4_t o[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int t = 0; t < tlive; ++t) {
+      float x[16][4];
+      tile_scores(t, x);
+      const float mt = sm[t * 16 + c16];
+      const float msafe = (mt == kNegInf) ? 0.0f : mt;
+      const float ct = (mt == kNegInf) ? 0.0f : exp_(mt - M) * invL;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float p[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[r] = exp_(x[2 * j][r] - msafe) * ct;
+          p[4 + r] = exp_(x[2 * j + 1][r] - msafe) * ct;
+        }
+        const u32x4 pa = {pack2<DT>(p[0], p[1]), pack2<DT>(p[2], p[3]), pack2<DT>(p[4], p[5]),
+                          pack2<DT>(p[6], p[7])};
+        if (a.probs && qvalid) {
+          uint16_t *prow = static_cast<uint16_t *>(a.probs) + row * a.N;
+          const int key0 = t * kTile + 32 * j + 8 * g;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (key0 + e < N) prow[key0 + e] = (uint16_t)(pa[e >> 1] >> (16 * (e & 1)));
+        }
+        // B operand: keys t*256 + 32j + 8g .. +7 of dims 16db + c16 (one 16-byte load of V^T)
+        const uint32_t soff = (uint32_t)((t * kTile + 32 * j) * ESZ);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const u32x4 vv = bload4(vbuf, (uint32_t)(((16 * db + c16) * Np + 8 * g) * ESZ), soff);
+          o[db] = mfma32<DT>(pa, vv, o[db]);
+        }
+      }
+    }
+
+    // ---- O rows q0 + 4g + r, dims 16db + c16: round once, write ----
+    uint16_t *orow = static_cast<uint16_t *>(a.out) + bh * a.Sq * D;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int qq = q0 + 4 * g + r;
+      if (qq < Sq) {
+#pragma unroll
+        for (int db = 0; db < DB; db += 2) {
+          const uint32_t w2 = pack2<DT>(o[db][r], o[db + 1][r]);
+          orow[(int64_t)qq * D + 16 * db + c16] = (uint16_t)(w2 & 0xffffu);
+          orow[(int64_t)qq * D + 16 * (db + 1) + c16] = (uint16_t)(w2 >> 16);
+        }
+      }
+    }
+    wave_sync();  // LDS is reused by the wave's next unit
+  }
+}
+
+// V [B, Hkv, N, D] -> V^T [B, Hkv, D, Np], keys N .. Np-1 zero.  One
+// workgroup per (head, 64-key block): 64 keys x D dims through LDS.
+template <int D>
+__global__ __launch_bounds__(256) void vt_kernel(const uint16_t *v, uint16_t *vt, int64_t heads,
+                                                 int64_t N, int64_t Np) {
+  __shared__ uint16_t tile[64][D + 2];
+  const int64_t kblocks = Np / 64;
+  const int64_t hb = blockIdx.x / kblocks;
+  const int64_t k0 = (blockIdx.x % kblocks) * 64;
+  if (hb >= heads) return;
+  const uint16_t *src = v + hb * N * D;
+  uint16_t *dst = vt + hb * (int64_t)D * Np;
+  for (int i = threadIdx.x; i < 64 * D; i += 256) {
+    const int kk = i / D, d = i % D;
+    tile[kk][d] = (k0 + kk < N) ? src[(k0 + kk) * D + d] : (uint16_t)0;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * D; i += 256) {
+    const int d = i / 64, kk = i % 64;
+    dst[(int64_t)d * Np + k0 + kk] = tile[kk][d];
+  }
+}
+
+template <int DT, int D>
+hipError_t attn_launch(const AttnArgs &a, int64_t blocks, hipStream_t st) {
+  const int64_t heads = a.B * a.Hkv;
+  const int64_t vblocks = heads * (a.Np / 64);
+  hipLaunchKernelGGL((vt_kernel<D>), dim3((unsigned)vblocks), dim3(256), 0, st,
+                     static_cast<const uint16_t *>(a.v), static_cast<uint16_t *>(a.vt), heads, a.N,
+                     (int64_t)a.Np);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_fwd_kernel<DT, D>), dim3((unsigned)blocks), dim3(kWave * kAttnWaves), 0,
+                     st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd(int dtype, const AttnArgs &a, int64_t blocks, hipStream_t st) {
+  if (dtype == 1) return a.D == 64 ? attn_launch<1, 64>(a, blocks, st) : attn_launch<1, 128>(a, blocks, st);
+  return a.D == 64 ? attn_launch<2, 64>(a, blocks, st) : attn_launch<2, 128>(a, blocks, st);
+}
+
+}  // namespace jas

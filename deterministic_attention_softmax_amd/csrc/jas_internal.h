@@ -55,6 +55,23 @@ struct BwdArgs {
   int vec_io;         // 16-byte path: rows are whole aligned 16-byte chunks
 };
 
+// Fused attention forward (QK, the row softmax, PV).
+struct AttnArgs {
+  const void *q, *k, *v;  // [B,H,Sq,D], [B,Hkv,N,D], [B,Hkv,N,D]
+  void *vt;               // workspace: V^T [B,Hkv,D,Np], keys past N zero
+  void *out;              // [B,H,Sq,D]
+  const float *mask;      // nullptr when no mask
+  int64_t msb, msh, msq;
+  Exclusion ex;
+  const float *sink;      // nullptr when no sink
+  float *p_sink, *lse;    // [rows] or nullptr
+  void *probs;            // optional [B,H,Sq,N], dtype
+  float *scores;          // optional [B,H,Sq,N], binary32
+  float scale;
+  int64_t B, H, Hkv, Sq, N;
+  int D, T, Np;           // head dim, tiles, keys padded to whole tiles
+};
+
 struct DsinkArgs {
   const float *v;
   float *d_sink;
@@ -92,5 +109,6 @@ hipError_t launch_bwd_f16(const BwdArgs &a, const Geometry &g, hipStream_t strea
 hipError_t launch_fwd(int dtype, const FwdArgs &a, const Geometry &g, hipStream_t stream);
 hipError_t launch_bwd(int dtype, const BwdArgs &a, const Geometry &g, hipStream_t stream);
 hipError_t launch_dsink(const DsinkArgs &a, hipStream_t stream);
+hipError_t launch_attn_fwd(int dtype, const AttnArgs &a, int64_t blocks, hipStream_t stream);
 
 }  // namespace jas

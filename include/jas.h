@@ -220,6 +220,66 @@ jas_status_t jas_bwd_ex(const jas_desc_t *desc, const void *probs, const void *d
                         float *d_sink, void *workspace, size_t workspace_bytes,
                         const jas_launch_t *launch, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Fused attention forward: scores = scale * Q K^T on the matrix cores, the
+ * row softmax above on those binary32 scores (bit for bit what jas_fwd
+ * computes from them), P rounded once to the tensor dtype, out = P V.
+ * (RL-Kernel PR #453, Summary: the softmax sits between the QK GEMM and the
+ * AV GEMM; RL-Kernel PR #240, Fixed Reduction Contract: one writer per
+ * score and per output element, a fixed accumulation order, no split of the
+ * key range; its Path Status: MHA, MQA and GQA head layouts, causal and
+ * padding masks.)
+ *
+ * Arithmetic: dot_j is the head-dimension sum of q_d*k_jd accumulated by
+ * v_mfma_f32_16x16x32 (bf16 / fp16 inputs, exact products, binary32
+ * accumulation in the instruction's fixed internal order, 32 dims per step
+ * in ascending steps); s_j = fl(scale * dot_j); the softmax of jas_fwd on
+ * s (mask, causal, key lengths, sink, lse exactly as there); P_j rounded to
+ * the dtype; out_d = the key sum of P_j*v_jd accumulated the same way, 32
+ * keys per step in ascending steps, rounded once to the dtype.  The scores
+ * differ from a sequential binary32 dot product only in summation order.
+ * ------------------------------------------------------------------------ */
+
+/* Longest key range of the fused attention (keys per row). */
+#define JAS_ATTN_MAX_KEYS 16384
+
+/* Extra flags of jas_attn_fwd: also write P (dtype) / the scores (binary32),
+ * [batch, heads, q_len, kv_len] each.  Meant for checking and for a backward
+ * that needs P; they cost a full write of the matrix. */
+enum { JAS_FLAG_PROBS = 1u << 5, JAS_FLAG_SCORES = 1u << 6 };
+
+typedef struct {
+  int64_t batch, heads, kv_heads;  /* heads a multiple of kv_heads; query head h reads
+                                      key/value head h / (heads / kv_heads) */
+  int64_t q_len, kv_len;           /* queries and keys per (batch, head); kv_len >= 1 */
+  int64_t head_dim;                /* 64 or 128 */
+  int32_t dtype;                   /* JAS_DTYPE_BF16 or JAS_DTYPE_F16 */
+  uint32_t flags;                  /* MASK, SINK, CAUSAL, KEY_LEN, LSE, PROBS, SCORES */
+  float scale;                     /* score scale, e.g. 1/sqrt(head_dim) */
+  int64_t mask_stride_b, mask_stride_h, mask_stride_q; /* as in jas_desc_t */
+} jas_attn_desc_t;
+
+/* Bytes of device workspace jas_attn_fwd needs: a transposed copy of V,
+ * batch*kv_heads*head_dim*ceil(kv_len/256)*256 elements, rounded up to 256
+ * bytes.  0 for a NULL or invalid desc. */
+size_t jas_attn_workspace_bytes(const jas_attn_desc_t *desc);
+
+/* Fused attention forward.
+ *   q [batch, heads, q_len, head_dim], k and v [batch, kv_heads, kv_len,
+ *   head_dim], contiguous, dtype; 16-byte aligned.
+ *   out [batch, heads, q_len, head_dim] written (dtype).
+ *   mask, key_len, sink: as for jas_fwd (mask element (b, h, q, key)).
+ *   lse, p_sink: binary32 [batch*heads*q_len], required iff JAS_FLAG_LSE /
+ *   JAS_FLAG_SINK.  probs / scores: required iff JAS_FLAG_PROBS /
+ *   JAS_FLAG_SCORES.
+ *   workspace: device scratch of jas_attn_workspace_bytes(desc) bytes,
+ *   16-byte aligned; its contents on entry do not matter.
+ * Outputs must not overlap each other, the inputs or the workspace. */
+jas_status_t jas_attn_fwd(const jas_attn_desc_t *desc, const void *q, const void *k,
+                          const void *v, const float *mask, const int32_t *key_len,
+                          const float *sink, void *out, float *lse, float *p_sink, void *probs,
+                          float *scores, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static text for a status code. */
 const char *jas_status_str(jas_status_t status);
 

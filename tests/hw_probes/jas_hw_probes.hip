@@ -13,6 +13,10 @@
 //    (subnormals kept, overflow to infinity).
 //  * log2 sweep: every binary32 in [1, 32768] (the range of a row's sum L)
 //    through v_log_f32 against log2 in double rounded to binary32.
+//  * MFMA operand layout: one 16x16x32 bf16 / fp16 product with the operands
+//    placed by the layout the attention kernel assumes (A: lane = row +
+//    16*(k/8), element k%8; B: lane = col + 16*(k/8), element k%8; D: lane =
+//    col + 16*(row/4), element row%4).
 //
 // Each thread handles kPer consecutive inputs; each workgroup writes its own
 // four result words, no atomics.
@@ -25,6 +29,9 @@ constexpr int kPer = 64;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ inline float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
@@ -174,6 +181,30 @@ __global__ void log2_sweep(uint32_t first, uint32_t count, uint32_t *out) {
   }
 }
 
+// A: 16x32 row-major, B: 32x16 row-major (16-bit patterns), D: 16x16 fp32.
+// One wave.
+__global__ void mfma_layout(const uint16_t *A, const uint16_t *B, float *D, int f16) {
+  const int l = threadIdx.x & 63;
+  const int rc = l % 16, kg = l / 16;
+  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (f16) {
+    f16x8_t a, b;
+    for (int i = 0; i < 8; ++i) {
+      a[i] = __builtin_bit_cast(_Float16, A[rc * 32 + kg * 8 + i]);
+      b[i] = __builtin_bit_cast(_Float16, B[(kg * 8 + i) * 16 + rc]);
+    }
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+  } else {
+    bf16x8_t a, b;
+    for (int i = 0; i < 8; ++i) {
+      a[i] = __builtin_bit_cast(__bf16, A[rc * 32 + kg * 8 + i]);
+      b[i] = __builtin_bit_cast(__bf16, B[(kg * 8 + i) * 16 + rc]);
+    }
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+  }
+  for (int r = 0; r < 4; ++r) D[(kg * 4 + r) * 16 + rc] = acc[r];
+}
+
 // Plain copy of n16 16-byte words: each thread moves 4 words per trip, all
 // four loads issued before the stores; grid-stride over the buffer.  A
 // bandwidth ceiling for kernels that read and write once, and a calibration
@@ -262,6 +293,12 @@ int probe_copy16(const void *src, void *dst, uint64_t n16, int nontemporal, int 
     hipLaunchKernelGGL(copy16<false>, dim3(g), dim3(256), 0, (hipStream_t)stream,
                        (const u32x4 *)src, (u32x4 *)dst, n16);
   return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// A: 512 16-bit words, B: 512, D: 256 floats (device).
+int probe_mfma_layout(const uint16_t *A, const uint16_t *B, float *D, int f16) {
+  hipLaunchKernelGGL(mfma_layout, dim3(1), dim3(64), 0, 0, A, B, D, f16);
+  return hipDeviceSynchronize() == hipSuccess ? 0 : -1;
 }
 
 int probe_permlane_layout(uint32_t *out) {  // out: 256 words

@@ -176,3 +176,42 @@ def test_binding_rejects_host_tensors():
         jas.fwd(s)
     with pytest.raises(ValueError, match="device memory"):
         jas.bwd(s, s)
+
+
+def adesc(B=1, H=4, Hkv=2, Sq=16, N=300, D=128, dtype=jas.JAS_DTYPE_BF16, flags=0):
+    return jas.make_attn_desc(B, H, Hkv, Sq, N, D, dtype, flags, 0.125)
+
+
+def attn(d, q=A, k=B_, v=C, out=D, mask=None, key_len=None, sink=None, lse=None, p_sink=None,
+         probs=None, scores=None, ws=E, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = jas.jas_attn_workspace_bytes(d)
+    return jas.jas_attn_fwd(d, q, k, v, mask, key_len, sink, out, lse, p_sink, probs, scores, ws,
+                            ws_bytes, None)
+
+
+def test_attention_validation():
+    # every call fails validation: a call that passed would launch on fake addresses
+    assert jas.jas_attn_workspace_bytes(adesc()) == 1 * 2 * 128 * 512 * 2
+    assert jas.jas_attn_workspace_bytes(adesc(D=96)) == 0
+    assert attn(adesc(dtype=jas.JAS_DTYPE_F32)) == 3
+    assert attn(adesc(D=96)) == 7
+    assert attn(adesc(N=jas.JAS_ATTN_MAX_KEYS + 1)) == 7
+    assert attn(adesc(H=3, Hkv=2)) == 2
+    assert attn(adesc(N=0)) == 2
+    assert attn(adesc(flags=1 << 7)) == 4
+    assert attn(adesc(), mask=W) == 4                     # pointer without its flag
+    assert attn(adesc(), probs=W) == 4
+    assert attn(adesc(flags=jas.JAS_FLAG_LSE)) == 1       # flag without its pointer
+    assert attn(adesc(flags=jas.JAS_FLAG_SCORES)) == 1
+    assert attn(adesc(), q=None) == 1
+    assert attn(adesc(), ws=None) == 6
+    assert attn(adesc(), ws_bytes=16) == 6
+    assert attn(adesc(), q=A + 8) == 9                    # 16-byte alignment of q, k, v, ws
+    assert attn(adesc(), ws=E + 8) == 9
+    assert attn(adesc(), out=A) == 5                      # out over q
+    assert attn(adesc(), ws=B_ + 64) == 5                 # workspace over k
+    assert attn(adesc(flags=jas.JAS_FLAG_LSE), lse=D + 4) == 5   # lse inside out
+    L = jas.lib()
+    assert L.jas_attn_fwd(None, A, B_, C, None, None, None, D, None, None, None, None, E, 0,
+                          None) == 1

@@ -1,0 +1,176 @@
+"""GPU: the fused attention forward (QK on MFMA, the row softmax, PV on MFMA)
+against the oracle's fixed-order attention.
+
+RL-Kernel PR #453, Summary: the softmax between the QK GEMM and the AV GEMM;
+RL-Kernel PR #240, Fixed Reduction Contract (one writer per score and per
+output element, fixed accumulation order) and Path Status (MHA / MQA / GQA,
+causal and padding masks).
+
+The matrix cores accumulate in their own fixed order, not the oracle's
+ascending one, so:
+  * scores are within the bound of two binary32 summation orders,
+    (D + 2) * 2^-24 * scale * sum_d |q_d k_d|;
+  * P (written on request) is, byte for byte, jas_fwd of the kernel's own
+    scores rounded to the dtype -- the softmax inside the fused kernel is the
+    library's; lse and p_sink likewise;
+  * the output is within eps * (sum_j P_j |v_j| + |out|) of the oracle's,
+    eps = 2^-8 (bf16) or 2^-11 (fp16): a score difference can move a P_j
+    across a rounding boundary of the dtype.
+Invariance: a query's bytes do not depend on the batch or on its block.
+"""
+import numpy as np
+import pytest
+import torch
+
+import deterministic_attention_softmax_amd as jas
+import oracle
+import synth
+from tests.gpu_util import assert_lse_close, dev, log
+
+pytestmark = pytest.mark.gpu
+U = 2.0 ** -24
+
+
+def f64(a):
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def draw(seed, B, H, Hkv, Sq, N, D, dt, std=1.0):
+    q = synth.normal((B, H, Sq, D), std, seed, "cpu", dt)
+    k = synth.normal((B, Hkv, N, D), std, seed + 1, "cpu", dt)
+    v = synth.normal((B, Hkv, N, D), 1.0, seed + 2, "cpu", dt)
+    return q, k, v
+
+
+def check(q, k, v, scale, mask=None, mask_strides=None, sink=None, causal=False, kl=None):
+    B, H, Sq, D = q.shape
+    Hkv, N = k.shape[1], k.shape[2]
+    dt = q.dtype
+    klt = None if kl is None else torch.tensor(kl, dtype=torch.int32, device=dev())
+    r = jas.attn_fwd(q.to(dev()), k.to(dev()), v.to(dev()), scale=scale,
+                     mask=None if mask is None else mask.to(dev()), mask_strides=mask_strides,
+                     sink=None if sink is None else sink.to(dev()), causal=causal, key_len=klt,
+                     want_lse=True, want_probs=True, want_scores=True)
+    torch.cuda.synchronize()
+    o = oracle.attn_fwd(synth.to_numpy_bits(q), synth.to_numpy_bits(k), synth.to_numpy_bits(v),
+                        np.float32(scale), mask=None if mask is None else mask.numpy(),
+                        mask_strides=mask_strides or (0, 0, 0), causal=causal,
+                        key_len=None if kl is None else np.array(kl, np.int32),
+                        sink=None if sink is None else sink.numpy(), want_probs=True,
+                        want_scores=True)
+    # scores: two summation orders of the same exact products
+    g = H // Hkv
+    qf, kf, vf = f64(synth.to_numpy_bits(q)), f64(synth.to_numpy_bits(k)), f64(synth.to_numpy_bits(v))
+    absS = np.zeros((B, H, Sq, N))
+    for b in range(B):
+        for h in range(H):
+            absS[b, h] = abs(scale) * (np.abs(qf[b, h]) @ np.abs(kf[b, h // g]).T)
+    S = r["scores"].cpu().numpy()
+    err = np.abs(S.astype(np.float64) - o["scores"].astype(np.float64))
+    assert np.all(err <= (D + 2) * U * absS + 1e-30), f"scores: worst {np.max(err / (absS + 1e-30))}"
+    # the softmax inside the kernel is jas_fwd's, on the kernel's own scores
+    Pf, psf, lsef = jas.fwd(r["scores"], mask=None if mask is None else mask.to(dev()),
+                            mask_strides=mask_strides, sink=None if sink is None else sink.to(dev()),
+                            causal=causal, key_len=klt, want_lse=True)
+    torch.cuda.synchronize()
+    want_P = synth.to_numpy_bits(Pf.to(dt))
+    assert synth.to_numpy_bits(r["probs"]).tobytes() == want_P.tobytes(), "P is not jas_fwd(S)"
+    assert r["lse"].cpu().numpy().tobytes() == lsef.cpu().numpy().tobytes()
+    if sink is not None:
+        assert r["p_sink"].cpu().numpy().tobytes() == psf.cpu().numpy().tobytes()
+    assert_lse_close(r["lse"].cpu().numpy(), o["lse"], "lse vs oracle")
+    # the output against the oracle's
+    eps = 2.0 ** -8 if dt == torch.bfloat16 else 2.0 ** -11
+    Po = f64(o["probs"])
+    mass = np.zeros((B, H, Sq, D))
+    for b in range(B):
+        for h in range(H):
+            mass[b, h] = Po[b, h] @ np.abs(vf[b, h // g])
+    got = f64(synth.to_numpy_bits(r["out"]))
+    want = f64(o["out"])
+    lim = eps * (mass + np.abs(want)) + 1e-30
+    bad = np.count_nonzero(~(np.abs(got - want) <= lim))
+    assert bad == 0, f"out: {bad} elements outside tolerance"
+    return r
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("shape", [(1, 2, 2, 16, 256), (2, 4, 4, 37, 600), (1, 4, 1, 5, 1000),
+                                   (1, 2, 2, 1, 1), (1, 6, 2, 33, 257)])
+def test_attention_against_oracle(shape, dt, D):
+    B, H, Hkv, Sq, N = shape
+    log(f"attention {dt} B={B} H={H} Hkv={Hkv} Sq={Sq} N={N} D={D}")
+    q, k, v = draw(Sq * 7 + N + D, B, H, Hkv, Sq, N, D, dt)
+    check(q, k, v, 1.0 / np.sqrt(D))
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
+def test_attention_mask_sink_causal_key_len(dt):
+    B, H, Hkv, Sq, N, D = 2, 4, 2, 40, 700, 128
+    q, k, v = draw(31, B, H, Hkv, Sq, N, D, dt, std=1.5)
+    mask = torch.zeros((B, 1, 1, N))
+    mask[0, ..., 650:] = float("-inf")
+    mask[1, ..., :3] = -1.5
+    sink = synth.normal((H,), 1.0, 32, "cpu")
+    log(f"attention {dt} with mask, sink, causal, key lengths")
+    check(q, k, v, 0.09, mask=mask, mask_strides=(N, 0, 0), sink=sink, causal=True, kl=[700, 420])
+    check(q, k, v, 0.09, sink=sink, kl=[0, 5])            # an empty batch entry: P = 0, p_sink = 1
+    check(q, k, v, 0.09, causal=True)                     # Sq < N: the last queries see all keys
+
+
+def test_attention_more_queries_than_keys_causal():
+    # queries before the first visible key are fully masked rows: out = 0
+    B, H, Sq, N, D = 1, 2, 50, 30, 64
+    q, k, v = draw(41, B, H, H, Sq, N, D, torch.bfloat16)
+    r = check(q, k, v, 0.125, causal=True)
+    assert torch.all(r["out"][:, :, :Sq - N] == 0)
+
+
+def test_attention_batch_and_block_invariance():
+    # a (batch, head)'s bytes do not move with the batch around it, nor with
+    # the other query blocks of the call
+    H, Hkv, Sq, N, D = 4, 2, 48, 900, 128
+    q1, k1, v1 = draw(51, 1, H, Hkv, Sq, N, D, torch.bfloat16)
+    r1 = jas.attn_fwd(q1.to(dev()), k1.to(dev()), v1.to(dev()), want_lse=True)
+    qo, ko, vo = draw(52, 3, H, Hkv, Sq, N, D, torch.bfloat16)
+    qo[1], ko[1], vo[1] = q1[0], k1[0], v1[0]
+    r3 = jas.attn_fwd(qo.to(dev()), ko.to(dev()), vo.to(dev()), want_lse=True)
+    r16 = jas.attn_fwd(q1[:, :, :16].contiguous().to(dev()), k1.to(dev()), v1.to(dev()))
+    torch.cuda.synchronize()
+    assert synth.to_numpy_bits(r3["out"][1]).tobytes() == synth.to_numpy_bits(r1["out"][0]).tobytes()
+    assert r3["lse"].view(3, H, Sq)[1].cpu().numpy().tobytes() == r1["lse"].cpu().numpy().tobytes()
+    assert synth.to_numpy_bits(r16["out"]).tobytes() == \
+        synth.to_numpy_bits(r1["out"][:, :, :16].contiguous()).tobytes()
+
+
+def test_joint_attention_1x24x4352x128_sampled():
+    # the joint image+text attention shape (24 heads, 4,096 image + 256 text
+    # keys, head dim 128) with the per-batch padding mask; 4 sampled queries
+    # per head against the oracle
+    B, H, S, D = 1, 24, 4352, 128
+    log("fused attention bf16 [1,24,4352,128], padding mask, sampled queries")
+    q = synth.normal((B, H, S, D), 1.0, 61, dev(), torch.bfloat16)
+    k = synth.normal((B, H, S, D), 1.0, 62, dev(), torch.bfloat16)
+    v = synth.normal((B, H, S, D), 1.0, 63, dev(), torch.bfloat16)
+    mask = torch.zeros((B, 1, 1, S), device=dev())
+    mask[..., S - 77:] = float("-inf")
+    r = jas.attn_fwd(q, k, v, mask=mask, mask_strides=(S, 0, 0), want_lse=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(64)
+    qi = np.sort(rng.choice(S, 4, replace=False))
+    qs = q[:, :, torch.as_tensor(qi, device=dev())].contiguous()
+    o = oracle.attn_fwd(synth.to_numpy_bits(qs), synth.to_numpy_bits(k), synth.to_numpy_bits(v),
+                        np.float32(1.0 / np.sqrt(D)), mask=mask.cpu().numpy(),
+                        mask_strides=(S, 0, 0), want_probs=True)
+    got = f64(synth.to_numpy_bits(r["out"][:, :, torch.as_tensor(qi, device=dev())]))
+    want = f64(o["out"])
+    Po = f64(o["probs"])
+    vf = f64(synth.to_numpy_bits(v))
+    mass = np.einsum("bhqk,bhkd->bhqd", Po, np.abs(vf))
+    assert np.all(np.abs(got - want) <= 2.0 ** -8 * (mass + np.abs(want)) + 1e-30)
+    lse = r["lse"].view(B, H, S)[:, :, torch.as_tensor(qi, device=dev())].cpu().numpy().reshape(-1)
+    assert_lse_close(lse, o["lse"], "joint lse")

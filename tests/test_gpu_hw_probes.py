@@ -12,6 +12,8 @@ rests on (test-only kernels in tests/hw_probes/):
 * v_log_f32 over every binary32 in [1, 32768] (the range of a row's sum of
   exponentials), the logarithm behind the row log-sum-exp: its largest error.
 * the lane layout of the permlane16/32 swaps used by the tile trees.
+* the operand and result layout of the 16x16x32 bf16 / fp16 MFMA the
+  attention kernel uses.
 """
 import ctypes
 import os
@@ -36,6 +38,8 @@ def probes():
     L.probe_f16_sweep.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint32]
     L.probe_log2_sweep.restype = ctypes.c_int
     L.probe_log2_sweep.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_uint32]
+    L.probe_mfma_layout.restype = ctypes.c_int
+    L.probe_mfma_layout.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
     L.probe_permlane_layout.restype = ctypes.c_int
     L.probe_permlane_layout.argtypes = [ctypes.c_void_p]
     return L
@@ -93,6 +97,23 @@ def test_v_log_f32_on_row_sum_range():
     mx, nd = int(r[:, 0].max()), int(r[:, 1].sum())
     log(f"v_log_f32 on [1, 32768]: max {mx} ulp, {nd} of {count} differ from log2 rounded")
     assert mx <= 2
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
+def test_mfma_16x16x32_layout(dt):
+    L = probes()
+    g = torch.Generator().manual_seed(21)
+    A = torch.randint(-4, 5, (16, 32), generator=g).to(dt)
+    B = torch.randint(-4, 5, (32, 16), generator=g).to(dt)
+    want = A.double() @ B.double()       # small integers: exact in fp32
+    Ad = A.contiguous().view(torch.int16).to("cuda")
+    Bd = B.contiguous().view(torch.int16).to("cuda")
+    D = torch.zeros(256, dtype=torch.float32, device="cuda")
+    assert L.probe_mfma_layout(Ad.data_ptr(), Bd.data_ptr(), D.data_ptr(),
+                               int(dt == torch.float16)) == 0
+    got = D.cpu().double().view(16, 16)
+    log(f"mfma 16x16x32 {dt}: max |diff| {float((got - want).abs().max())}")
+    assert torch.equal(got, want)
 
 
 def test_permlane_swap_layout():
