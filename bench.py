@@ -57,6 +57,16 @@ WORKLOADS = {
 }
 
 
+# fused attention forward (jas_attn_fwd): name: (description, B, H, Hkv, S, N, D, mask, causal, sink)
+ATTN_WORKLOADS = {
+    "attn4352": ("fused attention forward bf16 q/k/v [1,24,4352,128] (joint image+text shape), "
+                 "per-batch text padding mask", 1, 24, 24, 4352, 4352, 128, True, False, False),
+    "attn8192_causal": ("fused attention forward bf16 q/k/v [1,32,8192,128], causal flag, "
+                        "per-head sink", 1, 32, 32, 8192, 8192, 128, False, True, True),
+}
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
 def row_kends(wl, key_len):
     """Visible keys of every row (int64 [B*H*S]): the causal condition
     key <= N - S + q and the batch entry's key length, clamped to [0, N]."""
@@ -108,7 +118,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="joint4352", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="joint4352",
+                    choices=sorted(WORKLOADS) + sorted(ATTN_WORKLOADS))
     ap.add_argument("--no-check", action="store_true", help="skip the parity check before timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -389,6 +400,130 @@ def summarize_profiles(prof_dir, wl):
     print("\n".join(out + [""] + md))
 
 
+def attn_flops(B, H, S, N, D, causal):
+    """Useful FLOPs of attention forward: 2*S*N*D for QK and as many for PV
+    per (batch, head), over the visible (query, key) pairs."""
+    pairs = S * N
+    if causal:
+        q = np.arange(S)
+        pairs = int(np.clip(q + (N - S) + 1, 0, N).sum())
+    return 4.0 * B * H * pairs * D
+
+
+def bench_attention(args):
+    import torch
+    import deterministic_attention_softmax_amd as jas
+    import oracle
+    import synth
+    jas.lib()  # fail loudly when the HIP library is missing
+    dev = torch.device("cuda:0")
+    wl = args.workload
+    desc, B, H, Hkv, S, N, D, has_mask, causal, has_sink = ATTN_WORKLOADS[wl]
+    log(f"workload {wl}: {desc}")
+    q = synth.normal((B, H, S, D), 1.0, 81, dev, torch.bfloat16)
+    k = synth.normal((B, Hkv, N, D), 1.0, 82, dev, torch.bfloat16)
+    v = synth.normal((B, Hkv, N, D), 1.0, 83, dev, torch.bfloat16)
+    mask = sink = None
+    if has_mask:
+        _, mask, _, _ = synth.joint_attention_bf16(seed=3, device="cpu", B=B, H=1, S=1, N=N)
+        mask = mask.to(dev).view(B, 1, 1, N)
+    if has_sink:
+        sink = synth.normal((H,), 1.0, 84, dev)
+    scale = 1.0 / np.sqrt(D)
+    out = torch.empty_like(q)
+    d = jas.make_attn_desc(B, H, Hkv, S, N, D, jas.JAS_DTYPE_BF16, 0, scale)
+    ws = torch.empty(jas.jas_attn_workspace_bytes(d), dtype=torch.uint8, device=dev)
+
+    def step():
+        return jas.attn_fwd(q, k, v, scale=scale, mask=mask,
+                            mask_strides=None if mask is None else (N, 0, 0), sink=sink,
+                            causal=causal, want_lse=True, out=out, workspace=ws)
+
+    check = None
+    if not args.no_check:
+        r = step()
+        torch.cuda.synchronize()
+        qi = np.sort(np.random.default_rng(85).choice(S, 2, replace=False))
+        if causal:
+            qi = np.array([S - 2, S - 1])  # the sub-call keeps the causal offset of the last rows
+        it = torch.as_tensor(qi, device=dev)
+        qs = q[:, :, it].contiguous()
+        o = oracle.attn_fwd(synth.to_numpy_bits(qs), synth.to_numpy_bits(k), synth.to_numpy_bits(v),
+                            np.float32(scale), mask=None if mask is None else mask.cpu().numpy(),
+                            mask_strides=(N, 0, 0), causal=causal,
+                            sink=None if sink is None else sink.cpu().numpy())
+        got = (synth.to_numpy_bits(r["out"][:, :, it]).astype(np.uint32) << 16).view(np.float32)
+        want = (o["out"].astype(np.uint32) << 16).view(np.float32)
+        rel = np.abs(got.astype(np.float64) - want) / np.maximum(np.abs(want), 1e-3)
+        check = {"sampled_queries": int(len(qi) * B * H), "out_max_rel": float(rel.max())}
+        assert check["out_max_rel"] < 2.0 ** -6, f"attention parity: {check}"
+        log(f"parity check: {check}")
+    stream = torch.cuda.current_stream()
+    t_end = time.perf_counter() + 0.5
+    while time.perf_counter() < t_end:
+        step()
+        torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        step()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    step_ms = wall * 1e3 / args.steps
+    flops = attn_flops(B, H, S, N, D, causal)
+    tflops = flops / (step_ms * 1e-3) / 1e12
+    ktf = flops / (ms.mean() * 1e-3) / 1e12
+    log(f"attention {ms.mean():.3f} ms per call, {ktf:.0f} TFLOP/s")
+    res = {
+        "metric": "fused attention forward TFLOP/s (useful 4*B*H*pairs*D) vs MFMA bf16 dense peak",
+        "value": round(tflops, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": desc, "batch": B, "heads": H, "kv_heads": Hkv, "q_len": S,
+                   "kv_len": N, "head_dim": D, "mask": has_mask, "causal": causal,
+                   "sink": has_sink, "useful_flops": flops},
+        "roofline": {"bound": "mfma", "kernel": "jas_attn_fwd (V transpose + fused kernel)",
+                     "achieved": round(ktf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ktf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": flops, "avg_launch_ms": round(float(ms.mean()), 4)},
+        "parity": check,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        kq = 1
+        t = 0.0
+        k_np, v_np = synth.to_numpy_bits(k), synth.to_numpy_bits(v)
+        m_np = None if mask is None else mask.cpu().numpy()
+        s_np = None if sink is None else sink.cpu().numpy()
+        while True:
+            q_np = synth.to_numpy_bits(q[:, :, S - kq:].contiguous())
+            t0 = time.perf_counter()
+            oracle.attn_fwd(q_np, k_np, v_np, np.float32(scale), mask=m_np,
+                            mask_strides=(N, 0, 0), causal=causal, sink=s_np)
+            t = time.perf_counter() - t0
+            if t > args.cpu_seconds / 4 or kq >= S:
+                break
+            kq = min(S, kq * 4)
+        # the last kq queries keep their causal offset (key <= N - S + q)
+        qq = np.arange(S - kq, S)
+        pairs = int(np.clip(qq + (N - S) + 1, 0, N).sum()) if causal else kq * N
+        f = 4.0 * B * H * pairs * D
+        res["cpu_baseline"] = {"value": round(f / t / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": oracle.default_threads(), "kind": "oracle",
+                               "sample": f"the last {kq} queries of every head ({B * H * kq} rows "
+                                         f"x {N} keys), {t:.1f} s"}
+    print(json.dumps(res), flush=True)
+    if args.json_out:
+        os.makedirs(os.path.dirname(os.path.abspath(args.json_out)), exist_ok=True)
+        json.dump(res, open(args.json_out, "w"))
+
+
 def main():
     args = parse()
     if args.summarize_profiles:
@@ -398,6 +533,9 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.workload in ATTN_WORKLOADS:
+        bench_attention(args)
+        return
     import torch
     import deterministic_attention_softmax_amd as jas
     jas.lib()  # fail loudly when the HIP library is missing

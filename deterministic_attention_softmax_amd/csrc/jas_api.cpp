@@ -425,8 +425,8 @@ jas_status_t attn_fwd_impl(const jas_attn_desc_t *d, const void *q, const void *
   a.D = (int)D;
   a.T = dm.T;
   a.Np = (int)dm.Np;
-  const int64_t units = d->batch * d->heads * ((d->q_len + 15) / 16);
-  int64_t blocks = (units + 3) / 4;  // 4 waves, one 16-query unit each
+  // one workgroup (4 waves of 16 queries) per 64 queries of a (batch, head)
+  int64_t blocks = d->batch * d->heads * ((d->q_len + 63) / 64);
   if (blocks > 0x7fffffff) blocks = 0x7fffffff;
   if (jas::launch_attn_fwd(d->dtype, a, blocks, (hipStream_t)stream) != hipSuccess)
     return JAS_ERR_HIP;

@@ -7,33 +7,36 @@
 // element has one writer; the head dimension and the keys are accumulated
 // in a fixed order, with no split of the key range).
 //
-// Mapping to CDNA4.  One wavefront owns 16 queries of one (batch, head).
-// Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32
-// (bf16 or fp16): A = 16 keys x 32 dims of K, B = 32 dims x 16 queries of
-// Q (kept in registers for the whole row), so lane l holds, for query
-// l%16, four consecutive keys of a 16-key block.  A 256-key tile is 8 pairs
-// of such blocks; the keys are assigned so that lane group g (= l/16) of
-// block pair j holds keys 32j + 8g .. 32j + 8g + 7 (the even block the
-// first four, the odd block the next four).  The softmax tile tree is then
-// exact: in-lane pairs and quads, the two blocks of a pair in-lane, lane
-// groups g and g^1 with permlane16_swap, groups {0,1} and {2,3} with
-// permlane32_swap, then the 8 block pairs in registers -- the balanced
-// pairwise tree over the tile's keys in order.  The same registers, rounded
-// to the tensor dtype, are the A operand of the PV product (16 queries x
-// 32 keys, lane group g holding 8 consecutive keys), so P never leaves the
-// registers; B is 32 keys x 16 dims of V, read from a transposed copy of V
-// (dims x keys, zero-padded to whole tiles) that the library writes into
-// the caller's workspace first.
+// Mapping to CDNA4.  A workgroup of 4 waves owns 64 queries of one
+// (batch, head), each wave 16 of them.  Scores are computed transposed,
+// S^T = K Q^T, with v_mfma_f32_16x16x32 (bf16 or fp16): A = 16 keys x 32
+// dims of K, B = 32 dims x 16 queries of Q (kept in registers for the whole
+// row), so lane l holds, for query l%16, four consecutive keys of a 16-key
+// block.  Keys go through the workgroup 32 at a time: K (32 keys x D) and
+// the transposed V (D x 32 keys) are loaded with coalesced 16-byte loads
+// into double-buffered LDS while the previous 32 keys are computed on.  In
+// each 32-key step the A rows are assigned so that lane group g (= l/16)
+// holds keys 8g .. 8g + 7 (the first block the first four, the second block
+// the next four).  The softmax tile tree is then exact: in-lane pairs and
+// quads, the two blocks in-lane, lane groups g and g^1 with
+// permlane16_swap, groups {0,1} and {2,3} with permlane32_swap, then the 8
+// steps of the 256-key tile in registers -- the balanced pairwise tree over
+// the tile's keys in order.  The same registers, rounded to the tensor
+// dtype, are the A operand of the PV product (16 queries x 32 keys, lane
+// group g holding 8 consecutive keys), so P never leaves the registers; B
+// is 32 keys x 16 dims of V, read from the LDS copy of the transposed V,
+// which the library writes into the caller's workspace first (dims x keys,
+// zero-padded to whole tiles).
 //
 // The softmax is done in two passes over the keys, so that P is exactly the
 // row softmax of the binary32 scores (the bits jas_fwd gives on them):
-// pass 1 computes every tile's (max, sum) into LDS; each lane then folds its
-// query's tile states in tile order (and the sink); pass 2 recomputes the
-// scores, forms P = e * c_t, rounds it, and accumulates P V into fp32
-// registers over the tiles in order.  The scores are recomputed rather than
-// stored: QK is computed twice, PV once.  Accumulation inside one MFMA
-// follows the hardware's fixed order; every launch computes every output
-// the same way, so results do not depend on batch, position or grid.
+// pass 1 computes each tile's (max, sum), keeps the max in LDS, and merges
+// the pair into the query's running state in tile order (then the sink);
+// pass 2 recomputes the scores 32 keys at a time, forms P = e * c_t, rounds
+// it, and accumulates P V into fp32 registers in key order.  QK is computed
+// twice, PV once.  Accumulation inside one MFMA follows the hardware's
+// fixed order; every launch computes every output the same way, so results
+// do not depend on batch, position or grid.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -88,30 +91,37 @@ __device__ __forceinline__ float groups4_max(float v) {
 template <int DT, int D>
 __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const AttnArgs a) {
   constexpr int ESZ = 2;
-  constexpr int DS = D / 32;  // k-steps of the QK product
-  constexpr int DB = D / 16;  // 16-dim column blocks of the output
-  __shared__ float lds_st[kAttnWaves][2][kMaxTiles * 16];  // per wave: tile max, tile sum
+  constexpr int DS = D / 32;       // k-steps of the QK product
+  constexpr int DB = D / 16;       // 16-dim column blocks of the output
+  constexpr int SUB = 32;          // keys per staged sub-tile (one PV k-step)
+  constexpr int KROW = D + 8;      // LDS row of K (elements; padded against bank conflicts)
+  constexpr int VROW = SUB + 8;    // LDS row of V^T
+  constexpr int KCH = SUB * D / 8 / (kWave * kAttnWaves);  // 16-byte chunks per thread
+  constexpr int VCH = D * SUB / 8 / (kWave * kAttnWaves);
+  static_assert(KCH >= 1 && VCH >= 1, "sub-tile smaller than the workgroup");
+  __shared__ __align__(16) uint16_t lk[2][SUB * KROW];
+  __shared__ __align__(16) uint16_t lv[2][D * VROW];
+  __shared__ float lds_m[kAttnWaves][kMaxTiles * 16];  // per wave: tile maxima
 
-  const int lane = threadIdx.x & (kWave - 1);
-  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int c16 = lane & 15;  // the lane's query (S^T column) and A/B operand row
   const int g = lane >> 4;    // lane group: keys 8g .. 8g+7 of each 32-key step
   const int N = (int)a.N, T = a.T, Np = a.Np;
   const int Sq = (int)a.Sq;
-  const int64_t qblocks = (a.Sq + 15) / 16;
-  const int64_t units = a.B * a.H * qblocks;
-  float *sm = lds_st[w][0];
-  float *sl = lds_st[w][1];
+  const int64_t qgroups = (a.Sq + 63) / 64;  // 64 queries per workgroup
+  const int64_t units = a.B * a.H * qgroups;
+  float *sm = lds_m[w];
   const bool has_sink = a.sink != nullptr;
   const bool write_all = a.probs != nullptr || a.scores != nullptr;
 
-  for (int64_t u = (int64_t)blockIdx.x * kAttnWaves + w; u < units;
-       u += (int64_t)gridDim.x * kAttnWaves) {
-    const int64_t qb = u % qblocks, bh = u / qblocks;
+  for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+    const int64_t qg = u % qgroups, bh = u / qgroups;
     const int64_t h = bh % a.H, b = bh / a.H;
     const int64_t hk = h / (a.H / a.Hkv);
-    const int q0 = (int)(qb * 16);
-    const int q = q0 + c16;  // this lane's query
+    const int q0 = (int)(qg * 64) + 16 * w;  // this wave's 16 queries
+    const int q = q0 + c16;                  // this lane's query
     const bool qvalid = q < Sq;
     const int64_t row = bh * a.Sq + (qvalid ? q : Sq - 1);
 
@@ -127,12 +137,12 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
     for (int ds = 0; ds < DS; ++ds)
       qv[ds] = bload4(qbuf, (uint32_t)((c16 * D + 8 * g) * ESZ), (uint32_t)((q0 * D + ds * 32) * ESZ));
 
-    // visible keys of the lane's query, and of the wave's last query
+    // visible keys of the lane's query, and of the workgroup's last query
     int64_t ke = N, km = N;
     if (a.ex.causal) {
       const int64_t off = (int64_t)N - Sq + 1;
       ke = (q + off < ke) ? q + off : ke;
-      const int qlast = (q0 + 15 < Sq) ? q0 + 15 : Sq - 1;
+      const int64_t qlast = (qg * 64 + 63 < Sq) ? qg * 64 + 63 : Sq - 1;
       km = (qlast + off < km) ? qlast + off : km;
     }
     if (a.ex.key_len) {
@@ -143,90 +153,126 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
     const int kend = (int)(ke < 0 ? 0 : ke);
     int kmax = __builtin_amdgcn_readfirstlane((int)(km < 0 ? 0 : km));
     if (write_all) kmax = N;
-    const int tlive = (kmax + kTile - 1) / kTile;  // tiles that hold a visible key
+    const int tlive = (kmax + kTile - 1) / kTile;  // tiles holding a visible key (same in all waves)
     const float *mrow = a.mask ? a.mask + b * a.msb + h * a.msh + (int64_t)(qvalid ? q : Sq - 1) * a.msq
                                : nullptr;
 
-    // scores of tile t (keys t*256 + 32j + 8g + 4hb + r in acc[2j + hb][r]),
-    // scaled, masked, cut: x; the raw scaled scores stay in s when asked for
-    auto tile_scores = [&](int t, float (&x)[16][4]) {
-      f32x4_t acc[16];
+    // ---- staging: sub-tile `it` (keys 32*it .. +31) of K, and of V^T ----
+    u32x4 pk[KCH], pv[VCH];
+    auto fetch_k = [&](int it) {
 #pragma unroll
-      for (int kb = 0; kb < 16; ++kb) {
-        acc[kb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        // A row c16 of block kb = 2j + hb is key t*256 + 32j + 8(c16/4) + 4hb + c16%4
-        const int key = t * kTile + 32 * (kb >> 1) + 8 * (c16 >> 2) + 4 * (kb & 1) + (c16 & 3);
-#pragma unroll
-        for (int ds = 0; ds < DS; ++ds) {
-          const u32x4 kv = bload4(kbuf, (uint32_t)((key * D + 8 * g) * ESZ), (uint32_t)(ds * 32 * ESZ));
-          acc[kb] = mfma32<DT>(kv, qv[ds], acc[kb]);
-        }
+      for (int c = 0; c < KCH; ++c) {
+        const int ch = tid + c * kWave * kAttnWaves;
+        const int r = ch / (D / 8), c8 = ch % (D / 8);
+        pk[c] = bload4(kbuf, (uint32_t)(((SUB * it + r) * D + 8 * c8) * ESZ), 0u);
       }
+    };
+    auto put_k = [&](int buf) {
 #pragma unroll
-      for (int kb = 0; kb < 16; ++kb) {
+      for (int c = 0; c < KCH; ++c) {
+        const int ch = tid + c * kWave * kAttnWaves;
+        const int r = ch / (D / 8), c8 = ch % (D / 8);
+        *reinterpret_cast<u32x4 *>(&lk[buf][r * KROW + 8 * c8]) = pk[c];
+      }
+    };
+    auto fetch_v = [&](int it) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = t * kTile + 32 * (kb >> 1) + 8 * g + 4 * (kb & 1) + r;
-          const float s = a.scale * acc[kb][r];
-          if (a.scores && qvalid && key < N) a.scores[row * a.N + key] = s;
-          float v = s;
-          if (mrow && key < kend) v = v + mrow[key];
-          x[kb][r] = (key < kend) ? v : kNegInf;
-        }
+      for (int c = 0; c < VCH; ++c) {
+        const int ch = tid + c * kWave * kAttnWaves;
+        const int d = ch / (SUB / 8), k8 = ch % (SUB / 8);
+        pv[c] = bload4(vbuf, (uint32_t)((d * Np + SUB * it + 8 * k8) * ESZ), 0u);
+      }
+    };
+    auto put_v = [&](int buf) {
+#pragma unroll
+      for (int c = 0; c < VCH; ++c) {
+        const int ch = tid + c * kWave * kAttnWaves;
+        const int d = ch / (SUB / 8), k8 = ch % (SUB / 8);
+        *reinterpret_cast<u32x4 *>(&lv[buf][d * VROW + 8 * k8]) = pv[c];
+      }
+    };
+    // S^T of sub-tile it from LDS buffer buf: blocks hb = 0, 1 (keys
+    // 32it + 8(c16/4) + 4hb + c16%4 as A rows), raw dot products
+    auto qk_sub = [&](int buf, f32x4_t &s0, f32x4_t &s1) {
+      s0 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      s1 = s0;
+      const int r0 = 8 * (c16 >> 2) + (c16 & 3);
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) {
+        const u32x4 k0 = *reinterpret_cast<const u32x4 *>(&lk[buf][r0 * KROW + 32 * ds + 8 * g]);
+        const u32x4 k1 = *reinterpret_cast<const u32x4 *>(&lk[buf][(r0 + 4) * KROW + 32 * ds + 8 * g]);
+        s0 = mfma32<DT>(k0, qv[ds], s0);
+        s1 = mfma32<DT>(k1, qv[ds], s1);
+      }
+    };
+    // scaled, masked and cut scores of the lane's 8 keys 32it + 8g + 4hb + r
+    auto make_x = [&](int it, const f32x4_t &s0, const f32x4_t &s1, float (&x)[8]) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int key = SUB * it + 8 * g + e;
+        const float s = a.scale * ((e < 4) ? s0[e] : s1[e - 4]);
+        if (a.scores && qvalid && key < N) a.scores[row * a.N + key] = s;
+        float v = s;
+        if (mrow && key < kend) v = v + mrow[key];
+        x[e] = (key < kend) ? v : kNegInf;
       }
     };
 
-    // ---- pass 1: tile states (max, sum) into LDS ----
-    for (int t = 0; t < T; ++t) {
-      float m = kNegInf, l = 0.0f;
-      if (t < tlive) {
-        float x[16][4];
-        tile_scores(t, x);
-        float mx = kNegInf;
-#pragma unroll
-        for (int kb = 0; kb < 16; ++kb)
-          mx = fmax2(mx, fmax2(fmax2(x[kb][0], x[kb][1]), fmax2(x[kb][2], x[kb][3])));
-        m = groups4_max(mx);
-        const float msafe = (m == kNegInf) ? 0.0f : m;
-        float pj[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {  // 8 keys of the lane group: (4 + 4), in key order
-          float e0[4], e1[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            e0[r] = exp_(x[2 * j][r] - msafe);
-            e1[r] = exp_(x[2 * j + 1][r] - msafe);
-          }
-          const float s0 = (e0[0] + e0[1]) + (e0[2] + e0[3]);
-          const float s1 = (e1[0] + e1[1]) + (e1[2] + e1[3]);
-          pj[j] = groups4_sum(s0 + s1);  // 32 keys
-        }
-        l = ((pj[0] + pj[1]) + (pj[2] + pj[3])) + ((pj[4] + pj[5]) + (pj[6] + pj[7]));
-      }
-      if (g == 0) {
-        sm[t * 16 + c16] = m;
-        sl[t * 16 + c16] = l;
-      }
-    }
-    wave_sync();
-
-    // ---- the fold of the lane's query, tile by tile in order, then the sink ----
+    // ---- pass 1: per tile (max, sum), folded into the row state in tile order ----
     float M = kNegInf, L = 0.0f;
-    for (int t = 0; t < T; ++t) {
-      const float mt = sm[t * 16 + c16], lt = sl[t * 16 + c16];
-      const float Mn = fmax2(M, mt);
+    if (tlive > 0) {
+      fetch_k(0);
+      put_k(0);
+    }
+    __syncthreads();
+    for (int t = 0; t < tlive; ++t) {
+      float x[8][8];  // [32-key step j][key 8g + e]
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int it = 8 * t + j;
+        const bool more = it + 1 < 8 * tlive;
+        if (more) fetch_k(it + 1);
+        f32x4_t s0, s1;
+        qk_sub(j & 1, s0, s1);
+        make_x(it, s0, s1, x[j]);
+        if (more) put_k((j + 1) & 1);
+        __syncthreads();
+      }
+      float mx = kNegInf;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) mx = fmax2(mx, fmax2(x[j][e], x[j][e + 1]));
+      const float m = groups4_max(mx);
+      const float msafe = (m == kNegInf) ? 0.0f : m;
+      float pj[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float e8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) e8[e] = exp_(x[j][e] - msafe);
+        const float s0 = (e8[0] + e8[1]) + (e8[2] + e8[3]);
+        const float s1 = (e8[4] + e8[5]) + (e8[6] + e8[7]);
+        pj[j] = groups4_sum(s0 + s1);  // the step's 32 keys
+      }
+      const float l = ((pj[0] + pj[1]) + (pj[2] + pj[3])) + ((pj[4] + pj[5]) + (pj[6] + pj[7]));
+      if (g == 0) sm[t * 16 + c16] = m;
+      // merge (m, l) into the row state
+      const float Mn = fmax2(M, m);
       if (Mn == kNegInf) {
         M = kNegInf;
         L = 0.0f;
       } else {
         const float fa = (M == kNegInf) ? 0.0f : exp_(M - Mn);
-        const float fb = (mt == kNegInf) ? 0.0f : exp_(mt - Mn);
+        const float fb = (m == kNegInf) ? 0.0f : exp_(m - Mn);
         const float La = L * fa;
-        const float lb = lt * fb;
+        const float lb = l * fb;
         L = La + lb;
         M = Mn;
       }
     }
+    // tiles past every visible key of the workgroup hold only -inf: (-inf, 0)
+    // states, which leave (M, L) as they are
     float sigma = 0.0f;
     if (has_sink) {
       sigma = a.sink[h];
@@ -249,40 +295,55 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
       if (a.lse) a.lse[row] = (L == 0.0f) ? kNegInf : M + ln_(L);
     }
 
-    // ---- pass 2: P = e * c_t rounded to the dtype, O += P V over the tiles ----
+    // ---- pass 2: P = e * c_t rounded to the dtype, O += P V, sub-tile by sub-tile ----
     f32x4_t o[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    if (tlive > 0) {
+      fetch_k(0);
+      fetch_v(0);
+      put_k(0);
+      put_v(0);
+    }
+    __syncthreads();
     for (int t = 0; t < tlive; ++t) {
-      float x[16][4];
-      tile_scores(t, x);
       const float mt = sm[t * 16 + c16];
       const float msafe = (mt == kNegInf) ? 0.0f : mt;
       const float ct = (mt == kNegInf) ? 0.0f : exp_(mt - M) * invL;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        float p[8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          p[r] = exp_(x[2 * j][r] - msafe) * ct;
-          p[4 + r] = exp_(x[2 * j + 1][r] - msafe) * ct;
+        const int it = 8 * t + j;
+        const bool more = it + 1 < 8 * tlive;
+        if (more) {
+          fetch_k(it + 1);
+          fetch_v(it + 1);
         }
+        f32x4_t s0, s1;
+        qk_sub(j & 1, s0, s1);
+        float x[8], p[8];
+        make_x(it, s0, s1, x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] = exp_(x[e] - msafe) * ct;
         const u32x4 pa = {pack2<DT>(p[0], p[1]), pack2<DT>(p[2], p[3]), pack2<DT>(p[4], p[5]),
                           pack2<DT>(p[6], p[7])};
         if (a.probs && qvalid) {
           uint16_t *prow = static_cast<uint16_t *>(a.probs) + row * a.N;
-          const int key0 = t * kTile + 32 * j + 8 * g;
+          const int key0 = SUB * it + 8 * g;
 #pragma unroll
           for (int e = 0; e < 8; ++e)
             if (key0 + e < N) prow[key0 + e] = (uint16_t)(pa[e >> 1] >> (16 * (e & 1)));
         }
-        // B operand: keys t*256 + 32j + 8g .. +7 of dims 16db + c16 (one 16-byte load of V^T)
-        const uint32_t soff = (uint32_t)((t * kTile + 32 * j) * ESZ);
+        // B operand: keys 32it + 8g .. +7 of dims 16db + c16
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const u32x4 vv = bload4(vbuf, (uint32_t)(((16 * db + c16) * Np + 8 * g) * ESZ), soff);
+          const u32x4 vv = *reinterpret_cast<const u32x4 *>(&lv[j & 1][(16 * db + c16) * VROW + 8 * g]);
           o[db] = mfma32<DT>(pa, vv, o[db]);
         }
+        if (more) {
+          put_k((j + 1) & 1);
+          put_v((j + 1) & 1);
+        }
+        __syncthreads();
       }
     }
 
@@ -300,7 +361,7 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
         }
       }
     }
-    wave_sync();  // LDS is reused by the wave's next unit
+    __syncthreads();  // LDS is reused by the workgroup's next unit
   }
 }
 
