@@ -88,7 +88,13 @@ __device__ __forceinline__ float groups4_max(float v) {
   return fmax2(h[0], h[1]);
 }
 
-template <int DT, int D>
+__device__ __forceinline__ float bload1f(const Buf &b, uint32_t voff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(b.r, (int)voff, 0, 0));
+}
+
+// MASK: an additive mask is given; WRITE: the scores and / or P are written
+// out as well (for checking), which the fast path does not carry.
+template <int DT, int D, bool MASK, bool WRITE>
 __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const AttnArgs a) {
   constexpr int ESZ = 2;
   constexpr int DS = D / 32;       // k-steps of the QK product
@@ -114,7 +120,7 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
   const int64_t units = a.B * a.H * qgroups;
   float *sm = lds_m[w];
   const bool has_sink = a.sink != nullptr;
-  const bool write_all = a.probs != nullptr || a.scores != nullptr;
+  constexpr bool write_all = WRITE;
 
   for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
     const int64_t qg = u % qgroups, bh = u / qgroups;
@@ -154,8 +160,26 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
     int kmax = __builtin_amdgcn_readfirstlane((int)(km < 0 ? 0 : km));
     if (write_all) kmax = N;
     const int tlive = (kmax + kTile - 1) / kTile;  // tiles holding a visible key (same in all waves)
-    const float *mrow = a.mask ? a.mask + b * a.msb + h * a.msh + (int64_t)(qvalid ? q : Sq - 1) * a.msq
-                               : nullptr;
+    // keys below the workgroup's smallest cut need no select
+    int64_t kn = N;
+    if (a.ex.causal) {
+      const int64_t off = (int64_t)N - Sq + 1;
+      kn = (qg * 64 + off < kn) ? qg * 64 + off : kn;
+    }
+    if (a.ex.key_len) {
+      const int64_t l = a.ex.key_len[b];
+      kn = l < kn ? l : kn;
+    }
+    const int kmin = __builtin_amdgcn_readfirstlane((int)(kn < 0 ? 0 : kn));
+    // the mask of (b, h) as one buffer: the lane's row at q * msq, keys at
+    // +key; the buffer ends with the last row's key N - 1, so keys past N of
+    // the last row read 0 (they are cut anyway)
+    Buf mbuf(nullptr, 0u);
+    uint32_t moff = 0;
+    if constexpr (MASK) {
+      mbuf = Buf(a.mask + b * a.msb + h * a.msh, (uint32_t)((((int64_t)Sq - 1) * a.msq + N) * 4));
+      moff = (uint32_t)((int64_t)(qvalid ? q : Sq - 1) * a.msq * 4);
+    }
 
     // ---- staging: sub-tile `it` (keys 32*it .. +31) of K, and of V^T ----
     u32x4 pk[KCH], pv[VCH];
@@ -205,16 +229,30 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
         s1 = mfma32<DT>(k1, qv[ds], s1);
       }
     };
+    // the mask of the lane's 8 keys 32it + 8g .. +7 (loaded ahead of use)
+    auto load_mask = [&](int it, float (&mk)[8]) {
+      if constexpr (MASK) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mk[e] = bload1f(mbuf, moff + (uint32_t)((SUB * it + 8 * g + e) * 4));
+      }
+    };
     // scaled, masked and cut scores of the lane's 8 keys 32it + 8g + 4hb + r
-    auto make_x = [&](int it, const f32x4_t &s0, const f32x4_t &s1, float (&x)[8]) {
+    auto make_x = [&](int it, const f32x4_t &s0, const f32x4_t &s1, const float (&mk)[8],
+                      float (&x)[8]) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int key = SUB * it + 8 * g + e;
         const float s = a.scale * ((e < 4) ? s0[e] : s1[e - 4]);
-        if (a.scores && qvalid && key < N) a.scores[row * a.N + key] = s;
-        float v = s;
-        if (mrow && key < kend) v = v + mrow[key];
-        x[e] = (key < kend) ? v : kNegInf;
+        if constexpr (WRITE) {
+          const int key = SUB * it + 8 * g + e;
+          if (a.scores && qvalid && key < N) a.scores[row * a.N + key] = s;
+        }
+        x[e] = s;
+        if constexpr (MASK) x[e] = x[e] + mk[e];
+      }
+      if (SUB * it + SUB > kmin) {  // the step reaches some query's cut (uniform)
+        const int nv = kend - (SUB * it + 8 * g);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = (e < nv) ? x[e] : kNegInf;
       }
     };
 
@@ -232,9 +270,11 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
         const int it = 8 * t + j;
         const bool more = it + 1 < 8 * tlive;
         if (more) fetch_k(it + 1);
+        float mk[8];
+        load_mask(it, mk);
         f32x4_t s0, s1;
         qk_sub(j & 1, s0, s1);
-        make_x(it, s0, s1, x[j]);
+        make_x(it, s0, s1, mk, x[j]);
         if (more) put_k((j + 1) & 1);
         __syncthreads();
       }
@@ -318,20 +358,24 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
           fetch_k(it + 1);
           fetch_v(it + 1);
         }
+        float mk[8];
+        load_mask(it, mk);
         f32x4_t s0, s1;
         qk_sub(j & 1, s0, s1);
         float x[8], p[8];
-        make_x(it, s0, s1, x);
+        make_x(it, s0, s1, mk, x);
 #pragma unroll
         for (int e = 0; e < 8; ++e) p[e] = exp_(x[e] - msafe) * ct;
         const u32x4 pa = {pack2<DT>(p[0], p[1]), pack2<DT>(p[2], p[3]), pack2<DT>(p[4], p[5]),
                           pack2<DT>(p[6], p[7])};
-        if (a.probs && qvalid) {
-          uint16_t *prow = static_cast<uint16_t *>(a.probs) + row * a.N;
-          const int key0 = SUB * it + 8 * g;
+        if constexpr (WRITE) {
+          if (a.probs && qvalid) {
+            uint16_t *prow = static_cast<uint16_t *>(a.probs) + row * a.N;
+            const int key0 = SUB * it + 8 * g;
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (key0 + e < N) prow[key0 + e] = (uint16_t)(pa[e >> 1] >> (16 * (e & 1)));
+            for (int e = 0; e < 8; ++e)
+              if (key0 + e < N) prow[key0 + e] = (uint16_t)(pa[e >> 1] >> (16 * (e & 1)));
+          }
         }
         // B operand: keys 32it + 8g .. +7 of dims 16db + c16
 #pragma unroll
@@ -397,8 +441,15 @@ hipError_t attn_launch(const AttnArgs &a, int64_t blocks, hipStream_t st) {
                      (int64_t)a.Np);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_fwd_kernel<DT, D>), dim3((unsigned)blocks), dim3(kWave * kAttnWaves), 0,
-                     st, a);
+  const dim3 grid((unsigned)blocks), block(kWave * kAttnWaves);
+  const bool mask = a.mask != nullptr, write = a.probs != nullptr || a.scores != nullptr;
+  if (mask) {
+    if (write) hipLaunchKernelGGL((attn_fwd_kernel<DT, D, true, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<DT, D, true, false>), grid, block, 0, st, a);
+  } else {
+    if (write) hipLaunchKernelGGL((attn_fwd_kernel<DT, D, false, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<DT, D, false, false>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 
