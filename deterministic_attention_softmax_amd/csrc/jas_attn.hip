@@ -191,12 +191,15 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
         pk[c] = bload4(kbuf, (uint32_t)(((SUB * it + r) * D + 8 * c8) * ESZ), 0u);
       }
     };
+    // key k = 8g + 4hb + r of the sub-tile is kept at LDS row 16hb + 4g + r,
+    // so the A rows of one block are 16 consecutive LDS rows
     auto put_k = [&](int buf) {
 #pragma unroll
       for (int c = 0; c < KCH; ++c) {
         const int ch = tid + c * kWave * kAttnWaves;
         const int r = ch / (D / 8), c8 = ch % (D / 8);
-        *reinterpret_cast<u32x4 *>(&lk[buf][r * KROW + 8 * c8]) = pk[c];
+        const int pr = 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
+        *reinterpret_cast<u32x4 *>(&lk[buf][pr * KROW + 8 * c8]) = pk[c];
       }
     };
     auto fetch_v = [&](int it) {
@@ -216,15 +219,15 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
       }
     };
     // S^T of sub-tile it from LDS buffer buf: blocks hb = 0, 1 (keys
-    // 32it + 8(c16/4) + 4hb + c16%4 as A rows), raw dot products
+    // 32it + 8(c16/4) + 4hb + c16%4 as A rows, LDS rows 16hb + c16), raw dot
+    // products
     auto qk_sub = [&](int buf, f32x4_t &s0, f32x4_t &s1) {
       s0 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
       s1 = s0;
-      const int r0 = 8 * (c16 >> 2) + (c16 & 3);
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds) {
-        const u32x4 k0 = *reinterpret_cast<const u32x4 *>(&lk[buf][r0 * KROW + 32 * ds + 8 * g]);
-        const u32x4 k1 = *reinterpret_cast<const u32x4 *>(&lk[buf][(r0 + 4) * KROW + 32 * ds + 8 * g]);
+        const u32x4 k0 = *reinterpret_cast<const u32x4 *>(&lk[buf][c16 * KROW + 32 * ds + 8 * g]);
+        const u32x4 k1 = *reinterpret_cast<const u32x4 *>(&lk[buf][(16 + c16) * KROW + 32 * ds + 8 * g]);
         s0 = mfma32<DT>(k0, qv[ds], s0);
         s1 = mfma32<DT>(k1, qv[ds], s1);
       }
