@@ -524,10 +524,82 @@ def bench_attention(args):
         json.dump(res, open(args.json_out, "w"))
 
 
+ATTN_PMC_SETS = [
+    "SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_VALU_MFMA_BUSY_CYCLES "
+    "SQ_WAIT_INST_LDS SQ_LDS_BANK_CONFLICT SQ_WAIT_ANY",
+    "SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_VMEM SQ_INST_LEVEL_VMEM "
+    "SQ_LDS_ADDR_CONFLICT SQ_CYCLES",
+]
+
+
+def summarize_attn_profiles(prof_dir, wl):
+    """Write profiles/kernel_trace_jas_<wl>.md from rocprofv3 output under
+    prof_dir: the kernel trace (trace/) and, when present, the two SQ counter
+    passes (pmc1/, pmc2/) of the fused attention kernel."""
+    import csv
+    desc, B, H, Hkv, S, N, D, has_mask, causal, has_sink = ATTN_WORKLOADS[wl]
+    os.makedirs(PROFILES, exist_ok=True)
+    rows = list(csv.DictReader(open(os.path.join(prof_dir, "trace", f"{wl}_kernel_stats.csv"))))
+    line_path = os.path.join(prof_dir, "trace", "bench_line.json")
+    line = json.load(open(line_path)) if os.path.exists(line_path) else None
+    out = [f"# rocprofv3 kernel trace: jas fused attention, workload {wl}", "",
+           f"Workload: {desc}.", "", "Commands (repository root, MI355X, ROCm 7.2):", "", "```",
+           f"rocprofv3 --kernel-trace --stats --output-format csv -d {prof_dir}/trace -o {wl} -- "
+           f"python3 bench.py --workload {wl} --steps 10 --warmup 3 --no-cpu-baseline "
+           f"--json-out {prof_dir}/trace/bench_line.json"]
+    for i, cs in enumerate(ATTN_PMC_SETS, 1):
+        out.append(f"rocprofv3 --pmc {cs} --output-format csv -d {prof_dir}/pmc{i} -o {wl} -- "
+                   f"python3 bench.py --workload {wl} --steps 2 --warmup 1 --no-check --no-cpu-baseline")
+    out += [f"python3 bench.py --workload {wl} --summarize-profiles {prof_dir}", "```", "",
+            "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    flops = attn_flops(B, H, S, N, D, causal)
+    avg_attn = None
+    for r in rows:
+        n = r["Name"]
+        if "attn_fwd_kernel" not in n and "vt_kernel" not in n:
+            continue
+        name = re.sub(r"\([^()]*\)$", "", n).replace("void ", "")
+        a = float(r["AverageNs"]) / 1e3
+        if "attn_fwd_kernel" in n:
+            avg_attn = a
+        out.append(f"| `{name}` | {r['Calls']} | {a:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                   f"{float(r['MaxNs']) / 1e3:.1f} |")
+    if avg_attn:
+        out += ["", f"Fused kernel alone: {flops / (avg_attn * 1e-6) / 1e12:.0f} TFLOP/s of useful "
+                f"attention FLOPs ({flops:.4g} per call; the kernel also recomputes QK once)."]
+    if line:
+        out += ["", "The same run's bench.py line (HIP events around the whole call, transpose "
+                f"included): {line['roofline']['avg_launch_ms'] * 1e3:.1f} us, {line['value']} TFLOP/s."]
+    counters = {}
+    for i in (1, 2):
+        path = os.path.join(prof_dir, f"pmc{i}", f"{wl}_counter_collection.csv")
+        if not os.path.exists(path):
+            continue
+        for r in csv.DictReader(open(path)):
+            if "attn_fwd_kernel" in r["Kernel_Name"]:
+                counters.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if counters:
+        m = {c: float(np.mean(v)) for c, v in counters.items()}
+        out += ["", "SQ counters of the fused kernel (mean per dispatch, chip totals):", "",
+                "| counter | value |", "|---|---|"]
+        out += [f"| {c} | {m[c]:.4g} |" for c in sorted(m)]
+        if "SQ_INSTS_VALU" in m and "SQ_INSTS_MFMA" in m:
+            out += ["", f"VALU instructions per MFMA: {m['SQ_INSTS_VALU'] / m['SQ_INSTS_MFMA']:.2f}."]
+        if "SQ_ACTIVE_INST_VALU" in m and "SQ_WAVE_CYCLES" in m:
+            out.append(f"VALU-active share of wave cycles: "
+                       f"{m['SQ_ACTIVE_INST_VALU'] / m['SQ_WAVE_CYCLES']:.3f}; waiting share: "
+                       f"{m['SQ_WAIT_ANY'] / m['SQ_WAVE_CYCLES']:.3f}.")
+    open(os.path.join(PROFILES, f"kernel_trace_jas_{wl}.md"), "w").write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
 def main():
     args = parse()
     if args.summarize_profiles:
-        summarize_profiles(args.summarize_profiles, args.workload)
+        if args.workload in ATTN_WORKLOADS:
+            summarize_attn_profiles(args.summarize_profiles, args.workload)
+        else:
+            summarize_profiles(args.summarize_profiles, args.workload)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
