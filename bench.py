@@ -84,12 +84,13 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 
 def kernel_source_hash():
-    """sha256 over the kernel sources (every .h / .hip file of csrc/, in name
-    order): a traffic record is only used while it still matches."""
+    """sha256 over the sources of the row-softmax kernels (every .h / .hip
+    file of csrc/ except the fused attention's, in name order): a traffic
+    record is only used while it still matches."""
     import hashlib
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".h", ".hip")):
+        if name.endswith((".h", ".hip")) and name != "jas_attn.hip":
             h.update(name.encode())
             with open(os.path.join(CSRC, name), "rb") as f:
                 h.update(f.read())
