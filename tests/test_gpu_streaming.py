@@ -150,3 +150,44 @@ def test_long_rows_full_size_sampled():
     P_rows[np.arange(N)[None, :] >= kend[:, None]] = 0
     dS_o, _ = oracle_rows_bwd(P_rows, gather_rows(gin, idx), N)
     assert_bitexact(gather_rows(dS, idx), dS_o, "long dS")
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_streaming_in_place_and_padded_rows(dt):
+    # in place: pass 2 reads every segment again before it writes it (the
+    # last segment first), so probs == scores and dscores == probs are safe;
+    # padded rows (ld > N) keep the padding untouched; both give the bytes
+    # of the plain call
+    B, H, S, N = 1, 2, 3, 40000
+    log(f"streaming in place and padded rows: {dt} N={N}")
+    s = synth.normal((B, H, S, N), 2.0, 700, "cpu", dt).to(dev())
+    g = synth.normal((B, H, S, N), 1.0, 701, "cpu", dt).to(dev())
+    sink = synth.normal((H,), 1.0, 702, "cpu").to(dev())
+    P0, ps0 = jas.fwd(s, sink=sink, causal=True)
+    dS0, d0 = jas.bwd(P0, g, p_sink=ps0, causal=True)
+    x = s.clone()
+    jas.fwd(x, sink=sink, causal=True, out=x, p_sink=torch.empty_like(ps0))
+    y = P0.clone()
+    jas.bwd(y, g, p_sink=ps0, causal=True, out=y)
+    torch.cuda.synchronize()
+    assert synth.to_numpy_bits(x).tobytes() == synth.to_numpy_bits(P0).tobytes()
+    assert synth.to_numpy_bits(y).tobytes() == synth.to_numpy_bits(dS0).tobytes()
+    for pad in (8, 3):   # 16-byte rows stay on the vector path; 3 takes the element path
+        ld = N + pad
+        big = torch.full((B * H * S * ld,), 5.0, dtype=dt, device=dev())
+        sv = big.view(B, H, S, ld)[..., :N]
+        sv.copy_(s)
+        pbig = torch.full_like(big, 7.0)
+        pv = pbig.view(B, H, S, ld)[..., :N]
+        jas.fwd(sv, sink=sink, causal=True, out=pv, p_sink=torch.empty_like(ps0))
+        gbig = torch.full_like(big, 3.0)
+        gv = gbig.view(B, H, S, ld)[..., :N]
+        gv.copy_(g)
+        dbig = torch.full_like(big, 9.0)
+        dv = dbig.view(B, H, S, ld)[..., :N]
+        jas.bwd(pv, gv, p_sink=ps0, causal=True, out=dv)
+        torch.cuda.synchronize()
+        assert synth.to_numpy_bits(pv.contiguous()).tobytes() == synth.to_numpy_bits(P0).tobytes()
+        assert synth.to_numpy_bits(dv.contiguous()).tobytes() == synth.to_numpy_bits(dS0).tobytes()
+        assert torch.all(pbig.view(B, H, S, ld)[..., N:] == 7.0)
+        assert torch.all(dbig.view(B, H, S, ld)[..., N:] == 9.0)
