@@ -88,8 +88,14 @@ __device__ __forceinline__ float groups4_max(float v) {
   return fmax2(h[0], h[1]);
 }
 
-__device__ __forceinline__ float bload1f(const Buf &b, uint32_t voff) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(b.r, (int)voff, 0, 0));
+// The hardware hands workgroups to the 8 XCDs round-robin (workgroup i to
+// XCD i % 8), and each XCD has its own L2.  Renumber so that the workgroups
+// on one XCD take consecutive units, i.e. neighbouring query blocks of one
+// (batch, head), whose K and V then stay in that XCD's L2.  A bijection on
+// [0, G) for any G; which workgroup computes a unit never changes its bytes.
+__device__ __forceinline__ int64_t xcd_unit(int64_t bid, int64_t G) {
+  const int64_t x = bid % 8, per = G / 8, rem = G % 8;
+  return (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + bid / 8;
 }
 
 // MASK: an additive mask is given; WRITE: the scores and / or P are written
@@ -100,14 +106,18 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
   constexpr int DS = D / 32;       // k-steps of the QK product
   constexpr int DB = D / 16;       // 16-dim column blocks of the output
   constexpr int SUB = 32;          // keys per staged sub-tile (one PV k-step)
-  constexpr int KROW = D + 8;      // LDS row of K (elements; padded against bank conflicts)
-  constexpr int VROW = SUB + 8;    // LDS row of V^T
+  // LDS rows: a 16-byte read by each lane of 16 rows (lane groups 16 bytes
+  // apart) is free of bank conflicts on gfx950 when the row stride is 32
+  // modulo 64 bytes (measured; strides 16 modulo 32 bytes cost 4 extra
+  // cycles per read): K rows of D + 16 elements, V^T rows of 48
+  constexpr int KROW = D + 16;     // LDS row of K (elements)
+  constexpr int VROW = SUB + 16;   // LDS row of V^T
   constexpr int KCH = SUB * D / 8 / (kWave * kAttnWaves);  // 16-byte chunks per thread
   constexpr int VCH = D * SUB / 8 / (kWave * kAttnWaves);
   static_assert(KCH >= 1 && VCH >= 1, "sub-tile smaller than the workgroup");
   __shared__ __align__(16) uint16_t lk[2][SUB * KROW];
   __shared__ __align__(16) uint16_t lv[2][D * VROW];
-  __shared__ float lds_m[kAttnWaves][kMaxTiles * 16];  // per wave: tile maxima
+  extern __shared__ float lds_m[];  // per wave T x 16 tile maxima (sized at launch)
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -118,11 +128,11 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
   const int Sq = (int)a.Sq;
   const int64_t qgroups = (a.Sq + 63) / 64;  // 64 queries per workgroup
   const int64_t units = a.B * a.H * qgroups;
-  float *sm = lds_m[w];
+  float *sm = lds_m + w * a.T * 16;
   const bool has_sink = a.sink != nullptr;
   constexpr bool write_all = WRITE;
 
-  for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+  for (int64_t u = xcd_unit(blockIdx.x, gridDim.x); u < units; u += gridDim.x) {
     const int64_t qg = u % qgroups, bh = u / qgroups;
     const int64_t h = bh % a.H, b = bh / a.H;
     const int64_t hk = h / (a.H / a.Hkv);
@@ -178,7 +188,7 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
     uint32_t moff = 0;
     if constexpr (MASK) {
       mbuf = Buf(a.mask + b * a.msb + h * a.msh, (uint32_t)((((int64_t)Sq - 1) * a.msq + N) * 4));
-      moff = (uint32_t)((int64_t)(qvalid ? q : Sq - 1) * a.msq * 4);
+      moff = (uint32_t)((int64_t)(qvalid ? q : Sq - 1) * a.msq * 4) + 32u * (uint32_t)g;
     }
 
     // ---- staging: sub-tile `it` (keys 32*it .. +31) of K, and of V^T ----
@@ -188,7 +198,7 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
       for (int c = 0; c < KCH; ++c) {
         const int ch = tid + c * kWave * kAttnWaves;
         const int r = ch / (D / 8), c8 = ch % (D / 8);
-        pk[c] = bload4(kbuf, (uint32_t)(((SUB * it + r) * D + 8 * c8) * ESZ), 0u);
+        pk[c] = bload4(kbuf, (uint32_t)((r * D + 8 * c8) * ESZ), (uint32_t)(SUB * it * D * ESZ));
       }
     };
     // key k = 8g + 4hb + r of the sub-tile is kept at LDS row 16hb + 4g + r,
@@ -207,7 +217,7 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
       for (int c = 0; c < VCH; ++c) {
         const int ch = tid + c * kWave * kAttnWaves;
         const int d = ch / (SUB / 8), k8 = ch % (SUB / 8);
-        pv[c] = bload4(vbuf, (uint32_t)((d * Np + SUB * it + 8 * k8) * ESZ), 0u);
+        pv[c] = bload4(vbuf, (uint32_t)((d * Np + 8 * k8) * ESZ), (uint32_t)(SUB * it * ESZ));
       }
     };
     auto put_v = [&](int buf) {
@@ -232,15 +242,16 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
         s1 = mfma32<DT>(k1, qv[ds], s1);
       }
     };
-    // the mask of the lane's 8 keys 32it + 8g .. +7 (loaded ahead of use)
-    auto load_mask = [&](int it, float (&mk)[8]) {
+    // the mask of the lane's 8 keys 32it + 8g .. +7: two 16-byte loads, the
+    // step's offset in the scalar operand (issued one step ahead of use)
+    auto load_mask = [&](int it, u32x4 (&mk)[2]) {
       if constexpr (MASK) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) mk[e] = bload1f(mbuf, moff + (uint32_t)((SUB * it + 8 * g + e) * 4));
+        mk[0] = bload4(mbuf, moff, (uint32_t)(SUB * 4 * it));
+        mk[1] = bload4(mbuf, moff + 16u, (uint32_t)(SUB * 4 * it));
       }
     };
     // scaled, masked and cut scores of the lane's 8 keys 32it + 8g + 4hb + r
-    auto make_x = [&](int it, const f32x4_t &s0, const f32x4_t &s1, const float (&mk)[8],
+    auto make_x = [&](int it, const f32x4_t &s0, const f32x4_t &s1, const u32x4 (&mk)[2],
                       float (&x)[8]) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -250,7 +261,12 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
           if (a.scores && qvalid && key < N) a.scores[row * a.N + key] = s;
         }
         x[e] = s;
-        if constexpr (MASK) x[e] = x[e] + mk[e];
+        if constexpr (MASK) {
+          // copy the word out first: a bit cast of a vector element in place
+          // reads the vector's first element
+          const uint32_t mw = mk[e >> 2][e & 3];
+          x[e] = x[e] + __builtin_bit_cast(float, mw);
+        }
       }
       if (SUB * it + SUB > kmin) {  // the step reaches some query's cut (uniform)
         const int nv = kend - (SUB * it + 8 * g);
@@ -260,25 +276,37 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
     };
 
     // ---- pass 1: per tile (max, sum), folded into the row state in tile order ----
+    // Software pipeline, one step deep: in step `it` the wave issues the QK
+    // product of step it + 1 (K sub-tile it + 1, already in LDS) and the
+    // mask of step it + 1, then runs the VALU work of step it on the
+    // product issued one step earlier, so the matrix cores and the VALU
+    // overlap.  K sub-tile it + 2 is loaded into registers at the start of
+    // step it and written to the LDS buffer of sub-tile it (read by every
+    // wave in step it - 1) before the step's barrier.
     float M = kNegInf, L = 0.0f;
+    f32x4_t sa[2], sb[2];  // raw S^T of a step (blocks 0 and 1), by step parity
+    u32x4 mk[2][2];
     if (tlive > 0) {
       fetch_k(0);
       put_k(0);
+      fetch_k(1);
+      put_k(1);
+      __syncthreads();
+      load_mask(0, mk[0]);
+      qk_sub(0, sa[0], sb[0]);
+      __syncthreads();  // every wave has read sub-tile 0 before step 0 overwrites it
     }
-    __syncthreads();
     for (int t = 0; t < tlive; ++t) {
       float x[8][8];  // [32-key step j][key 8g + e]
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int it = 8 * t + j;
-        const bool more = it + 1 < 8 * tlive;
-        if (more) fetch_k(it + 1);
-        float mk[8];
-        load_mask(it, mk);
-        f32x4_t s0, s1;
-        qk_sub(j & 1, s0, s1);
-        make_x(it, s0, s1, mk, x[j]);
-        if (more) put_k((j + 1) & 1);
+        const int cur = j & 1, nxt = cur ^ 1;  // it is 8t + j: parity of j
+        fetch_k(it + 2);
+        load_mask(it + 1, mk[nxt]);
+        qk_sub(nxt, sa[nxt], sb[nxt]);
+        make_x(it, sa[cur], sb[cur], mk[cur], x[j]);
+        put_k(cur);
         __syncthreads();
       }
       float mx = kNegInf;
@@ -342,13 +370,21 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
     f32x4_t o[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    // the same pipeline: step it issues QK of step it + 1, forms P of step
+    // it, accumulates P V of step it (V sub-tile it in LDS), and writes K
+    // sub-tile it + 2 and V sub-tile it + 1 to LDS before its barrier
     if (tlive > 0) {
       fetch_k(0);
-      fetch_v(0);
       put_k(0);
+      fetch_k(1);
+      put_k(1);
+      fetch_v(0);
       put_v(0);
+      __syncthreads();
+      load_mask(0, mk[0]);
+      qk_sub(0, sa[0], sb[0]);
+      __syncthreads();
     }
-    __syncthreads();
     for (int t = 0; t < tlive; ++t) {
       const float mt = sm[t * 16 + c16];
       const float msafe = (mt == kNegInf) ? 0.0f : mt;
@@ -356,17 +392,13 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int it = 8 * t + j;
-        const bool more = it + 1 < 8 * tlive;
-        if (more) {
-          fetch_k(it + 1);
-          fetch_v(it + 1);
-        }
-        float mk[8];
-        load_mask(it, mk);
-        f32x4_t s0, s1;
-        qk_sub(j & 1, s0, s1);
+        const int cur = j & 1, nxt = cur ^ 1;
+        fetch_k(it + 2);
+        fetch_v(it + 1);
+        load_mask(it + 1, mk[nxt]);
+        qk_sub(nxt, sa[nxt], sb[nxt]);
         float x[8], p[8];
-        make_x(it, s0, s1, mk, x);
+        make_x(it, sa[cur], sb[cur], mk[cur], x);
 #pragma unroll
         for (int e = 0; e < 8; ++e) p[e] = exp_(x[e] - msafe) * ct;
         const u32x4 pa = {pack2<DT>(p[0], p[1]), pack2<DT>(p[2], p[3]), pack2<DT>(p[4], p[5]),
@@ -383,13 +415,11 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
         // B operand: keys 32it + 8g .. +7 of dims 16db + c16
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const u32x4 vv = *reinterpret_cast<const u32x4 *>(&lv[j & 1][(16 * db + c16) * VROW + 8 * g]);
+          const u32x4 vv = *reinterpret_cast<const u32x4 *>(&lv[cur][(16 * db + c16) * VROW + 8 * g]);
           o[db] = mfma32<DT>(pa, vv, o[db]);
         }
-        if (more) {
-          put_k((j + 1) & 1);
-          put_v((j + 1) & 1);
-        }
+        put_k(cur);
+        put_v(nxt);
         __syncthreads();
       }
     }
@@ -445,13 +475,14 @@ hipError_t attn_launch(const AttnArgs &a, int64_t blocks, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)blocks), block(kWave * kAttnWaves);
+  const size_t dyn = (size_t)kAttnWaves * a.T * 16 * sizeof(float);
   const bool mask = a.mask != nullptr, write = a.probs != nullptr || a.scores != nullptr;
   if (mask) {
-    if (write) hipLaunchKernelGGL((attn_fwd_kernel<DT, D, true, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((attn_fwd_kernel<DT, D, true, false>), grid, block, 0, st, a);
+    if (write) hipLaunchKernelGGL((attn_fwd_kernel<DT, D, true, true>), grid, block, dyn, st, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<DT, D, true, false>), grid, block, dyn, st, a);
   } else {
-    if (write) hipLaunchKernelGGL((attn_fwd_kernel<DT, D, false, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((attn_fwd_kernel<DT, D, false, false>), grid, block, 0, st, a);
+    if (write) hipLaunchKernelGGL((attn_fwd_kernel<DT, D, false, true>), grid, block, dyn, st, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<DT, D, false, false>), grid, block, dyn, st, a);
   }
   return hipGetLastError();
 }
