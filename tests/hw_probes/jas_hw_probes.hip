@@ -243,6 +243,28 @@ __global__ void permlane_layout(uint32_t *out) {
 }
 }  // namespace
 
+// LDS bank-conflict probe: every lane reads 16-byte words at
+// (lane % 16) * rs + (lane / 16) * gs (+ 64 * k + 1024 * it) bytes, wrapped
+// into a 32 KB window of the workgroup's LDS, many times.  The pattern is
+// the one the attention kernel's operand reads follow (16 rows, lane groups
+// 16 bytes apart); rs is the row stride.
+__global__ __launch_bounds__(256) void lds_read(uint32_t *out, int rs, int gs, int iters) {
+  __shared__ __align__(16) uint32_t lds[8192];  // 32 KB
+  for (int i = threadIdx.x; i < 8192; i += 256) lds[i] = (uint32_t)i;
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const uint32_t base = (uint32_t)((lane & 15) * rs + (lane >> 4) * gs);
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t a = (base + (uint32_t)(k * 64) + (uint32_t)it * 1024u) & 0x7ff0u;  // 16-aligned, < 32 KB
+      acc ^= *reinterpret_cast<const u32x4 *>(&lds[a / 4]);
+    }
+  }
+  out[blockIdx.x * 256 + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+}
+
 extern "C" {
 // Sweep [first, first+count) (negative binary32 bit patterns).  out holds
 // 4 words per workgroup; returns the number of workgroups used, or -1.
@@ -304,5 +326,14 @@ int probe_mfma_layout(const uint16_t *A, const uint16_t *B, float *D, int f16) {
 int probe_permlane_layout(uint32_t *out) {  // out: 256 words
   hipLaunchKernelGGL(permlane_layout, dim3(1), dim3(64), 0, 0, out);
   return hipDeviceSynchronize() == hipSuccess ? 0 : -1;
+}
+
+// out: blocks * 256 words (device); launches `blocks` workgroups of the LDS
+// read probe on `stream` and returns 0, or -1 on a bad argument.
+int probe_lds_read(uint32_t *out, int blocks, int rs, int gs, int iters, void *stream) {
+  if (!out || blocks <= 0 || rs < 0 || gs < 0 || iters <= 0) return -1;
+  hipLaunchKernelGGL(lds_read, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, out, rs, gs,
+                     iters);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 }
