@@ -355,6 +355,13 @@ struct RowIdx {
 constexpr int kBufWord3 = 0x00020000;
 constexpr int kAuxNT = 2;  // nontemporal: the row is streamed once
 
+// A cache policy as a type, for lambdas that take it as a compile-time
+// argument (the load builtins need an immediate).
+template <int V>
+struct AuxC {
+  static constexpr int value = V;
+};
+
 struct Buf {
   __amdgpu_buffer_rsrc_t r;
   __device__ __forceinline__ Buf(const void *base, uint32_t bytes)
@@ -769,11 +776,14 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void fwd_stream_kernel(const F
 
     Chunk raw[CPL];
     float e[CPL][KPL];
-    auto load_segment = [&](int g) {
+    // aux: the cache policy (normal for a segment read again in pass 2, so
+    // that the second read can hit the caches; nontemporal for a last read)
+    auto load_segment = [&](int g, auto aux) {
+      constexpr int AX = decltype(aux)::value;
 #pragma unroll
       for (int s = 0; s < CPL; ++s) {
         const int sb = (g * SPS + s * WPR + ix.wir) * TPS * kTile;
-        if constexpr (VEC) raw[s] = bload<kAuxNT>(sbuf, voff, (uint32_t)(sb * ESZ));
+        if constexpr (VEC) raw[s] = bload<AX>(sbuf, voff, (uint32_t)(sb * ESZ));
         else raw[s] = load_chunk_elems<DT>(srow, sb + ix.loff, kend, kFill);
       }
     };
@@ -815,7 +825,10 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void fwd_stream_kernel(const F
 
     // ---- pass 1: tile states of every segment into LDS ----
     for (int g = 0; g < nseg; ++g) {
-      if (g < nseg_read) load_segment(g);
+      if (g < nseg_read) {
+        if (g != nseg - 1) load_segment(g, AuxC<0>{});  // read again in pass 2
+        else load_segment(g, AuxC<kAuxNT>{});
+      }
 #pragma unroll
       for (int s = 0; s < CPL; ++s) {
         const int t = (g * SPS + s * WPR + ix.wir) * TPS + ix.half;
@@ -898,7 +911,7 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void fwd_stream_kernel(const F
     // ---- pass 2: rescale, convert once, write; last segment first ----
     for (int g = nseg - 1; g >= 0; --g) {
       const bool again = g != nseg - 1;
-      if (again && g < nseg_read) load_segment(g);
+      if (again && g < nseg_read) load_segment(g, AuxC<kAuxNT>{});
 #pragma unroll
       for (int s = 0; s < CPL; ++s) {
         const int gs = g * SPS + s * WPR + ix.wir;
@@ -962,13 +975,14 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void bwd_stream_kernel(const B
     const int lim = kend - ix.loff;
 
     Chunk rp[CPL], rg[CPL];
-    auto load_segment = [&](int g) {
+    auto load_segment = [&](int g, auto aux) {  // aux: cache policy, as in the forward
+      constexpr int AX = decltype(aux)::value;
 #pragma unroll
       for (int s = 0; s < CPL; ++s) {
         const int sb = (g * SPS + s * WPR + ix.wir) * TPS * kTile;
         if constexpr (VEC) {
-          rp[s] = bload<kAuxNT>(pbuf, voff, (uint32_t)(sb * ESZ));
-          rg[s] = bload<kAuxNT>(gbuf, voff, (uint32_t)(sb * ESZ));
+          rp[s] = bload<AX>(pbuf, voff, (uint32_t)(sb * ESZ));
+          rg[s] = bload<AX>(gbuf, voff, (uint32_t)(sb * ESZ));
           if constexpr (EXCL) {
             if (sb + TPS * kTile > kend && sb < kread) {  // the slot holding the cut (uniform)
               const int nv = lim - sb;
@@ -990,7 +1004,8 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void bwd_stream_kernel(const B
 
     // ---- pass 1: tile sums of P*dP into LDS ----
     for (int g = 0; g < nseg; ++g) {
-      load_segment(g);
+      if (g != nseg - 1) load_segment(g, AuxC<0>{});  // read again in pass 2
+      else load_segment(g, AuxC<kAuxNT>{});
 #pragma unroll
       for (int s = 0; s < CPL; ++s) {
         const int t = (g * SPS + s * WPR + ix.wir) * TPS + ix.half;
@@ -1024,7 +1039,7 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void bwd_stream_kernel(const B
 
     // ---- pass 2: dS = P * (dP - delta), convert once, write; last segment first ----
     for (int g = nseg - 1; g >= 0; --g) {
-      if (g != nseg - 1) load_segment(g);
+      if (g != nseg - 1) load_segment(g, AuxC<kAuxNT>{});
 #pragma unroll
       for (int s = 0; s < CPL; ++s) {
         const int gs = g * SPS + s * WPR + ix.wir;
