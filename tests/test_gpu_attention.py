@@ -122,6 +122,24 @@ def test_attention_mask_sink_causal_key_len(dt):
     check(q, k, v, 0.09, causal=True)                     # Sq < N: the last queries see all keys
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
+def test_attention_mask_rows_per_head_and_query(dt, D):
+    # one mask row per (batch, head, query) at an odd row stride, so rows
+    # start on 4-byte boundaries only (the kernel reads the mask 16 bytes at
+    # a time), with -inf entries and a causal cut
+    B, H, Hkv, Sq, N = 2, 3, 3, 37, 333
+    ld = N + 1
+    q, k, v = draw(71 + D, B, H, Hkv, Sq, N, D, dt, std=1.2)
+    mask = synth.normal((B * H * Sq * ld,), 1.0, 72 + D, "cpu")
+    mask[::7] = float("-inf")
+    log(f"attention {dt} D={D}: mask rows per head and query, row stride {ld}")
+    check(q, k, v, 0.1, mask=mask, mask_strides=(H * Sq * ld, Sq * ld, ld), causal=True)
+    # the mask broadcast over queries, one row per head
+    mh = synth.normal((H * N + 3,), 2.0, 73 + D, "cpu")
+    check(q, k, v, 0.1, mask=mh, mask_strides=(0, N + 1, 0))
+
+
 def test_attention_more_queries_than_keys_causal():
     # queries before the first visible key are fully masked rows: out = 0
     B, H, Sq, N, D = 1, 2, 50, 30, 64
