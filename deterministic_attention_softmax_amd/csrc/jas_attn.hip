@@ -133,7 +133,9 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
   constexpr bool write_all = WRITE;
 
   for (int64_t u = xcd_unit(blockIdx.x, gridDim.x); u < units; u += gridDim.x) {
-    const int64_t qg = u % qgroups, bh = u / qgroups;
+    // causal: a head's query blocks in decreasing cost (the last block sees
+    // the most keys), so the cheapest units are the last ones dispatched
+    const int64_t qg = a.ex.causal ? qgroups - 1 - u % qgroups : u % qgroups, bh = u / qgroups;
     const int64_t h = bh % a.H, b = bh / a.H;
     const int64_t hk = h / (a.H / a.Hkv);
     const int q0 = (int)(qg * 64) + 16 * w;  // this wave's 16 queries
@@ -443,25 +445,39 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
 }
 
 // V [B, Hkv, N, D] -> V^T [B, Hkv, D, Np], keys N .. Np-1 zero.  One
-// workgroup per (head, 64-key block): 64 keys x D dims through LDS.
+// workgroup per (head, 64-key block): 16-byte loads of 8 dims of a key,
+// scattered into an LDS tile [D][64 keys], then 16-byte stores of 8 keys
+// of a dim.  The tile row is 72 elements (144 bytes) so that the 8 lanes
+// writing one key's 8 dims fall in different banks.
 template <int D>
 __global__ __launch_bounds__(256) void vt_kernel(const uint16_t *v, uint16_t *vt, int64_t heads,
                                                  int64_t N, int64_t Np) {
-  __shared__ uint16_t tile[64][D + 2];
+  constexpr int TROW = 72;
+  __shared__ __align__(16) uint16_t tile[D * TROW];
   const int64_t kblocks = Np / 64;
   const int64_t hb = blockIdx.x / kblocks;
   const int64_t k0 = (blockIdx.x % kblocks) * 64;
   if (hb >= heads) return;
   const uint16_t *src = v + hb * N * D;
   uint16_t *dst = vt + hb * (int64_t)D * Np;
-  for (int i = threadIdx.x; i < 64 * D; i += 256) {
-    const int kk = i / D, d = i % D;
-    tile[kk][d] = (k0 + kk < N) ? src[(k0 + kk) * D + d] : (uint16_t)0;
+  constexpr int CH = 64 * D / 8 / 256;  // 16-byte chunks per thread
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int i = threadIdx.x + 256 * c;
+    const int kk = i / (D / 8), d8 = i % (D / 8);
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (k0 + kk < N) w = *reinterpret_cast<const u32x4 *>(src + (k0 + kk) * D + 8 * d8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      tile[(8 * d8 + e) * TROW + kk] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < 64 * D; i += 256) {
-    const int d = i / 64, kk = i % 64;
-    dst[(int64_t)d * Np + k0 + kk] = tile[kk][d];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int i = threadIdx.x + 256 * c;
+    const int d = i / 8, k8 = i % 8;
+    *reinterpret_cast<u32x4 *>(dst + (int64_t)d * Np + k0 + 8 * k8) =
+        *reinterpret_cast<const u32x4 *>(&tile[d * TROW + 8 * k8]);
   }
 }
 
