@@ -176,6 +176,11 @@ def test_binding_rejects_host_tensors():
         jas.fwd(s)
     with pytest.raises(ValueError, match="device memory"):
         jas.bwd(s, s)
+    # the autograd Function marshals into the same calls: no host fallback
+    from deterministic_attention_softmax_amd.autograd import softmax
+    x = s.clone().requires_grad_(True)
+    with pytest.raises(ValueError, match="device memory"):
+        softmax(x)
 
 
 def adesc(B=1, H=4, Hkv=2, Sq=16, N=300, D=128, dtype=jas.JAS_DTYPE_BF16, flags=0):

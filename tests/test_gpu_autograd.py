@@ -1,0 +1,103 @@
+"""GPU: the autograd Function over jas_fwd / jas_bwd.
+
+RL-Kernel PR #453, Fixed-order backward and its unified gradient check
+(batch 2, 257 keys); ROCm TransformerEngine PR #678, Description (the sink
+gradient); RL-Kernel PR #240's review of its autograd wrapper (tensors
+through save_for_backward, a once-differentiable backward).
+
+* the bytes of P, dS and d_sink through autograd are those of the direct
+  library calls on the same upstream gradient;
+* on fp32 inputs the gradients agree with torch's own autograd of a float64
+  softmax whose denominator carries the sink as an extra column, under a
+  bound scaled by the backward's condition (|dS| + P (|dP| + |delta|));
+* a second derivative is refused with an error.
+"""
+import pytest
+import torch
+
+import deterministic_attention_softmax_amd as jas
+from deterministic_attention_softmax_amd.autograd import softmax as jas_softmax
+import synth
+from tests.gpu_util import dev, log
+
+pytestmark = pytest.mark.gpu
+
+
+def bits(t):
+    return synth.to_numpy_bits(t.detach()).tobytes()
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16, torch.float16])
+def test_autograd_bytes_equal_direct_calls(dt):
+    B, H, S, N = 2, 4, 9, 257
+    log(f"autograd vs direct calls: {dt}")
+    s = synth.normal((B, H, S, N), 3.0, 801, "cpu", dt).to(dev())
+    g = synth.normal((B, H, S, N), 1.0, 802, "cpu", dt).to(dev())
+    sink = synth.normal((H,), 1.0, 803, "cpu").to(dev())
+    mask = torch.zeros((B, 1, 1, N), device=dev())
+    mask[1, ..., 200:] = float("-inf")
+    for kw in (dict(), dict(mask=mask, mask_strides=(N, 0, 0)), dict(causal=True)):
+        x = s.clone().requires_grad_(True)
+        sk = sink.clone().requires_grad_(True)
+        P, ps = jas_softmax(x, sink=sk, **kw)
+        P.backward(g)
+        P0, ps0 = jas.fwd(s, sink=sink, **kw)
+        dS0, d0 = jas.bwd(P0, g, p_sink=ps0, causal=kw.get("causal", False))
+        torch.cuda.synchronize()
+        assert bits(P) == bits(P0) and bits(ps) == bits(ps0)
+        assert bits(x.grad) == bits(dS0), sorted(kw)
+        assert bits(sk.grad) == bits(d0), sorted(kw)
+        assert not ps.requires_grad
+    # without a sink: one output, scores gradient only
+    x = s.clone().requires_grad_(True)
+    P = jas_softmax(x)
+    (P * g).sum().backward()
+    dS0, _ = jas.bwd(jas.fwd(s)[0], g)
+    torch.cuda.synchronize()
+    assert bits(x.grad) == bits(dS0)
+
+
+def test_autograd_against_float64_softmax_gradients():
+    # the unified gradient-check shape: fp32 [2,4,257,257], scores N(0, 9)
+    s, g = synth.grad_check_fp32(seed=811)
+    s, g = s.to(dev()), g.to(dev())
+    B, H, S, N = s.shape
+    sink = synth.normal((H,), 1.0, 812, "cpu").to(dev())
+    log("autograd vs float64 torch softmax with a sink column, fp32 [2,4,257,257]")
+    x = s.clone().requires_grad_(True)
+    sk = sink.clone().requires_grad_(True)
+    P, _ = jas_softmax(x, sink=sk)
+    loss = (P * g).sum()
+    loss.backward()
+    # float64 reference: softmax over [scores, sigma_h], the sink column dropped
+    x64 = s.double().clone().requires_grad_(True)
+    sk64 = sink.double().clone().requires_grad_(True)
+    col = sk64.view(1, H, 1, 1).expand(B, H, S, 1)
+    P64 = torch.softmax(torch.cat([x64, col], dim=-1), dim=-1)[..., :N]
+    (P64 * g.double()).sum().backward()
+    P64d = P64.detach()
+    g64 = g.double()
+    delta = (P64d * g64).sum(-1, keepdim=True)
+    # the binary32 delta carries an error of a few units of sum_i P_i |dP_i|
+    # (a sum of 257 products), so the bounds scale with that sum
+    mass = (P64d * g64.abs()).sum(-1, keepdim=True)
+    bound = 2.0 ** -16 * (x64.grad.abs() + P64d * (g64.abs() + mass)) + 1e-30
+    err = (x.grad.double() - x64.grad).abs()
+    assert torch.all(err <= bound), f"dS worst ratio {float((err / bound).max())}"
+    # P: a few roundings, plus the exponent's argument u = (x - max) log2(e)
+    # rounded to binary32, which moves 2^u by |u| 2^-24 ln 2 relative
+    u = (torch.cat([s.double(), sink.double().view(1, H, 1, 1).expand(B, H, S, 1)], -1)
+         .amax(-1, keepdim=True) - s.double()) * 1.4426950408889634
+    assert torch.all((P.double() - P64d).abs() <= P64d * (2.0 ** -20 + u * 2.0 ** -22) + 1e-37)
+    ps64 = 1.0 - P64d.sum(-1)
+    scale = (ps64.abs() * (mass + delta.abs()).squeeze(-1)).sum(dim=(0, 2))
+    assert torch.all((sk.grad.double() - sk64.grad).abs() <= 2.0 ** -14 * scale + 1e-12)
+
+
+def test_second_derivative_is_refused():
+    s = synth.normal((1, 2, 3, 300), 1.0, 821, "cpu", torch.float32).to(dev())
+    x = s.clone().requires_grad_(True)
+    P = jas_softmax(x)
+    (gx,) = torch.autograd.grad((P * P).sum(), x, create_graph=True)
+    with pytest.raises(RuntimeError):
+        gx.sum().backward()
