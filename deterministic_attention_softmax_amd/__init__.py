@@ -151,9 +151,13 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
-def _stream():
+def _on_device(t, fn, *args):
+    """Call a library entry point with ``t``'s device current and that
+    device's current stream as the last argument, so that the launch goes
+    to the device holding the tensors whatever device is current."""
     import torch
-    return torch.cuda.current_stream().cuda_stream
+    with torch.cuda.device(t.device):
+        return fn(*args, torch.cuda.current_stream(t.device).cuda_stream)
 
 
 def make_desc(shape, dtype_code, flags=0, ld=None, mask_strides=(0, 0, 0)):
@@ -279,9 +283,9 @@ def fwd(scores, mask=None, mask_strides=None, sink=None, out=None, p_sink=None, 
         if lse is None:
             lse = torch.empty(rows, dtype=torch.float32, device=scores.device)
         _check_vec(lse, scores, torch.float32, rows, "lse")
-    st = jas_fwd_ex(d, _ptr(scores), _ptr(mask), _ptr(key_len), _ptr(sink), _ptr(out),
-                    _ptr(p_sink) if sink is not None else None, _ptr(lse) if want_lse else None,
-                    _launch(launch), _stream())
+    st = _on_device(scores, jas_fwd_ex, d, _ptr(scores), _ptr(mask), _ptr(key_len), _ptr(sink),
+                    _ptr(out), _ptr(p_sink) if sink is not None else None,
+                    _ptr(lse) if want_lse else None, _launch(launch))
     if st != 0:
         raise JasError(st, "jas_fwd")
     ps = p_sink if sink is not None else None
@@ -313,10 +317,10 @@ def bwd(probs, dprobs, p_sink=None, out=None, d_sink=None, workspace=None, launc
             workspace = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device=probs.device)
         _check_vec(d_sink, probs, torch.float32, H, "d_sink")
         _check_vec(workspace, probs, torch.uint8, ws_bytes, "workspace")
-    st = jas_bwd_ex(d, _ptr(probs), _ptr(dprobs), _ptr(key_len), _ptr(p_sink), _ptr(out),
-                    _ptr(d_sink) if p_sink is not None else None,
+    st = _on_device(probs, jas_bwd_ex, d, _ptr(probs), _ptr(dprobs), _ptr(key_len), _ptr(p_sink),
+                    _ptr(out), _ptr(d_sink) if p_sink is not None else None,
                     _ptr(workspace) if p_sink is not None else None,
-                    workspace.numel() if workspace is not None else 0, _launch(launch), _stream())
+                    workspace.numel() if workspace is not None else 0, _launch(launch))
     if st != 0:
         raise JasError(st, "jas_bwd")
     return out, (d_sink if p_sink is not None else None)
@@ -417,9 +421,9 @@ def attn_fwd(q, k, v, scale=None, mask=None, mask_strides=None, sink=None, causa
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     _check_vec(workspace, q, torch.uint8, ws_bytes, "workspace")
-    st = jas_attn_fwd(d, _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(key_len), _ptr(sink),
-                      _ptr(out), _ptr(res["lse"]), _ptr(res["p_sink"]), _ptr(res["probs"]),
-                      _ptr(res["scores"]), _ptr(workspace), workspace.numel(), _stream())
+    st = _on_device(q, jas_attn_fwd, d, _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(key_len),
+                    _ptr(sink), _ptr(out), _ptr(res["lse"]), _ptr(res["p_sink"]), _ptr(res["probs"]),
+                    _ptr(res["scores"]), _ptr(workspace), workspace.numel())
     if st != 0:
         raise JasError(st, "jas_attn_fwd")
     return res

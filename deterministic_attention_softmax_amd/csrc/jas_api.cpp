@@ -23,13 +23,24 @@ struct Dims {
   int T;            // tiles per row
 };
 
+// A C caller may store any int in an enum-typed argument or field; reading
+// a value outside the enumerators through the C++ enum type is undefined,
+// so values are validated through their bytes.
+template <typename E>
+int enum_bits(const E &e) {
+  static_assert(sizeof(E) == sizeof(int), "the C enums of jas.h are int-sized");
+  int v;
+  memcpy(&v, &e, sizeof v);
+  return v;
+}
+
 bool mul_ok(int64_t a, int64_t b, int64_t *out) { return !__builtin_mul_overflow(a, b, out); }
 bool add_ok(int64_t a, int64_t b, int64_t *out) { return !__builtin_add_overflow(a, b, out); }
 
 jas_status_t check_desc(const jas_desc_t *d, Dims *dims) {
   if (!d) return JAS_ERR_NULL_POINTER;
-  if (d->dtype != JAS_DTYPE_F32 && d->dtype != JAS_DTYPE_BF16 && d->dtype != JAS_DTYPE_F16)
-    return JAS_ERR_BAD_DTYPE;
+  const int dt = enum_bits(d->dtype);
+  if (dt != JAS_DTYPE_F32 && dt != JAS_DTYPE_BF16 && dt != JAS_DTYPE_F16) return JAS_ERR_BAD_DTYPE;
   if (d->flags & ~(uint32_t)(JAS_FLAG_MASK | JAS_FLAG_SINK | JAS_FLAG_CAUSAL | JAS_FLAG_KEY_LEN |
                              JAS_FLAG_LSE))
     return JAS_ERR_BAD_FLAGS;
@@ -309,7 +320,8 @@ struct AttnDims {
 
 jas_status_t check_attn_desc(const jas_attn_desc_t *d, AttnDims *dm) {
   if (!d) return JAS_ERR_NULL_POINTER;
-  if (d->dtype != JAS_DTYPE_BF16 && d->dtype != JAS_DTYPE_F16) return JAS_ERR_BAD_DTYPE;
+  const int dt = enum_bits(d->dtype);
+  if (dt != JAS_DTYPE_BF16 && dt != JAS_DTYPE_F16) return JAS_ERR_BAD_DTYPE;
   const uint32_t known = JAS_FLAG_MASK | JAS_FLAG_SINK | JAS_FLAG_CAUSAL | JAS_FLAG_KEY_LEN |
                          JAS_FLAG_LSE | JAS_FLAG_PROBS | JAS_FLAG_SCORES;
   if (d->flags & ~known) return JAS_ERR_BAD_FLAGS;
@@ -487,7 +499,7 @@ jas_status_t jas_attn_fwd(const jas_attn_desc_t *desc, const void *q, const void
 }
 
 const char *jas_status_str(jas_status_t s) {
-  switch (s) {
+  switch (enum_bits(s)) {
     case JAS_OK: return "ok";
     case JAS_ERR_NULL_POINTER: return "a required pointer is NULL";
     case JAS_ERR_BAD_SHAPE: return "invalid shape, row stride or mask stride";
