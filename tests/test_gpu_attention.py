@@ -148,6 +148,20 @@ def test_attention_more_queries_than_keys_causal():
     assert torch.all(r["out"][:, :, :Sq - N] == 0)
 
 
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
+def test_attention_at_the_key_limit(dt):
+    # 16,384 keys, the most one call takes: 64 tiles of maxima per wave in
+    # LDS; grouped heads, a mask, the sink and the causal cut, a ragged
+    # query block
+    B, H, Hkv, Sq, N, D = 1, 2, 1, 70, 16384, 128
+    log(f"attention at the key limit: {dt} N={N}")
+    q, k, v = draw(91, B, H, Hkv, Sq, N, D, dt)
+    mask = synth.normal((B, 1, 1, N), 1.0, 92, "cpu")
+    mask[..., 5000:5300] = float("-inf")
+    sink = synth.normal((H,), 1.0, 93, "cpu")
+    check(q, k, v, 1.0 / np.sqrt(D), mask=mask, mask_strides=(N, 0, 0), sink=sink, causal=True)
+
+
 def test_attention_batch_and_block_invariance():
     # a (batch, head)'s bytes do not move with the batch around it, nor with
     # the other query blocks of the call
