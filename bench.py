@@ -33,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+ROTATE_BYTES = 1 << 30  # timed steps touch at least this many bytes of buffers
 METRIC = "fwd+bwd softmax HBM GB/s and rows/s (bf16, 4,352 keys) vs 8 TB/s roofline"
 
 WORKLOADS = {
@@ -435,14 +436,25 @@ def bench_attention(args):
     d = jas.make_attn_desc(B, H, Hkv, S, N, D, jas.JAS_DTYPE_BF16, 0, scale)
     ws = torch.empty(jas.jas_attn_workspace_bytes(d), dtype=torch.uint8, device=dev)
 
+    # rotated buffer sets (copies of the same inputs), as in the softmax bench:
+    # consecutive calls do not find each other's q, k, v and out in the
+    # Infinity Cache (within one call K and V are shared by design)
+    set_bytes = 2 * (2 * q.numel() + 2 * k.numel()) + ws.numel()
+    nsets = max(1, -(-ROTATE_BYTES // set_bytes))
+    sets = [(q, k, v, out, ws)] + [(q.clone(), k.clone(), v.clone(), torch.empty_like(q),
+                                    torch.empty_like(ws)) for _ in range(nsets - 1)]
+    nstep = [0]
+
     def step():
-        return jas.attn_fwd(q, k, v, scale=scale, mask=mask,
+        qi, ki, vi, oi, wi = sets[nstep[0] % nsets]
+        nstep[0] += 1
+        return jas.attn_fwd(qi, ki, vi, scale=scale, mask=mask,
                             mask_strides=None if mask is None else (N, 0, 0), sink=sink,
-                            causal=causal, want_lse=True, out=out, workspace=ws)
+                            causal=causal, want_lse=True, out=oi, workspace=wi)
 
     check = None
     if not args.no_check:
-        r = step()
+        r = step()  # the first set: q, k, v themselves
         torch.cuda.synchronize()
         qi = np.sort(np.random.default_rng(85).choice(S, 2, replace=False))
         if causal:
@@ -489,6 +501,7 @@ def bench_attention(args):
         "config": {"workload": desc, "batch": B, "heads": H, "kv_heads": Hkv, "q_len": S,
                    "kv_len": N, "head_dim": D, "mask": has_mask, "causal": causal,
                    "sink": has_sink, "useful_flops": flops},
+        "buffer_sets": nsets,
         "roofline": {"bound": "mfma", "kernel": "jas_attn_fwd (V transpose + fused kernel)",
                      "achieved": round(ktf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(ktf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
@@ -629,21 +642,32 @@ def main():
         check = check_parity(wl, s, mask, sink, g, key_len)
         log(f"parity check: {check}")
 
-    P = torch.empty_like(s)
-    dS = torch.empty_like(s) if backward else None
+    # Buffer sets rotated from step to step so that the timed steps touch at
+    # least ROTATE_BYTES: a workload smaller than the 256 MB Infinity Cache
+    # would otherwise be served from it on repeated steps.  Extra sets hold
+    # copies of the same inputs.
+    set_bytes = s.numel() * esz * (4 if backward else 2)
+    nsets = max(1, -(-ROTATE_BYTES // set_bytes))
+    sets = [(s, g, torch.empty_like(s), torch.empty_like(s) if backward else None)]
+    for _ in range(nsets - 1):
+        sets.append((s.clone(), g.clone() if backward else None, torch.empty_like(s),
+                     torch.empty_like(s) if backward else None))
     ps = torch.empty(rows, dtype=torch.float32, device=dev) if has_sink else None
     dsk = torch.empty(H, dtype=torch.float32, device=dev) if has_sink else None
     ws = torch.empty(max(4, rows * 4 + 256), dtype=torch.uint8, device=dev) if has_sink else None
     stream = torch.cuda.current_stream()
+    nstep = [0]
 
     def step(ev=None):
+        si, gi, P, dS = sets[nstep[0] % nsets]
+        nstep[0] += 1
         if ev:
             ev[0].record(stream)
-        jas.fwd(s, mask=mask, sink=sink, out=P, p_sink=ps, causal=causal, key_len=key_len)
+        jas.fwd(si, mask=mask, sink=sink, out=P, p_sink=ps, causal=causal, key_len=key_len)
         if ev:
             ev[1].record(stream)
         if backward:
-            jas.bwd(P, g, p_sink=ps, out=dS, d_sink=dsk, workspace=ws, causal=causal,
+            jas.bwd(P, gi, p_sink=ps, out=dS, d_sink=dsk, workspace=ws, causal=causal,
                     key_len=key_len)
         if ev:
             ev[2].record(stream)
@@ -689,6 +713,7 @@ def main():
                    "rows": rows, "mask": has_mask, "sink": has_sink, "exclusion": excl,
                    "visible_keys": V, "backward": backward},
         "rows_per_s": round(rows / (step_ms * 1e-3), 1),
+        "buffer_sets": nsets,
         "fwd_ms": round(float(fwd_ms.mean()), 4), "fwd_gbs": round(fwd_gbs, 1),
         "bwd_ms": round(float(bwd_ms.mean()), 4) if backward else None,
         "bwd_gbs": round(bwd_gbs, 1) if backward else None,
