@@ -265,6 +265,29 @@ __global__ __launch_bounds__(256) void lds_read(uint32_t *out, int rs, int gs, i
   out[blockIdx.x * 256 + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
 }
 
+// VALU issue-rate probe: 8 independent chains per lane of one operation
+// (OP 0: v_exp_f32, OP 1: v_mul_f32), registers only.
+template <int OP>
+__global__ __launch_bounds__(256) void valu_rate(float *out, int iters) {
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = -0.5f - 1e-6f * (float)(threadIdx.x + i);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if constexpr (OP == 0) v[i] = __builtin_amdgcn_exp2f(v[i]);
+        else v[i] = v[i] * 1.0001f;
+      }
+    }
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += v[i];
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
 extern "C" {
 // Sweep [first, first+count) (negative binary32 bit patterns).  out holds
 // 4 words per workgroup; returns the number of workgroups used, or -1.
@@ -334,6 +357,17 @@ int probe_lds_read(uint32_t *out, int blocks, int rs, int gs, int iters, void *s
   if (!out || blocks <= 0 || rs < 0 || gs < 0 || iters <= 0) return -1;
   hipLaunchKernelGGL(lds_read, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, out, rs, gs,
                      iters);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// out: blocks * 256 floats (device); op 0: v_exp_f32, 1: v_mul_f32; each
+// thread issues iters * 128 operations.  Launches on `stream`; 0 or -1.
+int probe_valu_rate(float *out, int blocks, int op, int iters, void *stream) {
+  if (!out || blocks <= 0 || iters <= 0 || (op != 0 && op != 1)) return -1;
+  if (op == 0)
+    hipLaunchKernelGGL(valu_rate<0>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, out, iters);
+  else
+    hipLaunchKernelGGL(valu_rate<1>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, out, iters);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 }
