@@ -211,6 +211,7 @@ jas_status_t fwd_impl(const jas_desc_t *d, const void *scores, const float *mask
   st = choose_geometry(d->dtype, dm.T, dm.rows, false, launch, &g);
   if (st != JAS_OK) return st;
   jas::FwdArgs a;
+  a.stash = 0;  // the streaming launcher decides
   a.scores = scores;
   a.probs = probs;
   a.mask = has_mask ? mask : nullptr;
@@ -290,6 +291,7 @@ jas_status_t bwd_impl(const jas_desc_t *d, const void *probs, const void *dprobs
 
   {
     jas::BwdArgs a;
+    a.stash = 0;  // the streaming launcher decides
     a.probs = probs;
     a.dprobs = dprobs;
     a.dscores = dscores;

@@ -734,6 +734,17 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void bwd_kernel(const BwdArgs 
 // on the same inputs, so every output has the one-pass kernels' bits.
 // ---------------------------------------------------------------------------
 
+// Start of the streaming kernels' segment stash in their dynamic LDS, in
+// 4-byte words after `used` words of tile states (16-byte aligned).
+__host__ __device__ constexpr int stash_offset_words(int used) { return (used + 3) & ~3; }
+
+// The stash holds one segment's chunks: 256 threads x CPL x 16 bytes.  It is
+// used where that is at most 32 KB, which keeps the workgroups per CU the
+// register budget allows (a 32 KB stash fits 4 per CU).
+constexpr int kStashMaxBytes = 32 * 1024;
+template <int CPL>
+constexpr size_t stash_bytes() { return (size_t)CPL * kWave * kBlockWaves * 16; }
+
 template <int DT, int CPL, bool VEC, bool MASK, bool EXCL>
 __global__ __launch_bounds__(kWave * kBlockWaves) void fwd_stream_kernel(const FwdArgs a) {
   using C = Cfg<DT>;
@@ -746,6 +757,9 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void fwd_stream_kernel(const F
   float *lds_m = smem;            // [T] tile maxima
   float *lds_l = smem + T;        // [T] tile sums
   float *lds_row = smem + 2 * T;  // the row's M and invL
+  // with a.stash: the raw chunks of segment nseg - 2 (the first one pass 2
+  // would read again), CPL x 256 threads x 16 bytes, each thread's own
+  Chunk *lds_stash = reinterpret_cast<Chunk *>(smem + stash_offset_words(2 * T + 2));
 
   const RowIdx<DT, WPR> ix;
   const int lane = ix.lane;
@@ -824,10 +838,15 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void fwd_stream_kernel(const F
     const int nseg_read = EXCL ? (kend + SPS * TPS * kTile - 1) / (SPS * TPS * kTile) : nseg;
 
     // ---- pass 1: tile states of every segment into LDS ----
+    const bool stash = a.stash && nseg >= 2;
     for (int g = 0; g < nseg; ++g) {
       if (g < nseg_read) {
         if (g != nseg - 1) load_segment(g, AuxC<0>{});  // read again in pass 2
         else load_segment(g, AuxC<kAuxNT>{});
+        if (stash && g == nseg - 2) {
+#pragma unroll
+          for (int s = 0; s < CPL; ++s) lds_stash[s * kWave * WPR + threadIdx.x] = raw[s];
+        }
       }
 #pragma unroll
       for (int s = 0; s < CPL; ++s) {
@@ -911,7 +930,14 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void fwd_stream_kernel(const F
     // ---- pass 2: rescale, convert once, write; last segment first ----
     for (int g = nseg - 1; g >= 0; --g) {
       const bool again = g != nseg - 1;
-      if (again && g < nseg_read) load_segment(g, AuxC<kAuxNT>{});
+      if (again && g < nseg_read) {
+        if (stash && g == nseg - 2) {
+#pragma unroll
+          for (int s = 0; s < CPL; ++s) raw[s] = lds_stash[s * kWave * WPR + threadIdx.x];
+        } else {
+          load_segment(g, AuxC<kAuxNT>{});
+        }
+      }
 #pragma unroll
       for (int s = 0; s < CPL; ++s) {
         const int gs = g * SPS + s * WPR + ix.wir;
@@ -954,6 +980,8 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void bwd_stream_kernel(const B
   const int T = a.s.T;
   float *lds_d = smem;            // [T] tile sums of P*dP
   float *lds_row = smem + T;      // delta
+  // with a.stash: segment nseg - 2's P chunks (as masked), each thread's own
+  Chunk *lds_stash = reinterpret_cast<Chunk *>(smem + stash_offset_words(T + 1));
 
   const RowIdx<DT, WPR> ix;
   const int lane = ix.lane;
@@ -1002,10 +1030,24 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void bwd_stream_kernel(const B
       }
     };
 
+    auto load_g = [&](int g) {  // dP only, for the segment whose P is in LDS
+#pragma unroll
+      for (int s = 0; s < CPL; ++s) {
+        const int sb = (g * SPS + s * WPR + ix.wir) * TPS * kTile;
+        if constexpr (VEC) rg[s] = bload<kAuxNT>(gbuf, voff, (uint32_t)(sb * ESZ));
+        else rg[s] = load_chunk_elems<DT>(grow, sb + ix.loff, N, 0u);
+      }
+    };
+    const bool stash = a.stash && nseg >= 2;
+
     // ---- pass 1: tile sums of P*dP into LDS ----
     for (int g = 0; g < nseg; ++g) {
       if (g != nseg - 1) load_segment(g, AuxC<0>{});  // read again in pass 2
       else load_segment(g, AuxC<kAuxNT>{});
+      if (stash && g == nseg - 2) {
+#pragma unroll
+        for (int s = 0; s < CPL; ++s) lds_stash[s * kWave * WPR + threadIdx.x] = rp[s];
+      }
 #pragma unroll
       for (int s = 0; s < CPL; ++s) {
         const int t = (g * SPS + s * WPR + ix.wir) * TPS + ix.half;
@@ -1039,7 +1081,15 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void bwd_stream_kernel(const B
 
     // ---- pass 2: dS = P * (dP - delta), convert once, write; last segment first ----
     for (int g = nseg - 1; g >= 0; --g) {
-      if (g != nseg - 1) load_segment(g, AuxC<kAuxNT>{});
+      if (g != nseg - 1) {
+        if (stash && g == nseg - 2) {
+#pragma unroll
+          for (int s = 0; s < CPL; ++s) rp[s] = lds_stash[s * kWave * WPR + threadIdx.x];
+          load_g(g);
+        } else {
+          load_segment(g, AuxC<kAuxNT>{});
+        }
+      }
 #pragma unroll
       for (int s = 0; s < CPL; ++s) {
         const int gs = g * SPS + s * WPR + ix.wir;
@@ -1077,9 +1127,12 @@ constexpr int kStreamCplF32[] = {8, 16};
 constexpr int kStreamCplBf16[] = {4, 8};
 
 template <int DT, int CPL>
-hipError_t launch_fwd_stream(const FwdArgs &a, const Geometry &g, hipStream_t st) {
+hipError_t launch_fwd_stream(const FwdArgs &a0, const Geometry &g, hipStream_t st) {
   const dim3 grid((unsigned)g.blocks), block(kWave * kBlockWaves);
-  const size_t lds = (size_t)(2 * a.s.T + 2) * sizeof(float);
+  FwdArgs a = a0;
+  a.stash = stash_bytes<CPL>() <= kStashMaxBytes;
+  const size_t lds = (size_t)stash_offset_words(2 * a.s.T + 2) * sizeof(float) +
+                     (a.stash ? stash_bytes<CPL>() : 0);
   const bool mask = a.mask != nullptr, excl = a.ex.causal || a.ex.key_len;
 #define JAS_FWD_STREAM(V, MK, EX)                                                              \
   hipLaunchKernelGGL((fwd_stream_kernel<DT, CPL, V, MK, EX>), grid, block, lds, st, a)
@@ -1095,9 +1148,12 @@ hipError_t launch_fwd_stream(const FwdArgs &a, const Geometry &g, hipStream_t st
 }
 
 template <int DT, int CPL>
-hipError_t launch_bwd_stream(const BwdArgs &a, const Geometry &g, hipStream_t st) {
+hipError_t launch_bwd_stream(const BwdArgs &a0, const Geometry &g, hipStream_t st) {
   const dim3 grid((unsigned)g.blocks), block(kWave * kBlockWaves);
-  const size_t lds = (size_t)(a.s.T + 1) * sizeof(float);
+  BwdArgs a = a0;
+  a.stash = stash_bytes<CPL>() <= kStashMaxBytes;
+  const size_t lds = (size_t)stash_offset_words(a.s.T + 1) * sizeof(float) +
+                     (a.stash ? stash_bytes<CPL>() : 0);
   const bool excl = a.ex.causal || a.ex.key_len;
   if (a.vec_io) {
     if (excl) hipLaunchKernelGGL((bwd_stream_kernel<DT, CPL, true, true>), grid, block, lds, st, a);
