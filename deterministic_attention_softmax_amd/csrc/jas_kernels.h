@@ -788,26 +788,31 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void fwd_stream_kernel(const F
     const uint32_t voff = (uint32_t)(ix.loff * ESZ);
     const int lim = kend - ix.loff;
 
-    Chunk raw[CPL];
-    float e[CPL][KPL];
+    // Two register sets of one segment's raw chunks: the one being reduced
+    // and the next one, loaded meanwhile.  Exponentials are not kept: pass 2
+    // recomputes them for every segment from the raw chunks and the tile
+    // maxima, the operations of pass 1 on the same inputs.
+    Chunk cur[CPL], nxt[CPL];
+#pragma unroll
+    for (int s = 0; s < CPL; ++s) cur[s] = nxt[s] = Chunk{{0u, 0u, 0u, 0u}};
     // aux: the cache policy (normal for a segment read again in pass 2, so
     // that the second read can hit the caches; nontemporal for a last read)
-    auto load_segment = [&](int g, auto aux) {
+    auto load_segment = [&](Chunk (&dst)[CPL], int g, auto aux) {
       constexpr int AX = decltype(aux)::value;
 #pragma unroll
       for (int s = 0; s < CPL; ++s) {
         const int sb = (g * SPS + s * WPR + ix.wir) * TPS * kTile;
-        if constexpr (VEC) raw[s] = bload<AX>(sbuf, voff, (uint32_t)(sb * ESZ));
-        else raw[s] = load_chunk_elems<DT>(srow, sb + ix.loff, kend, kFill);
+        if constexpr (VEC) dst[s] = bload<AX>(sbuf, voff, (uint32_t)(sb * ESZ));
+        else dst[s] = load_chunk_elems<DT>(srow, sb + ix.loff, kend, kFill);
       }
     };
     // the slot's keys as binary32 with the mask added and every key past
     // the row or the cut at -inf; false when the whole slot is past them
-    auto slot_x = [&](int g, int s, float (&x)[KPL]) -> bool {
+    auto slot_x = [&](int g, int s, const Chunk &raw, float (&x)[KPL]) -> bool {
       const int sb = (g * SPS + s * WPR + ix.wir) * TPS * kTile;
       if (sb >= kend) return false;  // uniform
       const int j0 = sb + ix.loff;
-      unpack<DT>(raw[s], x);
+      unpack<DT>(raw, x);
       if constexpr (MASK) {
         if constexpr (VEC) {
 #pragma unroll
@@ -836,37 +841,41 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void fwd_stream_kernel(const F
 
     // segments wholly past the cut hold only -inf keys: nothing to load
     const int nseg_read = EXCL ? (kend + SPS * TPS * kTile - 1) / (SPS * TPS * kTile) : nseg;
+    auto load_pass1 = [&](Chunk (&dst)[CPL], int g) {
+      if (g != nseg - 1) load_segment(dst, g, AuxC<0>{});  // read again in pass 2
+      else load_segment(dst, g, AuxC<kAuxNT>{});
+    };
 
     // ---- pass 1: tile states of every segment into LDS ----
     const bool stash = a.stash && nseg >= 2;
+    if (nseg_read > 0) load_pass1(cur, 0);
     for (int g = 0; g < nseg; ++g) {
-      if (g < nseg_read) {
-        if (g != nseg - 1) load_segment(g, AuxC<0>{});  // read again in pass 2
-        else load_segment(g, AuxC<kAuxNT>{});
-        if (stash && g == nseg - 2) {
+      if (g + 1 < nseg_read) load_pass1(nxt, g + 1);
+      if (stash && g == nseg - 2 && g < nseg_read) {
 #pragma unroll
-          for (int s = 0; s < CPL; ++s) lds_stash[s * kWave * WPR + threadIdx.x] = raw[s];
-        }
+        for (int s = 0; s < CPL; ++s) lds_stash[s * kWave * WPR + threadIdx.x] = cur[s];
       }
 #pragma unroll
       for (int s = 0; s < CPL; ++s) {
         const int t = (g * SPS + s * WPR + ix.wir) * TPS + ix.half;
         float x[KPL];
         float m = kNegInf, l = 0.0f;
-        if (slot_x(g, s, x)) {
+        if (slot_x(g, s, cur[s], x)) {
           m = tile_max<DT>(lane_tree_max<KPL>(x));
           const float msafe = (m == kNegInf) ? 0.0f : m;
+          float e[KPL];
 #pragma unroll
-          for (int k = 0; k < KPL; ++k) e[s][k] = exp_(x[k] - msafe);
-          l = tile_sum<DT>(lane_tree_sum<KPL>(e[s]));
-        } else {
-#pragma unroll
-          for (int k = 0; k < KPL; ++k) e[s][k] = 0.0f;
+          for (int k = 0; k < KPL; ++k) e[k] = exp_(x[k] - msafe);
+          l = tile_sum<DT>(lane_tree_sum<KPL>(e));
         }
         if (ix.cil == 0 && t < T) {
           lds_m[t] = m;
           lds_l[t] = l;
         }
+      }
+      if (g + 1 < nseg) {
+#pragma unroll
+        for (int s = 0; s < CPL; ++s) cur[s] = nxt[s];
       }
     }
     __syncthreads();
@@ -928,14 +937,16 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void fwd_stream_kernel(const F
     const float M = lds_row[0], invL = lds_row[1];
 
     // ---- pass 2: rescale, convert once, write; last segment first ----
+    // cur holds the last segment; the one before it comes from the stash or
+    // is read again, each loaded while the current one is written
     for (int g = nseg - 1; g >= 0; --g) {
-      const bool again = g != nseg - 1;
-      if (again && g < nseg_read) {
-        if (stash && g == nseg - 2) {
+      const int gp = g - 1;
+      if (gp >= 0 && gp < nseg_read) {
+        if (stash && gp == nseg - 2) {
 #pragma unroll
-          for (int s = 0; s < CPL; ++s) raw[s] = lds_stash[s * kWave * WPR + threadIdx.x];
+          for (int s = 0; s < CPL; ++s) nxt[s] = lds_stash[s * kWave * WPR + threadIdx.x];
         } else {
-          load_segment(g, AuxC<kAuxNT>{});
+          load_segment(nxt, gp, AuxC<kAuxNT>{});
         }
       }
 #pragma unroll
@@ -945,25 +956,28 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void fwd_stream_kernel(const F
           const int sb = gs * TPS * kTile;
           const int t = gs * TPS + ix.half;
           const float mt = lds_m[t < T ? t : T - 1];
-          if (again) {
-            float x[KPL];
-            if (slot_x(g, s, x)) {
-              const float msafe = (mt == kNegInf) ? 0.0f : mt;
+          float e[KPL];
+          float x[KPL];
+          if (slot_x(g, s, cur[s], x)) {
+            const float msafe = (mt == kNegInf) ? 0.0f : mt;
 #pragma unroll
-              for (int k = 0; k < KPL; ++k) e[s][k] = exp_(x[k] - msafe);
-            } else {
+            for (int k = 0; k < KPL; ++k) e[k] = exp_(x[k] - msafe);
+          } else {
 #pragma unroll
-              for (int k = 0; k < KPL; ++k) e[s][k] = 0.0f;
-            }
+            for (int k = 0; k < KPL; ++k) e[k] = 0.0f;
           }
           const float cs = (mt == kNegInf) ? 0.0f : exp_(mt - M) * invL;
           float p[KPL];
 #pragma unroll
-          for (int k = 0; k < KPL; ++k) p[k] = e[s][k] * cs;
+          for (int k = 0; k < KPL; ++k) p[k] = e[k] * cs;
           const Chunk out = pack<DT>(p);
           if constexpr (VEC) bstore(pbuf, voff, (uint32_t)(sb * ESZ), out);
           else store_chunk_elems<DT>(prow, sb + ix.loff, N, out);
         }
+      }
+      if (g > 0) {
+#pragma unroll
+        for (int s = 0; s < CPL; ++s) cur[s] = nxt[s];
       }
     }
     __syncthreads();  // LDS is reused by the next row
