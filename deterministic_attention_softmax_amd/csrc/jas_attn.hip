@@ -14,7 +14,13 @@
 // row), so lane l holds, for query l%16, four consecutive keys of a 16-key
 // block.  Keys go through the workgroup 32 at a time: K (32 keys x D) and
 // the transposed V (D x 32 keys) are loaded with coalesced 16-byte loads
-// into double-buffered LDS while the previous 32 keys are computed on.  In
+// into double-buffered LDS, K two steps and V one step ahead of use, and
+// each step issues the next step's QK product before its own softmax work
+// (a one-step software pipeline).  LDS row strides are 32 modulo 64 bytes,
+// which gfx950 serves without bank conflicts for these reads.  Workgroups
+// are renumbered so that one XCD works on neighbouring query blocks of one
+// head (its K and V stay in that XCD's L2); with the causal flag a head's
+// blocks go longest first.  In
 // each 32-key step the A rows are assigned so that lane group g (= l/16)
 // holds keys 8g .. 8g + 7 (the first block the first four, the second block
 // the next four).  The softmax tile tree is then exact: in-lane pairs and
