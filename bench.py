@@ -223,7 +223,7 @@ def cpu_baseline(wl, s, mask, sink, g, key_len, target_s):
     sk_all = None if sink is None else sink.cpu().numpy()
     s2, g2 = s.reshape(-1, N), (g.reshape(-1, N) if backward else None)
 
-    def run(k):
+    def run(k, threads=threads):
         rows = np.unique(np.linspace(0, B * H * S - 1, k).round().astype(np.int64))
         heads = (rows // S) % H
         t = 0.0
@@ -251,12 +251,32 @@ def cpu_baseline(wl, s, mask, sink, g, key_len, target_s):
     t0, _, _ = run(k0)
     k = int(min(B * H * S, max(k0, k0 * target_s / max(t0, 1e-3))))
     t, k, nbytes = run(k)
+    # the same oracle on one thread, on a sample of about a fifth of the time
+    t1p, _, _ = run(k0, threads=1)
+    k1 = int(min(B * H * S, max(k0, k0 * (target_s / 5) / max(t1p, 1e-3))))
+    t1, k1, nbytes1 = run(k1, threads=1)
     return {
         "value": round(nbytes / t / 1e9, 4), "unit": "GB/s",
         "rows_per_s": round(k / t, 1), "cores": threads, "kind": "oracle",
         "sample": f"{k} rows spread evenly over the whole workload ({k * N} elements), "
                   f"{'fwd+bwd' if backward else 'fwd'}, {t:.1f} s of oracle time",
+        "cpu_model": cpu_model(),
+        "one_thread": {"value": round(nbytes1 / t1 / 1e9, 4), "unit": "GB/s",
+                       "rows_per_s": round(k1 / t1, 1),
+                       "sample": f"{k1} rows spread evenly, {t1:.1f} s of oracle time"},
     }
+
+
+def cpu_model():
+    """The host CPU's model name (Linux), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def torch_index(idx, device):
@@ -531,7 +551,8 @@ def bench_attention(args):
         res["cpu_baseline"] = {"value": round(f / t / 1e12, 6), "unit": "TFLOP/s",
                                "cores": oracle.default_threads(), "kind": "oracle",
                                "sample": f"the last {kq} queries of every head ({B * H * kq} rows "
-                                         f"x {N} keys), {t:.1f} s"}
+                                         f"x {N} keys), {t:.1f} s",
+                               "cpu_model": cpu_model()}
     print(json.dumps(res), flush=True)
     if args.json_out:
         os.makedirs(os.path.dirname(os.path.abspath(args.json_out)), exist_ok=True)
