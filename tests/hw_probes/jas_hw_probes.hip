@@ -288,6 +288,38 @@ __global__ __launch_bounds__(256) void valu_rate(float *out, int iters) {
   out[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// HBM stream probe: NR 16-byte reads (NR = 1 or 2 arrays) and NW writes
+// (0 or 1) per element, grid-stride, CH chunks in flight per thread,
+// nontemporal.  The attainable rate of each access mix on this machine.
+template <int NR, int NW, int CH>
+__global__ __launch_bounds__(256) void stream_mix(const u32x4 *a, const u32x4 *b, u32x4 *d,
+                                                  uint64_t n16) {
+  const uint64_t step = (uint64_t)gridDim.x * 256 * CH;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (uint64_t base = (uint64_t)blockIdx.x * 256 * CH; base < n16; base += step) {
+    u32x4 x[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const uint64_t i = base + (uint64_t)c * 256 + threadIdx.x;
+      x[c] = u32x4{0u, 0u, 0u, 0u};
+      if (i < n16) {
+        x[c] = __builtin_nontemporal_load(a + i);
+        if constexpr (NR == 2) x[c] ^= __builtin_nontemporal_load(b + i);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const uint64_t i = base + (uint64_t)c * 256 + threadIdx.x;
+      if constexpr (NW == 1) {
+        if (i < n16) __builtin_nontemporal_store(x[c], d + i);
+      } else {
+        acc ^= x[c];
+      }
+    }
+  }
+  if constexpr (NW == 0) d[blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
 extern "C" {
 // Sweep [first, first+count) (negative binary32 bit patterns).  out holds
 // 4 words per workgroup; returns the number of workgroups used, or -1.
@@ -368,6 +400,34 @@ int probe_valu_rate(float *out, int blocks, int op, int iters, void *stream) {
     hipLaunchKernelGGL(valu_rate<0>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, out, iters);
   else
     hipLaunchKernelGGL(valu_rate<1>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, out, iters);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// Stream probe launch: mix 0 = read a, write d (copy); 1 = read a and b,
+// write d; 2 = read a only (d receives blocks * 256 words).  a, b, d hold
+// n16 16-byte words (d at least blocks * 256 for mix 2), 16-byte aligned.
+// chunks: 1, 2 or 4.  Enqueues on `stream`; 0 or -1.
+int probe_stream_mix(const void *a, const void *b, void *d, uint64_t n16, int mix, int chunks,
+                     int blocks, void *stream) {
+  if (!a || !d || (mix == 1 && !b) || blocks <= 0 || ((uintptr_t)a | (uintptr_t)d) % 16 ||
+      (b && (uintptr_t)b % 16) || (mix == 2 && n16 < (uint64_t)blocks * 256))
+    return -1;
+  const dim3 g((unsigned)blocks), blk(256);
+  hipStream_t st = (hipStream_t)stream;
+  const u32x4 *A = (const u32x4 *)a, *B = (const u32x4 *)b;
+  u32x4 *D = (u32x4 *)d;
+#define JAS_MIX(NR, NW)                                                                    \
+  do {                                                                                     \
+    if (chunks == 1) hipLaunchKernelGGL((stream_mix<NR, NW, 1>), g, blk, 0, st, A, B, D, n16); \
+    else if (chunks == 2) hipLaunchKernelGGL((stream_mix<NR, NW, 2>), g, blk, 0, st, A, B, D, n16); \
+    else if (chunks == 4) hipLaunchKernelGGL((stream_mix<NR, NW, 4>), g, blk, 0, st, A, B, D, n16); \
+    else return -1;                                                                        \
+  } while (0)
+  if (mix == 0) JAS_MIX(1, 1);
+  else if (mix == 1) JAS_MIX(2, 1);
+  else if (mix == 2) JAS_MIX(1, 0);
+  else return -1;
+#undef JAS_MIX
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 }
