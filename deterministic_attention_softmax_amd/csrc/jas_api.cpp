@@ -339,6 +339,13 @@ jas_status_t check_attn_desc(const jas_attn_desc_t *d, AttnDims *dm) {
   // one (batch, head)'s Q, K and V^T are addressed with 32-bit byte offsets
   int64_t qbytes = 0;
   if (!mul_ok(d->q_len, d->head_dim * 2, &qbytes) || qbytes > 0x7fffffff) return JAS_ERR_UNSUPPORTED;
+  // so is one (batch, head)'s mask: its last query row ends within 2 GiB
+  if (d->flags & JAS_FLAG_MASK) {
+    int64_t mq = 0, mext = 0;
+    if (!mul_ok(d->q_len > 0 ? d->q_len - 1 : 0, d->mask_stride_q, &mq) ||
+        !add_ok(mq, d->kv_len, &mext) || !mul_ok(mext, 4, &mext) || mext > 0x7fffffff)
+      return JAS_ERR_UNSUPPORTED;
+  }
   const int T = (int)((d->kv_len + jas::kTile - 1) / jas::kTile);
   const int64_t Np = (int64_t)T * jas::kTile;
   int64_t ws = 0;

@@ -204,6 +204,11 @@ def test_attention_validation():
     assert attn(adesc(N=jas.JAS_ATTN_MAX_KEYS + 1)) == 7
     assert attn(adesc(H=3, Hkv=2)) == 2
     assert attn(adesc(N=0)) == 2
+    # one (batch, head)'s mask must end within 2 GiB: 40,000 query rows of
+    # 16,384 keys do not
+    big = adesc(Sq=40000, N=16384, flags=jas.JAS_FLAG_MASK)
+    big.mask_stride_q = 16384
+    assert attn(big, mask=W) == 7
     assert attn(adesc(flags=1 << 7)) == 4
     assert attn(adesc(), mask=W) == 4                     # pointer without its flag
     assert attn(adesc(), probs=W) == 4
