@@ -36,13 +36,16 @@ def test_autograd_bytes_equal_direct_calls(dt):
     sink = synth.normal((H,), 1.0, 803, "cpu").to(dev())
     mask = torch.zeros((B, 1, 1, N), device=dev())
     mask[1, ..., 200:] = float("-inf")
-    for kw in (dict(), dict(mask=mask, mask_strides=(N, 0, 0)), dict(causal=True)):
+    kl = torch.tensor([N, 100], dtype=torch.int32, device=dev())
+    for kw in (dict(), dict(mask=mask, mask_strides=(N, 0, 0)), dict(causal=True),
+               dict(key_len=kl, causal=True)):
         x = s.clone().requires_grad_(True)
         sk = sink.clone().requires_grad_(True)
         P, ps = jas_softmax(x, sink=sk, **kw)
         P.backward(g)
         P0, ps0 = jas.fwd(s, sink=sink, **kw)
-        dS0, d0 = jas.bwd(P0, g, p_sink=ps0, causal=kw.get("causal", False))
+        dS0, d0 = jas.bwd(P0, g, p_sink=ps0, causal=kw.get("causal", False),
+                          key_len=kw.get("key_len"))
         torch.cuda.synchronize()
         assert bits(P) == bits(P0) and bits(ps) == bits(ps0)
         assert bits(x.grad) == bits(dS0), sorted(kw)
