@@ -729,9 +729,12 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void bwd_kernel(const BwdArgs 
 // LDS; wave 0 then folds the states in tile order, 64 tiles at a time with
 // the running state carried from block to block (the same left fold);
 // pass 2 writes the outputs segment by segment, last segment first: that
-// one is still in registers, the others are read again and their
-// exponentials recomputed from the saved tile maxima -- the same operations
-// on the same inputs, so every output has the one-pass kernels' bits.
+// one is still in registers, the one before it waits in an LDS stash, the
+// others are read again (the forward loads the next segment while it
+// writes the current one).  The forward recomputes every segment's
+// exponentials from the raw chunks and the saved tile maxima -- the same
+// operations on the same inputs, so every output has the one-pass kernels'
+// bits.
 // ---------------------------------------------------------------------------
 
 // Start of the streaming kernels' segment stash in their dynamic LDS, in
