@@ -96,9 +96,10 @@ extern "C" {
 /* Largest supported row length (keys per row).  Rows of up to 16,384 keys
  * are held in registers for one pass over HBM; longer rows are streamed
  * (RL-Kernel PR #453, Summary: rows are processed tile by tile, left to
- * right): the tile states of the whole row are kept on chip, and every
- * segment but the last is read a second time to write the outputs, with the
- * same arithmetic and so the same bits. */
+ * right): the tile states of the whole row are kept on chip, the last
+ * segment stays in registers and the one before it in LDS, and the other
+ * segments are read a second time to write the outputs, with the same
+ * arithmetic and so the same bits. */
 #define JAS_MAX_KEYS 262144
 
 /* Element type of scores, probs, dprobs and dscores.  mask, sink, p_sink,
