@@ -98,6 +98,31 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
+def attn_source_hash():
+    """sha256 over the fused attention's sources (jas_attn.hip and the
+    headers it includes, in name order), for its traffic records."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in ("jas_attn.hip", "jas_internal.h", "jas_kernels.h"):
+        h.update(name.encode())
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def load_attn_traffic(wl):
+    """HBM bytes per fused attention call (V transpose and fused kernel) from
+    the committed PMC record, or None when there is none or the sources
+    changed since."""
+    path = traffic_record_path(wl)
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("attn_source_sha256") != attn_source_hash():
+        return None
+    return int(rec["call"]["hbm_bytes_per_call"])
+
+
 def traffic_record_path(wl):
     return os.path.join(PROFILES, f"pmc_traffic_jas_{wl}.json")
 
@@ -524,9 +549,11 @@ def bench_attention(args):
         "buffer_sets": nsets,
         "roofline": {"bound": "mfma", "kernel": "jas_attn_fwd (V transpose + fused kernel)",
                      "achieved": round(ktf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(ktf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(ktf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": load_attn_traffic(wl),
                      "flops_per_launch": flops, "avg_launch_ms": round(float(ms.mean()), 4)},
         "parity": check,
+        # the copy kernel the PMC traffic records are calibrated on (1 GiB moved)
+        "copy_ceiling": copy_ceiling(1 << 30, stream),
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
@@ -626,6 +653,73 @@ def summarize_attn_profiles(prof_dir, wl):
                        f"{m['SQ_WAIT_ANY'] / m['SQ_WAVE_CYCLES']:.3f}.")
     open(os.path.join(PROFILES, f"kernel_trace_jas_{wl}.md"), "w").write("\n".join(out) + "\n")
     print("\n".join(out))
+    if os.path.isdir(os.path.join(prof_dir, "fetch")) and os.path.isdir(os.path.join(prof_dir, "write")):
+        summarize_attn_traffic(prof_dir, wl)
+
+
+def summarize_attn_traffic(prof_dir, wl):
+    """profiles/pmc_traffic_jas_<wl>.{md,json}: HBM bytes per fused attention
+    call (the V transpose and the fused kernel) from FETCH_SIZE / WRITE_SIZE,
+    calibrated on the copy kernel bench.py runs in the same process."""
+    import csv
+    desc, B, H, Hkv, S, N, D, has_mask, causal, has_sink = ATTN_WORKLOADS[wl]
+
+    def kind(name):
+        if "attn_fwd_kernel" in name:
+            return "attn"
+        if "vt_kernel" in name:
+            return "vt"
+        if "copy16<false>" in name:
+            return "copy"
+        return None
+
+    counters = {}
+    for cname, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+        for r in csv.DictReader(open(os.path.join(prof_dir, sub, f"{wl}_counter_collection.csv"))):
+            k = kind(r["Kernel_Name"])
+            if k is not None and r["Counter_Name"] == cname:
+                counters.setdefault((k, cname), []).append(float(r["Counter_Value"]) * 1024.0)
+    line = json.load(open(os.path.join(prof_dir, "fetch", "bench_line.json")))
+    copy_bytes = line["copy_ceiling"]["bytes"] / 2
+    fac = {c: copy_bytes / np.mean(counters[("copy", c)]) for c in ("FETCH_SIZE", "WRITE_SIZE")}
+    # algorithmic bytes of one call: q, k, v read and out written once each
+    alg_r = 2 * (B * H * S * D + 2 * B * Hkv * N * D)
+    alg_w = 2 * B * H * S * D
+    rec = {"workload": wl, "attn_source_sha256": attn_source_hash(),
+           "calibration": {"copy_bytes_read": copy_bytes, "copy_bytes_written": copy_bytes,
+                           "fetch_factor": round(fac["FETCH_SIZE"], 4),
+                           "write_factor": round(fac["WRITE_SIZE"], 4)},
+           "kernels": {}}
+    md = [f"# rocprofv3 HBM traffic: jas fused attention, workload {wl}", "",
+          f"Workload: {desc}.", "", "Commands (repository root):", "", "```"]
+    for c, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+        md.append(f"rocprofv3 --pmc {c} --output-format csv -d {prof_dir}/{sub} -o {wl} -- "
+                  f"python3 bench.py --workload {wl} --steps 2 --warmup 1 --no-cpu-baseline --no-check "
+                  f"--json-out {prof_dir}/{sub}/bench_line.json")
+    md += [f"python3 bench.py --workload {wl} --summarize-profiles {prof_dir}", "```", "",
+           "Counters are KiB per dispatch, scaled by what each reads for the 16-byte copy kernel of "
+           f"known size in the same process ({copy_bytes / 1e6:.1f} MB read and written): "
+           f"FETCH_SIZE x {fac['FETCH_SIZE']:.4f}, WRITE_SIZE x {fac['WRITE_SIZE']:.4f}.", "",
+           "| kernel | dispatches | HBM read MB | HBM written MB |", "|---|---|---|---|"]
+    tot_r = tot_w = 0.0
+    for k in ("vt", "attn"):
+        rd = float(np.mean(counters[(k, "FETCH_SIZE")])) * fac["FETCH_SIZE"]
+        wr = float(np.mean(counters[(k, "WRITE_SIZE")])) * fac["WRITE_SIZE"]
+        tot_r, tot_w = tot_r + rd, tot_w + wr
+        rec["kernels"][k] = {"hbm_read_bytes": int(rd), "hbm_write_bytes": int(wr)}
+        md.append(f"| {'V transpose' if k == 'vt' else 'fused attention'} | "
+                  f"{len(counters[(k, 'FETCH_SIZE')])} | {rd / 1e6:.1f} | {wr / 1e6:.1f} |")
+    rec["call"] = {"hbm_bytes_per_call": int(tot_r + tot_w), "algorithmic_bytes_per_call": alg_r + alg_w}
+    md += ["", f"Per call: {tot_r / 1e6:.1f} MB read and {tot_w / 1e6:.1f} MB written, against "
+           f"{alg_r / 1e6:.1f} MB and {alg_w / 1e6:.1f} MB of algorithmic bytes (q, k and v read once, "
+           f"out written once; mask, lse and sink values not counted): "
+           f"{(tot_r + tot_w) / (alg_r + alg_w):.3f} x.  The excess is the transposed copy of V "
+           "(written and read once) and K / V read by several XCDs.", "",
+           f"Attention source sha256 at measurement: `{rec['attn_source_sha256']}`; bench.py reports "
+           "the per-call bytes as `roofline.traffic` only while the sources still hash to it."]
+    open(os.path.join(PROFILES, f"pmc_traffic_jas_{wl}.md"), "w").write("\n".join(md) + "\n")
+    json.dump(rec, open(traffic_record_path(wl), "w"), indent=1)
+    print("\n".join(md))
 
 
 def main():
