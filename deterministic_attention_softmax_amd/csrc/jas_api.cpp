@@ -527,7 +527,9 @@ const char *jas_contract(void) {
   return "jas/1 tile=256 tree=balanced-pairwise-by-key fold=left-to-right sink=merged-last "
          "exclusion=suffix(causal,key_len) lse=M+fl(log2(L)*ln2),v_log_f32 "
          "acc=fp32 exp=2^fl(y*log2e),flush<2^-126,v_exp_f32 div=ieee cvt=rne(bf16,f16) "
-         "fpcontract=off atomics=none dsink=256-row-chunks,left-fold arch=gfx950";
+         "fpcontract=off atomics=none dsink=256-row-chunks,left-fold "
+         "attn=qk,pv:mfma_f32_16x16x32(32-per-step,ascending),s=fl(scale*dot),two-pass,"
+         "p=rne(dtype) arch=gfx950";
 }
 
 }  // extern "C"

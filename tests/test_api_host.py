@@ -38,6 +38,7 @@ def test_library_exports_every_declared_function():
 def test_contract_and_status_strings():
     c = jas.jas_contract()
     assert "tile=256" in c and "gfx950" in c and "atomics=none" in c
+    assert "attn=" in c and "two-pass" in c
     for code in range(10):
         assert jas.jas_status_str(code) and jas.jas_status_str(code) != "unknown status"
     assert jas.jas_status_str(99) == "unknown status"
