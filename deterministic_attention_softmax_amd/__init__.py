@@ -3,9 +3,9 @@ MI355X (gfx950).
 
 The C ABI (include/jas.h) is the product; this module only marshals
 arguments.  ``jas_fwd`` / ``jas_bwd`` / ``jas_fwd_ex`` / ``jas_bwd_ex`` /
-``jas_bwd_workspace_bytes`` / ``jas_status_str`` / ``jas_contract`` call the C
-functions of the same names with raw pointers.  ``fwd`` and ``bwd`` take torch
-tensors: torch provides device memory and the current stream, every step of
+``jas_bwd_workspace_bytes`` / ``jas_launch_plan`` / ``jas_status_str`` /
+``jas_contract`` call the C functions of the same names with raw pointers.
+``fwd`` and ``bwd`` take torch tensors: torch provides device memory and the current stream, every step of
 the computation runs in the library's HIP kernels.  There is no fallback: if
 ``libjas.so`` is missing the first call raises.
 """
@@ -18,7 +18,7 @@ __all__ = [
     "JAS_MAX_KEYS", "JAS_ATTN_MAX_KEYS",
     "STATUS", "JasError", "jas_desc_t", "jas_launch_t", "jas_attn_desc_t", "lib", "jas_fwd",
     "jas_fwd_ex", "jas_bwd", "jas_bwd_ex", "jas_bwd_workspace_bytes", "jas_attn_fwd",
-    "jas_attn_workspace_bytes", "jas_status_str", "jas_contract", "make_desc",
+    "jas_attn_workspace_bytes", "jas_launch_plan", "jas_status_str", "jas_contract", "make_desc",
     "make_attn_desc", "fwd", "bwd", "attn_fwd", "LIB_PATH",
 ]
 
@@ -93,6 +93,8 @@ def lib():
                                  _VP]
         L.jas_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.jas_bwd_workspace_bytes.argtypes = [_DP]
+        L.jas_launch_plan.restype = ctypes.c_int
+        L.jas_launch_plan.argtypes = [_DP, ctypes.c_int, _LP, _LP]
         L.jas_status_str.restype = ctypes.c_char_p
         L.jas_status_str.argtypes = [ctypes.c_int]
         L.jas_contract.restype = ctypes.c_char_p
@@ -135,6 +137,15 @@ def jas_bwd_ex(desc, probs, dprobs, key_len, p_sink, dscores, d_sink, workspace,
 
 def jas_bwd_workspace_bytes(desc):
     return int(lib().jas_bwd_workspace_bytes(ctypes.byref(desc)))
+
+
+def jas_launch_plan(desc, backward, launch=None):
+    """(status, jas_launch_t) of the geometry jas_fwd_ex / jas_bwd_ex would
+    launch; host only."""
+    plan = jas_launch_t()
+    lp = ctypes.byref(launch) if launch is not None else None
+    st = lib().jas_launch_plan(ctypes.byref(desc), int(backward), lp, ctypes.byref(plan))
+    return st, plan
 
 
 def jas_status_str(status):

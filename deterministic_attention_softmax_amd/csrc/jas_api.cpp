@@ -493,6 +493,26 @@ jas_status_t jas_bwd_ex(const jas_desc_t *desc, const void *probs, const void *d
                   workspace_bytes, launch, stream);
 }
 
+jas_status_t jas_launch_plan(const jas_desc_t *desc, int backward, const jas_launch_t *launch,
+                             jas_launch_t *plan) {
+  if (!plan) return JAS_ERR_NULL_POINTER;
+  *plan = jas_launch_t{0, 0, 0, 0, 0};
+  if (backward != 0 && backward != 1) return JAS_ERR_BAD_FLAGS;
+  Dims dm;
+  const jas_status_t st = check_desc(desc, &dm);
+  if (st != JAS_OK) return st;
+  if (dm.rows == 0) return JAS_OK;  // no row kernel runs
+  Geometry g;
+  const jas_status_t sg = choose_geometry(desc->dtype, dm.T, dm.rows, backward != 0, launch, &g);
+  if (sg != JAS_OK) return sg;
+  plan->waves_per_row = g.wpr;
+  plan->chunks_per_lane = g.cpl;
+  plan->rows_per_block = g.rpb;
+  plan->max_blocks = (int32_t)g.blocks;
+  plan->streaming = g.stream;
+  return JAS_OK;
+}
+
 size_t jas_attn_workspace_bytes(const jas_attn_desc_t *desc) {
   AttnDims dm;
   if (check_attn_desc(desc, &dm) != JAS_OK) return 0;

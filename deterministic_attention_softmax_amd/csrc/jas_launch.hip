@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "jas_kernels.h"
 
 namespace jas {
@@ -84,18 +86,22 @@ int default_stream_cpl(int dtype) { return dtype == 0 ? kStreamCplF32[1] : kStre
 
 // Default waves per row for a row of `nslots` wave-wide chunks (the
 // chunks-per-lane size then is the smallest compiled one that covers the
-// row).  Measured on MI355X, bf16 (fp16 is laid out the same; fp32 rows are
-// twice as many slots for the same keys and registers): the forward runs fastest with one wavefront per
-// row up to 9 slots (4,608 keys), two up to 18, four beyond; the backward,
-// which keeps two inputs in registers, with one wavefront up to 4 slots and
-// four beyond.  Any choice gives the same bits.
+// row).  Measured on MI355X, bf16 (fp16 is laid out the same; an fp32 row
+// is twice as many slots for the same keys and registers): the forward runs
+// fastest with one wavefront per row up to 9 slots (4,608 keys), two up to
+// 18, four beyond; the backward, which keeps two inputs in registers, with
+// one wavefront up to 4 slots and four beyond.  Each threshold is capped at
+// what the compiled chunk sizes cover (17 per lane for fp32), so every row
+// up to 16,384 keys has a geometry.  Any choice gives the same bits.
 int default_wpr(int dtype, int nslots, bool backward) {
-  const int u = dtype == 0 ? 2 : 1;  // slots per 16-bit-type slot of keys
-  const int cap = 4 * (dtype == 0 ? 17 : 9);
-  if (nslots > cap) return 0;
+  int n = 0;
+  const int *c = compiled_cpls(dtype, &n);
+  const int top = c[n - 1];                 // largest compiled chunks per lane
+  const int u = dtype == 0 ? 2 : 1;         // slots per 16-bit-type slot of keys
+  if (nslots > 4 * top) return 0;
   if (backward) return nslots <= 4 * u ? 1 : 4;
-  if (nslots <= 9 * u) return 1;
-  if (nslots <= 18 * u) return 2;
+  if (nslots <= std::min(9 * u, top)) return 1;
+  if (nslots <= std::min(18 * u, 2 * top)) return 2;
   return 4;
 }
 

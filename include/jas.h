@@ -221,6 +221,19 @@ jas_status_t jas_bwd_ex(const jas_desc_t *desc, const void *probs, const void *d
                         float *d_sink, void *workspace, size_t workspace_bytes,
                         const jas_launch_t *launch, void *stream);
 
+/* The row-kernel geometry jas_fwd_ex (backward = 0) or jas_bwd_ex
+ * (backward = 1) would launch for this descriptor and override (NULL =
+ * default): waves_per_row, chunks_per_lane, rows_per_block, max_blocks = the
+ * grid size, streaming = 1 for the streaming kernels.  Host only: reads no
+ * device memory and enqueues nothing.  Returns the status those calls give
+ * for the shape and override (before any pointer check); *plan is all zeros
+ * on an error and for zero rows (no row kernel runs).  JAS_ERR_NULL_POINTER
+ * for a NULL plan, JAS_ERR_BAD_FLAGS for backward outside {0, 1}.  Every
+ * geometry gives the same bits (RL-Kernel PR #453, Summary: batch-invariant
+ * order). */
+jas_status_t jas_launch_plan(const jas_desc_t *desc, int backward, const jas_launch_t *launch,
+                             jas_launch_t *plan);
+
 /* ------------------------------------------------------------------------
  * Fused attention forward: scores = scale * Q K^T on the matrix cores, the
  * row softmax above on those binary32 scores (bit for bit what jas_fwd

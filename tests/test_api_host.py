@@ -226,3 +226,45 @@ def test_attention_validation():
     L = jas.lib()
     assert L.jas_attn_fwd(None, A, B_, C, None, None, None, D, None, None, None, None, E, 0,
                           None) == 1
+
+
+def _plan_covers(d, backward):
+    st, p = jas.jas_launch_plan(d, backward)
+    assert st == 0, (d.keys, d.dtype, backward, jas.STATUS.get(st, st))
+    if p.streaming:
+        assert d.keys > 16384 and p.waves_per_row == 4 and p.rows_per_block == 1
+        return p
+    kps = 256 if d.dtype == jas.JAS_DTYPE_F32 else 512          # keys per 64-lane slot
+    assert p.waves_per_row in (1, 2, 4) and p.waves_per_row * p.rows_per_block <= 4
+    assert p.waves_per_row * p.chunks_per_lane * kps >= d.keys, (d.keys, d.dtype, p.waves_per_row,
+                                                                 p.chunks_per_lane)
+    return p
+
+
+@pytest.mark.parametrize("dtype", [jas.JAS_DTYPE_F32, jas.JAS_DTYPE_BF16, jas.JAS_DTYPE_F16])
+def test_default_geometry_exists_for_every_row_length(dtype):
+    # every row length up to the one-pass limit, and a sample beyond it, gets
+    # a default geometry that holds the row, forward and backward (an fp32
+    # row of 4,353 to 4,608 keys once had none)
+    for N in list(range(1, 16385)) + [16385, 20000, 65536, 262143, 262144]:
+        for backward in (0, 1):
+            _plan_covers(desc(B=1, H=1, S=1, N=N, dtype=dtype), backward)
+    st, _ = jas.jas_launch_plan(desc(N=262145, dtype=dtype), 0)
+    assert jas.STATUS.get(st) == "JAS_ERR_UNSUPPORTED"
+
+
+def test_launch_plan_reports_overrides_and_errors():
+    d = desc(B=2, H=3, S=5, N=1000, dtype=jas.JAS_DTYPE_BF16)
+    st, p = jas.jas_launch_plan(d, 0, jas._launch((2, 1, 2, 0, 0)))
+    assert st == 0 and (p.waves_per_row, p.chunks_per_lane, p.rows_per_block) == (2, 1, 2)
+    assert p.max_blocks == (30 + 1) // 2 and p.streaming == 0
+    st, p = jas.jas_launch_plan(d, 1, jas._launch((0, 0, 0, 4, 1)))
+    assert st == 0 and p.streaming == 1 and p.max_blocks == 4 and p.waves_per_row == 4
+    st, p = jas.jas_launch_plan(d, 0, jas._launch((1, 1, 0, 0, 0)))   # 1 x 1 slot < 1000 keys
+    assert jas.STATUS.get(st) == "JAS_ERR_UNSUPPORTED"
+    assert (p.waves_per_row, p.chunks_per_lane, p.max_blocks) == (0, 0, 0)
+    st, p = jas.jas_launch_plan(d, 2)
+    assert jas.STATUS.get(st) == "JAS_ERR_BAD_FLAGS"
+    st, p = jas.jas_launch_plan(desc(B=0), 0)                          # no rows: no launch
+    assert st == 0 and p.max_blocks == 0
+    assert jas.lib().jas_launch_plan(ctypes.byref(d), 0, None, None) == 1

@@ -13,9 +13,13 @@ ascending one, so:
   * P (written on request) is, byte for byte, jas_fwd of the kernel's own
     scores rounded to the dtype -- the softmax inside the fused kernel is the
     library's; lse and p_sink likewise;
-  * the output is within eps * (sum_j P_j |v_j| + |out|) of the oracle's,
-    eps = 2^-8 (bf16) or 2^-11 (fp16): a score difference can move a P_j
-    across a rounding boundary of the dtype.
+  * the output is P.V of the kernel's own P within the binary32 sum's
+    bound and one rounding;
+  * the output is within a bound built from its sources of the oracle's:
+    both sides round each p_j to the dtype once (u = 2^-8 bf16, 2^-11 fp16;
+    a score difference can move a p_j across a rounding boundary on one side
+    only, so 2u), the score and mask-add differences, both binary32 sums,
+    fp16 subnormals, and the output's own rounding.
 Invariance: a query's bytes do not depend on the batch or on its block.
 """
 import numpy as np
@@ -25,7 +29,7 @@ import torch
 import deterministic_attention_softmax_amd as jas
 import oracle
 import synth
-from tests.gpu_util import assert_lse_close, dev, log
+from tests.gpu_util import F32_ATOL, F32_RTOL, assert_lse_close, dev, log
 
 pytestmark = pytest.mark.gpu
 U = 2.0 ** -24
@@ -82,18 +86,46 @@ def check(q, k, v, scale, mask=None, mask_strides=None, sink=None, causal=False,
     if sink is not None:
         assert r["p_sink"].cpu().numpy().tobytes() == psf.cpu().numpy().tobytes()
     assert_lse_close(r["lse"].cpu().numpy(), o["lse"], "lse vs oracle")
-    # the output against the oracle's
-    eps = 2.0 ** -8 if dt == torch.bfloat16 else 2.0 ** -11
-    Po = f64(o["probs"])
-    mass = np.zeros((B, H, Sq, D))
+    # the output: the P.V of the kernel's own P, and the oracle's output
+    u = 2.0 ** -8 if dt == torch.bfloat16 else 2.0 ** -11      # unit roundoff of the dtype
+    # absolute error per rounded p_j: half the dtype's least subnormal (fp16),
+    # or the binary32 softmax's absolute floor near its flush point (bf16)
+    eta = F32_ATOL if dt == torch.bfloat16 else 2.0 ** -25
+    Pg, Po = f64(synth.to_numpy_bits(r["probs"])), f64(o["probs"])
+    mass_g, mass_o, exact_g = (np.zeros((B, H, Sq, D)) for _ in range(3))
+    sum_v = np.zeros((B, H, 1, D))
     for b in range(B):
         for h in range(H):
-            mass[b, h] = Po[b, h] @ np.abs(vf[b, h // g])
+            va = np.abs(vf[b, h // g])
+            mass_g[b, h], mass_o[b, h] = Pg[b, h] @ va, Po[b, h] @ va
+            exact_g[b, h] = Pg[b, h] @ vf[b, h // g]
+            sum_v[b, h, 0] = va.sum(axis=0)
     got = f64(synth.to_numpy_bits(r["out"]))
     want = f64(o["out"])
-    lim = eps * (mass + np.abs(want)) + 1e-30
+    # binary32 sums of exact products: n additions in sequence err by at most
+    # gamma_n = n*U/(1 - n*U) of the sum of magnitudes; the matrix cores add
+    # 32-key steps to one accumulator (n <= N/32 + 32), the oracle key by key
+    n_g = -(-N // 32) + 32
+    gam_g, gam_o = n_g * U / (1 - n_g * U), N * U / (1 - N * U)
+    lim_g = u * np.abs(got) * (1 + 2 * u) + gam_g * mass_g + 2 * eta
+    bad = np.count_nonzero(~(np.abs(got - exact_g) <= lim_g))
+    assert bad == 0, f"out is not P.V of the kernel's P: {bad} elements"
+    # against the oracle.  Each side rounds its binary32 p_j to the dtype once
+    # (|fl(p) - p| <= u*p + eta), so a score difference can move one p_j across
+    # a rounding boundary on one side only: |P_g - P_o| <= 2u*p + 2*eta +
+    # |p_g - p_o|.  The two binary32 p_j differ by the softmax's own agreement
+    # with the oracle on equal inputs (F32_RTOL, the fp32 softmax bound)
+    # and by exp(2*dx) - 1, dx the row's largest difference of s_j + mask_j
+    # (the score bound above plus one rounding of the mask add on each side).
+    mmax = 0.0 if mask is None else float(np.max(np.abs(np.nan_to_num(
+        mask.numpy(), neginf=0.0)), initial=0.0))
+    dx = (D + 4) * U * absS.max(axis=3, keepdims=True) + 2 * U * mmax
+    rel_p = F32_RTOL + np.expm1(2 * dx)
+    lim = (u * (np.abs(got) + np.abs(want)) * (1 + 2 * u)
+           + (2 * u + rel_p + gam_g + gam_o) * (1 + 4 * u) * mass_o
+           + 4 * eta * sum_v + 2 * eta)
     bad = np.count_nonzero(~(np.abs(got - want) <= lim))
-    assert bad == 0, f"out: {bad} elements outside tolerance"
+    assert bad == 0, f"out: {bad} elements outside tolerance, worst {np.max(np.abs(got - want) / lim)}"
     return r
 
 

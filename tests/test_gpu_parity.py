@@ -83,6 +83,18 @@ def test_row_lengths(N, dt):
     run_fwd_bwd_full(s, g, sink=sink)
 
 
+@pytest.mark.parametrize("N", [4353, 4374, 4522, 4608, 8705, 9169, 9196, 9216])
+def test_fp32_rows_at_the_chunk_size_limits(N):
+    # fp32 rows of 18 and of 35 to 36 tiles: one or two wavefronts' largest
+    # compiled register share (17 chunks per lane) no longer holds the row,
+    # so the default geometry takes more wavefronts per row
+    log(f"fp32 N={N} at the chunk-size limits")
+    s = synth.normal((1, 2, 3, N), 3.0, N, "cpu", torch.float32)
+    g = synth.normal((1, 2, 3, N), 1.0, N + 1, "cpu", torch.float32)
+    sink = synth.normal((2,), 1.0, N + 2, "cpu")
+    run_fwd_bwd_full(s, g, sink=sink)
+
+
 def test_rows_16384x4352_forward_all_rows():
     # bf16 [1,1,16384,4352], N(0,1) scaled by sqrt(128) then 1/sqrt(128), x8 on 0.1%
     log("bf16 16384 x 4352 forward, all rows")
