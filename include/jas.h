@@ -1,6 +1,7 @@
 /*
  * jas.h -- fixed-order, batch-invariant row softmax for AMD Instinct MI355X
- * (gfx950): forward, backward, optional per-head sink.
+ * (gfx950): forward, backward, optional per-head sink, and a fused attention
+ * forward built on the same softmax.
  *
  * What the library computes (the pages it follows):
  *   - RL-Kernel PR #453, "[WS1][kernels] Add fixed-order joint-attention
