@@ -151,6 +151,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target wall time of the CPU oracle sample")
+    ap.add_argument("--attn-query-blocks", type=int, default=0, choices=(0, 1, 2),
+                    help="fused attention: 16-query blocks per wavefront (0 = library default)")
     ap.add_argument("--json-out", metavar="PATH", help="also write the result line to PATH")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="summarise rocprofv3 output under DIR (trace/, fetch/, write/) into profiles/")
@@ -495,7 +497,8 @@ def bench_attention(args):
         nstep[0] += 1
         return jas.attn_fwd(qi, ki, vi, scale=scale, mask=mask,
                             mask_strides=None if mask is None else (N, 0, 0), sink=sink,
-                            causal=causal, want_lse=True, out=oi, workspace=wi)
+                            causal=causal, want_lse=True, out=oi, workspace=wi,
+                            query_blocks=args.attn_query_blocks)
 
     check = None
     if not args.no_check:
@@ -545,7 +548,8 @@ def bench_attention(args):
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": desc, "batch": B, "heads": H, "kv_heads": Hkv, "q_len": S,
                    "kv_len": N, "head_dim": D, "mask": has_mask, "causal": causal,
-                   "sink": has_sink, "useful_flops": flops},
+                   "sink": has_sink, "useful_flops": flops,
+                   "query_blocks_per_wave": args.attn_query_blocks or "library default"},
         "buffer_sets": nsets,
         "roofline": {"bound": "mfma", "kernel": "jas_attn_fwd (V transpose + fused kernel)",
                      "achieved": round(ktf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

@@ -17,7 +17,7 @@ __all__ = [
     "JAS_FLAG_CAUSAL", "JAS_FLAG_KEY_LEN", "JAS_FLAG_LSE", "JAS_FLAG_PROBS", "JAS_FLAG_SCORES",
     "JAS_MAX_KEYS", "JAS_ATTN_MAX_KEYS",
     "STATUS", "JasError", "jas_desc_t", "jas_launch_t", "jas_attn_desc_t", "lib", "jas_fwd",
-    "jas_fwd_ex", "jas_bwd", "jas_bwd_ex", "jas_bwd_workspace_bytes", "jas_attn_fwd",
+    "jas_fwd_ex", "jas_bwd", "jas_bwd_ex", "jas_bwd_workspace_bytes", "jas_attn_fwd", "jas_attn_fwd_ex",
     "jas_attn_workspace_bytes", "jas_launch_plan", "jas_status_str", "jas_contract", "make_desc",
     "make_attn_desc", "fwd", "bwd", "attn_fwd", "LIB_PATH",
 ]
@@ -105,6 +105,9 @@ def lib():
         L.jas_attn_fwd.restype = ctypes.c_int
         L.jas_attn_fwd.argtypes = [_AP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                    ctypes.c_size_t, _VP]
+        L.jas_attn_fwd_ex.restype = ctypes.c_int
+        L.jas_attn_fwd_ex.argtypes = [_AP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                      _VP, ctypes.c_size_t, ctypes.c_int, _VP]
         _lib = L
     return _lib
 
@@ -360,6 +363,13 @@ def jas_attn_fwd(desc, q, k, v, mask, key_len, sink, out, lse, p_sink, probs, sc
                               probs, scores, workspace, workspace_bytes, stream)
 
 
+def jas_attn_fwd_ex(desc, q, k, v, mask, key_len, sink, out, lse, p_sink, probs, scores,
+                    workspace, workspace_bytes, query_blocks, stream):
+    return lib().jas_attn_fwd_ex(ctypes.byref(desc), q, k, v, mask, key_len, sink, out, lse,
+                                 p_sink, probs, scores, workspace, workspace_bytes, query_blocks,
+                                 stream)
+
+
 def _attn_tensor(t, name, like=None):
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be in device memory, not on {t.device}")
@@ -372,12 +382,14 @@ def _attn_tensor(t, name, like=None):
 
 def attn_fwd(q, k, v, scale=None, mask=None, mask_strides=None, sink=None, causal=False,
              key_len=None, want_lse=False, want_probs=False, want_scores=False, out=None,
-             workspace=None):
+             workspace=None, query_blocks=0):
     """Fused attention forward on device tensors: q [B, H, Sq, D], k and v
     [B, Hkv, N, D] (bf16 or fp16, contiguous), ``scale`` (default
     1/sqrt(D)).  Mask, sink, causal and key lengths as for :func:`fwd`.
     Returns a dict with ``out`` and, when asked (or a sink is given),
-    ``lse``, ``p_sink``, ``probs``, ``scores``."""
+    ``lse``, ``p_sink``, ``probs``, ``scores``.  ``query_blocks`` (0, 1 or 2)
+    is the launch's 16-query blocks per wavefront, 0 = the library's choice;
+    it never changes the results."""
     import math
     import torch
     _attn_tensor(q, "q")
@@ -432,9 +444,9 @@ def attn_fwd(q, k, v, scale=None, mask=None, mask_strides=None, sink=None, causa
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     _check_vec(workspace, q, torch.uint8, ws_bytes, "workspace")
-    st = _on_device(q, jas_attn_fwd, d, _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(key_len),
+    st = _on_device(q, jas_attn_fwd_ex, d, _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(key_len),
                     _ptr(sink), _ptr(out), _ptr(res["lse"]), _ptr(res["p_sink"]), _ptr(res["probs"]),
-                    _ptr(res["scores"]), _ptr(workspace), workspace.numel())
+                    _ptr(res["scores"]), _ptr(workspace), workspace.numel(), int(query_blocks))
     if st != 0:
         raise JasError(st, "jas_attn_fwd")
     return res

@@ -366,10 +366,11 @@ jas_status_t check_attn_desc(const jas_attn_desc_t *d, AttnDims *dm) {
 jas_status_t attn_fwd_impl(const jas_attn_desc_t *d, const void *q, const void *k, const void *v,
                            const float *mask, const int32_t *key_len, const float *sink,
                            void *out, float *lse, float *p_sink, void *probs, float *scores,
-                           void *ws, size_t ws_bytes, void *stream) {
+                           void *ws, size_t ws_bytes, int query_blocks, void *stream) {
   AttnDims dm;
   jas_status_t st = check_attn_desc(d, &dm);
   if (st != JAS_OK) return st;
+  if (query_blocks < 0 || query_blocks > 2) return JAS_ERR_BAD_FLAGS;
   const uint32_t f = d->flags;
   const bool has_mask = f & JAS_FLAG_MASK, has_sink = f & JAS_FLAG_SINK,
              has_klen = f & JAS_FLAG_KEY_LEN, has_lse = f & JAS_FLAG_LSE,
@@ -446,10 +447,8 @@ jas_status_t attn_fwd_impl(const jas_attn_desc_t *d, const void *q, const void *
   a.D = (int)D;
   a.T = dm.T;
   a.Np = (int)dm.Np;
-  // one workgroup (4 waves of 16 queries) per 64 queries of a (batch, head)
-  int64_t blocks = d->batch * d->heads * ((d->q_len + 63) / 64);
-  if (blocks > 0x7fffffff) blocks = 0x7fffffff;
-  if (jas::launch_attn_fwd(d->dtype, a, blocks, (hipStream_t)stream) != hipSuccess)
+  // one workgroup of 4 waves per 64 * query_blocks queries of a (batch, head)
+  if (jas::launch_attn_fwd(d->dtype, a, query_blocks, (hipStream_t)stream) != hipSuccess)
     return JAS_ERR_HIP;
   return JAS_OK;
 }
@@ -524,7 +523,16 @@ jas_status_t jas_attn_fwd(const jas_attn_desc_t *desc, const void *q, const void
                           const float *sink, void *out, float *lse, float *p_sink, void *probs,
                           float *scores, void *workspace, size_t workspace_bytes, void *stream) {
   return attn_fwd_impl(desc, q, k, v, mask, key_len, sink, out, lse, p_sink, probs, scores,
-                       workspace, workspace_bytes, stream);
+                       workspace, workspace_bytes, 0, stream);
+}
+
+jas_status_t jas_attn_fwd_ex(const jas_attn_desc_t *desc, const void *q, const void *k,
+                             const void *v, const float *mask, const int32_t *key_len,
+                             const float *sink, void *out, float *lse, float *p_sink, void *probs,
+                             float *scores, void *workspace, size_t workspace_bytes,
+                             int query_blocks, void *stream) {
+  return attn_fwd_impl(desc, q, k, v, mask, key_len, sink, out, lse, p_sink, probs, scores,
+                       workspace, workspace_bytes, query_blocks, stream);
 }
 
 const char *jas_status_str(jas_status_t s) {

@@ -7,12 +7,15 @@
 // element has one writer; the head dimension and the keys are accumulated
 // in a fixed order, with no split of the key range).
 //
-// Mapping to CDNA4.  A workgroup of 4 waves owns 64 queries of one
-// (batch, head), each wave 16 of them.  Scores are computed transposed,
-// S^T = K Q^T, with v_mfma_f32_16x16x32 (bf16 or fp16): A = 16 keys x 32
-// dims of K, B = 32 dims x 16 queries of Q (kept in registers for the whole
-// row), so lane l holds, for query l%16, four consecutive keys of a 16-key
-// block.  Keys go through the workgroup 32 at a time: K (32 keys x D) and
+// Mapping to CDNA4.  A workgroup of 4 waves owns 64 or 128 queries of one
+// (batch, head), each wave one or two blocks of 16 (QB).  Scores are
+// computed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32 (bf16 or
+// fp16): A = 16 keys x 32 dims of K, B = 32 dims x 16 queries of Q (kept in
+// registers for the whole row), so lane l holds, for query l%16 of a block,
+// four consecutive keys of a 16-key block.  With two query blocks every K
+// operand read from LDS (and every V^T operand in the PV product) feeds two
+// MFMAs, which halves the LDS bytes per product, the limit of the one-block
+// kernel.  Keys go through the workgroup 32 at a time: K (32 keys x D) and
 // the transposed V (D x 32 keys) are loaded with coalesced 16-byte loads
 // into double-buffered LDS, K two steps and V one step ahead of use, and
 // each step issues the next step's QK product before its own softmax work
@@ -105,13 +108,19 @@ __device__ __forceinline__ int64_t xcd_unit(int64_t bid, int64_t G) {
 }
 
 // MASK: an additive mask is given; WRITE: the scores and / or P are written
-// out as well (for checking), which the fast path does not carry.
-template <int DT, int D, bool MASK, bool WRITE>
+// out as well (for checking), which the fast path does not carry.  QB: blocks
+// of 16 queries per wave.  With QB = 2 each K and V^T operand read from LDS
+// feeds two MFMAs, one per query block, which halves the LDS bytes per
+// product.  Every query goes through the same operations, in the same order,
+// whatever QB is, so QB never changes a bit of the results.
+template <int DT, int D, bool MASK, bool WRITE, int QB>
 __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const AttnArgs a) {
   constexpr int ESZ = 2;
   constexpr int DS = D / 32;       // k-steps of the QK product
   constexpr int DB = D / 16;       // 16-dim column blocks of the output
   constexpr int SUB = 32;          // keys per staged sub-tile (one PV k-step)
+  constexpr int QW = 16 * QB;      // queries per wave
+  constexpr int QU = QW * kAttnWaves;  // queries per workgroup
   // LDS rows: a 16-byte read by each lane of 16 rows (lane groups 16 bytes
   // apart) is free of bank conflicts on gfx950 when the row stride is 32
   // modulo 64 bytes (measured; strides 16 modulo 32 bytes cost 4 extra
@@ -123,18 +132,18 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
   static_assert(KCH >= 1 && VCH >= 1, "sub-tile smaller than the workgroup");
   __shared__ __align__(16) uint16_t lk[2][SUB * KROW];
   __shared__ __align__(16) uint16_t lv[2][D * VROW];
-  extern __shared__ float lds_m[];  // per wave T x 16 tile maxima (sized at launch)
+  extern __shared__ float lds_m[];  // per wave T x QW tile maxima (sized at launch)
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int c16 = lane & 15;  // the lane's query (S^T column) and A/B operand row
+  const int c16 = lane & 15;  // the lane's query in each block (S^T column) and A/B operand row
   const int g = lane >> 4;    // lane group: keys 8g .. 8g+7 of each 32-key step
-  const int N = (int)a.N, T = a.T, Np = a.Np;
+  const int N = (int)a.N, T = a.T;
   const int Sq = (int)a.Sq;
-  const int64_t qgroups = (a.Sq + 63) / 64;  // 64 queries per workgroup
+  const int64_t qgroups = (a.Sq + QU - 1) / QU;  // QU queries per workgroup
   const int64_t units = a.B * a.H * qgroups;
-  float *sm = lds_m + w * a.T * 16;
+  float *sm = lds_m + w * a.T * QW;
   const bool has_sink = a.sink != nullptr;
   constexpr bool write_all = WRITE;
 
@@ -144,37 +153,62 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
     const int64_t qg = a.ex.causal ? qgroups - 1 - u % qgroups : u % qgroups, bh = u / qgroups;
     const int64_t h = bh % a.H, b = bh / a.H;
     const int64_t hk = h / (a.H / a.Hkv);
-    const int q0 = (int)(qg * 64) + 16 * w;  // this wave's 16 queries
-    const int q = q0 + c16;                  // this lane's query
-    const bool qvalid = q < Sq;
-    const int64_t row = bh * a.Sq + (qvalid ? q : Sq - 1);
+    const int qw = (int)(qg * QU) + QW * w;  // this wave's first query; block qb starts at qw + 16qb
+    int qq[QB];                              // this lane's query in each block
+    bool qvalid[QB];
+    int64_t row[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      qq[qb] = qw + 16 * qb + c16;
+      qvalid[qb] = qq[qb] < Sq;
+      row[qb] = bh * a.Sq + (qvalid[qb] ? qq[qb] : Sq - 1);
+    }
 
-    const Buf qbuf(static_cast<const char *>(a.q) + bh * a.Sq * D * ESZ, (uint32_t)(a.Sq * D * ESZ));
     const Buf kbuf(static_cast<const char *>(a.k) + (b * a.Hkv + hk) * a.N * D * ESZ,
                    (uint32_t)(a.N * D * ESZ));
-    const Buf vbuf(static_cast<const char *>(a.vt) + (b * a.Hkv + hk) * (int64_t)D * Np * ESZ,
-                   (uint32_t)((int64_t)D * Np * ESZ));
+    const Buf vbuf(static_cast<const char *>(a.vt) + (b * a.Hkv + hk) * (int64_t)D * a.Np * ESZ,
+                   (uint32_t)((int64_t)D * a.Np * ESZ));
 
-    // Q^T operand (B of the QK product): query q0 + c16, dims 32ds + 8g .. +7
-    u32x4 qv[DS];
+    // Q^T operand of block qb (B of the QK product): query qw + 16qb + c16,
+    // dims 32ds + 8g .. +7.  The block's buffer ends at the last query, so
+    // the lanes of queries past it read 0 through their own offsets.
+    u32x4 qv[QB][DS];
 #pragma unroll
-    for (int ds = 0; ds < DS; ++ds)
-      qv[ds] = bload4(qbuf, (uint32_t)((c16 * D + 8 * g) * ESZ), (uint32_t)((q0 * D + ds * 32) * ESZ));
+    for (int qb = 0; qb < QB; ++qb) {
+      const int q0 = qw + 16 * qb;
+      const int nq = Sq - q0 < 0 ? 0 : (Sq - q0 > 16 ? 16 : Sq - q0);
+      const Buf qbuf(static_cast<const char *>(a.q) + (bh * a.Sq + q0) * D * ESZ,
+                     (uint32_t)(nq * D * ESZ));
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds)
+        qv[qb][ds] = bload4(qbuf, (uint32_t)((c16 * D + 8 * g) * ESZ), (uint32_t)(ds * 32 * ESZ));
+    }
 
-    // visible keys of the lane's query, and of the workgroup's last query
-    int64_t ke = N, km = N;
+    // visible keys of the lane's queries, and of the workgroup's last query
+    int kend[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      int64_t ke = N;
+      if (a.ex.causal) {
+        const int64_t off = (int64_t)N - Sq + 1;
+        ke = (qq[qb] + off < ke) ? qq[qb] + off : ke;
+      }
+      if (a.ex.key_len) {
+        const int64_t l = a.ex.key_len[b];
+        ke = l < ke ? l : ke;
+      }
+      kend[qb] = (int)(ke < 0 ? 0 : ke);
+    }
+    int64_t km = N;
     if (a.ex.causal) {
       const int64_t off = (int64_t)N - Sq + 1;
-      ke = (q + off < ke) ? q + off : ke;
-      const int64_t qlast = (qg * 64 + 63 < Sq) ? qg * 64 + 63 : Sq - 1;
+      const int64_t qlast = (qg * QU + QU - 1 < Sq) ? qg * QU + QU - 1 : Sq - 1;
       km = (qlast + off < km) ? qlast + off : km;
     }
     if (a.ex.key_len) {
       const int64_t l = a.ex.key_len[b];
-      ke = l < ke ? l : ke;
       km = l < km ? l : km;
     }
-    const int kend = (int)(ke < 0 ? 0 : ke);
     int kmax = __builtin_amdgcn_readfirstlane((int)(km < 0 ? 0 : km));
     if (write_all) kmax = N;
     const int tlive = (kmax + kTile - 1) / kTile;  // tiles holding a visible key (same in all waves)
@@ -182,7 +216,7 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
     int64_t kn = N;
     if (a.ex.causal) {
       const int64_t off = (int64_t)N - Sq + 1;
-      kn = (qg * 64 + off < kn) ? qg * 64 + off : kn;
+      kn = (qg * QU + off < kn) ? qg * QU + off : kn;
     }
     if (a.ex.key_len) {
       const int64_t l = a.ex.key_len[b];
@@ -191,12 +225,14 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
     const int kmin = __builtin_amdgcn_readfirstlane((int)(kn < 0 ? 0 : kn));
     // the mask of (b, h) as one buffer: the lane's row at q * msq, keys at
     // +key; the buffer ends with the last row's key N - 1, so keys past N of
-    // the last row read 0 (they are cut anyway)
+    // the last row read 0 (they are cut anyway).  With QB > 1 the launch
+    // guarantees msq == 0 (one mask row for all queries of the head), so the
+    // query blocks share the mask registers.
     Buf mbuf(nullptr, 0u);
     uint32_t moff = 0;
     if constexpr (MASK) {
       mbuf = Buf(a.mask + b * a.msb + h * a.msh, (uint32_t)((((int64_t)Sq - 1) * a.msq + N) * 4));
-      moff = (uint32_t)((int64_t)(qvalid ? q : Sq - 1) * a.msq * 4) + 32u * (uint32_t)g;
+      moff = (uint32_t)((int64_t)(qvalid[0] ? qq[0] : Sq - 1) * a.msq * 4) + 32u * (uint32_t)g;
     }
 
     // ---- staging: sub-tile `it` (keys 32*it .. +31) of K, and of V^T ----
@@ -225,7 +261,7 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
       for (int c = 0; c < VCH; ++c) {
         const int ch = tid + c * kWave * kAttnWaves;
         const int d = ch / (SUB / 8), k8 = ch % (SUB / 8);
-        pv[c] = bload4(vbuf, (uint32_t)((d * Np + 8 * k8) * ESZ), (uint32_t)(SUB * it * ESZ));
+        pv[c] = bload4(vbuf, (uint32_t)((d * a.Np + 8 * k8) * ESZ), (uint32_t)(SUB * it * ESZ));
       }
     };
     auto put_v = [&](int buf) {
@@ -236,18 +272,25 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
         *reinterpret_cast<u32x4 *>(&lv[buf][d * VROW + 8 * k8]) = pv[c];
       }
     };
-    // S^T of sub-tile it from LDS buffer buf: blocks hb = 0, 1 (keys
-    // 32it + 8(c16/4) + 4hb + c16%4 as A rows, LDS rows 16hb + c16), raw dot
-    // products
-    auto qk_sub = [&](int buf, f32x4_t &s0, f32x4_t &s1) {
-      s0 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-      s1 = s0;
+    // S^T of sub-tile it from LDS buffer buf for every query block: key
+    // blocks hb = 0, 1 (keys 32it + 8(c16/4) + 4hb + c16%4 as A rows, LDS
+    // rows 16hb + c16), raw dot products.  Each A operand read feeds the
+    // MFMAs of all QB query blocks.
+    auto qk_sub = [&](int buf, f32x4_t (&s0)[QB], f32x4_t (&s1)[QB]) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        s0[qb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        s1[qb] = s0[qb];
+      }
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds) {
         const u32x4 k0 = *reinterpret_cast<const u32x4 *>(&lk[buf][c16 * KROW + 32 * ds + 8 * g]);
         const u32x4 k1 = *reinterpret_cast<const u32x4 *>(&lk[buf][(16 + c16) * KROW + 32 * ds + 8 * g]);
-        s0 = mfma32<DT>(k0, qv[ds], s0);
-        s1 = mfma32<DT>(k1, qv[ds], s1);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          s0[qb] = mfma32<DT>(k0, qv[qb][ds], s0[qb]);
+          s1[qb] = mfma32<DT>(k1, qv[qb][ds], s1[qb]);
+        }
       }
     };
     // the mask of the lane's 8 keys 32it + 8g .. +7: two 16-byte loads, the
@@ -259,14 +302,15 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
       }
     };
     // scaled, masked and cut scores of the lane's 8 keys 32it + 8g + 4hb + r
-    auto make_x = [&](int it, const f32x4_t &s0, const f32x4_t &s1, const u32x4 (&mk)[2],
+    // for query block qb
+    auto make_x = [&](int it, int qb, const f32x4_t &s0, const f32x4_t &s1, const u32x4 (&mk)[2],
                       float (&x)[8]) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float s = a.scale * ((e < 4) ? s0[e] : s1[e - 4]);
         if constexpr (WRITE) {
           const int key = SUB * it + 8 * g + e;
-          if (a.scores && qvalid && key < N) a.scores[row * a.N + key] = s;
+          if (a.scores && qvalid[qb] && key < N) a.scores[row[qb] * a.N + key] = s;
         }
         x[e] = s;
         if constexpr (MASK) {
@@ -277,7 +321,7 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
         }
       }
       if (SUB * it + SUB > kmin) {  // the step reaches some query's cut (uniform)
-        const int nv = kend - (SUB * it + 8 * g);
+        const int nv = kend[qb] - (SUB * it + 8 * g);
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = (e < nv) ? x[e] : kNegInf;
       }
@@ -291,8 +335,13 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
     // overlap.  K sub-tile it + 2 is loaded into registers at the start of
     // step it and written to the LDS buffer of sub-tile it (read by every
     // wave in step it - 1) before the step's barrier.
-    float M = kNegInf, L = 0.0f;
-    f32x4_t sa[2], sb[2];  // raw S^T of a step (blocks 0 and 1), by step parity
+    float M[QB], L[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      M[qb] = kNegInf;
+      L[qb] = 0.0f;
+    }
+    f32x4_t sa[2][QB], sb[2][QB];  // raw S^T of a step (key blocks 0 and 1), by step parity
     u32x4 mk[2][2];
     if (tlive > 0) {
       fetch_k(0);
@@ -305,7 +354,7 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
       __syncthreads();  // every wave has read sub-tile 0 before step 0 overwrites it
     }
     for (int t = 0; t < tlive; ++t) {
-      float x[8][8];  // [32-key step j][key 8g + e]
+      float x[QB][8][8];  // [query block][32-key step j][key 8g + e]
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int it = 8 * t + j;
@@ -313,71 +362,80 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
         fetch_k(it + 2);
         load_mask(it + 1, mk[nxt]);
         qk_sub(nxt, sa[nxt], sb[nxt]);
-        make_x(it, sa[cur], sb[cur], mk[cur], x[j]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) make_x(it, qb, sa[cur][qb], sb[cur][qb], mk[cur], x[qb][j]);
         put_k(cur);
         __syncthreads();
       }
-      float mx = kNegInf;
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = kNegInf;
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) mx = fmax2(mx, fmax2(x[j][e], x[j][e + 1]));
-      const float m = groups4_max(mx);
-      const float msafe = (m == kNegInf) ? 0.0f : m;
-      float pj[8];
+        for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float e8[8];
+          for (int e = 0; e < 8; e += 2) mx = fmax2(mx, fmax2(x[qb][j][e], x[qb][j][e + 1]));
+        const float m = groups4_max(mx);
+        const float msafe = (m == kNegInf) ? 0.0f : m;
+        float pj[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) e8[e] = exp_(x[j][e] - msafe);
-        const float s0 = (e8[0] + e8[1]) + (e8[2] + e8[3]);
-        const float s1 = (e8[4] + e8[5]) + (e8[6] + e8[7]);
-        pj[j] = groups4_sum(s0 + s1);  // the step's 32 keys
-      }
-      const float l = ((pj[0] + pj[1]) + (pj[2] + pj[3])) + ((pj[4] + pj[5]) + (pj[6] + pj[7]));
-      if (g == 0) sm[t * 16 + c16] = m;
-      // merge (m, l) into the row state
-      const float Mn = fmax2(M, m);
-      if (Mn == kNegInf) {
-        M = kNegInf;
-        L = 0.0f;
-      } else {
-        const float fa = (M == kNegInf) ? 0.0f : exp_(M - Mn);
-        const float fb = (m == kNegInf) ? 0.0f : exp_(m - Mn);
-        const float La = L * fa;
-        const float lb = l * fb;
-        L = La + lb;
-        M = Mn;
+        for (int j = 0; j < 8; ++j) {
+          float e8[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) e8[e] = exp_(x[qb][j][e] - msafe);
+          const float s0 = (e8[0] + e8[1]) + (e8[2] + e8[3]);
+          const float s1 = (e8[4] + e8[5]) + (e8[6] + e8[7]);
+          pj[j] = groups4_sum(s0 + s1);  // the step's 32 keys
+        }
+        const float l = ((pj[0] + pj[1]) + (pj[2] + pj[3])) + ((pj[4] + pj[5]) + (pj[6] + pj[7]));
+        if (g == 0) sm[t * QW + 16 * qb + c16] = m;
+        // merge (m, l) into the row state
+        const float Mn = fmax2(M[qb], m);
+        if (Mn == kNegInf) {
+          M[qb] = kNegInf;
+          L[qb] = 0.0f;
+        } else {
+          const float fa = (M[qb] == kNegInf) ? 0.0f : exp_(M[qb] - Mn);
+          const float fb = (m == kNegInf) ? 0.0f : exp_(m - Mn);
+          const float La = L[qb] * fa;
+          const float lb = l * fb;
+          L[qb] = La + lb;
+          M[qb] = Mn;
+        }
       }
     }
     // tiles past every visible key of the workgroup hold only -inf: (-inf, 0)
     // states, which leave (M, L) as they are
-    float sigma = 0.0f;
-    if (has_sink) {
-      sigma = a.sink[h];
-      const float Mn = fmax2(M, sigma);
-      if (Mn == kNegInf) {
-        M = kNegInf;
-        L = 0.0f;
-      } else {
-        const float fa = (M == kNegInf) ? 0.0f : exp_(M - Mn);
-        const float fb = (sigma == kNegInf) ? 0.0f : exp_(sigma - Mn);
-        const float La = L * fa;
-        const float lb = 1.0f * fb;
-        L = La + lb;
-        M = Mn;
+    const float sigma = has_sink ? a.sink[h] : 0.0f;
+    float invL[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if (has_sink) {
+        const float Mn = fmax2(M[qb], sigma);
+        if (Mn == kNegInf) {
+          M[qb] = kNegInf;
+          L[qb] = 0.0f;
+        } else {
+          const float fa = (M[qb] == kNegInf) ? 0.0f : exp_(M[qb] - Mn);
+          const float fb = (sigma == kNegInf) ? 0.0f : exp_(sigma - Mn);
+          const float La = L[qb] * fa;
+          const float lb = 1.0f * fb;
+          L[qb] = La + lb;
+          M[qb] = Mn;
+        }
       }
-    }
-    const float invL = (L == 0.0f) ? 0.0f : 1.0f / L;
-    if (g == 0 && qvalid) {
-      if (has_sink) a.p_sink[row] = (sigma == kNegInf) ? 0.0f : exp_(sigma - M) * invL;
-      if (a.lse) a.lse[row] = (L == 0.0f) ? kNegInf : M + ln_(L);
+      invL[qb] = (L[qb] == 0.0f) ? 0.0f : 1.0f / L[qb];
+      if (g == 0 && qvalid[qb]) {
+        if (has_sink) a.p_sink[row[qb]] = (sigma == kNegInf) ? 0.0f : exp_(sigma - M[qb]) * invL[qb];
+        if (a.lse) a.lse[row[qb]] = (L[qb] == 0.0f) ? kNegInf : M[qb] + ln_(L[qb]);
+      }
     }
 
     // ---- pass 2: P = e * c_t rounded to the dtype, O += P V, sub-tile by sub-tile ----
-    f32x4_t o[DB];
+    f32x4_t o[QB][DB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) o[db] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[qb][db] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     // the same pipeline: step it issues QK of step it + 1, forms P of step
     // it, accumulates P V of step it (V sub-tile it in LDS), and writes K
     // sub-tile it + 2 and V sub-tile it + 1 to LDS before its barrier
@@ -394,9 +452,13 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
       __syncthreads();
     }
     for (int t = 0; t < tlive; ++t) {
-      const float mt = sm[t * 16 + c16];
-      const float msafe = (mt == kNegInf) ? 0.0f : mt;
-      const float ct = (mt == kNegInf) ? 0.0f : exp_(mt - M) * invL;
+      float msafe[QB], ct[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float mt = sm[t * QW + 16 * qb + c16];
+        msafe[qb] = (mt == kNegInf) ? 0.0f : mt;
+        ct[qb] = (mt == kNegInf) ? 0.0f : exp_(mt - M[qb]) * invL[qb];
+      }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int it = 8 * t + j;
@@ -405,26 +467,31 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
         fetch_v(it + 1);
         load_mask(it + 1, mk[nxt]);
         qk_sub(nxt, sa[nxt], sb[nxt]);
-        float x[8], p[8];
-        make_x(it, sa[cur], sb[cur], mk[cur], x);
+        u32x4 pa[QB];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) p[e] = exp_(x[e] - msafe) * ct;
-        const u32x4 pa = {pack2<DT>(p[0], p[1]), pack2<DT>(p[2], p[3]), pack2<DT>(p[4], p[5]),
-                          pack2<DT>(p[6], p[7])};
-        if constexpr (WRITE) {
-          if (a.probs && qvalid) {
-            uint16_t *prow = static_cast<uint16_t *>(a.probs) + row * a.N;
-            const int key0 = SUB * it + 8 * g;
+        for (int qb = 0; qb < QB; ++qb) {
+          float x[8], p[8];
+          make_x(it, qb, sa[cur][qb], sb[cur][qb], mk[cur], x);
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (key0 + e < N) prow[key0 + e] = (uint16_t)(pa[e >> 1] >> (16 * (e & 1)));
+          for (int e = 0; e < 8; ++e) p[e] = exp_(x[e] - msafe[qb]) * ct[qb];
+          pa[qb] = u32x4{pack2<DT>(p[0], p[1]), pack2<DT>(p[2], p[3]), pack2<DT>(p[4], p[5]),
+                         pack2<DT>(p[6], p[7])};
+          if constexpr (WRITE) {
+            if (a.probs && qvalid[qb]) {
+              uint16_t *prow = static_cast<uint16_t *>(a.probs) + row[qb] * a.N;
+              const int key0 = SUB * it + 8 * g;
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                if (key0 + e < N) prow[key0 + e] = (uint16_t)(pa[qb][e >> 1] >> (16 * (e & 1)));
+            }
           }
         }
-        // B operand: keys 32it + 8g .. +7 of dims 16db + c16
+        // B operand: keys 32it + 8g .. +7 of dims 16db + c16, shared by the query blocks
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const u32x4 vv = *reinterpret_cast<const u32x4 *>(&lv[cur][(16 * db + c16) * VROW + 8 * g]);
-          o[db] = mfma32<DT>(pa, vv, o[db]);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32<DT>(pa[qb], vv, o[qb][db]);
         }
         put_k(cur);
         put_v(nxt);
@@ -432,17 +499,20 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
       }
     }
 
-    // ---- O rows q0 + 4g + r, dims 16db + c16: round once, write ----
+    // ---- O rows qw + 16qb + 4g + r, dims 16db + c16: round once, write ----
     uint16_t *orow = static_cast<uint16_t *>(a.out) + bh * a.Sq * D;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int qq = q0 + 4 * g + r;
-      if (qq < Sq) {
+    for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-        for (int db = 0; db < DB; db += 2) {
-          const uint32_t w2 = pack2<DT>(o[db][r], o[db + 1][r]);
-          orow[(int64_t)qq * D + 16 * db + c16] = (uint16_t)(w2 & 0xffffu);
-          orow[(int64_t)qq * D + 16 * (db + 1) + c16] = (uint16_t)(w2 >> 16);
+      for (int r = 0; r < 4; ++r) {
+        const int oq = qw + 16 * qb + 4 * g + r;
+        if (oq < Sq) {
+#pragma unroll
+          for (int db = 0; db < DB; db += 2) {
+            const uint32_t w2 = pack2<DT>(o[qb][db][r], o[qb][db + 1][r]);
+            orow[(int64_t)oq * D + 16 * db + c16] = (uint16_t)(w2 & 0xffffu);
+            orow[(int64_t)oq * D + 16 * (db + 1) + c16] = (uint16_t)(w2 >> 16);
+          }
         }
       }
     }
@@ -487,8 +557,48 @@ __global__ __launch_bounds__(256) void vt_kernel(const uint16_t *v, uint16_t *vt
   }
 }
 
+// Query blocks per wave.  Two blocks halve the LDS operand bytes per
+// product but need about 240 registers per lane (two waves per SIMD instead
+// of three) and twice the tile-maximum LDS.  The default takes them for the
+// fast path of head dimension 128 when the workgroup's LDS stays within
+// 64 KB and there are units enough for one round of the chip's workgroup
+// slots (256 CUs x 2).  Measured on MI355X, joint shape [1,24,4352,128]
+// with its padding mask: 0.584 ms with one block, 0.514 ms with two;
+// causal [1,32,8192,128] with the sink: 1.27 ms and 1.03 ms.  The query
+// blocks share one set of mask registers, so a mask that varies by query
+// always runs with one block, whatever was asked.  Every choice gives the
+// same bits.
+template <int D>
+int attn_query_blocks(const AttnArgs &a, bool write, int asked) {
+  constexpr size_t kStatic = 2 * 32 * (D + 16) * 2 + 2 * D * 48 * 2;  // lk + lv bytes
+  if (a.mask != nullptr && a.msq != 0) return 1;
+  if (kStatic + (size_t)kAttnWaves * a.T * 32 * sizeof(float) > 65536) return 1;
+  if (asked != 0) return asked;
+  if (write || D != 128) return 1;
+  const int64_t units2 = a.B * a.H * ((a.Sq + 127) / 128);
+  if (units2 < 2 * 256) return 1;
+  return 2;
+}
+
+template <int DT, int D, int QB>
+hipError_t attn_launch_qb(const AttnArgs &a, hipStream_t st) {
+  int64_t blocks = a.B * a.H * ((a.Sq + 64 * QB - 1) / (64 * QB));
+  if (blocks > 0x7fffffff) blocks = 0x7fffffff;
+  const dim3 grid((unsigned)blocks), block(kWave * kAttnWaves);
+  const size_t dyn = (size_t)kAttnWaves * a.T * 16 * QB * sizeof(float);
+  const bool mask = a.mask != nullptr, write = a.probs != nullptr || a.scores != nullptr;
+  if (mask) {
+    if (write) hipLaunchKernelGGL((attn_fwd_kernel<DT, D, true, true, QB>), grid, block, dyn, st, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<DT, D, true, false, QB>), grid, block, dyn, st, a);
+  } else {
+    if (write) hipLaunchKernelGGL((attn_fwd_kernel<DT, D, false, true, QB>), grid, block, dyn, st, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<DT, D, false, false, QB>), grid, block, dyn, st, a);
+  }
+  return hipGetLastError();
+}
+
 template <int DT, int D>
-hipError_t attn_launch(const AttnArgs &a, int64_t blocks, hipStream_t st) {
+hipError_t attn_launch(const AttnArgs &a, int qblocks, hipStream_t st) {
   const int64_t heads = a.B * a.Hkv;
   const int64_t vblocks = heads * (a.Np / 64);
   hipLaunchKernelGGL((vt_kernel<D>), dim3((unsigned)vblocks), dim3(256), 0, st,
@@ -496,24 +606,17 @@ hipError_t attn_launch(const AttnArgs &a, int64_t blocks, hipStream_t st) {
                      (int64_t)a.Np);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)blocks), block(kWave * kAttnWaves);
-  const size_t dyn = (size_t)kAttnWaves * a.T * 16 * sizeof(float);
-  const bool mask = a.mask != nullptr, write = a.probs != nullptr || a.scores != nullptr;
-  if (mask) {
-    if (write) hipLaunchKernelGGL((attn_fwd_kernel<DT, D, true, true>), grid, block, dyn, st, a);
-    else hipLaunchKernelGGL((attn_fwd_kernel<DT, D, true, false>), grid, block, dyn, st, a);
-  } else {
-    if (write) hipLaunchKernelGGL((attn_fwd_kernel<DT, D, false, true>), grid, block, dyn, st, a);
-    else hipLaunchKernelGGL((attn_fwd_kernel<DT, D, false, false>), grid, block, dyn, st, a);
-  }
-  return hipGetLastError();
+  const bool write = a.probs != nullptr || a.scores != nullptr;
+  qblocks = attn_query_blocks<D>(a, write, qblocks);
+  if (qblocks == 2) return attn_launch_qb<DT, D, 2>(a, st);
+  return attn_launch_qb<DT, D, 1>(a, st);
 }
 
 }  // namespace
 
-hipError_t launch_attn_fwd(int dtype, const AttnArgs &a, int64_t blocks, hipStream_t st) {
-  if (dtype == 1) return a.D == 64 ? attn_launch<1, 64>(a, blocks, st) : attn_launch<1, 128>(a, blocks, st);
-  return a.D == 64 ? attn_launch<2, 64>(a, blocks, st) : attn_launch<2, 128>(a, blocks, st);
+hipError_t launch_attn_fwd(int dtype, const AttnArgs &a, int qblocks, hipStream_t st) {
+  if (dtype == 1) return a.D == 64 ? attn_launch<1, 64>(a, qblocks, st) : attn_launch<1, 128>(a, qblocks, st);
+  return a.D == 64 ? attn_launch<2, 64>(a, qblocks, st) : attn_launch<2, 128>(a, qblocks, st);
 }
 
 }  // namespace jas

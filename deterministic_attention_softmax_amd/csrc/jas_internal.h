@@ -111,6 +111,7 @@ hipError_t launch_bwd_f16(const BwdArgs &a, const Geometry &g, hipStream_t strea
 hipError_t launch_fwd(int dtype, const FwdArgs &a, const Geometry &g, hipStream_t stream);
 hipError_t launch_bwd(int dtype, const BwdArgs &a, const Geometry &g, hipStream_t stream);
 hipError_t launch_dsink(const DsinkArgs &a, hipStream_t stream);
-hipError_t launch_attn_fwd(int dtype, const AttnArgs &a, int64_t blocks, hipStream_t stream);
+// qblocks: 16-query blocks per wave (1 or 2), 0 = chosen from the shape
+hipError_t launch_attn_fwd(int dtype, const AttnArgs &a, int qblocks, hipStream_t stream);
 
 }  // namespace jas

@@ -295,6 +295,21 @@ jas_status_t jas_attn_fwd(const jas_attn_desc_t *desc, const void *q, const void
                           const float *sink, void *out, float *lse, float *p_sink, void *probs,
                           float *scores, void *workspace, size_t workspace_bytes, void *stream);
 
+/* jas_attn_fwd with an explicit number of 16-query blocks per wavefront:
+ * 1 or 2, or 0 for the default the library picks from the shape (2 where
+ * the launch has work enough and its LDS fits, 1 otherwise; always 1 with
+ * JAS_FLAG_PROBS / JAS_FLAG_SCORES or a mask that varies by query).  Two
+ * blocks share every K and V operand read between two products.  Each query
+ * is computed by the same operations in the same order either way, so the
+ * outputs are identical for 0, 1 and 2 (RL-Kernel PR #240, Fixed Reduction
+ * Contract: results independent of the launch).  JAS_ERR_BAD_FLAGS for any
+ * other value; otherwise as jas_attn_fwd. */
+jas_status_t jas_attn_fwd_ex(const jas_attn_desc_t *desc, const void *q, const void *k,
+                             const void *v, const float *mask, const int32_t *key_len,
+                             const float *sink, void *out, float *lse, float *p_sink, void *probs,
+                             float *scores, void *workspace, size_t workspace_bytes,
+                             int query_blocks, void *stream);
+
 /* Static text for a status code. */
 const char *jas_status_str(jas_status_t status);
 

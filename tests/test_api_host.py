@@ -226,6 +226,15 @@ def test_attention_validation():
     L = jas.lib()
     assert L.jas_attn_fwd(None, A, B_, C, None, None, None, D, None, None, None, None, E, 0,
                           None) == 1
+    # jas_attn_fwd_ex: 16-query blocks per wavefront 0, 1 or 2; anything else
+    # is refused before a pointer is looked at
+    for qb in (-1, 3, 64):
+        assert jas.jas_attn_fwd_ex(adesc(), A, B_, C, None, None, None, D, None, None, None, None,
+                                   E, jas.jas_attn_workspace_bytes(adesc()), qb, None) == 4
+    assert jas.jas_attn_fwd_ex(adesc(dtype=jas.JAS_DTYPE_F32), A, B_, C, None, None, None, D, None,
+                               None, None, None, E, 0, 2, None) == 3
+    assert jas.jas_attn_fwd_ex(adesc(), None, B_, C, None, None, None, D, None, None, None, None,
+                               E, jas.jas_attn_workspace_bytes(adesc()), 2, None) == 1
 
 
 def _plan_covers(d, backward):

@@ -20,7 +20,8 @@ ascending one, so:
     a score difference can move a p_j across a rounding boundary on one side
     only, so 2u), the score and mask-add differences, both binary32 sums,
     fp16 subnormals, and the output's own rounding.
-Invariance: a query's bytes do not depend on the batch or on its block.
+Invariance: a query's bytes do not depend on the batch or on its block, nor
+on the launch's 16-query blocks per wavefront (1 or 2).
 """
 import numpy as np
 import pytest
@@ -42,6 +43,11 @@ def f64(a):
     return a.astype(np.float64)
 
 
+def raw_bytes(t):
+    """A device tensor's bytes (any dtype, numpy has no bf16)."""
+    return t.contiguous().view(torch.uint8).cpu().numpy().tobytes()
+
+
 def draw(seed, B, H, Hkv, Sq, N, D, dt, std=1.0):
     q = synth.normal((B, H, Sq, D), std, seed, "cpu", dt)
     k = synth.normal((B, Hkv, N, D), std, seed + 1, "cpu", dt)
@@ -49,7 +55,7 @@ def draw(seed, B, H, Hkv, Sq, N, D, dt, std=1.0):
     return q, k, v
 
 
-def check(q, k, v, scale, mask=None, mask_strides=None, sink=None, causal=False, kl=None):
+def check(q, k, v, scale, mask=None, mask_strides=None, sink=None, causal=False, kl=None, qb=0):
     B, H, Sq, D = q.shape
     Hkv, N = k.shape[1], k.shape[2]
     dt = q.dtype
@@ -57,7 +63,7 @@ def check(q, k, v, scale, mask=None, mask_strides=None, sink=None, causal=False,
     r = jas.attn_fwd(q.to(dev()), k.to(dev()), v.to(dev()), scale=scale,
                      mask=None if mask is None else mask.to(dev()), mask_strides=mask_strides,
                      sink=None if sink is None else sink.to(dev()), causal=causal, key_len=klt,
-                     want_lse=True, want_probs=True, want_scores=True)
+                     want_lse=True, want_probs=True, want_scores=True, query_blocks=qb)
     torch.cuda.synchronize()
     o = oracle.attn_fwd(synth.to_numpy_bits(q), synth.to_numpy_bits(k), synth.to_numpy_bits(v),
                         np.float32(scale), mask=None if mask is None else mask.numpy(),
@@ -129,15 +135,16 @@ def check(q, k, v, scale, mask=None, mask_strides=None, sink=None, causal=False,
     return r
 
 
+@pytest.mark.parametrize("qb", [1, 2])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
 @pytest.mark.parametrize("shape", [(1, 2, 2, 16, 256), (2, 4, 4, 37, 600), (1, 4, 1, 5, 1000),
-                                   (1, 2, 2, 1, 1), (1, 6, 2, 33, 257)])
-def test_attention_against_oracle(shape, dt, D):
+                                   (1, 2, 2, 1, 1), (1, 6, 2, 33, 257), (1, 2, 1, 150, 300)])
+def test_attention_against_oracle(shape, dt, D, qb):
     B, H, Hkv, Sq, N = shape
-    log(f"attention {dt} B={B} H={H} Hkv={Hkv} Sq={Sq} N={N} D={D}")
+    log(f"attention {dt} B={B} H={H} Hkv={Hkv} Sq={Sq} N={N} D={D} query blocks {qb}")
     q, k, v = draw(Sq * 7 + N + D, B, H, Hkv, Sq, N, D, dt)
-    check(q, k, v, 1.0 / np.sqrt(D))
+    check(q, k, v, 1.0 / np.sqrt(D), qb=qb)
 
 
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
@@ -148,10 +155,12 @@ def test_attention_mask_sink_causal_key_len(dt):
     mask[0, ..., 650:] = float("-inf")
     mask[1, ..., :3] = -1.5
     sink = synth.normal((H,), 1.0, 32, "cpu")
-    log(f"attention {dt} with mask, sink, causal, key lengths")
-    check(q, k, v, 0.09, mask=mask, mask_strides=(N, 0, 0), sink=sink, causal=True, kl=[700, 420])
-    check(q, k, v, 0.09, sink=sink, kl=[0, 5])            # an empty batch entry: P = 0, p_sink = 1
-    check(q, k, v, 0.09, causal=True)                     # Sq < N: the last queries see all keys
+    for qb in (1, 2):
+        log(f"attention {dt} with mask, sink, causal, key lengths; query blocks {qb}")
+        check(q, k, v, 0.09, mask=mask, mask_strides=(N, 0, 0), sink=sink, causal=True,
+              kl=[700, 420], qb=qb)
+        check(q, k, v, 0.09, sink=sink, kl=[0, 5], qb=qb)  # an empty batch entry: P = 0, p_sink = 1
+        check(q, k, v, 0.09, causal=True, qb=qb)           # Sq < N: the last queries see all keys
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -238,3 +247,53 @@ def test_joint_attention_1x24x4352x128_sampled():
     assert np.all(np.abs(got - want) <= 2.0 ** -8 * (mass + np.abs(want)) + 1e-30)
     lse = r["lse"].view(B, H, S)[:, :, torch.as_tensor(qi, device=dev())].cpu().numpy().reshape(-1)
     assert_lse_close(lse, o["lse"], "joint lse")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
+def test_attention_query_blocks_identical(dt, D):
+    # the fast path (no P / score output) with 1 and 2 blocks of 16 queries
+    # per wavefront and the library's own choice: identical bytes of out,
+    # lse and p_sink, on ragged query counts, grouped heads, a mask shared by
+    # the queries, the sink, the causal cut with Sq != N and key lengths
+    B, H, Hkv, N = 2, 4, 2, 777
+    for Sq, causal, kl, use_mask in ((1, False, None, False), (130, True, [777, 300], True),
+                                     (200, False, [5, 777], True), (777, True, None, False),
+                                     (900, True, None, True)):
+        log(f"attention {dt} D={D} Sq={Sq} causal={causal} key_len={kl}: query blocks 0 / 1 / 2")
+        q, k, v = draw(Sq + 17 * D, B, H, Hkv, Sq, N, D, dt, std=1.3)
+        q, k, v = q.to(dev()), k.to(dev()), v.to(dev())
+        mask = None
+        if use_mask:
+            mask = synth.normal((B, 1, 1, N), 1.0, Sq + 5, dev())
+            mask[0, ..., 400:460] = float("-inf")
+        sink = synth.normal((H,), 1.0, Sq + 6, dev())
+        klt = None if kl is None else torch.tensor(kl, dtype=torch.int32, device=dev())
+        rs = [jas.attn_fwd(q, k, v, scale=0.1, mask=mask,
+                           mask_strides=None if mask is None else (N, 0, 0), sink=sink,
+                           causal=causal, key_len=klt, want_lse=True, query_blocks=qb)
+              for qb in (0, 1, 2)]
+        torch.cuda.synchronize()
+        for key in ("out", "lse", "p_sink"):
+            ref = raw_bytes(rs[1][key])
+            assert raw_bytes(rs[0][key]) == ref, f"{key}: default != 1 block"
+            assert raw_bytes(rs[2][key]) == ref, f"{key}: 2 blocks != 1 block"
+
+
+def test_joint_attention_query_blocks_identical():
+    # the joint image+text shape, where the library picks 2 blocks per
+    # wavefront: the same bytes as with 1
+    B, H, S, D = 1, 24, 4352, 128
+    log("fused attention bf16 [1,24,4352,128], padding mask: query blocks 0 / 1 / 2")
+    q = synth.normal((B, H, S, D), 1.0, 81, dev(), torch.bfloat16)
+    k = synth.normal((B, H, S, D), 1.0, 82, dev(), torch.bfloat16)
+    v = synth.normal((B, H, S, D), 1.0, 83, dev(), torch.bfloat16)
+    mask = torch.zeros((B, 1, 1, S), device=dev())
+    mask[..., S - 100:] = float("-inf")
+    rs = [jas.attn_fwd(q, k, v, mask=mask, mask_strides=(S, 0, 0), want_lse=True, query_blocks=qb)
+          for qb in (0, 1, 2)]
+    torch.cuda.synchronize()
+    for key in ("out", "lse"):
+        ref = raw_bytes(rs[1][key])
+        assert raw_bytes(rs[0][key]) == ref
+        assert raw_bytes(rs[2][key]) == ref
