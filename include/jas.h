@@ -295,15 +295,18 @@ jas_status_t jas_attn_fwd(const jas_attn_desc_t *desc, const void *q, const void
                           const float *sink, void *out, float *lse, float *p_sink, void *probs,
                           float *scores, void *workspace, size_t workspace_bytes, void *stream);
 
-/* jas_attn_fwd with an explicit number of 16-query blocks per wavefront:
- * 1 or 2, or 0 for the default the library picks from the shape (2 where
- * the launch has work enough and its LDS fits, 1 otherwise; always 1 with
- * JAS_FLAG_PROBS / JAS_FLAG_SCORES or a mask that varies by query).  Two
- * blocks share every K and V operand read between two products.  Each query
- * is computed by the same operations in the same order either way, so the
- * outputs are identical for 0, 1 and 2 (RL-Kernel PR #240, Fixed Reduction
- * Contract: results independent of the launch).  JAS_ERR_BAD_FLAGS for any
- * other value; otherwise as jas_attn_fwd. */
+/* jas_attn_fwd with an explicit number of 16-query blocks per wavefront,
+ * query_blocks: 1, 2, or 0 for the library's choice.  Two blocks share every
+ * K and V operand read between two products.  The library runs 1 block,
+ * whatever was asked, when the mask varies by query (mask_stride_q != 0) or
+ * when two blocks' tile maxima would take the workgroup's LDS past 64 KB
+ * (more than 11,264 keys at head_dim 128).  Its own choice (0) is 2 for
+ * head_dim 128 without JAS_FLAG_PROBS / JAS_FLAG_SCORES when
+ * batch*heads*ceil(q_len/128) >= 512, else 1.  Each query is computed by
+ * the same operations in the same order either way, so the outputs are
+ * identical for 0, 1 and 2 (RL-Kernel PR #240, Fixed Reduction Contract:
+ * results independent of the launch).  JAS_ERR_BAD_FLAGS for any other
+ * value; otherwise as jas_attn_fwd. */
 jas_status_t jas_attn_fwd_ex(const jas_attn_desc_t *desc, const void *q, const void *k,
                              const void *v, const float *mask, const int32_t *key_len,
                              const float *sink, void *out, float *lse, float *p_sink, void *probs,
