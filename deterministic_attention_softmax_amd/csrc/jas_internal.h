@@ -42,7 +42,7 @@ struct FwdArgs {
   RowShape s;
   int vec_io;         // 16-byte path: rows (and mask rows) are whole aligned 16-byte chunks
   int vec_mask;       // mask rows start on 16-byte boundaries (or no mask)
-  int stash;          // streaming kernels: keep one segment in LDS (set by the launcher)
+  int stash;          // streaming kernels: segments kept in LDS (set by the launcher)
 };
 
 struct BwdArgs {
@@ -54,7 +54,7 @@ struct BwdArgs {
   Exclusion ex;
   RowShape s;
   int vec_io;         // 16-byte path: rows are whole aligned 16-byte chunks
-  int stash;          // streaming kernel: keep one segment's P in LDS (set by the launcher)
+  int stash;          // streaming kernel: segments whose P is kept in LDS (set by the launcher)
 };
 
 // Fused attention forward (QK, the row softmax, PV).

@@ -729,9 +729,10 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void bwd_kernel(const BwdArgs 
 // LDS; wave 0 then folds the states in tile order, 64 tiles at a time with
 // the running state carried from block to block (the same left fold);
 // pass 2 writes the outputs segment by segment, last segment first: that
-// one is still in registers, the one before it waits in an LDS stash, the
-// others are read again (the forward loads the next segment while it
-// writes the current one).  The forward recomputes every segment's
+// one is still in registers, the ones just before it wait in an LDS stash
+// (one segment in the forward, P of two in the backward), the others are
+// read again (the forward loads the next segment while it writes the
+// current one).  The forward recomputes every segment's
 // exponentials from the raw chunks and the saved tile maxima -- the same
 // operations on the same inputs, so every output has the one-pass kernels'
 // bits.
@@ -741,12 +742,36 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void bwd_kernel(const BwdArgs 
 // 4-byte words after `used` words of tile states (16-byte aligned).
 __host__ __device__ constexpr int stash_offset_words(int used) { return (used + 3) & ~3; }
 
-// The stash holds one segment's chunks: 256 threads x CPL x 16 bytes.  It is
-// used where that is at most 32 KB, which keeps the workgroups per CU the
-// register budget allows (a 32 KB stash fits 4 per CU).
-constexpr int kStashMaxBytes = 32 * 1024;
+// The stash holds the raw chunks of the segments just before the last one,
+// one segment being 256 threads x CPL x 16 bytes; pass 2 reads them from LDS
+// instead of reading them again.  Segments of more than 32 KB are not
+// stashed, and each direction has its own LDS budget, from measurements on
+// MI355X with bf16 rows of 65,536 keys (4 segments of 32 KB; 1, 2 and 3
+// segments stashed leave 3 or 4, 2 and 1 workgroups per CU):
+//   forward:  0.422, 0.595, 1.014 ms  -> 1 segment
+//   backward: 0.667, 0.639, 0.883 ms  -> 2 segments
+// The forward, which keeps a second register set of chunks to load ahead,
+// needs the workgroups more than it needs fewer second reads.
+constexpr int kStashSegMaxBytes = 32 * 1024;
+constexpr int kStashBudgetFwd = 32 * 1024;
+constexpr int kStashBudgetBwd = 64 * 1024;
 template <int CPL>
 constexpr size_t stash_bytes() { return (size_t)CPL * kWave * kBlockWaves * 16; }
+
+// Segments a streaming row of T tiles is cut into, and how many of them the
+// stash holds within `budget` bytes (never more than the row has before its
+// last segment).
+template <int DT, int CPL>
+__host__ __device__ constexpr int stream_segments(int T) {
+  return ((T + Cfg<DT>::TPS - 1) / Cfg<DT>::TPS + kBlockWaves * CPL - 1) / (kBlockWaves * CPL);
+}
+template <int DT, int CPL>
+constexpr int stash_segments(int T, int budget) {
+  if (stash_bytes<CPL>() > (size_t)kStashSegMaxBytes) return 0;
+  const int want = stream_segments<DT, CPL>(T) - 1;
+  const int fit = (int)((size_t)budget / stash_bytes<CPL>());
+  return want < fit ? (want > 0 ? want : 0) : fit;
+}
 
 template <int DT, int CPL, bool VEC, bool MASK, bool EXCL>
 __global__ __launch_bounds__(kWave * kBlockWaves) void fwd_stream_kernel(const FwdArgs a) {
@@ -760,8 +785,9 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void fwd_stream_kernel(const F
   float *lds_m = smem;            // [T] tile maxima
   float *lds_l = smem + T;        // [T] tile sums
   float *lds_row = smem + 2 * T;  // the row's M and invL
-  // with a.stash: the raw chunks of segment nseg - 2 (the first one pass 2
-  // would read again), CPL x 256 threads x 16 bytes, each thread's own
+  // a.stash segments' raw chunks, those just before the last segment (the
+  // first ones pass 2 would read again), CPL x 256 threads x 16 bytes each,
+  // each thread's own
   Chunk *lds_stash = reinterpret_cast<Chunk *>(smem + stash_offset_words(2 * T + 2));
 
   const RowIdx<DT, WPR> ix;
@@ -844,19 +870,21 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void fwd_stream_kernel(const F
 
     // segments wholly past the cut hold only -inf keys: nothing to load
     const int nseg_read = EXCL ? (kend + SPS * TPS * kTile - 1) / (SPS * TPS * kTile) : nseg;
+    // the stash holds segments gs0 .. nseg - 2
+    const int gs0 = nseg - 1 - (a.stash < nseg - 1 ? a.stash : nseg - 1);
     auto load_pass1 = [&](Chunk (&dst)[CPL], int g) {
-      if (g != nseg - 1) load_segment(dst, g, AuxC<0>{});  // read again in pass 2
+      if (g < gs0) load_segment(dst, g, AuxC<0>{});  // read again in pass 2
       else load_segment(dst, g, AuxC<kAuxNT>{});
     };
 
     // ---- pass 1: tile states of every segment into LDS ----
-    const bool stash = a.stash && nseg >= 2;
     if (nseg_read > 0) load_pass1(cur, 0);
     for (int g = 0; g < nseg; ++g) {
       if (g + 1 < nseg_read) load_pass1(nxt, g + 1);
-      if (stash && g == nseg - 2 && g < nseg_read) {
+      if (g >= gs0 && g < nseg - 1 && g < nseg_read) {
+        Chunk *st = lds_stash + (g - gs0) * CPL * kWave * WPR;
 #pragma unroll
-        for (int s = 0; s < CPL; ++s) lds_stash[s * kWave * WPR + threadIdx.x] = cur[s];
+        for (int s = 0; s < CPL; ++s) st[s * kWave * WPR + threadIdx.x] = cur[s];
       }
 #pragma unroll
       for (int s = 0; s < CPL; ++s) {
@@ -940,14 +968,15 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void fwd_stream_kernel(const F
     const float M = lds_row[0], invL = lds_row[1];
 
     // ---- pass 2: rescale, convert once, write; last segment first ----
-    // cur holds the last segment; the one before it comes from the stash or
-    // is read again, each loaded while the current one is written
+    // cur holds the last segment; the ones before it come from the stash or
+    // are read again, each loaded while the current one is written
     for (int g = nseg - 1; g >= 0; --g) {
       const int gp = g - 1;
       if (gp >= 0 && gp < nseg_read) {
-        if (stash && gp == nseg - 2) {
+        if (gp >= gs0) {
+          const Chunk *st = lds_stash + (gp - gs0) * CPL * kWave * WPR;
 #pragma unroll
-          for (int s = 0; s < CPL; ++s) nxt[s] = lds_stash[s * kWave * WPR + threadIdx.x];
+          for (int s = 0; s < CPL; ++s) nxt[s] = st[s * kWave * WPR + threadIdx.x];
         } else {
           load_segment(nxt, gp, AuxC<kAuxNT>{});
         }
@@ -997,7 +1026,8 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void bwd_stream_kernel(const B
   const int T = a.s.T;
   float *lds_d = smem;            // [T] tile sums of P*dP
   float *lds_row = smem + T;      // delta
-  // with a.stash: segment nseg - 2's P chunks (as masked), each thread's own
+  // a.stash segments' P chunks (as masked), those just before the last
+  // segment, each thread's own
   Chunk *lds_stash = reinterpret_cast<Chunk *>(smem + stash_offset_words(T + 1));
 
   const RowIdx<DT, WPR> ix;
@@ -1020,14 +1050,15 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void bwd_stream_kernel(const B
     const int lim = kend - ix.loff;
 
     Chunk rp[CPL], rg[CPL];
-    auto load_segment = [&](int g, auto aux) {  // aux: cache policy, as in the forward
-      constexpr int AX = decltype(aux)::value;
+    // auxp, auxg: cache policies of P and dP, as in the forward
+    auto load_segment = [&](int g, auto auxp, auto auxg) {
+      constexpr int AP = decltype(auxp)::value, AG = decltype(auxg)::value;
 #pragma unroll
       for (int s = 0; s < CPL; ++s) {
         const int sb = (g * SPS + s * WPR + ix.wir) * TPS * kTile;
         if constexpr (VEC) {
-          rp[s] = bload<AX>(pbuf, voff, (uint32_t)(sb * ESZ));
-          rg[s] = bload<AX>(gbuf, voff, (uint32_t)(sb * ESZ));
+          rp[s] = bload<AP>(pbuf, voff, (uint32_t)(sb * ESZ));
+          rg[s] = bload<AG>(gbuf, voff, (uint32_t)(sb * ESZ));
           if constexpr (EXCL) {
             if (sb + TPS * kTile > kend && sb < kread) {  // the slot holding the cut (uniform)
               const int nv = lim - sb;
@@ -1055,15 +1086,19 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void bwd_stream_kernel(const B
         else rg[s] = load_chunk_elems<DT>(grow, sb + ix.loff, N, 0u);
       }
     };
-    const bool stash = a.stash && nseg >= 2;
+    // the stash holds P of segments gs0 .. nseg - 2
+    const int gs0 = nseg - 1 - (a.stash < nseg - 1 ? a.stash : nseg - 1);
 
     // ---- pass 1: tile sums of P*dP into LDS ----
     for (int g = 0; g < nseg; ++g) {
-      if (g != nseg - 1) load_segment(g, AuxC<0>{});  // read again in pass 2
-      else load_segment(g, AuxC<kAuxNT>{});
-      if (stash && g == nseg - 2) {
+      // P and dP read again in pass 2 keep the normal cache policy
+      if (g < gs0) load_segment(g, AuxC<0>{}, AuxC<0>{});
+      else if (g < nseg - 1) load_segment(g, AuxC<kAuxNT>{}, AuxC<0>{});
+      else load_segment(g, AuxC<kAuxNT>{}, AuxC<kAuxNT>{});
+      if (g >= gs0 && g < nseg - 1) {
+        Chunk *st = lds_stash + (g - gs0) * CPL * kWave * WPR;
 #pragma unroll
-        for (int s = 0; s < CPL; ++s) lds_stash[s * kWave * WPR + threadIdx.x] = rp[s];
+        for (int s = 0; s < CPL; ++s) st[s * kWave * WPR + threadIdx.x] = rp[s];
       }
 #pragma unroll
       for (int s = 0; s < CPL; ++s) {
@@ -1099,12 +1134,13 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void bwd_stream_kernel(const B
     // ---- pass 2: dS = P * (dP - delta), convert once, write; last segment first ----
     for (int g = nseg - 1; g >= 0; --g) {
       if (g != nseg - 1) {
-        if (stash && g == nseg - 2) {
+        if (g >= gs0) {
+          const Chunk *st = lds_stash + (g - gs0) * CPL * kWave * WPR;
 #pragma unroll
-          for (int s = 0; s < CPL; ++s) rp[s] = lds_stash[s * kWave * WPR + threadIdx.x];
+          for (int s = 0; s < CPL; ++s) rp[s] = st[s * kWave * WPR + threadIdx.x];
           load_g(g);
         } else {
-          load_segment(g, AuxC<kAuxNT>{});
+          load_segment(g, AuxC<kAuxNT>{}, AuxC<kAuxNT>{});
         }
       }
 #pragma unroll
@@ -1147,9 +1183,9 @@ template <int DT, int CPL>
 hipError_t launch_fwd_stream(const FwdArgs &a0, const Geometry &g, hipStream_t st) {
   const dim3 grid((unsigned)g.blocks), block(kWave * kBlockWaves);
   FwdArgs a = a0;
-  a.stash = stash_bytes<CPL>() <= kStashMaxBytes;
+  a.stash = stash_segments<DT, CPL>(a.s.T, kStashBudgetFwd);
   const size_t lds = (size_t)stash_offset_words(2 * a.s.T + 2) * sizeof(float) +
-                     (a.stash ? stash_bytes<CPL>() : 0);
+                     (size_t)a.stash * stash_bytes<CPL>();
   const bool mask = a.mask != nullptr, excl = a.ex.causal || a.ex.key_len;
 #define JAS_FWD_STREAM(V, MK, EX)                                                              \
   hipLaunchKernelGGL((fwd_stream_kernel<DT, CPL, V, MK, EX>), grid, block, lds, st, a)
@@ -1168,9 +1204,9 @@ template <int DT, int CPL>
 hipError_t launch_bwd_stream(const BwdArgs &a0, const Geometry &g, hipStream_t st) {
   const dim3 grid((unsigned)g.blocks), block(kWave * kBlockWaves);
   BwdArgs a = a0;
-  a.stash = stash_bytes<CPL>() <= kStashMaxBytes;
+  a.stash = stash_segments<DT, CPL>(a.s.T, kStashBudgetBwd);
   const size_t lds = (size_t)stash_offset_words(a.s.T + 1) * sizeof(float) +
-                     (a.stash ? stash_bytes<CPL>() : 0);
+                     (size_t)a.stash * stash_bytes<CPL>();
   const bool excl = a.ex.causal || a.ex.key_len;
   if (a.vec_io) {
     if (excl) hipLaunchKernelGGL((bwd_stream_kernel<DT, CPL, true, true>), grid, block, lds, st, a);
