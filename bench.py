@@ -777,17 +777,45 @@ def main():
     stream = torch.cuda.current_stream()
     nstep = [0]
 
+    # The steps call jas_fwd / jas_bwd directly, with the descriptors and
+    # pointers of each buffer set built and checked once by the binding
+    # (fwd_prepared / bwd_prepared): no Python wrapper work between launches.
+    # The first set's outputs are compared, byte for byte, with those of the
+    # wrapper calls fwd / bwd on the same inputs.
+    runs = []
+    for si, gi, P, dS in sets:
+        rf, _ = jas.fwd_prepared(si, mask=mask, sink=sink, out=P, p_sink=ps, causal=causal,
+                                 key_len=key_len)
+        rb = None
+        if backward:
+            rb, _ = jas.bwd_prepared(P, gi, p_sink=ps, out=dS, d_sink=dsk, workspace=ws,
+                                     causal=causal, key_len=key_len)
+        runs.append((rf, rb))
+    runs[0][0]()
+    if backward:
+        runs[0][1]()
+    Pw, psw = jas.fwd(s, mask=mask, sink=sink, causal=causal, key_len=key_len)
+    same = torch.equal(Pw.view(torch.uint8), sets[0][2].view(torch.uint8))
+    if backward:
+        dSw, dskw = jas.bwd(Pw, g, p_sink=psw, causal=causal, key_len=key_len)
+        same = same and torch.equal(dSw.view(torch.uint8), sets[0][3].view(torch.uint8))
+        if has_sink:
+            same = same and torch.equal(dskw, dsk)
+    assert same, "prepared calls differ from the wrapper calls"
+    del Pw, psw
+    if backward:
+        del dSw, dskw
+
     def step(ev=None):
-        si, gi, P, dS = sets[nstep[0] % nsets]
+        rf, rb = runs[nstep[0] % nsets]
         nstep[0] += 1
         if ev:
             ev[0].record(stream)
-        jas.fwd(si, mask=mask, sink=sink, out=P, p_sink=ps, causal=causal, key_len=key_len)
+        rf()
         if ev:
             ev[1].record(stream)
         if backward:
-            jas.bwd(P, gi, p_sink=ps, out=dS, d_sink=dsk, workspace=ws, causal=causal,
-                    key_len=key_len)
+            rb()
         if ev:
             ev[2].record(stream)
 

@@ -19,7 +19,7 @@ __all__ = [
     "STATUS", "JasError", "jas_desc_t", "jas_launch_t", "jas_attn_desc_t", "lib", "jas_fwd",
     "jas_fwd_ex", "jas_bwd", "jas_bwd_ex", "jas_bwd_workspace_bytes", "jas_attn_fwd", "jas_attn_fwd_ex",
     "jas_attn_workspace_bytes", "jas_launch_plan", "jas_status_str", "jas_contract", "make_desc",
-    "make_attn_desc", "fwd", "bwd", "attn_fwd", "LIB_PATH",
+    "make_attn_desc", "fwd", "bwd", "fwd_prepared", "bwd_prepared", "attn_fwd", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libjas.so")
@@ -253,15 +253,10 @@ def _check_vec(t, like, dtype, count, name):
     return t
 
 
-def fwd(scores, mask=None, mask_strides=None, sink=None, out=None, p_sink=None, launch=None,
-        causal=False, key_len=None, lse=None, want_lse=False):
-    """Forward on device tensors.  ``scores`` [B,H,Sq,N] bf16/fp16/fp32 (rows
-    may have a stride ld >= N); ``mask`` fp32 addressed with ``mask_strides``
-    (b, h, q) in elements (default: a contiguous [B,H,Sq,N] tensor broadcast
-    by its own zero strides); ``sink`` fp32 [H]; ``causal`` excludes keys past
-    the causal condition; ``key_len`` int32 [B] excludes keys past each batch
-    entry's length.  Returns (probs, p_sink), or (probs, p_sink, lse) when
-    ``want_lse`` is set or an ``lse`` output (fp32 [B*H*Sq]) is given."""
+def _fwd_args(scores, mask, mask_strides, sink, out, p_sink, launch, causal, key_len, lse,
+              want_lse):
+    """Validate a forward and allocate its missing outputs: (arguments of
+    jas_fwd_ex without the stream, result tuple)."""
     import torch
     shape, ld = _shape4(scores)
     B, H, S, N = shape
@@ -297,20 +292,63 @@ def fwd(scores, mask=None, mask_strides=None, sink=None, out=None, p_sink=None, 
         if lse is None:
             lse = torch.empty(rows, dtype=torch.float32, device=scores.device)
         _check_vec(lse, scores, torch.float32, rows, "lse")
-    st = _on_device(scores, jas_fwd_ex, d, _ptr(scores), _ptr(mask), _ptr(key_len), _ptr(sink),
-                    _ptr(out), _ptr(p_sink) if sink is not None else None,
-                    _ptr(lse) if want_lse else None, _launch(launch))
+    args = (d, _ptr(scores), _ptr(mask), _ptr(key_len), _ptr(sink), _ptr(out),
+            _ptr(p_sink) if sink is not None else None, _ptr(lse) if want_lse else None,
+            _launch(launch))
+    ps = p_sink if sink is not None else None
+    return args, ((out, ps, lse) if want_lse else (out, ps))
+
+
+def fwd(scores, mask=None, mask_strides=None, sink=None, out=None, p_sink=None, launch=None,
+        causal=False, key_len=None, lse=None, want_lse=False):
+    """Forward on device tensors.  ``scores`` [B,H,Sq,N] bf16/fp16/fp32 (rows
+    may have a stride ld >= N); ``mask`` fp32 addressed with ``mask_strides``
+    (b, h, q) in elements (default: a contiguous [B,H,Sq,N] tensor broadcast
+    by its own zero strides); ``sink`` fp32 [H]; ``causal`` excludes keys past
+    the causal condition; ``key_len`` int32 [B] excludes keys past each batch
+    entry's length.  Returns (probs, p_sink), or (probs, p_sink, lse) when
+    ``want_lse`` is set or an ``lse`` output (fp32 [B*H*Sq]) is given."""
+    args, res = _fwd_args(scores, mask, mask_strides, sink, out, p_sink, launch, causal, key_len,
+                          lse, want_lse)
+    st = _on_device(scores, jas_fwd_ex, *args)
     if st != 0:
         raise JasError(st, "jas_fwd")
-    ps = p_sink if sink is not None else None
-    return (out, ps, lse) if want_lse else (out, ps)
+    return res
 
 
-def bwd(probs, dprobs, p_sink=None, out=None, d_sink=None, workspace=None, launch=None,
-        causal=False, key_len=None):
-    """Backward on device tensors (``causal`` / ``key_len`` as for the
-    forward: P is taken as +0 on excluded keys).  Returns (dscores, d_sink or
-    None)."""
+def fwd_prepared(scores, mask=None, mask_strides=None, sink=None, out=None, p_sink=None,
+                 launch=None, causal=False, key_len=None, lse=None, want_lse=False):
+    """:func:`fwd`'s checks and allocations done once: returns (run, result),
+    where ``run()`` enqueues the same forward again on the same tensors with
+    one call of jas_fwd_ex, on the stream current when this was called, and
+    raises on an error status.  For loops that time the library, or that
+    must not allocate; call ``run`` with the tensors' device current and
+    keep the tensors alive while it is used."""
+    import torch
+    args, res = _fwd_args(scores, mask, mask_strides, sink, out, p_sink, launch, causal, key_len,
+                          lse, want_lse)
+    with torch.cuda.device(scores.device):
+        stream = torch.cuda.current_stream(scores.device).cuda_stream
+    return _prepared(lib().jas_fwd_ex, args, stream, "jas_fwd"), res
+
+
+def _prepared(fn, args, stream, name):
+    d, rest, launch = args[0], args[1:-1], args[-1]
+    dp = ctypes.byref(d)
+    lp = ctypes.byref(launch) if launch is not None else None
+    keep = (d, launch)  # the structures the pointers above refer to
+
+    def run():
+        st = fn(dp, *rest, lp, stream)
+        if st != 0:
+            raise JasError(st, name)
+    run.keep = keep
+    return run
+
+
+def _bwd_args(probs, dprobs, p_sink, out, d_sink, workspace, launch, causal, key_len):
+    """Validate a backward and allocate its missing outputs: (arguments of
+    jas_bwd_ex without the stream, result tuple)."""
     import torch
     shape, ld = _shape4(probs)
     B, H, S, N = shape
@@ -331,13 +369,34 @@ def bwd(probs, dprobs, p_sink=None, out=None, d_sink=None, workspace=None, launc
             workspace = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device=probs.device)
         _check_vec(d_sink, probs, torch.float32, H, "d_sink")
         _check_vec(workspace, probs, torch.uint8, ws_bytes, "workspace")
-    st = _on_device(probs, jas_bwd_ex, d, _ptr(probs), _ptr(dprobs), _ptr(key_len), _ptr(p_sink),
-                    _ptr(out), _ptr(d_sink) if p_sink is not None else None,
-                    _ptr(workspace) if p_sink is not None else None,
-                    workspace.numel() if workspace is not None else 0, _launch(launch))
+    args = (d, _ptr(probs), _ptr(dprobs), _ptr(key_len), _ptr(p_sink), _ptr(out),
+            _ptr(d_sink) if p_sink is not None else None,
+            _ptr(workspace) if p_sink is not None else None,
+            workspace.numel() if workspace is not None else 0, _launch(launch))
+    return args, (out, (d_sink if p_sink is not None else None))
+
+
+def bwd(probs, dprobs, p_sink=None, out=None, d_sink=None, workspace=None, launch=None,
+        causal=False, key_len=None):
+    """Backward on device tensors (``causal`` / ``key_len`` as for the
+    forward: P is taken as +0 on excluded keys).  Returns (dscores, d_sink or
+    None)."""
+    args, res = _bwd_args(probs, dprobs, p_sink, out, d_sink, workspace, launch, causal, key_len)
+    st = _on_device(probs, jas_bwd_ex, *args)
     if st != 0:
         raise JasError(st, "jas_bwd")
-    return out, (d_sink if p_sink is not None else None)
+    return res
+
+
+def bwd_prepared(probs, dprobs, p_sink=None, out=None, d_sink=None, workspace=None, launch=None,
+                 causal=False, key_len=None):
+    """:func:`bwd` prepared once, as :func:`fwd_prepared`: returns (run,
+    result)."""
+    import torch
+    args, res = _bwd_args(probs, dprobs, p_sink, out, d_sink, workspace, launch, causal, key_len)
+    with torch.cuda.device(probs.device):
+        stream = torch.cuda.current_stream(probs.device).cuda_stream
+    return _prepared(lib().jas_bwd_ex, args, stream, "jas_bwd"), res
 
 
 # ---- fused attention ----------------------------------------------------------

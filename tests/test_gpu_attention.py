@@ -280,6 +280,25 @@ def test_attention_query_blocks_identical(dt, D):
             assert raw_bytes(rs[2][key]) == ref, f"{key}: 2 blocks != 1 block"
 
 
+def test_attention_query_blocks_per_query_mask():
+    # a mask that varies by query runs one block whatever is asked: the same
+    # bytes for 0, 1 and 2, and P still jas_fwd of the scores (oracle check
+    # with two blocks asked)
+    B, H, Hkv, Sq, N, D = 1, 2, 2, 140, 500, 128
+    q, k, v = draw(77, B, H, Hkv, Sq, N, D, torch.bfloat16)
+    mask = synth.normal((B * H * Sq * N,), 1.0, 78, "cpu")
+    mask[::5] = float("-inf")
+    strides = (H * Sq * N, Sq * N, N)
+    log("attention with a per-query mask: query blocks 0 / 1 / 2")
+    rs = [jas.attn_fwd(q.to(dev()), k.to(dev()), v.to(dev()), scale=0.1, mask=mask.to(dev()),
+                       mask_strides=strides, want_lse=True, query_blocks=qb) for qb in (0, 1, 2)]
+    torch.cuda.synchronize()
+    for key in ("out", "lse"):
+        ref = raw_bytes(rs[1][key])
+        assert raw_bytes(rs[0][key]) == ref and raw_bytes(rs[2][key]) == ref, key
+    check(q, k, v, 0.1, mask=mask, mask_strides=strides, qb=2)
+
+
 def test_joint_attention_query_blocks_identical():
     # the joint image+text shape, where the library picks 2 blocks per
     # wavefront: the same bytes as with 1

@@ -228,3 +228,27 @@ def test_fp16_joint_attention_1x24x4352x4352_sampled():
     torch.cuda.synchronize()
     dS_o, _ = oracle_rows_bwd(gather_rows(Pin, idx), gather_rows(gin, idx), N)
     assert_bitexact(gather_rows(dS, idx), dS_o, "fp16 joint dS")
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_prepared_calls_match_wrapper(dt):
+    # fwd_prepared / bwd_prepared (the checks done once, then one C call per
+    # run) write the bytes fwd / bwd write, with the mask, the sink, the lse
+    # and the causal cut; running them twice changes nothing
+    B, H, S, N = 2, 3, 40, 700
+    log(f"prepared calls {dt}")
+    s = synth.normal((B, H, S, N), 2.0, 501, dev(), dt)
+    g = synth.normal((B, H, S, N), 1.0, 502, dev(), dt)
+    mask = synth.normal((B, 1, 1, N), 1.0, 503, dev())
+    mask[1, ..., 600:] = float("-inf")
+    sink = synth.normal((H,), 1.0, 504, dev())
+    P_w, ps_w, lse_w = jas.fwd(s, mask=mask, sink=sink, causal=True, want_lse=True)
+    dS_w, dsk_w = jas.bwd(P_w, g, p_sink=ps_w, causal=True)
+    run_f, (P, ps, lse) = jas.fwd_prepared(s, mask=mask, sink=sink, causal=True, want_lse=True)
+    run_b, (dS, dsk) = jas.bwd_prepared(P, g, p_sink=ps, causal=True)
+    for _ in range(2):
+        run_f()
+        run_b()
+        torch.cuda.synchronize()
+        for a, b in ((P, P_w), (ps, ps_w), (lse, lse_w), (dS, dS_w), (dsk, dsk_w)):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
