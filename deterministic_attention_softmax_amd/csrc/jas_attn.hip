@@ -558,13 +558,14 @@ __global__ __launch_bounds__(256) void vt_kernel(const uint16_t *v, uint16_t *vt
 }
 
 // Query blocks per wave.  Two blocks halve the LDS operand bytes per
-// product but need about 240 registers per lane (two waves per SIMD instead
-// of three) and twice the tile-maximum LDS.  The default takes them for the
-// fast path of head dimension 128 when the workgroup's LDS stays within
-// 64 KB and there are units enough for one round of the chip's workgroup
-// slots (256 CUs x 2).  Measured on MI355X, joint shape [1,24,4352,128]
-// with its padding mask: 0.584 ms with one block, 0.514 ms with two;
-// causal [1,32,8192,128] with the sink: 1.27 ms and 1.03 ms.  The query
+// product but need 210-255 registers per lane (two waves per SIMD instead
+// of three or four) and twice the tile-maximum LDS.  The default takes them
+// for the fast path when the workgroup's LDS stays within 64 KB and there
+// are units enough for one round of the chip's workgroup slots (256 CUs x
+// 2).  Measured on MI355X, joint shape [1,24,4352,128] with its padding
+// mask: 0.584 ms with one block, 0.514 ms with two; causal
+// [1,32,8192,128] with the sink: 1.27 ms and 1.03 ms; head dimension 64,
+// the same two shapes: 0.429 / 0.377 ms and 0.815 / 0.700 ms.  The query
 // blocks share one set of mask registers, so a mask that varies by query
 // always runs with one block, whatever was asked.  Every choice gives the
 // same bits.
@@ -574,7 +575,7 @@ int attn_query_blocks(const AttnArgs &a, bool write, int asked) {
   if (a.mask != nullptr && a.msq != 0) return 1;
   if (kStatic + (size_t)kAttnWaves * a.T * 32 * sizeof(float) > 65536) return 1;
   if (asked != 0) return asked;
-  if (write || D != 128) return 1;
+  if (write) return 1;
   const int64_t units2 = a.B * a.H * ((a.Sq + 127) / 128);
   if (units2 < 2 * 256) return 1;
   return 2;

@@ -300,8 +300,8 @@ jas_status_t jas_attn_fwd(const jas_attn_desc_t *desc, const void *q, const void
  * K and V operand read between two products.  The library runs 1 block,
  * whatever was asked, when the mask varies by query (mask_stride_q != 0) or
  * when two blocks' tile maxima would take the workgroup's LDS past 64 KB
- * (more than 11,264 keys at head_dim 128).  Its own choice (0) is 2 for
- * head_dim 128 without JAS_FLAG_PROBS / JAS_FLAG_SCORES when
+ * (more than 11,264 keys at head_dim 128).  Its own choice (0) is 2
+ * without JAS_FLAG_PROBS / JAS_FLAG_SCORES when
  * batch*heads*ceil(q_len/128) >= 512, else 1.  Each query is computed by
  * the same operations in the same order either way, so the outputs are
  * identical for 0, 1 and 2 (RL-Kernel PR #240, Fixed Reduction Contract:
