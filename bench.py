@@ -111,9 +111,8 @@ def attn_source_hash():
 
 
 def load_attn_traffic(wl):
-    """HBM bytes per fused attention call (V transpose and fused kernel) from
-    the committed PMC record, or None when there is none or the sources
-    changed since."""
+    """HBM bytes per fused attention call from the committed PMC record, or
+    None when there is none or the sources changed since."""
     path = traffic_record_path(wl)
     if not os.path.exists(path):
         return None
@@ -481,23 +480,22 @@ def bench_attention(args):
     scale = 1.0 / np.sqrt(D)
     out = torch.empty_like(q)
     d = jas.make_attn_desc(B, H, Hkv, S, N, D, jas.JAS_DTYPE_BF16, 0, scale)
-    ws = torch.empty(jas.jas_attn_workspace_bytes(d), dtype=torch.uint8, device=dev)
 
     # rotated buffer sets (copies of the same inputs), as in the softmax bench:
     # consecutive calls do not find each other's q, k, v and out in the
     # Infinity Cache (within one call K and V are shared by design)
-    set_bytes = 2 * (2 * q.numel() + 2 * k.numel()) + ws.numel()
+    set_bytes = 2 * (2 * q.numel() + 2 * k.numel())
     nsets = max(1, -(-ROTATE_BYTES // set_bytes))
-    sets = [(q, k, v, out, ws)] + [(q.clone(), k.clone(), v.clone(), torch.empty_like(q),
-                                    torch.empty_like(ws)) for _ in range(nsets - 1)]
+    sets = [(q, k, v, out)] + [(q.clone(), k.clone(), v.clone(), torch.empty_like(q))
+                               for _ in range(nsets - 1)]
     nstep = [0]
 
     def step():
-        qi, ki, vi, oi, wi = sets[nstep[0] % nsets]
+        qi, ki, vi, oi = sets[nstep[0] % nsets]
         nstep[0] += 1
         return jas.attn_fwd(qi, ki, vi, scale=scale, mask=mask,
                             mask_strides=None if mask is None else (N, 0, 0), sink=sink,
-                            causal=causal, want_lse=True, out=oi, workspace=wi,
+                            causal=causal, want_lse=True, out=oi,
                             query_blocks=args.attn_query_blocks)
 
     check = None
@@ -551,7 +549,7 @@ def bench_attention(args):
                    "sink": has_sink, "useful_flops": flops,
                    "query_blocks_per_wave": args.attn_query_blocks or "library default"},
         "buffer_sets": nsets,
-        "roofline": {"bound": "mfma", "kernel": "jas_attn_fwd (V transpose + fused kernel)",
+        "roofline": {"bound": "mfma", "kernel": "jas_attn_fwd (fused kernel)",
                      "achieved": round(ktf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(ktf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": load_attn_traffic(wl),
                      "flops_per_launch": flops, "avg_launch_ms": round(float(ms.mean()), 4)},
@@ -622,7 +620,7 @@ def summarize_attn_profiles(prof_dir, wl):
     avg_attn = None
     for r in rows:
         n = r["Name"]
-        if "attn_fwd_kernel" not in n and "vt_kernel" not in n:
+        if "attn_fwd_kernel" not in n:
             continue
         name = re.sub(r"\([^()]*\)$", "", n).replace("void ", "")
         a = float(r["AverageNs"]) / 1e3
@@ -634,8 +632,8 @@ def summarize_attn_profiles(prof_dir, wl):
         out += ["", f"Fused kernel alone: {flops / (avg_attn * 1e-6) / 1e12:.0f} TFLOP/s of useful "
                 f"attention FLOPs ({flops:.4g} per call; the kernel also recomputes QK once)."]
     if line:
-        out += ["", "The same run's bench.py line (HIP events around the whole call, transpose "
-                f"included): {line['roofline']['avg_launch_ms'] * 1e3:.1f} us, {line['value']} TFLOP/s."]
+        out += ["", "The same run's bench.py line (HIP events around the whole call): "
+                f"{line['roofline']['avg_launch_ms'] * 1e3:.1f} us, {line['value']} TFLOP/s."]
     counters = {}
     for i in (1, 2):
         path = os.path.join(prof_dir, f"pmc{i}", f"{wl}_counter_collection.csv")
@@ -663,16 +661,15 @@ def summarize_attn_profiles(prof_dir, wl):
 
 def summarize_attn_traffic(prof_dir, wl):
     """profiles/pmc_traffic_jas_<wl>.{md,json}: HBM bytes per fused attention
-    call (the V transpose and the fused kernel) from FETCH_SIZE / WRITE_SIZE,
-    calibrated on the copy kernel bench.py runs in the same process."""
+    call (the fused kernel, which reads V in place) from FETCH_SIZE /
+    WRITE_SIZE, calibrated on the copy kernel bench.py runs in the same
+    process."""
     import csv
     desc, B, H, Hkv, S, N, D, has_mask, causal, has_sink = ATTN_WORKLOADS[wl]
 
     def kind(name):
         if "attn_fwd_kernel" in name:
             return "attn"
-        if "vt_kernel" in name:
-            return "vt"
         if "copy16<false>" in name:
             return "copy"
         return None
@@ -706,19 +703,19 @@ def summarize_attn_traffic(prof_dir, wl):
            f"FETCH_SIZE x {fac['FETCH_SIZE']:.4f}, WRITE_SIZE x {fac['WRITE_SIZE']:.4f}.", "",
            "| kernel | dispatches | HBM read MB | HBM written MB |", "|---|---|---|---|"]
     tot_r = tot_w = 0.0
-    for k in ("vt", "attn"):
+    for k in ("attn",):
         rd = float(np.mean(counters[(k, "FETCH_SIZE")])) * fac["FETCH_SIZE"]
         wr = float(np.mean(counters[(k, "WRITE_SIZE")])) * fac["WRITE_SIZE"]
         tot_r, tot_w = tot_r + rd, tot_w + wr
         rec["kernels"][k] = {"hbm_read_bytes": int(rd), "hbm_write_bytes": int(wr)}
-        md.append(f"| {'V transpose' if k == 'vt' else 'fused attention'} | "
+        md.append(f"| fused attention | "
                   f"{len(counters[(k, 'FETCH_SIZE')])} | {rd / 1e6:.1f} | {wr / 1e6:.1f} |")
     rec["call"] = {"hbm_bytes_per_call": int(tot_r + tot_w), "algorithmic_bytes_per_call": alg_r + alg_w}
     md += ["", f"Per call: {tot_r / 1e6:.1f} MB read and {tot_w / 1e6:.1f} MB written, against "
            f"{alg_r / 1e6:.1f} MB and {alg_w / 1e6:.1f} MB of algorithmic bytes (q, k and v read once, "
            f"out written once; mask, lse and sink values not counted): "
-           f"{(tot_r + tot_w) / (alg_r + alg_w):.3f} x.  The excess is the transposed copy of V "
-           "(written and read once) and K / V read by several XCDs.", "",
+           f"{(tot_r + tot_w) / (alg_r + alg_w):.3f} x.  The excess is K and V read by more than one "
+           "XCD (each XCD's L2 holds its own copy).", "",
            f"Attention source sha256 at measurement: `{rec['attn_source_sha256']}`; bench.py reports "
            "the per-call bytes as `roofline.traffic` only while the sources still hash to it."]
     open(os.path.join(PROFILES, f"pmc_traffic_jas_{wl}.md"), "w").write("\n".join(md) + "\n")

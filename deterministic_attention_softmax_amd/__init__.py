@@ -499,13 +499,17 @@ def attn_fwd(q, k, v, scale=None, mask=None, mask_strides=None, sink=None, causa
     if tuple(out.shape) != tuple(q.shape):
         raise ValueError("out must have q's shape")
     res["out"] = out
+    # the library needs no workspace (jas_attn_workspace_bytes is 0); one
+    # given is passed on and left untouched
     ws_bytes = jas_attn_workspace_bytes(d)
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    _check_vec(workspace, q, torch.uint8, ws_bytes, "workspace")
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _check_vec(workspace, q, torch.uint8, ws_bytes, "workspace")
     st = _on_device(q, jas_attn_fwd_ex, d, _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(key_len),
                     _ptr(sink), _ptr(out), _ptr(res["lse"]), _ptr(res["p_sink"]), _ptr(res["probs"]),
-                    _ptr(res["scores"]), _ptr(workspace), workspace.numel(), int(query_blocks))
+                    _ptr(res["scores"]), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                    int(query_blocks))
     if st != 0:
         raise JasError(st, "jas_attn_fwd")
     return res

@@ -314,10 +314,8 @@ jas_status_t bwd_impl(const jas_desc_t *d, const void *probs, const void *dprobs
 // ---- fused attention -------------------------------------------------------
 
 struct AttnDims {
-  int64_t rows;      // batch*heads*q_len
-  int64_t Np;        // keys padded to whole tiles
+  int64_t rows;  // batch*heads*q_len
   int T;
-  int64_t ws_bytes;  // V^T
 };
 
 jas_status_t check_attn_desc(const jas_attn_desc_t *d, AttnDims *dm) {
@@ -336,7 +334,8 @@ jas_status_t check_attn_desc(const jas_attn_desc_t *d, AttnDims *dm) {
   if (d->kv_len > JAS_ATTN_MAX_KEYS) return JAS_ERR_UNSUPPORTED;
   int64_t t = 0, rows = 0;
   if (!mul_ok(d->batch, d->heads, &t) || !mul_ok(t, d->q_len, &rows)) return JAS_ERR_BAD_SHAPE;
-  // one (batch, head)'s Q, K and V^T are addressed with 32-bit byte offsets
+  // one (batch, head)'s Q, K and V are addressed with 32-bit byte offsets
+  // (K and V: at most JAS_ATTN_MAX_KEYS x 128 x 2 bytes)
   int64_t qbytes = 0;
   if (!mul_ok(d->q_len, d->head_dim * 2, &qbytes) || qbytes > 0x7fffffff) return JAS_ERR_UNSUPPORTED;
   // so is one (batch, head)'s mask: its last query row ends within 2 GiB
@@ -347,19 +346,13 @@ jas_status_t check_attn_desc(const jas_attn_desc_t *d, AttnDims *dm) {
       return JAS_ERR_UNSUPPORTED;
   }
   const int T = (int)((d->kv_len + jas::kTile - 1) / jas::kTile);
-  const int64_t Np = (int64_t)T * jas::kTile;
-  int64_t ws = 0;
-  if (!mul_ok(d->batch, d->kv_heads, &t) || !mul_ok(t, d->head_dim * Np * 2, &ws))
-    return JAS_ERR_BAD_SHAPE;
   int64_t probe = 0;
+  if (!mul_ok(d->batch, d->kv_heads, &t) || !mul_ok(t, d->kv_len * d->head_dim * 2, &probe))
+    return JAS_ERR_BAD_SHAPE;
   if (!mul_ok(rows, d->kv_len * 4, &probe) || !mul_ok(rows, d->head_dim * 2, &probe))
     return JAS_ERR_BAD_SHAPE;
-  // the transpose of V runs one workgroup per (key/value head, 64 keys)
-  if (!mul_ok(t, Np / 64, &probe) || probe > 0x7fffffff) return JAS_ERR_UNSUPPORTED;
   dm->rows = rows;
-  dm->Np = Np;
   dm->T = T;
-  dm->ws_bytes = (ws + 255) & ~(int64_t)255;
   return JAS_OK;
 }
 
@@ -383,8 +376,9 @@ jas_status_t attn_fwd_impl(const jas_attn_desc_t *d, const void *q, const void *
   if ((has_mask && !mask) || (has_sink && (!sink || !p_sink)) || (has_klen && !key_len) ||
       (has_lse && !lse) || (has_probs && !probs) || (has_scores && !scores))
     return JAS_ERR_NULL_POINTER;
-  if (!ws || (int64_t)ws_bytes < dm.ws_bytes) return JAS_ERR_WORKSPACE;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(ws, 16) ||
+  (void)ws;  // no workspace is needed: any pointer and size are accepted
+  (void)ws_bytes;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
       !aligned(out, 2) || (probs && !aligned(probs, 2)) || (mask && !aligned(mask, 4)) ||
       (sink && !aligned(sink, 4)) || (p_sink && !aligned(p_sink, 4)) ||
       (lse && !aligned(lse, 4)) || (scores && !aligned(scores, 4)) ||
@@ -413,8 +407,7 @@ jas_status_t attn_fwd_impl(const jas_attn_desc_t *d, const void *q, const void *
   const Range outs[] = {range_of(out, qbytes), range_of(lse, has_lse ? dm.rows * 4 : 0),
                         range_of(p_sink, has_sink ? dm.rows * 4 : 0),
                         range_of(probs, has_probs ? dm.rows * d->kv_len * 2 : 0),
-                        range_of(scores, has_scores ? dm.rows * d->kv_len * 4 : 0),
-                        range_of(ws, dm.ws_bytes)};
+                        range_of(scores, has_scores ? dm.rows * d->kv_len * 4 : 0)};
   for (const Range &o : outs) {
     for (const Range &i : in)
       if (overlap(o, i)) return JAS_ERR_ALIASING;
@@ -426,7 +419,6 @@ jas_status_t attn_fwd_impl(const jas_attn_desc_t *d, const void *q, const void *
   a.q = q;
   a.k = k;
   a.v = v;
-  a.vt = ws;
   a.out = out;
   a.mask = has_mask ? mask : nullptr;
   a.msb = d->mask_stride_b;
@@ -446,7 +438,6 @@ jas_status_t attn_fwd_impl(const jas_attn_desc_t *d, const void *q, const void *
   a.N = d->kv_len;
   a.D = (int)D;
   a.T = dm.T;
-  a.Np = (int)dm.Np;
   // one workgroup of 4 waves per 64 * query_blocks queries of a (batch, head)
   if (jas::launch_attn_fwd(d->dtype, a, query_blocks, (hipStream_t)stream) != hipSuccess)
     return JAS_ERR_HIP;
@@ -513,9 +504,8 @@ jas_status_t jas_launch_plan(const jas_desc_t *desc, int backward, const jas_lau
 }
 
 size_t jas_attn_workspace_bytes(const jas_attn_desc_t *desc) {
-  AttnDims dm;
-  if (check_attn_desc(desc, &dm) != JAS_OK) return 0;
-  return (size_t)dm.ws_bytes;
+  (void)desc;  // the fused kernel reads V in place: no workspace for any shape
+  return 0;
 }
 
 jas_status_t jas_attn_fwd(const jas_attn_desc_t *desc, const void *q, const void *k,

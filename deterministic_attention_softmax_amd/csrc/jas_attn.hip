@@ -13,10 +13,10 @@
 // fp16): A = 16 keys x 32 dims of K, B = 32 dims x 16 queries of Q (kept in
 // registers for the whole row), so lane l holds, for query l%16 of a block,
 // four consecutive keys of a 16-key block.  With two query blocks every K
-// operand read from LDS (and every V^T operand in the PV product) feeds two
+// operand read from LDS (and every V operand in the PV product) feeds two
 // MFMAs, which halves the LDS bytes per product, the limit of the one-block
-// kernel.  Keys go through the workgroup 32 at a time: K (32 keys x D) and
-// the transposed V (D x 32 keys) are loaded with coalesced 16-byte loads
+// kernel.  Keys go through the workgroup 32 at a time: K and V (32 keys x
+// D each, as they lie in memory) are loaded with coalesced 16-byte loads
 // into double-buffered LDS, K two steps and V one step ahead of use, and
 // each step issues the next step's QK product before its own softmax work
 // (a one-step software pipeline).  LDS row strides are 32 modulo 64 bytes,
@@ -33,9 +33,8 @@
 // the tile's keys in order.  The same registers, rounded to the tensor
 // dtype, are the A operand of the PV product (16 queries x 32 keys, lane
 // group g holding 8 consecutive keys), so P never leaves the registers; B
-// is 32 keys x 16 dims of V, read from the LDS copy of the transposed V,
-// which the library writes into the caller's workspace first (dims x keys,
-// zero-padded to whole tiles).
+// is 32 keys x 16 dims of V, built from the LDS rows of V by gfx950's
+// transposed LDS read (ds_read_b64_tr_b16), so V needs no transposed copy.
 //
 // The softmax is done in two passes over the keys, so that P is exactly the
 // row softmax of the binary32 scores (the bits jas_fwd gives on them):
@@ -58,6 +57,8 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v2i16 __attribute__((ext_vector_type(2)));
 
 constexpr int kAttnWaves = 4;  // waves per workgroup, each on its own queries
 
@@ -109,7 +110,7 @@ __device__ __forceinline__ int64_t xcd_unit(int64_t bid, int64_t G) {
 
 // MASK: an additive mask is given; WRITE: the scores and / or P are written
 // out as well (for checking), which the fast path does not carry.  QB: blocks
-// of 16 queries per wave.  With QB = 2 each K and V^T operand read from LDS
+// of 16 queries per wave.  With QB = 2 each K and V operand read from LDS
 // feeds two MFMAs, one per query block, which halves the LDS bytes per
 // product.  Every query goes through the same operations, in the same order,
 // whatever QB is, so QB never changes a bit of the results.
@@ -124,14 +125,16 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
   // LDS rows: a 16-byte read by each lane of 16 rows (lane groups 16 bytes
   // apart) is free of bank conflicts on gfx950 when the row stride is 32
   // modulo 64 bytes (measured; strides 16 modulo 32 bytes cost 4 extra
-  // cycles per read): K rows of D + 16 elements, V^T rows of 48
+  // cycles per read): K rows of D + 16 elements.  V rows are D + 16 elements
+  // too, which with the row order of vrow() below spreads each transposed
+  // read's 8 rows of 32 bytes over different banks
   constexpr int KROW = D + 16;     // LDS row of K (elements)
-  constexpr int VROW = SUB + 16;   // LDS row of V^T
+  constexpr int VROW = D + 16;     // LDS row of V (one key's D dims)
   constexpr int KCH = SUB * D / 8 / (kWave * kAttnWaves);  // 16-byte chunks per thread
   constexpr int VCH = D * SUB / 8 / (kWave * kAttnWaves);
   static_assert(KCH >= 1 && VCH >= 1, "sub-tile smaller than the workgroup");
   __shared__ __align__(16) uint16_t lk[2][SUB * KROW];
-  __shared__ __align__(16) uint16_t lv[2][D * VROW];
+  __shared__ __align__(16) uint16_t lv[2][SUB * VROW];
   extern __shared__ float lds_m[];  // per wave T x QW tile maxima (sized at launch)
 
   const int tid = threadIdx.x;
@@ -166,8 +169,8 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
 
     const Buf kbuf(static_cast<const char *>(a.k) + (b * a.Hkv + hk) * a.N * D * ESZ,
                    (uint32_t)(a.N * D * ESZ));
-    const Buf vbuf(static_cast<const char *>(a.vt) + (b * a.Hkv + hk) * (int64_t)D * a.Np * ESZ,
-                   (uint32_t)((int64_t)D * a.Np * ESZ));
+    const Buf vbuf(static_cast<const char *>(a.v) + (b * a.Hkv + hk) * a.N * D * ESZ,
+                   (uint32_t)(a.N * D * ESZ));
 
     // Q^T operand of block qb (B of the QK product): query qw + 16qb + c16,
     // dims 32ds + 8g .. +7.  The block's buffer ends at the last query, so
@@ -235,7 +238,7 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
       moff = (uint32_t)((int64_t)(qvalid[0] ? qq[0] : Sq - 1) * a.msq * 4) + 32u * (uint32_t)g;
     }
 
-    // ---- staging: sub-tile `it` (keys 32*it .. +31) of K, and of V^T ----
+    // ---- staging: sub-tile `it` (keys 32*it .. +31) of K, and of V ----
     u32x4 pk[KCH], pv[VCH];
     auto fetch_k = [&](int it) {
 #pragma unroll
@@ -256,20 +259,27 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
         *reinterpret_cast<u32x4 *>(&lk[buf][pr * KROW + 8 * c8]) = pk[c];
       }
     };
+    // V rows as they are in memory: 16-byte chunks of 8 dims of one key;
+    // keys past N read 0 (outside the buffer), so 0 * V adds nothing
     auto fetch_v = [&](int it) {
 #pragma unroll
       for (int c = 0; c < VCH; ++c) {
         const int ch = tid + c * kWave * kAttnWaves;
-        const int d = ch / (SUB / 8), k8 = ch % (SUB / 8);
-        pv[c] = bload4(vbuf, (uint32_t)((d * a.Np + 8 * k8) * ESZ), (uint32_t)(SUB * it * ESZ));
+        const int r = ch / (D / 8), c8 = ch % (D / 8);
+        pv[c] = bload4(vbuf, (uint32_t)((r * D + 8 * c8) * ESZ), (uint32_t)(SUB * it * D * ESZ));
       }
     };
+    // key r of the sub-tile at LDS row vrow(r): bit 2 flipped for keys with
+    // bit 3 set, so that the 8 rows one transposed read touches (keys
+    // 8g + 0..3 or 8g + 4..7 of two neighbouring groups g) fall on
+    // different banks
+    auto vrow = [](int r) { return r ^ (((r >> 3) & 1) << 2); };
     auto put_v = [&](int buf) {
 #pragma unroll
       for (int c = 0; c < VCH; ++c) {
         const int ch = tid + c * kWave * kAttnWaves;
-        const int d = ch / (SUB / 8), k8 = ch % (SUB / 8);
-        *reinterpret_cast<u32x4 *>(&lv[buf][d * VROW + 8 * k8]) = pv[c];
+        const int r = ch / (D / 8), c8 = ch % (D / 8);
+        *reinterpret_cast<u32x4 *>(&lv[buf][vrow(r) * VROW + 8 * c8]) = pv[c];
       }
     };
     // S^T of sub-tile it from LDS buffer buf for every query block: key
@@ -494,10 +504,24 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
             }
           }
         }
-        // B operand: keys 32it + 8g .. +7 of dims 16db + c16, shared by the query blocks
+        // B operand: keys 32it + 8g .. +7 of dims 16db + c16, shared by the
+        // query blocks, built by two transposed LDS reads (gfx950
+        // ds_read_b64_tr_b16).  In each group of 16 lanes, lane j names the
+        // 4 dims 16db + 4(j%4) .. +3 of key 8g + j/4 (then 8g + 4 + j/4);
+        // the read hands lane i the 4 values of dim 16db + i for those 4
+        // keys, in key order.
+        const int vk0 = vrow(8 * g + (c16 >> 2)), vk1 = vrow(8 * g + 4 + (c16 >> 2));
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const u32x4 vv = *reinterpret_cast<const u32x4 *>(&lv[cur][(16 * db + c16) * VROW + 8 * g]);
+          const int dc = 16 * db + 4 * (c16 & 3);
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16 *)(&lv[cur][vk0 * VROW + dc]));
+          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16 *)(&lv[cur][vk1 * VROW + dc]));
+          const u32x4 vv = {__builtin_bit_cast(uint32_t, v2i16{lo[0], lo[1]}),
+                            __builtin_bit_cast(uint32_t, v2i16{lo[2], lo[3]}),
+                            __builtin_bit_cast(uint32_t, v2i16{hi[0], hi[1]}),
+                            __builtin_bit_cast(uint32_t, v2i16{hi[2], hi[3]})};
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32<DT>(pa[qb], vv, o[qb][db]);
         }
@@ -528,43 +552,6 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_fwd_kernel(const Attn
   }
 }
 
-// V [B, Hkv, N, D] -> V^T [B, Hkv, D, Np], keys N .. Np-1 zero.  One
-// workgroup per (head, 64-key block): 16-byte loads of 8 dims of a key,
-// scattered into an LDS tile [D][64 keys], then 16-byte stores of 8 keys
-// of a dim.  The tile row is 72 elements (144 bytes) so that the 8 lanes
-// writing one key's 8 dims fall in different banks.
-template <int D>
-__global__ __launch_bounds__(256) void vt_kernel(const uint16_t *v, uint16_t *vt, int64_t heads,
-                                                 int64_t N, int64_t Np) {
-  constexpr int TROW = 72;
-  __shared__ __align__(16) uint16_t tile[D * TROW];
-  const int64_t kblocks = Np / 64;
-  const int64_t hb = blockIdx.x / kblocks;
-  const int64_t k0 = (blockIdx.x % kblocks) * 64;
-  if (hb >= heads) return;
-  const uint16_t *src = v + hb * N * D;
-  uint16_t *dst = vt + hb * (int64_t)D * Np;
-  constexpr int CH = 64 * D / 8 / 256;  // 16-byte chunks per thread
-#pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const int i = threadIdx.x + 256 * c;
-    const int kk = i / (D / 8), d8 = i % (D / 8);
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (k0 + kk < N) w = *reinterpret_cast<const u32x4 *>(src + (k0 + kk) * D + 8 * d8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      tile[(8 * d8 + e) * TROW + kk] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-  }
-  __syncthreads();
-#pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const int i = threadIdx.x + 256 * c;
-    const int d = i / 8, k8 = i % 8;
-    *reinterpret_cast<u32x4 *>(dst + (int64_t)d * Np + k0 + 8 * k8) =
-        *reinterpret_cast<const u32x4 *>(&tile[d * TROW + 8 * k8]);
-  }
-}
-
 // Query blocks per wave.  Two blocks halve the LDS operand bytes per
 // product but need 210-255 registers per lane (two waves per SIMD instead
 // of three or four) and twice the tile-maximum LDS.  The default takes them
@@ -579,7 +566,7 @@ __global__ __launch_bounds__(256) void vt_kernel(const uint16_t *v, uint16_t *vt
 // same bits.
 template <int D>
 int attn_query_blocks(const AttnArgs &a, bool write, int asked) {
-  constexpr size_t kStatic = 2 * 32 * (D + 16) * 2 + 2 * D * 48 * 2;  // lk + lv bytes
+  constexpr size_t kStatic = 2 * (2 * 32 * (D + 16) * 2);  // lk + lv bytes
   if (a.mask != nullptr && a.msq != 0) return 1;
   if (kStatic + (size_t)kAttnWaves * a.T * 32 * sizeof(float) > 65536) return 1;
   if (asked != 0) return asked;
@@ -608,13 +595,6 @@ hipError_t attn_launch_qb(const AttnArgs &a, hipStream_t st) {
 
 template <int DT, int D>
 hipError_t attn_launch(const AttnArgs &a, int qblocks, hipStream_t st) {
-  const int64_t heads = a.B * a.Hkv;
-  const int64_t vblocks = heads * (a.Np / 64);
-  hipLaunchKernelGGL((vt_kernel<D>), dim3((unsigned)vblocks), dim3(256), 0, st,
-                     static_cast<const uint16_t *>(a.v), static_cast<uint16_t *>(a.vt), heads, a.N,
-                     (int64_t)a.Np);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const bool write = a.probs != nullptr || a.scores != nullptr;
   qblocks = attn_query_blocks<D>(a, write, qblocks);
   if (qblocks == 2) return attn_launch_qb<DT, D, 2>(a, st);

@@ -60,7 +60,6 @@ struct BwdArgs {
 // Fused attention forward (QK, the row softmax, PV).
 struct AttnArgs {
   const void *q, *k, *v;  // [B,H,Sq,D], [B,Hkv,N,D], [B,Hkv,N,D]
-  void *vt;               // workspace: V^T [B,Hkv,D,Np], keys past N zero
   void *out;              // [B,H,Sq,D]
   const float *mask;      // nullptr when no mask
   int64_t msb, msh, msq;
@@ -71,7 +70,7 @@ struct AttnArgs {
   float *scores;          // optional [B,H,Sq,N], binary32
   float scale;
   int64_t B, H, Hkv, Sq, N;
-  int D, T, Np;           // head dim, tiles, keys padded to whole tiles
+  int D, T;               // head dim, 256-key tiles
 };
 
 struct DsinkArgs {

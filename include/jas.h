@@ -274,9 +274,10 @@ typedef struct {
   int64_t mask_stride_b, mask_stride_h, mask_stride_q; /* as in jas_desc_t */
 } jas_attn_desc_t;
 
-/* Bytes of device workspace jas_attn_fwd needs: a transposed copy of V,
- * batch*kv_heads*head_dim*ceil(kv_len/256)*256 elements, rounded up to 256
- * bytes.  0 for a NULL or invalid desc. */
+/* Bytes of device workspace jas_attn_fwd needs: 0 for every desc.  The
+ * fused kernel reads V in place (its PV operands come from gfx950's
+ * transposed LDS reads), so it needs no transposed copy; the call and the
+ * workspace arguments remain so that callers that pass one keep working. */
 size_t jas_attn_workspace_bytes(const jas_attn_desc_t *desc);
 
 /* Fused attention forward.
@@ -287,9 +288,9 @@ size_t jas_attn_workspace_bytes(const jas_attn_desc_t *desc);
  *   lse, p_sink: binary32 [batch*heads*q_len], required iff JAS_FLAG_LSE /
  *   JAS_FLAG_SINK.  probs / scores: required iff JAS_FLAG_PROBS /
  *   JAS_FLAG_SCORES.
- *   workspace: device scratch of jas_attn_workspace_bytes(desc) bytes,
- *   16-byte aligned; its contents on entry do not matter.
- * Outputs must not overlap each other, the inputs or the workspace. */
+ *   workspace, workspace_bytes: not used (jas_attn_workspace_bytes is 0);
+ *   any value, NULL included, is accepted and nothing is written there.
+ * Outputs must not overlap each other or the inputs. */
 jas_status_t jas_attn_fwd(const jas_attn_desc_t *desc, const void *q, const void *k,
                           const void *v, const float *mask, const int32_t *key_len,
                           const float *sink, void *out, float *lse, float *p_sink, void *probs,
@@ -300,7 +301,7 @@ jas_status_t jas_attn_fwd(const jas_attn_desc_t *desc, const void *q, const void
  * K and V operand read between two products.  The library runs 1 block,
  * whatever was asked, when the mask varies by query (mask_stride_q != 0) or
  * when two blocks' tile maxima would take the workgroup's LDS past 64 KB
- * (more than 11,264 keys at head_dim 128).  Its own choice (0) is 2
+ * (more than 14,336 keys at head_dim 128).  Its own choice (0) is 2
  * without JAS_FLAG_PROBS / JAS_FLAG_SCORES when
  * batch*heads*ceil(q_len/128) >= 512, else 1.  Each query is computed by
  * the same operations in the same order either way, so the outputs are
