@@ -13,6 +13,8 @@
 //    (subnormals kept, overflow to infinity).
 //  * log2 sweep: every binary32 in [1, 32768] (the range of a row's sum L)
 //    through v_log_f32 against log2 in double rounded to binary32.
+//  * transposed LDS read (ds_read_b64_tr_b16) lane layout: which 16-bit
+//    elements each lane receives for given per-lane addresses.
 //  * MFMA operand layout: one 16x16x32 bf16 / fp16 product with the operands
 //    placed by the layout the attention kernel assumes (A: lane = row +
 //    16*(k/8), element k%8; B: lane = col + 16*(k/8), element k%8; D: lane =
@@ -233,6 +235,21 @@ __global__ __launch_bounds__(256) void copy16(const u32x4 *__restrict__ src, u32
   }
 }
 
+// lane layout of gfx950's transposed LDS read ds_read_b64_tr_b16: LDS holds
+// each 16-bit element's own index; lane l reads at element addr[l] (a
+// multiple of 4, checked on the host to lie inside the array) and writes
+// the 4 values it receives to out[4l .. 4l+3]
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+constexpr int kTrElems = 8192;  // 16 KB: 32 rows of the attention kernel's V stride fit
+__global__ void tr16_layout(const int *addr, uint16_t *out) {
+  __shared__ __align__(16) uint16_t lds[kTrElems];
+  for (int i = threadIdx.x; i < kTrElems; i += 64) lds[i] = (uint16_t)i;
+  __syncthreads();
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16 *)(lds + addr[threadIdx.x]));
+  for (int e = 0; e < 4; ++e) out[4 * threadIdx.x + e] = (uint16_t)r[e];
+}
+
 // lane layout of the gfx950 permlane swaps: out[2*lane], out[2*lane+1]
 __global__ void permlane_layout(uint32_t *out) {
   const uint32_t l = threadIdx.x;
@@ -376,6 +393,24 @@ int probe_copy16(const void *src, void *dst, uint64_t n16, int nontemporal, int 
 int probe_mfma_layout(const uint16_t *A, const uint16_t *B, float *D, int f16) {
   hipLaunchKernelGGL(mfma_layout, dim3(1), dim3(64), 0, 0, A, B, D, f16);
   return hipDeviceSynchronize() == hipSuccess ? 0 : -1;
+}
+
+// addr: 64 host ints (element indices), out: 256 device 16-bit words.
+// Returns -1 without launching when an address is not 8-byte aligned or
+// would read past the 8192-element array.
+int probe_tr16_layout(const int *addr_host, uint16_t *out) {
+  for (int l = 0; l < 64; ++l)
+    if (addr_host[l] < 0 || addr_host[l] % 4 != 0 || addr_host[l] + 4 > kTrElems) return -1;
+  int *d = nullptr;
+  if (hipMalloc(&d, 64 * sizeof(int)) != hipSuccess) return -1;
+  if (hipMemcpy(d, addr_host, 64 * sizeof(int), hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(d);
+    return -1;
+  }
+  hipLaunchKernelGGL(tr16_layout, dim3(1), dim3(64), 0, 0, d, out);
+  const hipError_t e = hipDeviceSynchronize();
+  (void)hipFree(d);
+  return e == hipSuccess ? 0 : -1;
 }
 
 int probe_permlane_layout(uint32_t *out) {  // out: 256 words

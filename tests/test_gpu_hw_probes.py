@@ -42,6 +42,8 @@ def probes():
     L.probe_mfma_layout.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
     L.probe_permlane_layout.restype = ctypes.c_int
     L.probe_permlane_layout.argtypes = [ctypes.c_void_p]
+    L.probe_tr16_layout.restype = ctypes.c_int
+    L.probe_tr16_layout.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_void_p]
     return L
 
 
@@ -127,3 +129,42 @@ def test_permlane_swap_layout():
     row_even = (lanes // 32) * 32 + (lanes % 16)
     assert np.array_equal(r[:, 0], row_even) and np.array_equal(r[:, 1], row_even + 16)
     assert np.array_equal(r[:, 2], lanes % 32) and np.array_equal(r[:, 3], lanes % 32 + 32)
+
+
+def test_ds_read_b64_tr_b16_layout():
+    # the fused attention builds its PV operand with this read: in each group
+    # of 16 lanes the 16 addressed 8-byte chunks form a 16 x 4 matrix C
+    # (C[j][p] = element p of lane j's chunk), and lane i receives
+    # C[4e + i/4][i % 4] for e = 0..3
+    L = probes()
+    VROW = 144  # the kernel's V row (head dim 128 + 16), elements
+
+    def vrow(r):
+        return r ^ (((r >> 3) & 1) << 2)
+
+    patterns = {"consecutive chunks": [4 * l for l in range(64)]}
+    for db, half in ((0, 0), (3, 1), (7, 0)):
+        patterns[f"attention V operand db={db} keys +{4 * half}"] = [
+            vrow(8 * (l // 16) + 4 * half + (l % 16) // 4) * VROW + 16 * db + 4 * (l % 4)
+            for l in range(64)]
+    for name, addr in patterns.items():
+        out = torch.zeros(256, dtype=torch.int16, device="cuda")
+        arr = (ctypes.c_int * 64)(*addr)
+        assert L.probe_tr16_layout(arr, out.data_ptr()) == 0, name
+        got = out.cpu().numpy().astype(np.int64).reshape(64, 4)
+        want = np.zeros((64, 4), np.int64)
+        for l in range(64):
+            g, i = l // 16, l % 16
+            for e in range(4):
+                want[l, e] = addr[16 * g + 4 * e + i // 4] + i % 4
+        log(f"ds_read_b64_tr_b16, {name}: {int((got != want).sum())} mismatches")
+        assert np.array_equal(got, want), name
+    # the attention operand: lane (g, c16) gets dim 16*db + c16 of keys
+    # 8g + 4*half .. +3, in key order
+    addr = patterns["attention V operand db=3 keys +4"]
+    out = torch.zeros(256, dtype=torch.int16, device="cuda")
+    assert L.probe_tr16_layout((ctypes.c_int * 64)(*addr), out.data_ptr()) == 0
+    got = out.cpu().numpy().astype(np.int64).reshape(64, 4)
+    for l in range(64):
+        g, c16 = l // 16, l % 16
+        assert [int(v) for v in got[l]] == [vrow(8 * g + 4 + e) * VROW + 48 + c16 for e in range(4)]
