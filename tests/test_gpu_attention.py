@@ -203,6 +203,26 @@ def test_attention_at_the_key_limit(dt):
     check(q, k, v, 1.0 / np.sqrt(D), mask=mask, mask_strides=(N, 0, 0), sink=sink, causal=True)
 
 
+def test_attention_two_blocks_at_their_lds_limit():
+    # 14,336 keys (56 tiles) at head dim 128: two query blocks' tile maxima
+    # bring the workgroup's LDS to exactly 64 KB, the most the library gives
+    # them; against the oracle, and the same bytes as one block
+    B, H, Hkv, Sq, N, D = 1, 2, 1, 70, 14336, 128
+    log(f"attention at the two-block LDS limit: N={N}")
+    q, k, v = draw(95, B, H, Hkv, Sq, N, D, torch.bfloat16)
+    mask = synth.normal((B, 1, 1, N), 1.0, 96, "cpu")
+    mask[..., 9000:9100] = float("-inf")
+    sink = synth.normal((H,), 1.0, 97, "cpu")
+    check(q, k, v, 1.0 / np.sqrt(D), mask=mask, mask_strides=(N, 0, 0), sink=sink, causal=True,
+          qb=2)
+    rs = [jas.attn_fwd(q.to(dev()), k.to(dev()), v.to(dev()), mask=mask.to(dev()),
+                       mask_strides=(N, 0, 0), sink=sink.to(dev()), causal=True, want_lse=True,
+                       query_blocks=qb) for qb in (1, 2)]
+    torch.cuda.synchronize()
+    for key in ("out", "lse", "p_sink"):
+        assert raw_bytes(rs[0][key]) == raw_bytes(rs[1][key]), key
+
+
 def test_attention_batch_and_block_invariance():
     # a (batch, head)'s bytes do not move with the batch around it, nor with
     # the other query blocks of the call
