@@ -86,12 +86,12 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 def kernel_source_hash():
     """sha256 over the sources of the row-softmax kernels (every .h / .hip
-    file of csrc/ except the fused attention's, in name order): a traffic
-    record is only used while it still matches."""
+    file of csrc/ except the fused attention's jas_attn.hip and jas_attn.h,
+    in name order): a traffic record is only used while it still matches."""
     import hashlib
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".h", ".hip")) and name != "jas_attn.hip":
+        if name.endswith((".h", ".hip")) and name not in ("jas_attn.hip", "jas_attn.h"):
             h.update(name.encode())
             with open(os.path.join(CSRC, name), "rb") as f:
                 h.update(f.read())
@@ -100,10 +100,10 @@ def kernel_source_hash():
 
 def attn_source_hash():
     """sha256 over the fused attention's sources (jas_attn.hip and the
-    headers it includes, in name order), for its traffic records."""
+    headers it includes), for its traffic records."""
     import hashlib
     h = hashlib.sha256()
-    for name in ("jas_attn.hip", "jas_internal.h", "jas_kernels.h"):
+    for name in ("jas_attn.hip", "jas_attn.h", "jas_internal.h", "jas_kernels.h"):
         h.update(name.encode())
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())

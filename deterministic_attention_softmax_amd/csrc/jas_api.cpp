@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include "jas.h"
+#include "jas_attn.h"
 #include "jas_internal.h"
 
 static_assert(JAS_MAX_KEYS == jas::kMaxStreamKeys, "the public row limit is the streaming kernels'");

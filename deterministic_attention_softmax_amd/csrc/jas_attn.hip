@@ -49,6 +49,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "jas_attn.h"
 #include "jas_kernels.h"
 
 namespace jas {

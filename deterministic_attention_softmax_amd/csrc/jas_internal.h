@@ -57,22 +57,6 @@ struct BwdArgs {
   int stash;          // streaming kernel: segments whose P is kept in LDS (set by the launcher)
 };
 
-// Fused attention forward (QK, the row softmax, PV).
-struct AttnArgs {
-  const void *q, *k, *v;  // [B,H,Sq,D], [B,Hkv,N,D], [B,Hkv,N,D]
-  void *out;              // [B,H,Sq,D]
-  const float *mask;      // nullptr when no mask
-  int64_t msb, msh, msq;
-  Exclusion ex;
-  const float *sink;      // nullptr when no sink
-  float *p_sink, *lse;    // [rows] or nullptr
-  void *probs;            // optional [B,H,Sq,N], dtype
-  float *scores;          // optional [B,H,Sq,N], binary32
-  float scale;
-  int64_t B, H, Hkv, Sq, N;
-  int D, T;               // head dim, 256-key tiles
-};
-
 struct DsinkArgs {
   const float *v;
   float *d_sink;
@@ -110,7 +94,5 @@ hipError_t launch_bwd_f16(const BwdArgs &a, const Geometry &g, hipStream_t strea
 hipError_t launch_fwd(int dtype, const FwdArgs &a, const Geometry &g, hipStream_t stream);
 hipError_t launch_bwd(int dtype, const BwdArgs &a, const Geometry &g, hipStream_t stream);
 hipError_t launch_dsink(const DsinkArgs &a, hipStream_t stream);
-// qblocks: 16-query blocks per wave (1 or 2), 0 = chosen from the shape
-hipError_t launch_attn_fwd(int dtype, const AttnArgs &a, int qblocks, hipStream_t stream);
 
 }  // namespace jas
