@@ -19,7 +19,8 @@ __all__ = [
     "STATUS", "JasError", "jas_desc_t", "jas_launch_t", "jas_attn_desc_t", "lib", "jas_fwd",
     "jas_fwd_ex", "jas_bwd", "jas_bwd_ex", "jas_bwd_workspace_bytes", "jas_attn_fwd", "jas_attn_fwd_ex",
     "jas_attn_workspace_bytes", "jas_launch_plan", "jas_status_str", "jas_contract", "make_desc",
-    "make_attn_desc", "fwd", "bwd", "fwd_prepared", "bwd_prepared", "attn_fwd", "LIB_PATH",
+    "make_attn_desc", "fwd", "bwd", "fwd_prepared", "bwd_prepared", "attn_fwd",
+    "attn_fwd_prepared", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libjas.so")
@@ -439,16 +440,10 @@ def _attn_tensor(t, name, like=None):
     return t
 
 
-def attn_fwd(q, k, v, scale=None, mask=None, mask_strides=None, sink=None, causal=False,
-             key_len=None, want_lse=False, want_probs=False, want_scores=False, out=None,
-             workspace=None, query_blocks=0):
-    """Fused attention forward on device tensors: q [B, H, Sq, D], k and v
-    [B, Hkv, N, D] (bf16 or fp16, contiguous), ``scale`` (default
-    1/sqrt(D)).  Mask, sink, causal and key lengths as for :func:`fwd`.
-    Returns a dict with ``out`` and, when asked (or a sink is given),
-    ``lse``, ``p_sink``, ``probs``, ``scores``.  ``query_blocks`` (0, 1 or 2)
-    is the launch's 16-query blocks per wavefront, 0 = the library's choice;
-    it never changes the results."""
+def _attn_args(q, k, v, scale, mask, mask_strides, sink, causal, key_len, want_lse, want_probs,
+               want_scores, out, workspace, query_blocks):
+    """Validate a fused attention call and allocate its outputs: (arguments
+    of jas_attn_fwd_ex without the stream, result dict)."""
     import math
     import torch
     _attn_tensor(q, "q")
@@ -506,10 +501,48 @@ def attn_fwd(q, k, v, scale=None, mask=None, mask_strides=None, sink=None, causa
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     if workspace is not None:
         _check_vec(workspace, q, torch.uint8, ws_bytes, "workspace")
-    st = _on_device(q, jas_attn_fwd_ex, d, _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(key_len),
-                    _ptr(sink), _ptr(out), _ptr(res["lse"]), _ptr(res["p_sink"]), _ptr(res["probs"]),
-                    _ptr(res["scores"]), _ptr(workspace), 0 if workspace is None else workspace.numel(),
-                    int(query_blocks))
+    args = (d, _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(key_len), _ptr(sink), _ptr(out),
+            _ptr(res["lse"]), _ptr(res["p_sink"]), _ptr(res["probs"]), _ptr(res["scores"]),
+            _ptr(workspace), 0 if workspace is None else workspace.numel(), int(query_blocks))
+    return args, res
+
+
+def attn_fwd(q, k, v, scale=None, mask=None, mask_strides=None, sink=None, causal=False,
+             key_len=None, want_lse=False, want_probs=False, want_scores=False, out=None,
+             workspace=None, query_blocks=0):
+    """Fused attention forward on device tensors: q [B, H, Sq, D], k and v
+    [B, Hkv, N, D] (bf16 or fp16, contiguous), ``scale`` (default
+    1/sqrt(D)).  Mask, sink, causal and key lengths as for :func:`fwd`.
+    Returns a dict with ``out`` and, when asked (or a sink is given),
+    ``lse``, ``p_sink``, ``probs``, ``scores``.  ``query_blocks`` (0, 1 or 2)
+    is the launch's 16-query blocks per wavefront, 0 = the library's choice;
+    it never changes the results."""
+    args, res = _attn_args(q, k, v, scale, mask, mask_strides, sink, causal, key_len, want_lse,
+                           want_probs, want_scores, out, workspace, query_blocks)
+    st = _on_device(q, jas_attn_fwd_ex, *args)
     if st != 0:
         raise JasError(st, "jas_attn_fwd")
     return res
+
+
+def attn_fwd_prepared(q, k, v, scale=None, mask=None, mask_strides=None, sink=None, causal=False,
+                      key_len=None, want_lse=False, want_probs=False, want_scores=False, out=None,
+                      workspace=None, query_blocks=0):
+    """:func:`attn_fwd` prepared once, as :func:`fwd_prepared`: returns (run,
+    result dict); ``run()`` is one call of jas_attn_fwd_ex on the same
+    tensors."""
+    import torch
+    args, res = _attn_args(q, k, v, scale, mask, mask_strides, sink, causal, key_len, want_lse,
+                           want_probs, want_scores, out, workspace, query_blocks)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    L = lib()
+    d, rest = args[0], args[1:]
+    dp = ctypes.byref(d)
+
+    def run():
+        st = L.jas_attn_fwd_ex(dp, *rest, stream)
+        if st != 0:
+            raise JasError(st, "jas_attn_fwd")
+    run.keep = d
+    return run, res

@@ -336,3 +336,22 @@ def test_joint_attention_query_blocks_identical():
         ref = raw_bytes(rs[1][key])
         assert raw_bytes(rs[0][key]) == ref
         assert raw_bytes(rs[2][key]) == ref
+
+
+def test_attention_prepared_call_matches_wrapper():
+    # attn_fwd_prepared (checks done once, then one C call per run) writes
+    # the bytes attn_fwd writes; running it twice changes nothing
+    B, H, Hkv, Sq, N, D = 2, 4, 2, 150, 900, 128
+    log("attention prepared call")
+    q, k, v = draw(111, B, H, Hkv, Sq, N, D, torch.bfloat16)
+    q, k, v = q.to(dev()), k.to(dev()), v.to(dev())
+    mask = synth.normal((B, 1, 1, N), 1.0, 112, dev())
+    sink = synth.normal((H,), 1.0, 113, dev())
+    kw = dict(scale=0.1, mask=mask, mask_strides=(N, 0, 0), sink=sink, causal=True, want_lse=True)
+    ref = jas.attn_fwd(q, k, v, **kw)
+    run, res = jas.attn_fwd_prepared(q, k, v, **kw)
+    for _ in range(2):
+        run()
+        torch.cuda.synchronize()
+        for key in ("out", "lse", "p_sink"):
+            assert raw_bytes(res[key]) == raw_bytes(ref[key]), key
