@@ -18,7 +18,7 @@ __all__ = [
     "JAS_MAX_KEYS", "JAS_ATTN_MAX_KEYS",
     "STATUS", "JasError", "jas_desc_t", "jas_launch_t", "jas_attn_desc_t", "lib", "jas_fwd",
     "jas_fwd_ex", "jas_bwd", "jas_bwd_ex", "jas_bwd_workspace_bytes", "jas_attn_fwd", "jas_attn_fwd_ex",
-    "jas_attn_workspace_bytes", "jas_launch_plan", "jas_status_str", "jas_contract", "make_desc",
+    "jas_launch_plan", "jas_status_str", "jas_contract", "make_desc",
     "make_attn_desc", "fwd", "bwd", "fwd_prepared", "bwd_prepared", "attn_fwd",
     "attn_fwd_prepared", "LIB_PATH",
 ]
@@ -101,14 +101,11 @@ def lib():
         L.jas_contract.restype = ctypes.c_char_p
         L.jas_contract.argtypes = []
         _AP = ctypes.POINTER(jas_attn_desc_t)
-        L.jas_attn_workspace_bytes.restype = ctypes.c_size_t
-        L.jas_attn_workspace_bytes.argtypes = [_AP]
         L.jas_attn_fwd.restype = ctypes.c_int
-        L.jas_attn_fwd.argtypes = [_AP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
-                                   ctypes.c_size_t, _VP]
+        L.jas_attn_fwd.argtypes = [_AP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]
         L.jas_attn_fwd_ex.restype = ctypes.c_int
         L.jas_attn_fwd_ex.argtypes = [_AP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
-                                      _VP, ctypes.c_size_t, ctypes.c_int, _VP]
+                                      ctypes.c_int, _VP]
         _lib = L
     return _lib
 
@@ -213,10 +210,27 @@ def _shape4(t):
         raise ValueError(f"tensors must be in device memory, not on {t.device}")
     if t.dim() != 4:
         raise ValueError("tensors are [batch, heads, q_rows, keys]")
-    if t.stride(3) != 1 or t.stride(2) < t.shape[3] or t.stride(1) != t.shape[2] * t.stride(2) \
-            or t.stride(0) != t.shape[1] * t.stride(1):
-        raise ValueError("rows must be contiguous with one row stride (ld)")
-    return t.shape, t.stride(2)
+    B, H, S, N = t.shape
+    bad = ValueError("rows must be contiguous with one row stride (ld)")
+    if N > 1 and t.stride(3) != 1:
+        raise bad
+    # row r = (b*H + h)*S + q starts at element r*ld: each row dimension of
+    # size above 1 must step by ld times the rows inside it (the stride of a
+    # dimension of size 1 never addresses anything, and torch leaves it free)
+    ld, inner = None, 1
+    for dim in (2, 1, 0):
+        if t.shape[dim] > 1:
+            if ld is None:
+                if t.stride(dim) % inner:
+                    raise bad
+                ld = t.stride(dim) // inner
+            elif t.stride(dim) != inner * ld:
+                raise bad
+        inner *= t.shape[dim]
+    ld = N if ld is None else ld
+    if ld < N:
+        raise bad
+    return t.shape, ld
 
 
 def _empty_rows_like(t, ld):
@@ -232,7 +246,8 @@ def _empty_rows_like(t, ld):
 def _check_out(out, like):
     if out.device != like.device:
         raise ValueError("every tensor must be on the scores' device")
-    if out.shape != like.shape or out.stride() != like.stride() or out.dtype != like.dtype:
+    if out.shape != like.shape or out.dtype != like.dtype or \
+            out.device.type != "cuda" or _shape4(out)[1] != _shape4(like)[1]:
         raise ValueError("the output must have the input's shape, dtype and row stride")
 
 
@@ -413,21 +428,15 @@ def make_attn_desc(B, H, Hkv, Sq, N, D, dtype_code, flags=0, scale=1.0, mask_str
     return d
 
 
-def jas_attn_workspace_bytes(desc):
-    return int(lib().jas_attn_workspace_bytes(ctypes.byref(desc)))
-
-
-def jas_attn_fwd(desc, q, k, v, mask, key_len, sink, out, lse, p_sink, probs, scores, workspace,
-                 workspace_bytes, stream):
+def jas_attn_fwd(desc, q, k, v, mask, key_len, sink, out, lse, p_sink, probs, scores, stream):
     return lib().jas_attn_fwd(ctypes.byref(desc), q, k, v, mask, key_len, sink, out, lse, p_sink,
-                              probs, scores, workspace, workspace_bytes, stream)
+                              probs, scores, stream)
 
 
 def jas_attn_fwd_ex(desc, q, k, v, mask, key_len, sink, out, lse, p_sink, probs, scores,
-                    workspace, workspace_bytes, query_blocks, stream):
+                    query_blocks, stream):
     return lib().jas_attn_fwd_ex(ctypes.byref(desc), q, k, v, mask, key_len, sink, out, lse,
-                                 p_sink, probs, scores, workspace, workspace_bytes, query_blocks,
-                                 stream)
+                                 p_sink, probs, scores, query_blocks, stream)
 
 
 def _attn_tensor(t, name, like=None):
@@ -441,7 +450,7 @@ def _attn_tensor(t, name, like=None):
 
 
 def _attn_args(q, k, v, scale, mask, mask_strides, sink, causal, key_len, want_lse, want_probs,
-               want_scores, out, workspace, query_blocks):
+               want_scores, out, query_blocks):
     """Validate a fused attention call and allocate its outputs: (arguments
     of jas_attn_fwd_ex without the stream, result dict)."""
     import math
@@ -494,22 +503,15 @@ def _attn_args(q, k, v, scale, mask, mask_strides, sink, causal, key_len, want_l
     if tuple(out.shape) != tuple(q.shape):
         raise ValueError("out must have q's shape")
     res["out"] = out
-    # the library needs no workspace (jas_attn_workspace_bytes is 0); one
-    # given is passed on and left untouched
-    ws_bytes = jas_attn_workspace_bytes(d)
-    if workspace is None and ws_bytes > 0:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    if workspace is not None:
-        _check_vec(workspace, q, torch.uint8, ws_bytes, "workspace")
     args = (d, _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(key_len), _ptr(sink), _ptr(out),
             _ptr(res["lse"]), _ptr(res["p_sink"]), _ptr(res["probs"]), _ptr(res["scores"]),
-            _ptr(workspace), 0 if workspace is None else workspace.numel(), int(query_blocks))
+            int(query_blocks))
     return args, res
 
 
 def attn_fwd(q, k, v, scale=None, mask=None, mask_strides=None, sink=None, causal=False,
              key_len=None, want_lse=False, want_probs=False, want_scores=False, out=None,
-             workspace=None, query_blocks=0):
+             query_blocks=0):
     """Fused attention forward on device tensors: q [B, H, Sq, D], k and v
     [B, Hkv, N, D] (bf16 or fp16, contiguous), ``scale`` (default
     1/sqrt(D)).  Mask, sink, causal and key lengths as for :func:`fwd`.
@@ -518,7 +520,7 @@ def attn_fwd(q, k, v, scale=None, mask=None, mask_strides=None, sink=None, causa
     is the launch's 16-query blocks per wavefront, 0 = the library's choice;
     it never changes the results."""
     args, res = _attn_args(q, k, v, scale, mask, mask_strides, sink, causal, key_len, want_lse,
-                           want_probs, want_scores, out, workspace, query_blocks)
+                           want_probs, want_scores, out, query_blocks)
     st = _on_device(q, jas_attn_fwd_ex, *args)
     if st != 0:
         raise JasError(st, "jas_attn_fwd")
@@ -527,13 +529,13 @@ def attn_fwd(q, k, v, scale=None, mask=None, mask_strides=None, sink=None, causa
 
 def attn_fwd_prepared(q, k, v, scale=None, mask=None, mask_strides=None, sink=None, causal=False,
                       key_len=None, want_lse=False, want_probs=False, want_scores=False, out=None,
-                      workspace=None, query_blocks=0):
+                      query_blocks=0):
     """:func:`attn_fwd` prepared once, as :func:`fwd_prepared`: returns (run,
     result dict); ``run()`` is one call of jas_attn_fwd_ex on the same
     tensors."""
     import torch
     args, res = _attn_args(q, k, v, scale, mask, mask_strides, sink, causal, key_len, want_lse,
-                           want_probs, want_scores, out, workspace, query_blocks)
+                           want_probs, want_scores, out, query_blocks)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
     L = lib()

@@ -360,7 +360,7 @@ jas_status_t check_attn_desc(const jas_attn_desc_t *d, AttnDims *dm) {
 jas_status_t attn_fwd_impl(const jas_attn_desc_t *d, const void *q, const void *k, const void *v,
                            const float *mask, const int32_t *key_len, const float *sink,
                            void *out, float *lse, float *p_sink, void *probs, float *scores,
-                           void *ws, size_t ws_bytes, int query_blocks, void *stream) {
+                           int query_blocks, void *stream) {
   AttnDims dm;
   jas_status_t st = check_attn_desc(d, &dm);
   if (st != JAS_OK) return st;
@@ -377,8 +377,6 @@ jas_status_t attn_fwd_impl(const jas_attn_desc_t *d, const void *q, const void *
   if ((has_mask && !mask) || (has_sink && (!sink || !p_sink)) || (has_klen && !key_len) ||
       (has_lse && !lse) || (has_probs && !probs) || (has_scores && !scores))
     return JAS_ERR_NULL_POINTER;
-  (void)ws;  // no workspace is needed: any pointer and size are accepted
-  (void)ws_bytes;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
       !aligned(out, 2) || (probs && !aligned(probs, 2)) || (mask && !aligned(mask, 4)) ||
       (sink && !aligned(sink, 4)) || (p_sink && !aligned(p_sink, 4)) ||
@@ -504,26 +502,20 @@ jas_status_t jas_launch_plan(const jas_desc_t *desc, int backward, const jas_lau
   return JAS_OK;
 }
 
-size_t jas_attn_workspace_bytes(const jas_attn_desc_t *desc) {
-  (void)desc;  // the fused kernel reads V in place: no workspace for any shape
-  return 0;
-}
-
 jas_status_t jas_attn_fwd(const jas_attn_desc_t *desc, const void *q, const void *k,
                           const void *v, const float *mask, const int32_t *key_len,
                           const float *sink, void *out, float *lse, float *p_sink, void *probs,
-                          float *scores, void *workspace, size_t workspace_bytes, void *stream) {
-  return attn_fwd_impl(desc, q, k, v, mask, key_len, sink, out, lse, p_sink, probs, scores,
-                       workspace, workspace_bytes, 0, stream);
+                          float *scores, void *stream) {
+  return attn_fwd_impl(desc, q, k, v, mask, key_len, sink, out, lse, p_sink, probs, scores, 0,
+                       stream);
 }
 
 jas_status_t jas_attn_fwd_ex(const jas_attn_desc_t *desc, const void *q, const void *k,
                              const void *v, const float *mask, const int32_t *key_len,
                              const float *sink, void *out, float *lse, float *p_sink, void *probs,
-                             float *scores, void *workspace, size_t workspace_bytes,
-                             int query_blocks, void *stream) {
+                             float *scores, int query_blocks, void *stream) {
   return attn_fwd_impl(desc, q, k, v, mask, key_len, sink, out, lse, p_sink, probs, scores,
-                       workspace, workspace_bytes, query_blocks, stream);
+                       query_blocks, stream);
 }
 
 const char *jas_status_str(jas_status_t s) {

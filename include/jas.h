@@ -66,7 +66,8 @@
  * Conventions for every entry point:
  *   - Tensor pointers are device pointers owned by the caller.  The library
  *     never allocates, frees or synchronizes; all work is enqueued on
- *     `stream` (a hipStream_t; NULL is the null stream) and the call returns
+ *     `stream` (a void * holding a hipStream_t, so this header needs no HIP
+ *     include; NULL is the null stream) and the call returns
  *     without waiting for it.
  *   - Validation is done entirely on the host before any HIP call; on any
  *     error nothing is enqueued and the status says why.  JAS_ERR_HIP means
@@ -191,8 +192,15 @@ jas_status_t jas_fwd_ex(const jas_desc_t *desc, const void *scores, const float 
                         float *lse, const jas_launch_t *launch, void *stream);
 
 /* Bytes of device workspace jas_bwd needs: 4*rows rounded up to 256 when
- * JAS_FLAG_SINK is set, else 0.  Depends on the shape and flags only (never
- * on pointers).  Returns 0 for a NULL or invalid desc. */
+ * JAS_FLAG_SINK is set, else 0.  The workspace holds each row's share
+ * -fl(p_sink*delta) of d_sink, which the d_sink kernel then reduces per head
+ * in a fixed order without atomics.  Depends on the shape and flags only,
+ * never on pointers, so a sizing call and the jas_bwd call that uses the
+ * workspace always agree on whether there is a sink (ROCm TransformerEngine
+ * PR #678, review of the backward's workspace-size query: the sizing pass
+ * and the execution pass must take the has-sink decision from the same
+ * predicate, never from whether the sink pointer is NULL, or the workspace
+ * is under-allocated).  Returns 0 for a NULL or invalid desc. */
 size_t jas_bwd_workspace_bytes(const jas_desc_t *desc);
 
 /* Backward on the stored probabilities.
@@ -274,12 +282,6 @@ typedef struct {
   int64_t mask_stride_b, mask_stride_h, mask_stride_q; /* as in jas_desc_t */
 } jas_attn_desc_t;
 
-/* Bytes of device workspace jas_attn_fwd needs: 0 for every desc.  The
- * fused kernel reads V in place (its PV operands come from gfx950's
- * transposed LDS reads), so it needs no transposed copy; the call and the
- * workspace arguments remain so that callers that pass one keep working. */
-size_t jas_attn_workspace_bytes(const jas_attn_desc_t *desc);
-
 /* Fused attention forward.
  *   q [batch, heads, q_len, head_dim], k and v [batch, kv_heads, kv_len,
  *   head_dim], contiguous, dtype; 16-byte aligned.
@@ -288,13 +290,13 @@ size_t jas_attn_workspace_bytes(const jas_attn_desc_t *desc);
  *   lse, p_sink: binary32 [batch*heads*q_len], required iff JAS_FLAG_LSE /
  *   JAS_FLAG_SINK.  probs / scores: required iff JAS_FLAG_PROBS /
  *   JAS_FLAG_SCORES.
- *   workspace, workspace_bytes: not used (jas_attn_workspace_bytes is 0);
- *   any value, NULL included, is accepted and nothing is written there.
- * Outputs must not overlap each other or the inputs. */
+ * Outputs must not overlap each other or the inputs.  No workspace: V is
+ * read in place (the PV operands come from gfx950's transposed LDS reads).
+ */
 jas_status_t jas_attn_fwd(const jas_attn_desc_t *desc, const void *q, const void *k,
                           const void *v, const float *mask, const int32_t *key_len,
                           const float *sink, void *out, float *lse, float *p_sink, void *probs,
-                          float *scores, void *workspace, size_t workspace_bytes, void *stream);
+                          float *scores, void *stream);
 
 /* jas_attn_fwd with an explicit number of 16-query blocks per wavefront,
  * query_blocks: 1, 2, or 0 for the library's choice.  Two blocks share every
@@ -311,10 +313,18 @@ jas_status_t jas_attn_fwd(const jas_attn_desc_t *desc, const void *q, const void
 jas_status_t jas_attn_fwd_ex(const jas_attn_desc_t *desc, const void *q, const void *k,
                              const void *v, const float *mask, const int32_t *key_len,
                              const float *sink, void *out, float *lse, float *p_sink, void *probs,
-                             float *scores, void *workspace, size_t workspace_bytes,
-                             int query_blocks, void *stream);
+                             float *scores, int query_blocks, void *stream);
 
-/* Static text for a status code. */
+/* Static text for a status code (never NULL; "unknown status" for a value
+ * outside jas_status_t).  Every entry point reports a refused call through
+ * its status instead of reaching the GPU with it: a flag whose pointer is
+ * NULL is JAS_ERR_NULL_POINTER before any launch (ROCm TransformerEngine
+ * PR #678, review of the sink pointer under has_sink: once the flag is set
+ * the pointer is a hard requirement, and a NULL one must be a clear error,
+ * not a GPU fault or a silent no-op), and the launch status is read after
+ * every launch and returned as JAS_ERR_HIP (RL-Kernel PR #240, review of
+ * the launch wrappers: a launch without an error check lets a bad launch
+ * surface later at an unrelated call). */
 const char *jas_status_str(jas_status_t status);
 
 /* Static fingerprint of the arithmetic contract: tile size, tree, merge

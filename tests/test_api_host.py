@@ -189,19 +189,12 @@ def adesc(B=1, H=4, Hkv=2, Sq=16, N=300, D=128, dtype=jas.JAS_DTYPE_BF16, flags=
 
 
 def attn(d, q=A, k=B_, v=C, out=D, mask=None, key_len=None, sink=None, lse=None, p_sink=None,
-         probs=None, scores=None, ws=E, ws_bytes=None):
-    if ws_bytes is None:
-        ws_bytes = jas.jas_attn_workspace_bytes(d)
-    return jas.jas_attn_fwd(d, q, k, v, mask, key_len, sink, out, lse, p_sink, probs, scores, ws,
-                            ws_bytes, None)
+         probs=None, scores=None):
+    return jas.jas_attn_fwd(d, q, k, v, mask, key_len, sink, out, lse, p_sink, probs, scores, None)
 
 
 def test_attention_validation():
     # every call fails validation: a call that passed would launch on fake addresses
-    # the fused kernel reads V in place: no workspace for any shape
-    assert jas.jas_attn_workspace_bytes(adesc()) == 0
-    assert jas.jas_attn_workspace_bytes(adesc(N=16384, Sq=4096)) == 0
-    assert jas.jas_attn_workspace_bytes(adesc(D=96)) == 0
     assert attn(adesc(dtype=jas.JAS_DTYPE_F32)) == 3
     assert attn(adesc(D=96)) == 7
     assert attn(adesc(N=jas.JAS_ATTN_MAX_KEYS + 1)) == 7
@@ -222,17 +215,16 @@ def test_attention_validation():
     assert attn(adesc(), out=A) == 5                      # out over q
     assert attn(adesc(flags=jas.JAS_FLAG_LSE), lse=D + 4) == 5   # lse inside out
     L = jas.lib()
-    assert L.jas_attn_fwd(None, A, B_, C, None, None, None, D, None, None, None, None, E, 0,
-                          None) == 1
+    assert L.jas_attn_fwd(None, A, B_, C, None, None, None, D, None, None, None, None, None) == 1
     # jas_attn_fwd_ex: 16-query blocks per wavefront 0, 1 or 2; anything else
     # is refused before a pointer is looked at
     for qb in (-1, 3, 64):
         assert jas.jas_attn_fwd_ex(adesc(), A, B_, C, None, None, None, D, None, None, None, None,
-                                   E, jas.jas_attn_workspace_bytes(adesc()), qb, None) == 4
+                                   qb, None) == 4
     assert jas.jas_attn_fwd_ex(adesc(dtype=jas.JAS_DTYPE_F32), A, B_, C, None, None, None, D, None,
-                               None, None, None, E, 0, 2, None) == 3
+                               None, None, None, 2, None) == 3
     assert jas.jas_attn_fwd_ex(adesc(), None, B_, C, None, None, None, D, None, None, None, None,
-                               E, jas.jas_attn_workspace_bytes(adesc()), 2, None) == 1
+                               2, None) == 1
 
 
 def _plan_covers(d, backward):

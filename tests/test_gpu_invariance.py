@@ -159,6 +159,32 @@ def bits_t(t):
     return t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32)
 
 
+def test_one_head_sliced_from_the_batch():
+    # one head's rows taken as a call of their own through a slice of the
+    # batch (torch leaves the size-1 batch and head dimensions' strides at
+    # the parent's values): the same bytes as in the whole call, with the
+    # mask, the sink, the causal cut, the lse and d_sink
+    B, H, S, N = 1, 5, 33, 1000
+    s = synth.normal((B, H, S, N), 2.0, 410, "cpu", torch.bfloat16).to(dev())
+    g = synth.normal((B, H, S, N), 1.0, 411, "cpu", torch.bfloat16).to(dev())
+    mask = torch.zeros((B, 1, 1, N), device=dev())
+    mask[..., 900:] = float("-inf")
+    sink = synth.normal((H,), 1.0, 412, "cpu").to(dev())
+    P, ps, lse = jas.fwd(s, mask=mask, sink=sink, causal=True, want_lse=True)
+    dS, dsk = jas.bwd(P, g, p_sink=ps, causal=True)
+    for h in (0, 3):
+        sh, gh = s[:, h:h + 1], g[:, h:h + 1]
+        assert sh.stride(0) != sh.shape[1] * sh.stride(1)   # the parent's batch stride
+        Ph, psh, lseh = jas.fwd(sh, mask=mask, sink=sink[h:h + 1], causal=True, want_lse=True)
+        dSh, dskh = jas.bwd(Ph, gh, p_sink=psh, causal=True)
+        torch.cuda.synchronize()
+        rows = slice(h * S, (h + 1) * S)
+        assert torch.equal(bits_t(Ph), bits_t(P[:, h:h + 1]))
+        assert torch.equal(bits_t(psh), bits_t(ps[rows])) and torch.equal(bits_t(lseh), bits_t(lse[rows]))
+        assert torch.equal(bits_t(dSh), bits_t(dS[:, h:h + 1]))
+        assert torch.equal(bits_t(dskh), bits_t(dsk[h:h + 1]))
+
+
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32, torch.float16])
 def test_degenerate_rows(dt):
     N = 600
