@@ -11,8 +11,13 @@
 //  * fp16 conversion sweep: every binary32 bit pattern through the packed
 //    binary32 -> binary16 conversion against round-to-nearest-even
 //    (subnormals kept, overflow to infinity).
-//  * log2 sweep: every binary32 in [1, 32768] (the range of a row's sum L)
-//    through v_log_f32 against log2 in double rounded to binary32.
+//  * log2 sweep: every binary32 in [1, 2^18 + 1] (the range of a row's sum L
+//    for rows of up to 262,144 keys and a sink) through v_log_f32 against
+//    log2 in double rounded to binary32.
+//  * copy16 / read2_write1: 16-byte streams (one read and one write, two
+//    reads and one write per word), the attainable HBM rates of the
+//    softmax forward's and backward's access mixes, and the calibration
+//    point of the HBM byte counters.
 //  * transposed LDS read (ds_read_b64_tr_b16) lane layout: which 16-bit
 //    elements each lane receives for given per-lane addresses.
 //  * MFMA operand layout: one 16x16x32 bf16 / fp16 product with the operands
@@ -260,81 +265,34 @@ __global__ void permlane_layout(uint32_t *out) {
 }
 }  // namespace
 
-// LDS bank-conflict probe: every lane reads 16-byte words at
-// (lane % 16) * rs + (lane / 16) * gs (+ 64 * k + 1024 * it) bytes, wrapped
-// into a 32 KB window of the workgroup's LDS, many times.  The pattern is
-// the one the attention kernel's operand reads follow (16 rows, lane groups
-// 16 bytes apart); rs is the row stride.
-__global__ __launch_bounds__(256) void lds_read(uint32_t *out, int rs, int gs, int iters) {
-  __shared__ __align__(16) uint32_t lds[8192];  // 32 KB
-  for (int i = threadIdx.x; i < 8192; i += 256) lds[i] = (uint32_t)i;
-  __syncthreads();
-  const int lane = threadIdx.x & 63;
-  const uint32_t base = (uint32_t)((lane & 15) * rs + (lane >> 4) * gs);
-  u32x4 acc = {0u, 0u, 0u, 0u};
-  for (int it = 0; it < iters; ++it) {
+// Two 16-byte reads (a and b) and one write (d) per word: the access mix
+// of the softmax backward (P and dP read, dS written), in the shape of
+// copy16 (4 words per thread per trip, every load before the stores).  The
+// attainable rate of that mix on this machine, beside copy16's for the forward.
+template <bool NT>
+__global__ __launch_bounds__(256) void read2_write1(const u32x4 *__restrict__ a,
+                                                    const u32x4 *__restrict__ b,
+                                                    u32x4 *__restrict__ d, uint64_t n16) {
+  const uint64_t stride = (uint64_t)gridDim.x * 256 * 4;
+  for (uint64_t base = (uint64_t)blockIdx.x * 256 * 4 + threadIdx.x; base < n16; base += stride) {
+    u32x4 x[4], y[4];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const uint32_t a = (base + (uint32_t)(k * 64) + (uint32_t)it * 1024u) & 0x7ff0u;  // 16-aligned, < 32 KB
-      acc ^= *reinterpret_cast<const u32x4 *>(&lds[a / 4]);
-    }
-  }
-  out[blockIdx.x * 256 + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
-}
-
-// VALU issue-rate probe: 8 independent chains per lane of one operation
-// (OP 0: v_exp_f32, OP 1: v_mul_f32), registers only.
-template <int OP>
-__global__ __launch_bounds__(256) void valu_rate(float *out, int iters) {
-  float v[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = -0.5f - 1e-6f * (float)(threadIdx.x + i);
-  for (int it = 0; it < iters; ++it) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if constexpr (OP == 0) v[i] = __builtin_amdgcn_exp2f(v[i]);
-        else v[i] = v[i] * 1.0001f;
-      }
-    }
-  }
-  float s = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) s += v[i];
-  out[blockIdx.x * 256 + threadIdx.x] = s;
-}
-
-// HBM stream probe: NR 16-byte reads (NR = 1 or 2 arrays) and NW writes
-// (0 or 1) per element, grid-stride, CH chunks in flight per thread,
-// nontemporal.  The attainable rate of each access mix on this machine.
-template <int NR, int NW, int CH>
-__global__ __launch_bounds__(256) void stream_mix(const u32x4 *a, const u32x4 *b, u32x4 *d,
-                                                  uint64_t n16) {
-  const uint64_t step = (uint64_t)gridDim.x * 256 * CH;
-  u32x4 acc = {0u, 0u, 0u, 0u};
-  for (uint64_t base = (uint64_t)blockIdx.x * 256 * CH; base < n16; base += step) {
-    u32x4 x[CH];
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const uint64_t i = base + (uint64_t)c * 256 + threadIdx.x;
-      x[c] = u32x4{0u, 0u, 0u, 0u};
-      if (i < n16) {
-        x[c] = __builtin_nontemporal_load(a + i);
-        if constexpr (NR == 2) x[c] ^= __builtin_nontemporal_load(b + i);
+    for (int i = 0; i < 4; ++i) {
+      const uint64_t k = base + (uint64_t)i * 256;
+      if (k < n16) {
+        x[i] = NT ? __builtin_nontemporal_load(a + k) : a[k];
+        y[i] = NT ? __builtin_nontemporal_load(b + k) : b[k];
       }
     }
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const uint64_t i = base + (uint64_t)c * 256 + threadIdx.x;
-      if constexpr (NW == 1) {
-        if (i < n16) __builtin_nontemporal_store(x[c], d + i);
-      } else {
-        acc ^= x[c];
+    for (int i = 0; i < 4; ++i) {
+      const uint64_t k = base + (uint64_t)i * 256;
+      if (k < n16) {
+        if (NT) __builtin_nontemporal_store(x[i] ^ y[i], d + k);
+        else d[k] = x[i] ^ y[i];
       }
     }
   }
-  if constexpr (NW == 0) d[blockIdx.x * 256 + threadIdx.x] = acc;
 }
 
 extern "C" {
@@ -418,51 +376,19 @@ int probe_permlane_layout(uint32_t *out) {  // out: 256 words
   return hipDeviceSynchronize() == hipSuccess ? 0 : -1;
 }
 
-// out: blocks * 256 words (device); launches `blocks` workgroups of the LDS
-// read probe on `stream` and returns 0, or -1 on a bad argument.
-int probe_lds_read(uint32_t *out, int blocks, int rs, int gs, int iters, void *stream) {
-  if (!out || blocks <= 0 || rs < 0 || gs < 0 || iters <= 0) return -1;
-  hipLaunchKernelGGL(lds_read, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, out, rs, gs,
-                     iters);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
-}
-
-// out: blocks * 256 floats (device); op 0: v_exp_f32, 1: v_mul_f32; each
-// thread issues iters * 128 operations.  Launches on `stream`; 0 or -1.
-int probe_valu_rate(float *out, int blocks, int op, int iters, void *stream) {
-  if (!out || blocks <= 0 || iters <= 0 || (op != 0 && op != 1)) return -1;
-  if (op == 0)
-    hipLaunchKernelGGL(valu_rate<0>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, out, iters);
+// Enqueue one pass of read2_write1 over n16 16-byte words of a, b and d
+// (16-byte aligned, d distinct from a and b) on `stream`; blocks = 0 picks
+// 2048.  Returns 0 or -1.
+int probe_read2_write1(const void *a, const void *b, void *d, uint64_t n16, int nontemporal,
+                       int blocks, void *stream) {
+  if (!a || !b || !d || ((uintptr_t)a | (uintptr_t)b | (uintptr_t)d) % 16) return -1;
+  const unsigned g = blocks > 0 ? (unsigned)blocks : 2048u;
+  if (nontemporal)
+    hipLaunchKernelGGL(read2_write1<true>, dim3(g), dim3(256), 0, (hipStream_t)stream,
+                       (const u32x4 *)a, (const u32x4 *)b, (u32x4 *)d, n16);
   else
-    hipLaunchKernelGGL(valu_rate<1>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, out, iters);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
-}
-
-// Stream probe launch: mix 0 = read a, write d (copy); 1 = read a and b,
-// write d; 2 = read a only (d receives blocks * 256 words).  a, b, d hold
-// n16 16-byte words (d at least blocks * 256 for mix 2), 16-byte aligned.
-// chunks: 1, 2 or 4.  Enqueues on `stream`; 0 or -1.
-int probe_stream_mix(const void *a, const void *b, void *d, uint64_t n16, int mix, int chunks,
-                     int blocks, void *stream) {
-  if (!a || !d || (mix == 1 && !b) || blocks <= 0 || ((uintptr_t)a | (uintptr_t)d) % 16 ||
-      (b && (uintptr_t)b % 16) || (mix == 2 && n16 < (uint64_t)blocks * 256))
-    return -1;
-  const dim3 g((unsigned)blocks), blk(256);
-  hipStream_t st = (hipStream_t)stream;
-  const u32x4 *A = (const u32x4 *)a, *B = (const u32x4 *)b;
-  u32x4 *D = (u32x4 *)d;
-#define JAS_MIX(NR, NW)                                                                    \
-  do {                                                                                     \
-    if (chunks == 1) hipLaunchKernelGGL((stream_mix<NR, NW, 1>), g, blk, 0, st, A, B, D, n16); \
-    else if (chunks == 2) hipLaunchKernelGGL((stream_mix<NR, NW, 2>), g, blk, 0, st, A, B, D, n16); \
-    else if (chunks == 4) hipLaunchKernelGGL((stream_mix<NR, NW, 4>), g, blk, 0, st, A, B, D, n16); \
-    else return -1;                                                                        \
-  } while (0)
-  if (mix == 0) JAS_MIX(1, 1);
-  else if (mix == 1) JAS_MIX(2, 1);
-  else if (mix == 2) JAS_MIX(1, 0);
-  else return -1;
-#undef JAS_MIX
+    hipLaunchKernelGGL(read2_write1<false>, dim3(g), dim3(256), 0, (hipStream_t)stream,
+                       (const u32x4 *)a, (const u32x4 *)b, (u32x4 *)d, n16);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 }
