@@ -100,6 +100,27 @@ def test_long_rows_against_oracle(dt, N):
 
 
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_near_uniform_long_row_lse(dt):
+    # L close to its largest value N + 1: every score within 2^-6 of 0 and a
+    # sink of 0, so each of the 262,144 keys adds nearly 1 and the hardware
+    # logarithm sees L near 2^18 (the top of its probed range)
+    N, B, H, S = 262144, 1, 2, 2
+    log(f"near-uniform long rows, lse: {dt} N={N}")
+    z = synth.normal((B, H, S, N), 1.0, 610, "cpu")
+    s = (torch.round(z * 2.0) * 2.0 ** -8).to(dt)   # multiples of 2^-8 in about [-2^-6, 2^-6]
+    sink = torch.zeros(H)
+    P, ps, lse = jas.fwd(s.to(dev()), sink=sink.to(dev()), want_lse=True)
+    torch.cuda.synchronize()
+    P_o, ps_o, lse_o = oracle.fwd(synth.to_numpy_bits(s), B, H, S, N, sink=sink.numpy(),
+                                  want_lse=True)
+    got = lse.cpu().numpy()
+    assert np.all(got > np.log(N) - 0.02) and np.all(got < np.log(N + 1) + 0.02), got
+    assert_lse_close(got, lse_o, f"lse N={N}")
+    assert_close(synth.to_numpy_bits(P), P_o, f"P N={N}")
+    assert_close(ps.cpu().numpy(), ps_o, "p_sink")
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
 def test_long_rows_with_exclusion(dt):
     N = 70000
     log(f"long rows with exclusion: {dt} N={N}")
