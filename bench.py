@@ -67,6 +67,14 @@ ATTN_WORKLOADS = {
 }
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
+# Seeds of every synthetic input, recorded in each result line.  One seed
+# draws a workload's scores, mask and dP (synth/ derives the streams from it);
+# the parity check's row sample has its own.
+SEEDS = {"joint4352": 3, "joint4352_keylen": 3, "rows4352": 2, "causal8192": 5,
+         "causal8192_skip": 5, "long65536": 7}
+ATTN_SEEDS = {"q": 81, "k": 82, "v": 83, "sink": 84, "mask": 3}
+CHECK_SEED = 7
+
 
 def row_kends(wl, key_len):
     """Visible keys of every row (int64 [B*H*S]): the causal condition
@@ -85,13 +93,14 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 
 def kernel_source_hash():
-    """sha256 over the sources of the row-softmax kernels (every .h / .hip
-    file of csrc/ except the fused attention's jas_attn.hip and jas_attn.h,
-    in name order): a traffic record is only used while it still matches."""
+    """sha256 over the sources of the row-softmax kernels and of the host
+    code that picks their instance and geometry (every .h / .hip / .cpp file
+    of csrc/ except the fused attention's jas_attn.hip and jas_attn.h, in
+    name order): a traffic record is only used while it still matches."""
     import hashlib
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".h", ".hip")) and name not in ("jas_attn.hip", "jas_attn.h"):
+        if name.endswith((".h", ".hip", ".cpp")) and name not in ("jas_attn.hip", "jas_attn.h"):
             h.update(name.encode())
             with open(os.path.join(CSRC, name), "rb") as f:
                 h.update(f.read())
@@ -99,11 +108,12 @@ def kernel_source_hash():
 
 
 def attn_source_hash():
-    """sha256 over the fused attention's sources (jas_attn.hip and the
-    headers it includes), for its traffic records."""
+    """sha256 over the fused attention's sources (jas_attn.hip, the headers
+    it includes and the host code that picks its launch), for its traffic
+    records."""
     import hashlib
     h = hashlib.sha256()
-    for name in ("jas_attn.hip", "jas_attn.h", "jas_internal.h", "jas_kernels.h"):
+    for name in ("jas_attn.hip", "jas_attn.h", "jas_internal.h", "jas_kernels.h", "jas_api.cpp"):
         h.update(name.encode())
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
@@ -167,18 +177,19 @@ def make_inputs(wl, dev):
     import synth
     _, B, H, S, N, dt, has_mask, has_sink, excl, _ = WORKLOADS[wl]
     mask = sink = g = key_len = None
+    seed = SEEDS[wl]
     if wl.startswith("joint4352"):
-        s, mask, g, pads = synth.joint_attention_bf16(seed=3, device=dev, B=B, H=H, S=S, N=N)
+        s, mask, g, pads = synth.joint_attention_bf16(seed=seed, device=dev, B=B, H=H, S=S, N=N)
         mask = mask.view(B, 1, 1, N)
         if excl == "key_len":
             mask = None
             key_len = torch.tensor([N - p for p in pads], dtype=torch.int32, device=dev)
     elif wl == "rows4352":
-        s = synth.rows_with_outliers_bf16(seed=2, device=dev, rows=S, N=N)
+        s = synth.rows_with_outliers_bf16(seed=seed, device=dev, rows=S, N=N)
     elif wl == "long65536":
-        s, g = synth.long_context_bf16(seed=7, device=dev, B=B, H=H, S=S, N=N)
+        s, g = synth.long_context_bf16(seed=seed, device=dev, B=B, H=H, S=S, N=N)
     else:
-        s, sink, g = synth.causal_sink_bf16(seed=5, device=dev, B=B, H=H, S=S)
+        s, sink, g = synth.causal_sink_bf16(seed=seed, device=dev, B=B, H=H, S=S)
     return s, mask, sink, g, key_len
 
 
@@ -206,7 +217,7 @@ def check_parity(wl, s, mask, sink, g, key_len):
     causal = excl == "causal"
     rows = B * H * S
     kend = row_kends(wl, None if key_len is None else key_len.cpu().numpy())
-    idx = np.unique(np.random.default_rng(7).choice(rows, 32, replace=False))
+    idx = np.unique(np.random.default_rng(CHECK_SEED).choice(rows, 32, replace=False))
     it = torch.as_tensor(idx, device=s.device)
     P, ps = jas.fwd(s, mask=mask, sink=sink, causal=causal, key_len=key_len)
     s_rows = synth.to_numpy_bits(s.reshape(-1, N).index_select(0, it))
@@ -233,6 +244,64 @@ def check_parity(wl, s, mask, sink, g, key_len):
     return {"fwd_max_ulp": ulp, "bwd_bitexact": True}
 
 
+def check_invariance(wl, run0, set0, s, mask, sink, g, key_len, ps, dsk):
+    """Byte identity before timing (RL-Kernel PR #240, Acceptance Criteria:
+    bitwise batch invariance; RL-Kernel PR #453, Benchmark: bytes checked
+    before timing).  The outputs of the prepared calls the timed steps make
+    are compared with: the same calls again (repeat), the binding's wrapper
+    calls (wrapper), a grid capped at 997 workgroups that loop over the rows
+    (capped_grid), and one head's rows computed as their own call of batch
+    1 x 1 head (sub_batch)."""
+    import torch
+    import deterministic_attention_softmax_amd as jas
+    _, B, H, S, N, _, _, _, excl, backward = WORKLOADS[wl]
+    causal = excl == "causal"
+    rf, rb = run0
+    _, _, P, dS = set0
+
+    def snap():
+        torch.cuda.synchronize()
+        return (P.clone(), dS.clone() if backward else None,
+                None if ps is None else ps.clone(), None if dsk is None else dsk.clone())
+
+    def same(x, y):
+        return x is None and y is None or torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+
+    def agree(ref, got, sel=slice(None)):
+        return all(same(None if r is None else r[sel], None if t is None else t[sel])
+                   for r, t in zip(ref, got))
+
+    def wrapped(launch=None, si=s, gi=g, sk=sink):
+        r = jas.fwd(si, mask=mask, sink=sk, causal=causal, key_len=key_len, launch=launch)
+        Pw, psw = r[0], r[1]
+        dSw = dskw = None
+        if backward:
+            dSw, dskw = jas.bwd(Pw, gi, p_sink=psw, causal=causal, key_len=key_len, launch=launch)
+        torch.cuda.synchronize()
+        return Pw, dSw, psw, dskw
+
+    rf()
+    if backward:
+        rb()
+    ref = snap()
+    rf()
+    if backward:
+        rb()
+    res = {"repeat": agree(ref, snap())}
+    res["wrapper"] = agree(ref, wrapped())
+    res["capped_grid"] = agree(ref, wrapped(launch=(0, 0, 0, 997, 0)))
+    h0 = H // 2  # one head of the B = 1 workloads: its rows, in order, as a call of its own
+    one = wrapped(si=s[:, h0:h0 + 1].contiguous(), gi=g[:, h0:h0 + 1].contiguous() if backward else None,
+                  sk=None if sink is None else sink[h0:h0 + 1].contiguous())
+    sub = (ref[0][:, h0:h0 + 1], None if ref[1] is None else ref[1][:, h0:h0 + 1],
+           None if ref[2] is None else ref[2].view(B, H, S)[:, h0:h0 + 1].reshape(-1),
+           None if ref[3] is None else ref[3][h0:h0 + 1])
+    res["sub_batch"] = B == 1 and all(
+        same(None if a is None else a.contiguous(), b) for a, b in zip(sub, one))
+    assert all(res.values()), f"outputs not byte-identical: {res}"
+    return res
+
+
 def cpu_baseline(wl, s, mask, sink, g, key_len, target_s):
     """The oracle, as it stands, on a bounded sample of the same rows: k rows
     spread evenly over the whole tensor, each handed to the oracle as its own
@@ -242,7 +311,8 @@ def cpu_baseline(wl, s, mask, sink, g, key_len, target_s):
     import oracle
     import synth
     _, B, H, S, N, _, _, _, excl, backward = WORKLOADS[wl]
-    threads = oracle.default_threads()
+    affinity, share, share_from = host_cpus()
+    threads = max(1, min(affinity, share))
     esz = 2
     kend = row_kends(wl, None if key_len is None else key_len.cpu().numpy())
     m_all = None if mask is None else mask.reshape(B, N).cpu().numpy()
@@ -284,6 +354,7 @@ def cpu_baseline(wl, s, mask, sink, g, key_len, target_s):
     return {
         "value": round(nbytes / t / 1e9, 4), "unit": "GB/s",
         "rows_per_s": round(k / t, 1), "cores": threads, "kind": "oracle",
+        "affinity_cores": affinity, "cpu_share": share, "cpu_share_from": share_from,
         "sample": f"{k} rows spread evenly over the whole workload ({k * N} elements), "
                   f"{'fwd+bwd' if backward else 'fwd'}, {t:.1f} s of oracle time",
         "cpu_model": cpu_model(),
@@ -291,6 +362,29 @@ def cpu_baseline(wl, s, mask, sink, g, key_len, target_s):
                        "rows_per_s": round(k1 / t1, 1),
                        "sample": f"{k1} rows spread evenly, {t1:.1f} s of oracle time"},
     }
+
+
+def host_cpus():
+    """(cores in this process's affinity mask, the CPU share granted to the
+    process, where that share comes from).  The share is the cgroup's CPU
+    quota when one is set, else OMP_NUM_THREADS, else the affinity count:
+    on a shared host the affinity mask can list every core of the machine
+    while the job is granted only a slice of them, and threads beyond the
+    slice only queue."""
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = os.cpu_count() or 1
+    try:
+        quota, period = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
+        if quota != "max":
+            return affinity, max(1, int(int(quota) // int(period))), "cgroup cpu.max"
+    except (OSError, ValueError):
+        pass
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        return affinity, int(omp), "OMP_NUM_THREADS"
+    return affinity, affinity, "affinity"
 
 
 def cpu_model():
@@ -310,12 +404,8 @@ def torch_index(idx, device):
     return torch.as_tensor(idx, device=device)
 
 
-def copy_ceiling(nbytes, stream, steps=10):
-    """A plain 16-byte copy of `nbytes` (the dominant kernel's bytes: half
-    read, half written) with the test-only probe kernel, if it is built: the
-    attainable read+write bandwidth on this machine."""
+def _probe_lib():
     import ctypes
-    import torch
     path = os.path.join(ROOT, "tests", "hw_probes", "libjas_hw_probes.so")
     if not os.path.exists(path):
         return None
@@ -323,22 +413,60 @@ def copy_ceiling(nbytes, stream, steps=10):
     L.probe_copy16.restype = ctypes.c_int
     L.probe_copy16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int,
                                ctypes.c_int, ctypes.c_void_p]
+    L.probe_read2_write1.restype = ctypes.c_int
+    L.probe_read2_write1.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_uint64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    return L
+
+
+def _time_launch(launch, stream, steps):
+    import torch
+    for _ in range(3):
+        launch()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def copy_ceiling(nbytes, stream, steps=10):
+    """Attainable rates of simple 16-byte streams moving `nbytes` (the
+    dominant kernel's bytes) with the test-only probe kernels, if built: a
+    copy (one read, one write per word: the forward's mix; also the
+    calibration point of the HBM byte counters) and two reads with one
+    write (the backward's mix), each with normal and nontemporal cache
+    policy and at two grid sizes; the best of each is reported."""
+    import torch
+    L = _probe_lib()
+    if L is None:
+        return None
+    out = {"unit": "GB/s"}
     n16 = max(1, nbytes // 32)
     src = torch.empty(n16 * 16, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
-    out = {}
     for nt in (0, 1):
-        for _ in range(3):
-            L.probe_copy16(src.data_ptr(), dst.data_ptr(), n16, nt, 0, stream.cuda_stream)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(steps):
-            L.probe_copy16(src.data_ptr(), dst.data_ptr(), n16, nt, 0, stream.cuda_stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / steps
+        ms = _time_launch(lambda: L.probe_copy16(src.data_ptr(), dst.data_ptr(), n16, nt, 0,
+                                                 stream.cuda_stream), stream, steps)
         out["nontemporal" if nt else "plain"] = round(2 * n16 * 16 / (ms * 1e-3) / 1e9, 1)
-    return {"unit": "GB/s", "bytes": 2 * n16 * 16, **out}
+    out["bytes"] = 2 * n16 * 16
+    del src, dst
+    n16 = max(1, nbytes // 48)
+    a = torch.empty(n16 * 16, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    d = torch.empty_like(a)
+    best = 0.0
+    for nt in (0, 1):
+        for blocks in (1024, 2048):
+            ms = _time_launch(lambda: L.probe_read2_write1(a.data_ptr(), b.data_ptr(), d.data_ptr(),
+                                                           n16, nt, blocks, stream.cuda_stream),
+                              stream, steps)
+            best = max(best, 3 * n16 * 16 / (ms * 1e-3) / 1e9)
+    out["r2w1"] = round(best, 1)
+    out["r2w1_bytes"] = 3 * n16 * 16
+    return out
 
 
 def _kernel_kind(name):
@@ -468,15 +596,16 @@ def bench_attention(args):
     wl = args.workload
     desc, B, H, Hkv, S, N, D, has_mask, causal, has_sink = ATTN_WORKLOADS[wl]
     log(f"workload {wl}: {desc}")
-    q = synth.normal((B, H, S, D), 1.0, 81, dev, torch.bfloat16)
-    k = synth.normal((B, Hkv, N, D), 1.0, 82, dev, torch.bfloat16)
-    v = synth.normal((B, Hkv, N, D), 1.0, 83, dev, torch.bfloat16)
+    q = synth.normal((B, H, S, D), 1.0, ATTN_SEEDS["q"], dev, torch.bfloat16)
+    k = synth.normal((B, Hkv, N, D), 1.0, ATTN_SEEDS["k"], dev, torch.bfloat16)
+    v = synth.normal((B, Hkv, N, D), 1.0, ATTN_SEEDS["v"], dev, torch.bfloat16)
     mask = sink = None
     if has_mask:
-        _, mask, _, _ = synth.joint_attention_bf16(seed=3, device="cpu", B=B, H=1, S=1, N=N)
+        _, mask, _, _ = synth.joint_attention_bf16(seed=ATTN_SEEDS["mask"], device="cpu", B=B, H=1,
+                                                   S=1, N=N)
         mask = mask.to(dev).view(B, 1, 1, N)
     if has_sink:
-        sink = synth.normal((H,), 1.0, 84, dev)
+        sink = synth.normal((H,), 1.0, ATTN_SEEDS["sink"], dev)
     scale = 1.0 / np.sqrt(D)
     out = torch.empty_like(q)
     d = jas.make_attn_desc(B, H, Hkv, S, N, D, jas.JAS_DTYPE_BF16, 0, scale)
@@ -506,7 +635,7 @@ def bench_attention(args):
     if not args.no_check:
         r = step()  # the first set: q, k, v themselves
         torch.cuda.synchronize()
-        qi = np.sort(np.random.default_rng(85).choice(S, 2, replace=False))
+        qi = np.sort(np.random.default_rng(CHECK_SEED).choice(S, 2, replace=False))
         if causal:
             qi = np.array([S - 2, S - 1])  # the sub-call keeps the causal offset of the last rows
         it = torch.as_tensor(qi, device=dev)
@@ -529,16 +658,20 @@ def bench_attention(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     t0 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = wall * 1e3 / args.steps
+    # per-call durations from a separate evented pass of as many calls
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     for i in range(args.steps):
         evs[i][0].record(stream)
         step()
         evs[i][1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     ms = np.array([a.elapsed_time(b) for a, b in evs])
-    step_ms = wall * 1e3 / args.steps
     flops = attn_flops(B, H, S, N, D, causal)
     tflops = flops / (step_ms * 1e-3) / 1e12
     ktf = flops / (ms.mean() * 1e-3) / 1e12
@@ -552,11 +685,13 @@ def bench_attention(args):
                    "kv_len": N, "head_dim": D, "mask": has_mask, "causal": causal,
                    "sink": has_sink, "useful_flops": flops,
                    "query_blocks_per_wave": args.attn_query_blocks or "library default"},
+        "seed": {**ATTN_SEEDS, "parity_rows": CHECK_SEED},
         "buffer_sets": nsets,
         "roofline": {"bound": "mfma", "kernel": "jas_attn_fwd (fused kernel)",
                      "achieved": round(ktf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(ktf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": load_attn_traffic(wl),
-                     "flops_per_launch": flops, "avg_launch_ms": round(float(ms.mean()), 4)},
+                     "flops_per_launch": flops, "avg_launch_ms": round(float(ms.mean()), 4),
+                     "median_launch_ms": round(float(np.median(ms)), 4)},
         "parity": check,
         # the copy kernel the PMC traffic records are calibrated on (1 GiB moved)
         "copy_ceiling": copy_ceiling(1 << 30, stream),
@@ -572,7 +707,8 @@ def bench_attention(args):
             q_np = synth.to_numpy_bits(q[:, :, S - kq:].contiguous())
             t0 = time.perf_counter()
             oracle.attn_fwd(q_np, k_np, v_np, np.float32(scale), mask=m_np,
-                            mask_strides=(N, 0, 0), causal=causal, sink=s_np)
+                            mask_strides=(N, 0, 0), causal=causal, sink=s_np,
+                            threads=max(1, min(host_cpus()[:2])))
             t = time.perf_counter() - t0
             if t > args.cpu_seconds / 4 or kq >= S:
                 break
@@ -581,8 +717,11 @@ def bench_attention(args):
         qq = np.arange(S - kq, S)
         pairs = int(np.clip(qq + (N - S) + 1, 0, N).sum()) if causal else kq * N
         f = 4.0 * B * H * pairs * D
+        affinity, share, share_from = host_cpus()
         res["cpu_baseline"] = {"value": round(f / t / 1e12, 6), "unit": "TFLOP/s",
-                               "cores": oracle.default_threads(), "kind": "oracle",
+                               "cores": max(1, min(affinity, share)), "kind": "oracle",
+                               "affinity_cores": affinity, "cpu_share": share,
+                               "cpu_share_from": share_from,
                                "sample": f"the last {kq} queries of every head ({B * H * kq} rows "
                                          f"x {N} keys), {t:.1f} s",
                                "cpu_model": cpu_model()}
@@ -781,8 +920,6 @@ def main():
     # The steps call jas_fwd / jas_bwd directly, with the descriptors and
     # pointers of each buffer set built and checked once by the binding
     # (fwd_prepared / bwd_prepared): no Python wrapper work between launches.
-    # The first set's outputs are compared, byte for byte, with those of the
-    # wrapper calls fwd / bwd on the same inputs.
     runs = []
     for si, gi, P, dS in sets:
         rf, _ = jas.fwd_prepared(si, mask=mask, sink=sink, out=P, p_sink=ps, causal=causal,
@@ -792,20 +929,10 @@ def main():
             rb, _ = jas.bwd_prepared(P, gi, p_sink=ps, out=dS, d_sink=dsk, workspace=ws,
                                      causal=causal, key_len=key_len)
         runs.append((rf, rb))
-    runs[0][0]()
-    if backward:
-        runs[0][1]()
-    Pw, psw = jas.fwd(s, mask=mask, sink=sink, causal=causal, key_len=key_len)
-    same = torch.equal(Pw.view(torch.uint8), sets[0][2].view(torch.uint8))
-    if backward:
-        dSw, dskw = jas.bwd(Pw, g, p_sink=psw, causal=causal, key_len=key_len)
-        same = same and torch.equal(dSw.view(torch.uint8), sets[0][3].view(torch.uint8))
-        if has_sink:
-            same = same and torch.equal(dskw, dsk)
-    assert same, "prepared calls differ from the wrapper calls"
-    del Pw, psw
-    if backward:
-        del dSw, dskw
+    invariance = None
+    if not args.no_check:
+        invariance = check_invariance(wl, runs[0], sets[0], s, mask, sink, g, key_len, ps, dsk)
+        log(f"invariance check: {invariance}")
 
     def step(ev=None):
         rf, rb = runs[nstep[0] % nsets]
@@ -829,16 +956,23 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    # The timed steps: one C call per kernel launch, nothing else between
+    # them, so the host enqueues ahead of the device and the wall time is
+    # the device's.
     t0 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = wall * 1e3 / args.steps
+    # Per-kernel durations from a separate pass of as many steps with HIP
+    # events around each launch (recorded on the launch stream).
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     fwd_ms = np.array([a.elapsed_time(b) for a, b, _ in evs])
     bwd_ms = np.array([b.elapsed_time(c) for _, b, c in evs]) if backward else np.zeros(1)
-    step_ms = wall * 1e3 / args.steps
 
     fwd_bytes = esz * (V + E) + (rows * 4 if has_sink else 0)
     bwd_bytes = esz * (V + 2 * E) + (rows * 12 if has_sink else 0) if backward else 0
@@ -846,11 +980,11 @@ def main():
     gbs = total_bytes / (step_ms * 1e-3) / 1e9
     fwd_gbs = fwd_bytes / (fwd_ms.mean() * 1e-3) / 1e9
     bwd_gbs = bwd_bytes / (bwd_ms.mean() * 1e-3) / 1e9 if backward else None
-    dom = ("jas bwd", bwd_gbs, bwd_bytes, bwd_ms.mean()) if backward else \
-          ("jas fwd", fwd_gbs, fwd_bytes, fwd_ms.mean())
-    log(f"fwd {fwd_ms.mean():.3f} ms ({fwd_gbs:.0f} GB/s)" +
-        (f", bwd {bwd_ms.mean():.3f} ms ({bwd_gbs:.0f} GB/s)" if backward else "") +
-        f", step {step_ms:.3f} ms")
+    dom = ("jas bwd", bwd_gbs, bwd_bytes, bwd_ms) if backward else \
+          ("jas fwd", fwd_gbs, fwd_bytes, fwd_ms)
+    log(f"fwd {fwd_ms.mean():.4f} ms (median {np.median(fwd_ms):.4f}, {fwd_gbs:.0f} GB/s)" +
+        (f", bwd {bwd_ms.mean():.4f} ms (median {np.median(bwd_ms):.4f}, {bwd_gbs:.0f} GB/s)"
+         if backward else "") + f", step {step_ms:.4f} ms")
 
     out = {
         "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
@@ -861,20 +995,31 @@ def main():
                    "rows": rows, "mask": has_mask, "sink": has_sink, "exclusion": excl,
                    "visible_keys": V, "backward": backward},
         "rows_per_s": round(rows / (step_ms * 1e-3), 1),
+        "seed": {"inputs": SEEDS[wl], "parity_rows": CHECK_SEED},
         "buffer_sets": nsets,
-        "fwd_ms": round(float(fwd_ms.mean()), 4), "fwd_gbs": round(fwd_gbs, 1),
+        "fwd_ms": round(float(fwd_ms.mean()), 4), "fwd_ms_median": round(float(np.median(fwd_ms)), 4),
+        "fwd_gbs": round(fwd_gbs, 1),
         "bwd_ms": round(float(bwd_ms.mean()), 4) if backward else None,
+        "bwd_ms_median": round(float(np.median(bwd_ms)), 4) if backward else None,
         "bwd_gbs": round(bwd_gbs, 1) if backward else None,
+        "kernel_times": "HIP events around each launch, in a separate pass of the same number "
+                        "of steps after the timed ones",
         "roofline": {"bound": "hbm", "kernel": dom[0], "achieved": round(dom[1], 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom[1] / HBM_PEAK_GBS, 4),
                      "traffic": load_traffic(wl, "bwd" if backward else "fwd"),
-                     "bytes_per_launch": dom[2], "avg_launch_ms": round(float(dom[3]), 4)},
+                     "bytes_per_launch": dom[2], "avg_launch_ms": round(float(dom[3].mean()), 4),
+                     "median_launch_ms": round(float(np.median(dom[3])), 4)},
         "parity": check,
+        "invariance": invariance,
     }
     out["copy_ceiling"] = copy_ceiling(dom[2], stream)
     if out["copy_ceiling"]:
-        best = max(out["copy_ceiling"]["plain"], out["copy_ceiling"]["nontemporal"])
+        # like for like: the forward's one read and one write against the
+        # copy, the backward's two reads and one write against that stream
+        cc = out["copy_ceiling"]
+        best = cc["r2w1"] if backward else max(cc["plain"], cc["nontemporal"])
         out["roofline"]["frac_of_copy"] = round(dom[1] / best, 4)
+        out["roofline"]["copy_mix"] = "2R+1W" if backward else "1R+1W"
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(wl, s, mask, sink, g, key_len, args.cpu_seconds)
