@@ -17,7 +17,8 @@ __all__ = [
     "JAS_FLAG_CAUSAL", "JAS_FLAG_KEY_LEN", "JAS_FLAG_LSE", "JAS_FLAG_PROBS", "JAS_FLAG_SCORES",
     "JAS_MAX_KEYS", "JAS_ATTN_MAX_KEYS",
     "STATUS", "JasError", "jas_desc_t", "jas_launch_t", "jas_attn_desc_t", "lib", "jas_fwd",
-    "jas_fwd_ex", "jas_bwd", "jas_bwd_ex", "jas_bwd_workspace_bytes", "jas_attn_fwd", "jas_attn_fwd_ex",
+    "jas_fwd_ex", "jas_bwd", "jas_bwd_ex", "jas_bwd_noalloc", "jas_bwd_workspace_bytes",
+    "jas_attn_fwd", "jas_attn_fwd_ex", "JAS_NOALLOC_MAX_ROWS",
     "jas_launch_plan", "jas_status_str", "jas_contract", "make_desc",
     "make_attn_desc", "fwd", "bwd", "fwd_prepared", "bwd_prepared", "attn_fwd",
     "attn_fwd_prepared", "LIB_PATH",
@@ -30,10 +31,11 @@ JAS_FLAG_MASK, JAS_FLAG_SINK, JAS_FLAG_CAUSAL, JAS_FLAG_KEY_LEN, JAS_FLAG_LSE = 
 JAS_FLAG_PROBS, JAS_FLAG_SCORES = 32, 64
 JAS_ATTN_MAX_KEYS = 16384
 JAS_MAX_KEYS = 262144
+JAS_NOALLOC_MAX_ROWS = 1048576
 STATUS = {
     0: "JAS_OK", 1: "JAS_ERR_NULL_POINTER", 2: "JAS_ERR_BAD_SHAPE", 3: "JAS_ERR_BAD_DTYPE",
     4: "JAS_ERR_BAD_FLAGS", 5: "JAS_ERR_ALIASING", 6: "JAS_ERR_WORKSPACE",
-    7: "JAS_ERR_UNSUPPORTED", 8: "JAS_ERR_HIP", 9: "JAS_ERR_ALIGNMENT",
+    7: "JAS_ERR_UNSUPPORTED", 8: "JAS_ERR_HIP", 9: "JAS_ERR_ALIGNMENT", 10: "JAS_ERR_SCRATCH",
 }
 
 
@@ -92,6 +94,8 @@ def lib():
         L.jas_bwd_ex.restype = ctypes.c_int
         L.jas_bwd_ex.argtypes = [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _LP,
                                  _VP]
+        L.jas_bwd_noalloc.restype = ctypes.c_int
+        L.jas_bwd_noalloc.argtypes = [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]
         L.jas_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.jas_bwd_workspace_bytes.argtypes = [_DP]
         L.jas_launch_plan.restype = ctypes.c_int
@@ -134,6 +138,11 @@ def jas_bwd_ex(desc, probs, dprobs, key_len, p_sink, dscores, d_sink, workspace,
     lp = ctypes.byref(launch) if launch is not None else None
     return lib().jas_bwd_ex(ctypes.byref(desc), probs, dprobs, key_len, p_sink, dscores, d_sink,
                             workspace, workspace_bytes, lp, stream)
+
+
+def jas_bwd_noalloc(desc, probs, dprobs, key_len, p_sink, dscores, d_sink, stream):
+    return lib().jas_bwd_noalloc(ctypes.byref(desc), probs, dprobs, key_len, p_sink, dscores,
+                                 d_sink, stream)
 
 
 def jas_bwd_workspace_bytes(desc):

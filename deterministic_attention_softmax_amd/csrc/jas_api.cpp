@@ -236,10 +236,14 @@ jas_status_t fwd_impl(const jas_desc_t *d, const void *scores, const float *mask
   return JAS_OK;
 }
 
+// The backward.  With `use_scratch` the per-row d_sink shares go to the
+// library's static device scratch instead of a caller's workspace (the
+// allocation-free entry point): `workspace` is then ignored, and the rows
+// are limited to JAS_NOALLOC_MAX_ROWS.
 jas_status_t bwd_impl(const jas_desc_t *d, const void *probs, const void *dprobs,
                       const int32_t *key_len, const float *p_sink, void *dscores, float *d_sink,
                       void *workspace, size_t workspace_bytes, const jas_launch_t *launch,
-                      void *stream) {
+                      void *stream, bool use_scratch = false) {
   Dims dm;
   jas_status_t st = check_desc(d, &dm);
   if (st != JAS_OK) return st;
@@ -264,7 +268,10 @@ jas_status_t bwd_impl(const jas_desc_t *d, const void *probs, const void *dprobs
       (key_len && !aligned(key_len, 4)))
     return JAS_ERR_ALIGNMENT;
   const size_t need = jas_bwd_workspace_bytes(d);
-  if (has_sink) {
+  if (has_sink && use_scratch) {
+    if (dm.rows > JAS_NOALLOC_MAX_ROWS) return JAS_ERR_SCRATCH;
+    workspace = nullptr;  // the scratch: looked up after validation, and outside every caller buffer
+  } else if (has_sink) {
     if (!workspace || workspace_bytes < need) return JAS_ERR_WORKSPACE;
     if (!aligned(workspace, 4)) return JAS_ERR_ALIGNMENT;
   }
@@ -290,6 +297,14 @@ jas_status_t bwd_impl(const jas_desc_t *d, const void *probs, const void *dprobs
   st = choose_geometry(d->dtype, dm.T, dm.rows, true, launch, &g);
   if (st != JAS_OK) return st;
 
+  if (has_sink && use_scratch) {
+    // every check has passed: find the scratch of the stream's device
+    int dev = -1;
+    const hipError_t e = stream ? hipStreamGetDevice((hipStream_t)stream, &dev) : hipGetDevice(&dev);
+    float *sp = nullptr;
+    if (e != hipSuccess || jas::scratch_address(dev, &sp) != hipSuccess) return JAS_ERR_HIP;
+    workspace = sp;
+  }
   {
     jas::BwdArgs a;
     a.stash = 0;  // the streaming launcher decides
@@ -482,6 +497,13 @@ jas_status_t jas_bwd_ex(const jas_desc_t *desc, const void *probs, const void *d
                   workspace_bytes, launch, stream);
 }
 
+jas_status_t jas_bwd_noalloc(const jas_desc_t *desc, const void *probs, const void *dprobs,
+                             const int32_t *key_len, const float *p_sink, void *dscores,
+                             float *d_sink, void *stream) {
+  return bwd_impl(desc, probs, dprobs, key_len, p_sink, dscores, d_sink, nullptr, 0, nullptr,
+                  stream, true);
+}
+
 jas_status_t jas_launch_plan(const jas_desc_t *desc, int backward, const jas_launch_t *launch,
                              jas_launch_t *plan) {
   if (!plan) return JAS_ERR_NULL_POINTER;
@@ -530,6 +552,7 @@ const char *jas_status_str(jas_status_t s) {
     case JAS_ERR_UNSUPPORTED: return "row length or launch geometry not supported";
     case JAS_ERR_HIP: return "the HIP runtime refused a launch";
     case JAS_ERR_ALIGNMENT: return "a pointer is not aligned to its element size";
+    case JAS_ERR_SCRATCH: return "more rows than the library's scratch holds (JAS_NOALLOC_MAX_ROWS)";
   }
   return "unknown status";
 }

@@ -95,4 +95,8 @@ hipError_t launch_fwd(int dtype, const FwdArgs &a, const Geometry &g, hipStream_
 hipError_t launch_bwd(int dtype, const BwdArgs &a, const Geometry &g, hipStream_t stream);
 hipError_t launch_dsink(const DsinkArgs &a, hipStream_t stream);
 
+// Device address of the library's static scratch (JAS_NOALLOC_MAX_ROWS
+// floats) on `device`, looked up on the first call for that device.
+hipError_t scratch_address(int device, float **out);
+
 }  // namespace jas

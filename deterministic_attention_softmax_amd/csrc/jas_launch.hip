@@ -5,7 +5,9 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
+#include "jas.h"
 #include "jas_kernels.h"
 
 namespace jas {
@@ -126,6 +128,49 @@ hipError_t launch_bwd(int dtype, const BwdArgs &a, const Geometry &g, hipStream_
 hipError_t launch_dsink(const DsinkArgs &a, hipStream_t st) {
   hipLaunchKernelGGL(dsink_kernel, dim3((unsigned)a.H), dim3(kWave * kDsinkWaves), 0, st, a);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// The library's own device scratch for jas_bwd_noalloc: the per-row d_sink
+// shares of up to JAS_NOALLOC_MAX_ROWS rows (4 MiB), in the module's static
+// device memory, so that the call allocates nothing.  Every GPU the library
+// runs on holds its own copy at its own address until the process ends.  In
+// host code `scratch` only names a host-side stand-in for the symbol; the
+// device address is looked up once per device, with that device current,
+// and only that address is handed to kernels.  The backward kernel writes
+// every row's share before the d_sink kernel reads it, so nothing in it has
+// to start at zero; calls on one GPU share it, so calls that overlap on one
+// GPU (concurrent streams) race.
+// ---------------------------------------------------------------------------
+
+namespace {
+constexpr int kScratchDevices = 64;
+static __device__ __align__(256) float scratch[JAS_NOALLOC_MAX_ROWS];
+std::mutex scratch_mu;
+float *scratch_ptr[kScratchDevices];  // device address of `scratch`, per device; null until looked up
+}  // namespace
+
+hipError_t scratch_address(int device, float **out) {
+  *out = nullptr;
+  if (device < 0 || device >= kScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[device] == nullptr) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != device) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    scratch_ptr[device] = static_cast<float *>(p);
+  }
+  *out = scratch_ptr[device];
+  return hipSuccess;
 }
 
 }  // namespace jas

@@ -132,7 +132,8 @@ typedef enum {
   JAS_ERR_WORKSPACE = 6,    /* workspace NULL or smaller than jas_bwd_workspace_bytes */
   JAS_ERR_UNSUPPORTED = 7,  /* keys > JAS_MAX_KEYS, or a launch override that cannot hold the row */
   JAS_ERR_HIP = 8,          /* the HIP runtime refused a launch */
-  JAS_ERR_ALIGNMENT = 9     /* a pointer is not aligned to its element size */
+  JAS_ERR_ALIGNMENT = 9,    /* a pointer is not aligned to its element size */
+  JAS_ERR_SCRATCH = 10      /* jas_bwd_noalloc with a sink: rows > JAS_NOALLOC_MAX_ROWS */
 } jas_status_t;
 
 /* Problem description, shared by forward and backward. */
@@ -223,6 +224,27 @@ size_t jas_bwd_workspace_bytes(const jas_desc_t *desc);
 jas_status_t jas_bwd(const jas_desc_t *desc, const void *probs, const void *dprobs,
                      const int32_t *key_len, const float *p_sink, void *dscores, float *d_sink,
                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* Rows jas_bwd_noalloc takes with a sink: its per-row d_sink shares live in
+ * a static device array of this many floats (4 MiB per GPU). */
+#define JAS_NOALLOC_MAX_ROWS 1048576
+
+/* jas_bwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments without the workspace, the same kernels and the same
+ * bits.  With JAS_FLAG_SINK the per-row d_sink shares go to a static device
+ * array of the library (JAS_NOALLOC_MAX_ROWS floats, one copy on each GPU
+ * the library runs on, held until the process ends); a call with more rows
+ * returns JAS_ERR_SCRATCH and enqueues nothing.  The call itself calls no
+ * allocating routine.  The array's device address is looked up on the first
+ * call on each device (the device of `stream`).  All calls on one GPU share
+ * the array and every call rewrites the part it uses before reading it, so
+ * its contents on entry never matter; calls that overlap on one GPU (on
+ * concurrent streams) race and must be ordered by the caller.  Without a
+ * sink it is jas_bwd without a workspace. */
+jas_status_t jas_bwd_noalloc(const jas_desc_t *desc, const void *probs, const void *dprobs,
+                             const int32_t *key_len, const float *p_sink, void *dscores,
+                             float *d_sink, void *stream);
 
 /* jas_bwd with an explicit launch geometry (NULL = default). */
 jas_status_t jas_bwd_ex(const jas_desc_t *desc, const void *probs, const void *dprobs,

@@ -39,7 +39,7 @@ def test_contract_and_status_strings():
     c = jas.jas_contract()
     assert "tile=256" in c and "gfx950" in c and "atomics=none" in c
     assert "attn=" in c and "two-pass" in c
-    for code in range(10):
+    for code in range(11):
         assert jas.jas_status_str(code) and jas.jas_status_str(code) != "unknown status"
     assert jas.jas_status_str(99) == "unknown status"
 
@@ -191,6 +191,27 @@ def adesc(B=1, H=4, Hkv=2, Sq=16, N=300, D=128, dtype=jas.JAS_DTYPE_BF16, flags=
 def attn(d, q=A, k=B_, v=C, out=D, mask=None, key_len=None, sink=None, lse=None, p_sink=None,
          probs=None, scores=None):
     return jas.jas_attn_fwd(d, q, k, v, mask, key_len, sink, out, lse, p_sink, probs, scores, None)
+
+
+def test_noalloc_validation():
+    # jas_bwd_noalloc: the checks of jas_bwd without the workspace, then the
+    # row limit of the library's scratch with a sink; every call below is
+    # refused before any HIP call
+    def nb(d, probs=A, dprobs=B_, p_sink=None, dscores=C, d_sink=None, key_len=None):
+        return jas.jas_bwd_noalloc(d, probs, dprobs, key_len, p_sink, dscores, d_sink, None)
+    sink = jas.JAS_FLAG_SINK
+    big = jas.JAS_NOALLOC_MAX_ROWS
+    assert nb(desc(B=1, H=1, S=big + 1, N=64, flags=sink), p_sink=D, d_sink=E) == 10
+    assert nb(desc(B=2, H=4, S=big // 8 + 1, N=64, flags=sink), p_sink=D, d_sink=E) == 10
+    assert jas.jas_status_str(10) == \
+        "more rows than the library's scratch holds (JAS_NOALLOC_MAX_ROWS)"
+    assert nb(desc(flags=sink), p_sink=None, d_sink=E) == 1       # flag without its pointer
+    assert nb(desc(flags=sink), p_sink=D, d_sink=None) == 1
+    assert nb(desc(), p_sink=D) == 4                               # pointer without its flag
+    assert nb(desc(flags=sink), probs=None, p_sink=D, d_sink=E) == 1
+    assert nb(desc(flags=sink), dscores=A, dprobs=A + 2, p_sink=D, d_sink=E) == 5
+    assert nb(desc(N=jas.JAS_MAX_KEYS + 1, flags=sink), p_sink=D, d_sink=E) == 7
+    assert jas.lib().jas_bwd_noalloc(None, A, B_, None, None, C, None, None) == 1
 
 
 def test_attention_validation():
