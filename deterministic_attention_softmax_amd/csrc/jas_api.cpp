@@ -147,10 +147,7 @@ jas_status_t choose_geometry(int dtype, int T, int64_t rows, bool backward, cons
     if (cpl == 0) return JAS_ERR_UNSUPPORTED;
   }
   if (!jas::cpl_compiled(dtype, wpr, cpl) || (int64_t)wpr * cpl < nslots) return JAS_ERR_UNSUPPORTED;
-  // one row per wavefront: 4 rows per workgroup; a row spread over several
-  // wavefronts: one row per workgroup (measured faster: its barriers then
-  // couple only the row's own waves)
-  if (rpb == 0) rpb = (wpr == 1) ? jas::kBlockWaves : 1;
+  if (rpb == 0) rpb = jas::default_rpb(dtype, nslots, wpr, backward);
   if (rpb < 1 || wpr * rpb > jas::kBlockWaves) return JAS_ERR_UNSUPPORTED;
   int64_t blocks = (rows + rpb - 1) / rpb;
   if (cap > 0 && blocks > cap) blocks = cap;

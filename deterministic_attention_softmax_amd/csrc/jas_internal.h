@@ -79,6 +79,7 @@ inline int tiles_per_slot(int dtype) { return dtype == 0 ? 1 : 2; }
 
 bool cpl_compiled(int dtype, int wpr, int cpl);
 int default_wpr(int dtype, int nslots, bool backward);
+int default_rpb(int dtype, int nslots, int wpr, bool backward);
 const int *compiled_cpls(int dtype, int *count);
 bool stream_cpl_compiled(int dtype, int cpl);
 int default_stream_cpl(int dtype);

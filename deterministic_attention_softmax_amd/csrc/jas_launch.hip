@@ -89,12 +89,16 @@ int default_stream_cpl(int dtype) { return dtype == 0 ? kStreamCplF32[1] : kStre
 // Default waves per row for a row of `nslots` wave-wide chunks (the
 // chunks-per-lane size then is the smallest compiled one that covers the
 // row).  Measured on MI355X, bf16 (fp16 is laid out the same; an fp32 row
-// is twice as many slots for the same keys and registers): the forward runs
-// fastest with one wavefront per row up to 9 slots (4,608 keys), two up to
-// 18, four beyond; the backward, which keeps two inputs in registers, with
-// one wavefront up to 4 slots and four beyond.  Each threshold is capped at
-// what the compiled chunk sizes cover (17 per lane for fp32), so every row
-// up to 16,384 keys has a geometry.  Any choice gives the same bits.
+// is twice as many slots for the same keys and registers): the 16-bit
+// forward runs fastest with one wavefront per row up to 5 slots (2,560
+// keys), two up to 18, four beyond (16,384 rows x N keys, with and without
+// a mask: at 6 to 9 slots two wavefronts take 3-12% less time than one, at
+// 2 and 3 slots 15-25% more); the fp32 forward with one wavefront up to 17
+// slots (4,352 keys), two up to 34; the backward, which keeps two inputs in
+// registers, with one wavefront up to 4 slots and four beyond.  Each
+// threshold is capped at what the compiled chunk sizes cover (17 per lane
+// for fp32), so every row up to 16,384 keys has a geometry.  Any choice
+// gives the same bits.
 int default_wpr(int dtype, int nslots, bool backward) {
   int n = 0;
   const int *c = compiled_cpls(dtype, &n);
@@ -102,9 +106,22 @@ int default_wpr(int dtype, int nslots, bool backward) {
   const int u = dtype == 0 ? 2 : 1;         // slots per 16-bit-type slot of keys
   if (nslots > 4 * top) return 0;
   if (backward) return nslots <= 4 * u ? 1 : 4;
-  if (nslots <= std::min(9 * u, top)) return 1;
+  if (nslots <= std::min(dtype == 0 ? 9 * u : 5, top)) return 1;
   if (nslots <= std::min(18 * u, 2 * top)) return 2;
   return 4;
+}
+
+// Default rows per workgroup for a row spread over `wpr` wavefronts: one row
+// per wavefront, 4 rows per workgroup; a 16-bit forward row of up to 9 slots
+// on two wavefronts, 2 rows (the 4,352-key rows: 48.4 us against 50.6 us
+// for one row per workgroup, and the joint shape with its mask unchanged);
+// any other row spread over several wavefronts, one row per workgroup
+// (measured faster: its barriers then couple only the row's own waves; 8,192
+// keys on two wavefronts: 1.38 ms against 1.51 ms with two rows).
+int default_rpb(int dtype, int nslots, int wpr, bool backward) {
+  if (wpr == 1) return kBlockWaves;
+  if (wpr == 2 && !backward && dtype != 0 && nslots <= 9) return 2;
+  return 1;
 }
 
 hipError_t launch_fwd(int dtype, const FwdArgs &a, const Geometry &g, hipStream_t st) {
