@@ -94,11 +94,19 @@ jas_status_t mask_bytes(const jas_desc_t *d, int64_t *bytes) {
   return JAS_OK;
 }
 
+// Rows of whole 16-byte chunks (row length and stride a multiple of the keys
+// in a chunk): the shape allows the 16-byte path (the pointers' alignment
+// decides the rest).
+bool whole_chunk_rows(const jas_desc_t *d) {
+  const int64_t kpc = jas::keys_per_chunk(d->dtype);
+  return d->keys % kpc == 0 && d->ld % kpc == 0;
+}
+
 // Launch geometry: the override when given (checked), else the default.
 // tiles are covered by slots of TPS tiles; a row needs ceil(T/TPS) slots,
 // spread over wpr waves holding cpl slots each.
 jas_status_t choose_geometry(int dtype, int T, int64_t rows, bool backward, const jas_launch_t *ov,
-                             Geometry *g) {
+                             Geometry *g, bool whole_chunks = true) {
   const int tps = jas::tiles_per_slot(dtype);
   const int nslots = (T + tps - 1) / tps;
   int ncpl = 0;
@@ -111,14 +119,20 @@ jas_status_t choose_geometry(int dtype, int T, int64_t rows, bool backward, cons
   if (ov && ov->streaming != 0 && ov->streaming != 1) return JAS_ERR_UNSUPPORTED;
   g->stream = 0;
   if (T > jas::kMaxTiles || (ov && ov->streaming)) {
-    // streaming: 4 waves and one row per workgroup, the row in segments
-    if ((wpr != 0 && wpr != jas::kBlockWaves) || rpb > 1) return JAS_ERR_UNSUPPORTED;
+    // streaming: one row per workgroup of 4 or 16 waves, the row in segments
+    if ((wpr != 0 && wpr != jas::kBlockWaves && wpr != jas::kStreamWideWaves) || rpb > 1)
+      return JAS_ERR_UNSUPPORTED;
+    // rows that cannot take 16-byte accesses run the 4-wave workgroup
+    if (wpr == 0) wpr = whole_chunks ? jas::default_stream_wpr(dtype, nslots, backward) : jas::kBlockWaves;
     if (cpl == 0) cpl = jas::default_stream_cpl(dtype);
     if (!jas::stream_cpl_compiled(dtype, cpl)) return JAS_ERR_UNSUPPORTED;
+    // the wide workgroup is compiled for 16-bit types and the larger segment only
+    if (wpr == jas::kStreamWideWaves && (dtype == JAS_DTYPE_F32 || cpl != jas::default_stream_cpl(dtype)))
+      return JAS_ERR_UNSUPPORTED;
     int64_t blocks = rows;
     if (cap > 0 && blocks > cap) blocks = cap;
     if (blocks > 0x7fffffff) blocks = 0x7fffffff;
-    g->wpr = jas::kBlockWaves;
+    g->wpr = wpr;
     g->cpl = cpl;
     g->rpb = 1;
     g->blocks = blocks;
@@ -206,7 +220,7 @@ jas_status_t fwd_impl(const jas_desc_t *d, const void *scores, const float *mask
     return JAS_ERR_ALIASING;
 
   Geometry g;
-  st = choose_geometry(d->dtype, dm.T, dm.rows, false, launch, &g);
+  st = choose_geometry(d->dtype, dm.T, dm.rows, false, launch, &g, whole_chunk_rows(d));
   if (st != JAS_OK) return st;
   jas::FwdArgs a;
   a.stash = 0;  // the streaming launcher decides
@@ -291,7 +305,7 @@ jas_status_t bwd_impl(const jas_desc_t *d, const void *probs, const void *dprobs
     return JAS_ERR_ALIASING;
 
   Geometry g;
-  st = choose_geometry(d->dtype, dm.T, dm.rows, true, launch, &g);
+  st = choose_geometry(d->dtype, dm.T, dm.rows, true, launch, &g, whole_chunk_rows(d));
   if (st != JAS_OK) return st;
 
   if (has_sink && use_scratch) {
@@ -511,7 +525,8 @@ jas_status_t jas_launch_plan(const jas_desc_t *desc, int backward, const jas_lau
   if (st != JAS_OK) return st;
   if (dm.rows == 0) return JAS_OK;  // no row kernel runs
   Geometry g;
-  const jas_status_t sg = choose_geometry(desc->dtype, dm.T, dm.rows, backward != 0, launch, &g);
+  const jas_status_t sg =
+      choose_geometry(desc->dtype, dm.T, dm.rows, backward != 0, launch, &g, whole_chunk_rows(desc));
   if (sg != JAS_OK) return sg;
   plan->waves_per_row = g.wpr;
   plan->chunks_per_lane = g.cpl;

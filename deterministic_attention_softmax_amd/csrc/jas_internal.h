@@ -15,6 +15,7 @@ constexpr int kMaxKeys = 16384;              // longest row of the one-pass kern
 constexpr int kMaxTiles = kMaxKeys / kTile;  // 64: one tile state per lane
 constexpr int kMaxStreamKeys = 262144;       // longest row of the streaming kernels
 constexpr int kBlockWaves = 4;     // waves per workgroup (256 threads)
+constexpr int kStreamWideWaves = 8;  // the wide streaming workgroup: one row on 512 threads
 
 struct RowShape {
   int64_t rows;   // batch * heads * q_rows
@@ -83,6 +84,7 @@ int default_rpb(int dtype, int nslots, int wpr, bool backward);
 const int *compiled_cpls(int dtype, int *count);
 bool stream_cpl_compiled(int dtype, int cpl);
 int default_stream_cpl(int dtype);
+int default_stream_wpr(int dtype, int nslots, bool backward);
 
 // one per element type, each in its own translation unit
 hipError_t launch_fwd_f32(const FwdArgs &a, const Geometry &g, hipStream_t stream);

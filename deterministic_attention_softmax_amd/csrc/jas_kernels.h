@@ -755,28 +755,33 @@ __host__ __device__ constexpr int stash_offset_words(int used) { return (used + 
 constexpr int kStashSegMaxBytes = 32 * 1024;
 constexpr int kStashBudgetFwd = 32 * 1024;
 constexpr int kStashBudgetBwd = 64 * 1024;
-template <int CPL>
-constexpr size_t stash_bytes() { return (size_t)CPL * kWave * kBlockWaves * 16; }
+// the wide workgroup (8 waves, two per CU): one segment of up to 64 KB in
+// the stash, in either direction
+constexpr int kWideStashSegMaxBytes = 64 * 1024;
+constexpr int kWideStashBudget = 64 * 1024;
+template <int CPL, int WPR = kBlockWaves>
+constexpr size_t stash_bytes() { return (size_t)CPL * kWave * WPR * 16; }
 
 // Segments a streaming row of T tiles is cut into, and how many of them the
 // stash holds within `budget` bytes (never more than the row has before its
 // last segment).
-template <int DT, int CPL>
+template <int DT, int CPL, int WPR = kBlockWaves>
 __host__ __device__ constexpr int stream_segments(int T) {
-  return ((T + Cfg<DT>::TPS - 1) / Cfg<DT>::TPS + kBlockWaves * CPL - 1) / (kBlockWaves * CPL);
+  return ((T + Cfg<DT>::TPS - 1) / Cfg<DT>::TPS + WPR * CPL - 1) / (WPR * CPL);
 }
-template <int DT, int CPL>
+template <int DT, int CPL, int WPR = kBlockWaves>
 constexpr int stash_segments(int T, int budget) {
-  if (stash_bytes<CPL>() > (size_t)kStashSegMaxBytes) return 0;
-  const int want = stream_segments<DT, CPL>(T) - 1;
-  const int fit = (int)((size_t)budget / stash_bytes<CPL>());
+  if constexpr (WPR != kBlockWaves) budget = kWideStashBudget;
+  const size_t seg_max = WPR == kBlockWaves ? kStashSegMaxBytes : kWideStashSegMaxBytes;
+  if (stash_bytes<CPL, WPR>() > seg_max) return 0;
+  const int want = stream_segments<DT, CPL, WPR>(T) - 1;
+  const int fit = (int)((size_t)budget / stash_bytes<CPL, WPR>());
   return want < fit ? (want > 0 ? want : 0) : fit;
 }
 
-template <int DT, int CPL, bool VEC, bool MASK, bool EXCL>
-__global__ __launch_bounds__(kWave * kBlockWaves) void fwd_stream_kernel(const FwdArgs a) {
+template <int DT, int CPL, int WPR, bool VEC, bool MASK, bool EXCL>
+__global__ __launch_bounds__(kWave * WPR) void fwd_stream_kernel(const FwdArgs a) {
   using C = Cfg<DT>;
-  constexpr int WPR = kBlockWaves;
   constexpr int KPL = C::KPL, TPS = C::TPS, ESZ = C::ESZ;
   constexpr uint32_t kFill = kNegInfBits<DT>;
   constexpr int SPS = WPR * CPL;  // slots per segment
@@ -1016,10 +1021,9 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void fwd_stream_kernel(const F
   }
 }
 
-template <int DT, int CPL, bool VEC, bool EXCL>
-__global__ __launch_bounds__(kWave * kBlockWaves) void bwd_stream_kernel(const BwdArgs a) {
+template <int DT, int CPL, int WPR, bool VEC, bool EXCL>
+__global__ __launch_bounds__(kWave * WPR) void bwd_stream_kernel(const BwdArgs a) {
   using C = Cfg<DT>;
-  constexpr int WPR = kBlockWaves;
   constexpr int KPL = C::KPL, TPS = C::TPS, ESZ = C::ESZ;
   constexpr int SPS = WPR * CPL;
   extern __shared__ float smem[];
@@ -1179,20 +1183,38 @@ constexpr int kCplBf16[] = {1, 2, 3, 5, 9};
 constexpr int kStreamCplF32[] = {8, 16};
 constexpr int kStreamCplBf16[] = {4, 8};
 
-template <int DT, int CPL>
+// A kernel whose LDS passes 64 KB asks for the larger allocation (up to the
+// 160 KB of a gfx950 CU) before its launch.
+template <typename K>
+hipError_t allow_lds(K kernel, size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+// The wide workgroup (8 waves) is built for 16-byte rows only: rows on the
+// element-wise path take the 4-wave one, with the same bits.
+template <int DT, int CPL, int WPR>
 hipError_t launch_fwd_stream(const FwdArgs &a0, const Geometry &g, hipStream_t st) {
-  const dim3 grid((unsigned)g.blocks), block(kWave * kBlockWaves);
+  if constexpr (WPR != kBlockWaves) {
+    if (!a0.vec_io) return launch_fwd_stream<DT, CPL, kBlockWaves>(a0, g, st);
+  }
+  const dim3 grid((unsigned)g.blocks), block(kWave * WPR);
   FwdArgs a = a0;
-  a.stash = stash_segments<DT, CPL>(a.s.T, kStashBudgetFwd);
+  a.stash = stash_segments<DT, CPL, WPR>(a.s.T, kStashBudgetFwd);
   const size_t lds = (size_t)stash_offset_words(2 * a.s.T + 2) * sizeof(float) +
-                     (size_t)a.stash * stash_bytes<CPL>();
+                     (size_t)a.stash * stash_bytes<CPL, WPR>();
   const bool mask = a.mask != nullptr, excl = a.ex.causal || a.ex.key_len;
 #define JAS_FWD_STREAM(V, MK, EX)                                                              \
-  hipLaunchKernelGGL((fwd_stream_kernel<DT, CPL, V, MK, EX>), grid, block, lds, st, a)
+  do {                                                                                         \
+    const hipError_t e = allow_lds(fwd_stream_kernel<DT, CPL, WPR, V, MK, EX>, lds);           \
+    if (e != hipSuccess) return e;                                                             \
+    hipLaunchKernelGGL((fwd_stream_kernel<DT, CPL, WPR, V, MK, EX>), grid, block, lds, st, a); \
+  } while (0)
   if (a.vec_io) {
     if (excl) { if (mask) JAS_FWD_STREAM(true, true, true); else JAS_FWD_STREAM(true, false, true); }
     else { if (mask) JAS_FWD_STREAM(true, true, false); else JAS_FWD_STREAM(true, false, false); }
-  } else {
+  } else if constexpr (WPR == kBlockWaves) {
     if (excl) { if (mask) JAS_FWD_STREAM(false, true, true); else JAS_FWD_STREAM(false, false, true); }
     else { if (mask) JAS_FWD_STREAM(false, true, false); else JAS_FWD_STREAM(false, false, false); }
   }
@@ -1200,21 +1222,31 @@ hipError_t launch_fwd_stream(const FwdArgs &a0, const Geometry &g, hipStream_t s
   return hipGetLastError();
 }
 
-template <int DT, int CPL>
+template <int DT, int CPL, int WPR>
 hipError_t launch_bwd_stream(const BwdArgs &a0, const Geometry &g, hipStream_t st) {
-  const dim3 grid((unsigned)g.blocks), block(kWave * kBlockWaves);
-  BwdArgs a = a0;
-  a.stash = stash_segments<DT, CPL>(a.s.T, kStashBudgetBwd);
-  const size_t lds = (size_t)stash_offset_words(a.s.T + 1) * sizeof(float) +
-                     (size_t)a.stash * stash_bytes<CPL>();
-  const bool excl = a.ex.causal || a.ex.key_len;
-  if (a.vec_io) {
-    if (excl) hipLaunchKernelGGL((bwd_stream_kernel<DT, CPL, true, true>), grid, block, lds, st, a);
-    else hipLaunchKernelGGL((bwd_stream_kernel<DT, CPL, true, false>), grid, block, lds, st, a);
-  } else {
-    if (excl) hipLaunchKernelGGL((bwd_stream_kernel<DT, CPL, false, true>), grid, block, lds, st, a);
-    else hipLaunchKernelGGL((bwd_stream_kernel<DT, CPL, false, false>), grid, block, lds, st, a);
+  if constexpr (WPR != kBlockWaves) {
+    if (!a0.vec_io) return launch_bwd_stream<DT, CPL, kBlockWaves>(a0, g, st);
   }
+  const dim3 grid((unsigned)g.blocks), block(kWave * WPR);
+  BwdArgs a = a0;
+  a.stash = stash_segments<DT, CPL, WPR>(a.s.T, kStashBudgetBwd);
+  const size_t lds = (size_t)stash_offset_words(a.s.T + 1) * sizeof(float) +
+                     (size_t)a.stash * stash_bytes<CPL, WPR>();
+  const bool excl = a.ex.causal || a.ex.key_len;
+#define JAS_BWD_STREAM(V, EX)                                                              \
+  do {                                                                                     \
+    const hipError_t e = allow_lds(bwd_stream_kernel<DT, CPL, WPR, V, EX>, lds);           \
+    if (e != hipSuccess) return e;                                                         \
+    hipLaunchKernelGGL((bwd_stream_kernel<DT, CPL, WPR, V, EX>), grid, block, lds, st, a); \
+  } while (0)
+  if (a.vec_io) {
+    if (excl) JAS_BWD_STREAM(true, true);
+    else JAS_BWD_STREAM(true, false);
+  } else if constexpr (WPR == kBlockWaves) {
+    if (excl) JAS_BWD_STREAM(false, true);
+    else JAS_BWD_STREAM(false, false);
+  }
+#undef JAS_BWD_STREAM
   return hipGetLastError();
 }
 
@@ -1287,8 +1319,14 @@ hipError_t fwd_dt(const FwdArgs &a, const Geometry &g, hipStream_t st) {
   if (g.stream) {
     constexpr int c0 = DT == 0 ? kStreamCplF32[0] : kStreamCplBf16[0];
     constexpr int c1 = DT == 0 ? kStreamCplF32[1] : kStreamCplBf16[1];
-    if (g.cpl == c0) return launch_fwd_stream<DT, c0>(a, g, st);
-    if (g.cpl == c1) return launch_fwd_stream<DT, c1>(a, g, st);
+    if (g.wpr == kStreamWideWaves) {  // 16-bit types only (fp32 chunks would not fit in registers)
+      if constexpr (DT != 0) {
+        if (g.cpl == c1) return launch_fwd_stream<DT, c1, kStreamWideWaves>(a, g, st);
+      }
+      return hipErrorInvalidValue;
+    }
+    if (g.cpl == c0) return launch_fwd_stream<DT, c0, kBlockWaves>(a, g, st);
+    if (g.cpl == c1) return launch_fwd_stream<DT, c1, kBlockWaves>(a, g, st);
     return hipErrorInvalidValue;
   }
   switch (g.wpr) {
@@ -1304,8 +1342,14 @@ hipError_t bwd_dt(const BwdArgs &a, const Geometry &g, hipStream_t st) {
   if (g.stream) {
     constexpr int c0 = DT == 0 ? kStreamCplF32[0] : kStreamCplBf16[0];
     constexpr int c1 = DT == 0 ? kStreamCplF32[1] : kStreamCplBf16[1];
-    if (g.cpl == c0) return launch_bwd_stream<DT, c0>(a, g, st);
-    if (g.cpl == c1) return launch_bwd_stream<DT, c1>(a, g, st);
+    if (g.wpr == kStreamWideWaves) {  // 16-bit types only (fp32 chunks would not fit in registers)
+      if constexpr (DT != 0) {
+        if (g.cpl == c1) return launch_bwd_stream<DT, c1, kStreamWideWaves>(a, g, st);
+      }
+      return hipErrorInvalidValue;
+    }
+    if (g.cpl == c0) return launch_bwd_stream<DT, c0, kBlockWaves>(a, g, st);
+    if (g.cpl == c1) return launch_bwd_stream<DT, c1, kBlockWaves>(a, g, st);
     return hipErrorInvalidValue;
   }
   switch (g.wpr) {

@@ -86,6 +86,23 @@ bool stream_cpl_compiled(int dtype, int cpl) {
 // 16-bit types, 4 x 16 for fp32.
 int default_stream_cpl(int dtype) { return dtype == 0 ? kStreamCplF32[1] : kStreamCplBf16[1]; }
 
+// Waves of a streaming workgroup.  The 16-bit backward takes 8 when the row
+// fits in two segments of the wide workgroup (8 waves x 8 chunks per lane:
+// 32,768 keys each): the last segment's P and dP stay in registers, the
+// first segment's P in the LDS stash, and only that segment's dP is read
+// twice (65,536-key rows: 0.572 ms against 0.646 ms with 4 waves, HBM bytes
+// 1.17 instead of 1.30 times the algorithmic ones).  Every other streaming
+// row takes 4 waves, whose segments of 16,384 keys let the one before the
+// last wait in LDS: the forward is faster so (65,536 keys: 0.418 ms against
+// 0.512 ms with 8 waves, which leave two workgroups per CU instead of three
+// and no next segment to load while one is reduced), and fp32 chunks in two
+// register sets would not fit the wide workgroup's registers at four waves
+// per SIMD.
+int default_stream_wpr(int dtype, int nslots, bool backward) {
+  if (dtype == 0 || !backward) return kBlockWaves;
+  return nslots <= 2 * kStreamWideWaves * default_stream_cpl(dtype) ? kStreamWideWaves : kBlockWaves;
+}
+
 // Default waves per row for a row of `nslots` wave-wide chunks (the
 // chunks-per-lane size then is the smallest compiled one that covers the
 // row).  Measured on MI355X, bf16 (fp16 is laid out the same; an fp32 row

@@ -248,11 +248,38 @@ def test_attention_validation():
                                2, None) == 1
 
 
+def test_streaming_workgroup_sizes():
+    # streaming: 4 waves, or 8 for 16-bit types (the larger segment only);
+    # the default takes 8 for the 16-bit backward on rows of whole chunks up
+    # to 65,536 keys, 4 for the forward
+    L = jas.jas_launch_t
+    for dt, wide_ok in ((jas.JAS_DTYPE_BF16, True), (jas.JAS_DTYPE_F16, True), (jas.JAS_DTYPE_F32, False)):
+        d = desc(N=40000, dtype=dt)
+        cpl = 16 if dt == jas.JAS_DTYPE_F32 else 8
+        st, p = jas.jas_launch_plan(d, 0, L(8, cpl, 1, 0, 1))
+        assert (st == 0) == wide_ok, (dt, st)
+        st, p = jas.jas_launch_plan(d, 1, L(8, cpl // 2, 1, 0, 1))
+        assert st == 7, (dt, st)                         # the wide workgroup: larger segment only
+        assert jas.jas_launch_plan(d, 0, L(16, cpl, 1, 0, 1))[0] == 7
+        st, p = jas.jas_launch_plan(d, 1)
+        assert st == 0 and p.streaming == 1 and p.waves_per_row == (8 if wide_ok else 4)
+        st, p = jas.jas_launch_plan(d, 0)
+        assert st == 0 and p.streaming == 1 and p.waves_per_row == 4
+    st, p = jas.jas_launch_plan(desc(N=65536), 1)
+    assert p.waves_per_row == 8
+    st, p = jas.jas_launch_plan(desc(N=65544), 1)
+    assert p.waves_per_row == 4                          # more than two wide segments
+    st, p = jas.jas_launch_plan(desc(N=40001), 1)
+    assert p.waves_per_row == 4                          # not whole 16-byte chunks
+
+
 def _plan_covers(d, backward):
     st, p = jas.jas_launch_plan(d, backward)
     assert st == 0, (d.keys, d.dtype, backward, jas.STATUS.get(st, st))
     if p.streaming:
-        assert d.keys > 16384 and p.waves_per_row == 4 and p.rows_per_block == 1
+        assert d.keys > 16384 and p.rows_per_block == 1
+        wide = (backward and d.dtype != jas.JAS_DTYPE_F32 and d.keys <= 65536 and d.keys % 8 == 0)
+        assert p.waves_per_row == (8 if wide else 4), (d.keys, d.dtype, p.waves_per_row)
         return p
     kps = 256 if d.dtype == jas.JAS_DTYPE_F32 else 512          # keys per 64-lane slot
     assert p.waves_per_row in (1, 2, 4) and p.waves_per_row * p.rows_per_block <= 4
@@ -278,8 +305,12 @@ def test_launch_plan_reports_overrides_and_errors():
     st, p = jas.jas_launch_plan(d, 0, jas._launch((2, 1, 2, 0, 0)))
     assert st == 0 and (p.waves_per_row, p.chunks_per_lane, p.rows_per_block) == (2, 1, 2)
     assert p.max_blocks == (30 + 1) // 2 and p.streaming == 0
-    st, p = jas.jas_launch_plan(d, 1, jas._launch((0, 0, 0, 4, 1)))
-    assert st == 0 and p.streaming == 1 and p.max_blocks == 4 and p.waves_per_row == 4
+    st, p = jas.jas_launch_plan(d, 1, jas._launch((0, 0, 0, 4, 1)))   # 16-bit backward: wide
+    assert st == 0 and p.streaming == 1 and p.max_blocks == 4 and p.waves_per_row == 8
+    st, p = jas.jas_launch_plan(d, 0, jas._launch((0, 0, 0, 4, 1)))   # the forward: 4 waves
+    assert st == 0 and p.streaming == 1 and p.waves_per_row == 4
+    st, p = jas.jas_launch_plan(d, 1, jas._launch((4, 0, 0, 4, 1)))
+    assert st == 0 and p.streaming == 1 and p.waves_per_row == 4
     st, p = jas.jas_launch_plan(d, 0, jas._launch((1, 1, 0, 0, 0)))   # 1 x 1 slot < 1000 keys
     assert jas.STATUS.get(st) == "JAS_ERR_UNSUPPORTED"
     assert (p.waves_per_row, p.chunks_per_lane, p.max_blocks) == (0, 0, 0)

@@ -53,6 +53,9 @@ def test_forced_streaming_matches_one_pass(dt, N):
         for cpl in STREAM_CPLS[dt]:
             got = run(s, g, launch=(4, cpl, 1, 0, 1), **kw)
             assert got == ref, f"streaming cpl={cpl} {sorted(kw)} changed the bytes"
+        if dt != torch.float32:  # the 16-wave workgroup (16-bit types)
+            got = run(s, g, launch=(8, 8, 1, 0, 1), **kw)
+            assert got == ref, f"wide streaming {sorted(kw)} changed the bytes"
 
 
 def long_case(dt, N, B=1, H=2, S=3, with_mask=False, with_sink=False, causal=False, kl=None,
@@ -142,7 +145,31 @@ def test_long_row_geometries_identical(dt):
     ref = run(s, g, sink=sink, causal=True)
     for cpl in STREAM_CPLS[dt]:
         for cap in (0, 5):
-            assert run(s, g, launch=(0, cpl, 0, cap, 1), sink=sink, causal=True) == ref, (cpl, cap)
+            assert run(s, g, launch=(4, cpl, 0, cap, 1), sink=sink, causal=True) == ref, (cpl, cap)
+    if dt != torch.float32:
+        for cap in (0, 5):
+            assert run(s, g, launch=(8, 8, 0, cap, 1), sink=sink, causal=True) == ref, cap
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("N", [16385, 40000, 65536, 65544, 131072])
+def test_wide_and_narrow_streaming_identical(dt, N):
+    # rows of whole 16-byte chunks: the 16-wave workgroup (the default up to
+    # 65,536 keys, the whole row in registers) and the 4-wave one (segments,
+    # an LDS stash, second reads) give the same bytes, with mask, sink,
+    # causal cut and lse; past 65,536 keys the wide workgroup reads segments
+    # again like the narrow one
+    B, H, S = 1, 2, 3
+    log(f"wide vs narrow streaming: {dt} N={N}")
+    s = synth.normal((B, H, S, N), 2.0, 520, "cpu", dt).to(dev())
+    g = synth.normal((B, H, S, N), 1.0, 521, "cpu", dt).to(dev())
+    mask = torch.zeros((B, 1, 1, N), device=dev())
+    mask[..., N // 3:N // 3 + 777] = float("-inf")
+    sink = synth.normal((H,), 1.0, 522, "cpu").to(dev())
+    kw = dict(mask=mask, sink=sink, causal=True)
+    ref = run(s, g, launch=(4, 8, 1, 0, 1), **kw)
+    assert run(s, g, launch=(8, 8, 1, 0, 1), **kw) == ref
+    assert run(s, g, **kw) == ref
 
 
 def test_long_rows_full_size_sampled():
