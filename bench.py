@@ -664,14 +664,18 @@ def bench_attention(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_ms = wall * 1e3 / args.steps
-    # per-call durations from a separate evented pass of as many calls
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        evs[i][0].record(stream)
-        step()
-        evs[i][1].record(stream)
-    torch.cuda.synchronize()
-    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    # per-call durations: HIP events on the launch stream around `steps`
+    # back-to-back calls, five times; the duration per call of each of the five
+    ms = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1) / args.steps)
+    ms = np.array(ms)
     flops = attn_flops(B, H, S, N, D, causal)
     tflops = flops / (step_ms * 1e-3) / 1e12
     ktf = flops / (ms.mean() * 1e-3) / 1e12
@@ -934,18 +938,12 @@ def main():
         invariance = check_invariance(wl, runs[0], sets[0], s, mask, sink, g, key_len, ps, dsk)
         log(f"invariance check: {invariance}")
 
-    def step(ev=None):
+    def step():
         rf, rb = runs[nstep[0] % nsets]
         nstep[0] += 1
-        if ev:
-            ev[0].record(stream)
         rf()
-        if ev:
-            ev[1].record(stream)
         if backward:
             rb()
-        if ev:
-            ev[2].record(stream)
 
     # bring clocks and page mappings to steady state (untimed, before the
     # warmup steps proper)
@@ -965,14 +963,24 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_ms = wall * 1e3 / args.steps
-    # Per-kernel durations from a separate pass of as many steps with HIP
-    # events around each launch (recorded on the launch stream).
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    fwd_ms = np.array([a.elapsed_time(b) for a, b, _ in evs])
-    bwd_ms = np.array([b.elapsed_time(c) for _, b, c in evs]) if backward else np.zeros(1)
+    # Per-kernel durations: HIP events on the launch stream around K
+    # back-to-back launches of one direction (over the same buffer sets),
+    # five times; the duration per launch of each of the five.  No event
+    # sits between two launches, so a short kernel is not charged for the
+    # event records.
+    def kernel_ms(which, reps=5):
+        out = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(args.steps):
+                runs[i % nsets][which]()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1) / args.steps)
+        return np.array(out)
+    fwd_ms = kernel_ms(0)
+    bwd_ms = kernel_ms(1) if backward else np.zeros(1)
 
     fwd_bytes = esz * (V + E) + (rows * 4 if has_sink else 0)
     bwd_bytes = esz * (V + 2 * E) + (rows * 12 if has_sink else 0) if backward else 0
@@ -1002,8 +1010,9 @@ def main():
         "bwd_ms": round(float(bwd_ms.mean()), 4) if backward else None,
         "bwd_ms_median": round(float(np.median(bwd_ms)), 4) if backward else None,
         "bwd_gbs": round(bwd_gbs, 1) if backward else None,
-        "kernel_times": "HIP events around each launch, in a separate pass of the same number "
-                        "of steps after the timed ones",
+        "kernel_times": "HIP events on the launch stream around `steps` back-to-back launches of "
+                        "one direction, 5 repetitions after the timed steps: mean and median of the "
+                        "5 per-launch durations",
         "roofline": {"bound": "hbm", "kernel": dom[0], "achieved": round(dom[1], 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom[1] / HBM_PEAK_GBS, 4),
                      "traffic": load_traffic(wl, "bwd" if backward else "fwd"),
