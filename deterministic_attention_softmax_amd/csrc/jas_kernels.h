@@ -742,16 +742,20 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void bwd_kernel(const BwdArgs 
 // 4-byte words after `used` words of tile states (16-byte aligned).
 __host__ __device__ constexpr int stash_offset_words(int used) { return (used + 3) & ~3; }
 
-// The stash holds the raw chunks of the segments just before the last one,
+// The stash holds the raw chunks of the segments just before those that stay
+// in registers (the forward keeps the last two, the backward the last one),
 // one segment being 256 threads x CPL x 16 bytes; pass 2 reads them from LDS
 // instead of reading them again.  Segments of more than 32 KB are not
 // stashed, and each direction has its own LDS budget, from measurements on
 // MI355X with bf16 rows of 65,536 keys (4 segments of 32 KB; 1, 2 and 3
-// segments stashed leave 3 or 4, 2 and 1 workgroups per CU):
+// segments stashed leave 3 or 4, 2 and 1 workgroups per CU), taken when
+// both directions kept only the last segment in registers:
 //   forward:  0.422, 0.595, 1.014 ms  -> 1 segment
 //   backward: 0.667, 0.639, 0.883 ms  -> 2 segments
 // The forward, which keeps a second register set of chunks to load ahead,
-// needs the workgroups more than it needs fewer second reads.
+// needs the workgroups more than it needs fewer second reads; holding the
+// segment before the last in that second set too leaves one segment of the
+// four to read twice (0.393 ms against 0.416 ms).
 constexpr int kStashSegMaxBytes = 32 * 1024;
 constexpr int kStashBudgetFwd = 32 * 1024;
 constexpr int kStashBudgetBwd = 64 * 1024;
@@ -769,12 +773,14 @@ template <int DT, int CPL, int WPR = kBlockWaves>
 __host__ __device__ constexpr int stream_segments(int T) {
   return ((T + Cfg<DT>::TPS - 1) / Cfg<DT>::TPS + WPR * CPL - 1) / (WPR * CPL);
 }
+// held: segments that stay in registers between the passes (the forward
+// keeps the last two, the backward the last one).
 template <int DT, int CPL, int WPR = kBlockWaves>
-constexpr int stash_segments(int T, int budget) {
+constexpr int stash_segments(int T, int budget, int held) {
   if constexpr (WPR != kBlockWaves) budget = kWideStashBudget;
   const size_t seg_max = WPR == kBlockWaves ? kStashSegMaxBytes : kWideStashSegMaxBytes;
   if (stash_bytes<CPL, WPR>() > seg_max) return 0;
-  const int want = stream_segments<DT, CPL, WPR>(T) - 1;
+  const int want = stream_segments<DT, CPL, WPR>(T) - held;
   const int fit = (int)((size_t)budget / stash_bytes<CPL, WPR>());
   return want < fit ? (want > 0 ? want : 0) : fit;
 }
@@ -822,13 +828,15 @@ __global__ __launch_bounds__(kWave * WPR) void fwd_stream_kernel(const FwdArgs a
     const uint32_t voff = (uint32_t)(ix.loff * ESZ);
     const int lim = kend - ix.loff;
 
-    // Two register sets of one segment's raw chunks: the one being reduced
-    // and the next one, loaded meanwhile.  Exponentials are not kept: pass 2
-    // recomputes them for every segment from the raw chunks and the tile
-    // maxima, the operations of pass 1 on the same inputs.
-    Chunk cur[CPL], nxt[CPL];
+    // Two register sets of one segment's raw chunks, A and B, taking turns:
+    // one is reduced while the next segment loads into the other, so at the
+    // end of pass 1 the last two segments are both still in registers.
+    // Exponentials are not kept: pass 2 recomputes them for every segment
+    // from the raw chunks and the tile maxima, the operations of pass 1 on
+    // the same inputs.
+    Chunk A[CPL], B[CPL];
 #pragma unroll
-    for (int s = 0; s < CPL; ++s) cur[s] = nxt[s] = Chunk{{0u, 0u, 0u, 0u}};
+    for (int s = 0; s < CPL; ++s) A[s] = B[s] = Chunk{{0u, 0u, 0u, 0u}};
     // aux: the cache policy (normal for a segment read again in pass 2, so
     // that the second read can hit the caches; nontemporal for a last read)
     auto load_segment = [&](Chunk (&dst)[CPL], int g, auto aux) {
@@ -875,28 +883,34 @@ __global__ __launch_bounds__(kWave * WPR) void fwd_stream_kernel(const FwdArgs a
 
     // segments wholly past the cut hold only -inf keys: nothing to load
     const int nseg_read = EXCL ? (kend + SPS * TPS * kTile - 1) / (SPS * TPS * kTile) : nseg;
-    // the stash holds segments gs0 .. nseg - 2
-    const int gs0 = nseg - 1 - (a.stash < nseg - 1 ? a.stash : nseg - 1);
+    // the last two segments stay in registers; the stash holds the ones
+    // just before them, gs0 .. nseg - 3; the rest are read again
+    const int before = nseg > 2 ? nseg - 2 : 0;  // segments before the last two
+    const int gs0 = nseg - 2 - (a.stash < before ? a.stash : before);
     auto load_pass1 = [&](Chunk (&dst)[CPL], int g) {
       if (g < gs0) load_segment(dst, g, AuxC<0>{});  // read again in pass 2
       else load_segment(dst, g, AuxC<kAuxNT>{});
     };
 
     // ---- pass 1: tile states of every segment into LDS ----
-    if (nseg_read > 0) load_pass1(cur, 0);
-    for (int g = 0; g < nseg; ++g) {
-      if (g + 1 < nseg_read) load_pass1(nxt, g + 1);
-      if (g >= gs0 && g < nseg - 1 && g < nseg_read) {
+    // segment g in c while segment g + 1 loads into n
+    // (the scheduling barrier keeps a segment's loads from rising above the
+    // work on the one before: three register sets live at once would cost
+    // occupancy)
+    auto p1seg = [&](Chunk (&c)[CPL], Chunk (&n)[CPL], int g) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (g + 1 < nseg_read) load_pass1(n, g + 1);
+      if (g >= gs0 && g < nseg - 2 && g < nseg_read) {
         Chunk *st = lds_stash + (g - gs0) * CPL * kWave * WPR;
 #pragma unroll
-        for (int s = 0; s < CPL; ++s) st[s * kWave * WPR + threadIdx.x] = cur[s];
+        for (int s = 0; s < CPL; ++s) st[s * kWave * WPR + threadIdx.x] = c[s];
       }
 #pragma unroll
       for (int s = 0; s < CPL; ++s) {
         const int t = (g * SPS + s * WPR + ix.wir) * TPS + ix.half;
         float x[KPL];
         float m = kNegInf, l = 0.0f;
-        if (slot_x(g, s, cur[s], x)) {
+        if (slot_x(g, s, c[s], x)) {
           m = tile_max<DT>(lane_tree_max<KPL>(x));
           const float msafe = (m == kNegInf) ? 0.0f : m;
           float e[KPL];
@@ -909,10 +923,11 @@ __global__ __launch_bounds__(kWave * WPR) void fwd_stream_kernel(const FwdArgs a
           lds_l[t] = l;
         }
       }
-      if (g + 1 < nseg) {
-#pragma unroll
-        for (int s = 0; s < CPL; ++s) cur[s] = nxt[s];
-      }
+    };
+    if (nseg_read > 0) load_pass1(A, 0);
+    for (int g = 0; g < nseg; g += 2) {  // even segments in A, odd ones in B
+      p1seg(A, B, g);
+      if (g + 1 < nseg) p1seg(B, A, g + 1);
     }
     __syncthreads();
 
@@ -973,17 +988,19 @@ __global__ __launch_bounds__(kWave * WPR) void fwd_stream_kernel(const FwdArgs a
     const float M = lds_row[0], invL = lds_row[1];
 
     // ---- pass 2: rescale, convert once, write; last segment first ----
-    // cur holds the last segment; the ones before it come from the stash or
-    // are read again, each loaded while the current one is written
-    for (int g = nseg - 1; g >= 0; --g) {
+    // Segment g is written from c; while it is, segment g - 1 comes into n
+    // from the stash or a second read (when asked: the segment before the
+    // last is already in the other register set).
+    auto p2seg = [&](Chunk (&c)[CPL], Chunk (&n)[CPL], int g, bool fetch) {
+      __builtin_amdgcn_sched_barrier(0);
       const int gp = g - 1;
-      if (gp >= 0 && gp < nseg_read) {
+      if (fetch && gp >= 0 && gp < nseg_read) {
         if (gp >= gs0) {
           const Chunk *st = lds_stash + (gp - gs0) * CPL * kWave * WPR;
 #pragma unroll
-          for (int s = 0; s < CPL; ++s) nxt[s] = st[s * kWave * WPR + threadIdx.x];
+          for (int s = 0; s < CPL; ++s) n[s] = st[s * kWave * WPR + threadIdx.x];
         } else {
-          load_segment(nxt, gp, AuxC<kAuxNT>{});
+          load_segment(n, gp, AuxC<kAuxNT>{});
         }
       }
 #pragma unroll
@@ -995,7 +1012,7 @@ __global__ __launch_bounds__(kWave * WPR) void fwd_stream_kernel(const FwdArgs a
           const float mt = lds_m[t < T ? t : T - 1];
           float e[KPL];
           float x[KPL];
-          if (slot_x(g, s, cur[s], x)) {
+          if (slot_x(g, s, c[s], x)) {
             const float msafe = (mt == kNegInf) ? 0.0f : mt;
 #pragma unroll
             for (int k = 0; k < KPL; ++k) e[k] = exp_(x[k] - msafe);
@@ -1012,10 +1029,20 @@ __global__ __launch_bounds__(kWave * WPR) void fwd_stream_kernel(const FwdArgs a
           else store_chunk_elems<DT>(prow, sb + ix.loff, N, out);
         }
       }
-      if (g > 0) {
+    };
+    // the last segment into B, the one before it into A
+    if (((nseg - 1) & 1) == 0) {
 #pragma unroll
-        for (int s = 0; s < CPL; ++s) cur[s] = nxt[s];
+      for (int s = 0; s < CPL; ++s) {
+        const Chunk t = A[s];
+        A[s] = B[s];
+        B[s] = t;
       }
+    }
+    p2seg(B, A, nseg - 1, false);
+    for (int g = nseg - 2; g >= 0; g -= 2) {
+      p2seg(A, B, g, true);
+      if (g >= 1) p2seg(B, A, g - 1, true);
     }
     __syncthreads();  // LDS is reused by the next row
   }
@@ -1201,7 +1228,7 @@ hipError_t launch_fwd_stream(const FwdArgs &a0, const Geometry &g, hipStream_t s
   }
   const dim3 grid((unsigned)g.blocks), block(kWave * WPR);
   FwdArgs a = a0;
-  a.stash = stash_segments<DT, CPL, WPR>(a.s.T, kStashBudgetFwd);
+  a.stash = stash_segments<DT, CPL, WPR>(a.s.T, kStashBudgetFwd, 2);
   const size_t lds = (size_t)stash_offset_words(2 * a.s.T + 2) * sizeof(float) +
                      (size_t)a.stash * stash_bytes<CPL, WPR>();
   const bool mask = a.mask != nullptr, excl = a.ex.causal || a.ex.key_len;
@@ -1229,7 +1256,7 @@ hipError_t launch_bwd_stream(const BwdArgs &a0, const Geometry &g, hipStream_t s
   }
   const dim3 grid((unsigned)g.blocks), block(kWave * WPR);
   BwdArgs a = a0;
-  a.stash = stash_segments<DT, CPL, WPR>(a.s.T, kStashBudgetBwd);
+  a.stash = stash_segments<DT, CPL, WPR>(a.s.T, kStashBudgetBwd, 1);
   const size_t lds = (size_t)stash_offset_words(a.s.T + 1) * sizeof(float) +
                      (size_t)a.stash * stash_bytes<CPL, WPR>();
   const bool excl = a.ex.causal || a.ex.key_len;

@@ -92,12 +92,12 @@ int default_stream_cpl(int dtype) { return dtype == 0 ? kStreamCplF32[1] : kStre
 // first segment's P in the LDS stash, and only that segment's dP is read
 // twice (65,536-key rows: 0.572 ms against 0.646 ms with 4 waves, HBM bytes
 // 1.17 instead of 1.30 times the algorithmic ones).  Every other streaming
-// row takes 4 waves, whose segments of 16,384 keys let the one before the
-// last wait in LDS: the forward is faster so (65,536 keys: 0.418 ms against
-// 0.512 ms with 8 waves, which leave two workgroups per CU instead of three
-// and no next segment to load while one is reduced), and fp32 chunks in two
-// register sets would not fit the wide workgroup's registers at four waves
-// per SIMD.
+// row takes 4 waves, whose segments of 16,384 keys let the last two stay in
+// registers and the one before them wait in LDS: the forward is faster so
+// (65,536 keys: 0.400 ms against 0.485 ms with 8 waves, whose two segments
+// both stay in registers but at 170 VGPRs leave one workgroup per CU), and
+// fp32 chunks in two register sets would not fit the wide workgroup's
+// registers at four waves per SIMD.
 int default_stream_wpr(int dtype, int nslots, bool backward) {
   if (dtype == 0 || !backward) return kBlockWaves;
   return nslots <= 2 * kStreamWideWaves * default_stream_cpl(dtype) ? kStreamWideWaves : kBlockWaves;
