@@ -438,31 +438,45 @@ def copy_ceiling(nbytes, stream, steps=10):
     copy (one read, one write per word: the forward's mix; also the
     calibration point of the HBM byte counters) and two reads with one
     write (the backward's mix), each with normal and nontemporal cache
-    policy and at two grid sizes; the best of each is reported."""
+    policy and at two grid sizes; the best of each is reported.  Like the
+    timed steps, successive launches rotate over enough buffer sets to touch
+    ROTATE_BYTES, so a small stream is not served from the Infinity Cache."""
     import torch
     L = _probe_lib()
     if L is None:
         return None
     out = {"unit": "GB/s"}
+    sets = max(1, -(-ROTATE_BYTES // max(1, nbytes)))
+    out["buffer_sets"] = sets
+
+    def rotating(launch_on):  # launch_on(i) launches on buffer set i
+        k = [0]
+
+        def launch():
+            launch_on(k[0] % sets)
+            k[0] += 1
+        return launch
+
     n16 = max(1, nbytes // 32)
-    src = torch.empty(n16 * 16, dtype=torch.uint8, device="cuda")
-    dst = torch.empty_like(src)
+    src = [torch.empty(n16 * 16, dtype=torch.uint8, device="cuda") for _ in range(sets)]
+    dst = [torch.empty_like(x) for x in src]
     for nt in (0, 1):
-        ms = _time_launch(lambda: L.probe_copy16(src.data_ptr(), dst.data_ptr(), n16, nt, 0,
-                                                 stream.cuda_stream), stream, steps)
+        ms = _time_launch(rotating(lambda i: L.probe_copy16(src[i].data_ptr(), dst[i].data_ptr(), n16,
+                                                            nt, 0, stream.cuda_stream)),
+                          stream, max(steps, sets))
         out["nontemporal" if nt else "plain"] = round(2 * n16 * 16 / (ms * 1e-3) / 1e9, 1)
     out["bytes"] = 2 * n16 * 16
     del src, dst
     n16 = max(1, nbytes // 48)
-    a = torch.empty(n16 * 16, dtype=torch.uint8, device="cuda")
-    b = torch.empty_like(a)
-    d = torch.empty_like(a)
+    a = [torch.empty(n16 * 16, dtype=torch.uint8, device="cuda") for _ in range(sets)]
+    b = [torch.empty_like(x) for x in a]
+    d = [torch.empty_like(x) for x in a]
     best = 0.0
     for nt in (0, 1):
         for blocks in (1024, 2048):
-            ms = _time_launch(lambda: L.probe_read2_write1(a.data_ptr(), b.data_ptr(), d.data_ptr(),
-                                                           n16, nt, blocks, stream.cuda_stream),
-                              stream, steps)
+            ms = _time_launch(rotating(lambda i: L.probe_read2_write1(
+                a[i].data_ptr(), b[i].data_ptr(), d[i].data_ptr(), n16, nt, blocks, stream.cuda_stream)),
+                stream, max(steps, sets))
             best = max(best, 3 * n16 * 16 / (ms * 1e-3) / 1e9)
     out["r2w1"] = round(best, 1)
     out["r2w1_bytes"] = 3 * n16 * 16
