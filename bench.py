@@ -152,8 +152,8 @@ def load_traffic(wl, kernel):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="joint4352",
                     choices=sorted(WORKLOADS) + sorted(ATTN_WORKLOADS))
     ap.add_argument("--no-check", action="store_true", help="skip the parity check before timing")
