@@ -154,11 +154,11 @@ def test_long_row_geometries_identical(dt):
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
 @pytest.mark.parametrize("N", [16385, 40000, 65536, 65544, 131072])
 def test_wide_and_narrow_streaming_identical(dt, N):
-    # rows of whole 16-byte chunks: the 16-wave workgroup (the default up to
-    # 65,536 keys, the whole row in registers) and the 4-wave one (segments,
-    # an LDS stash, second reads) give the same bytes, with mask, sink,
-    # causal cut and lse; past 65,536 keys the wide workgroup reads segments
-    # again like the narrow one
+    # rows of whole 16-byte chunks: the 8-wave workgroup (segments of 32,768
+    # keys; the backward's default up to 65,536 keys) and the 4-wave one
+    # (segments of 16,384 keys) give the same bytes, with mask, sink, causal
+    # cut and lse, whatever each holds in registers, keeps in its LDS stash
+    # or reads twice
     B, H, S = 1, 2, 3
     log(f"wide vs narrow streaming: {dt} N={N}")
     s = synth.normal((B, H, S, N), 2.0, 520, "cpu", dt).to(dev())
@@ -170,6 +170,30 @@ def test_wide_and_narrow_streaming_identical(dt, N):
     ref = run(s, g, launch=(4, 8, 1, 0, 1), **kw)
     assert run(s, g, launch=(8, 8, 1, 0, 1), **kw) == ref
     assert run(s, g, **kw) == ref
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_key_lengths_at_segment_edges(dt):
+    # Key lengths just below, at and just past the segment boundaries of
+    # every streaming geometry (16-bit: 8,192 and 16,384 keys a segment with
+    # 4 waves, 32,768 with 8; fp32: 8,192 and 16,384), so that the
+    # last segment read is each of the ones the forward holds in registers,
+    # keeps in its LDS stash or reads twice.  The bytes agree across
+    # geometries, and with the oracle.
+    N = 70000
+    kl = [1, 8191, 8192, 16384, 16385, 32767, 32769, 49152, 49153, 65536, 65537, N]
+    B, H, S = len(kl), 1, 2
+    log(f"key lengths at segment edges: {dt} N={N}")
+    s = synth.normal((B, H, S, N), 2.0, 530, "cpu", dt).to(dev())
+    g = synth.normal((B, H, S, N), 1.0, 531, "cpu", dt).to(dev())
+    sink = synth.normal((H,), 1.0, 532, "cpu").to(dev())
+    key_len = torch.tensor(kl, dtype=torch.int32, device=dev())
+    ref = run(s, g, sink=sink, key_len=key_len)
+    for cpl in STREAM_CPLS[dt]:
+        assert run(s, g, launch=(4, cpl, 1, 0, 1), sink=sink, key_len=key_len) == ref, cpl
+    if dt != torch.float32:
+        assert run(s, g, launch=(8, 8, 1, 0, 1), sink=sink, key_len=key_len) == ref
+    long_case(dt, N, B=B, H=H, S=S, with_sink=True, kl=kl, seed=533)
 
 
 def test_long_rows_full_size_sampled():
