@@ -438,7 +438,7 @@ def copy_ceiling(nbytes, stream, steps=10):
     copy (one read, one write per word: the forward's mix; also the
     calibration point of the HBM byte counters) and two reads with one
     write (the backward's mix), each with normal and nontemporal cache
-    policy and at two grid sizes; the best of each is reported.  Like the
+    policy and at several grid sizes; the best of each is reported.  Like the
     timed steps, successive launches rotate over enough buffer sets to touch
     ROTATE_BYTES, so a small stream is not served from the Infinity Cache."""
     import torch
@@ -457,14 +457,20 @@ def copy_ceiling(nbytes, stream, steps=10):
             k[0] += 1
         return launch
 
+    def grids(n16):  # persistent grids, and one workgroup per 1,024 words (a whole pass)
+        return sorted({1024, 2048, 8192, 16384, max(1, -(-n16 // 1024))})
+
     n16 = max(1, nbytes // 32)
     src = [torch.empty(n16 * 16, dtype=torch.uint8, device="cuda") for _ in range(sets)]
     dst = [torch.empty_like(x) for x in src]
     for nt in (0, 1):
-        ms = _time_launch(rotating(lambda i: L.probe_copy16(src[i].data_ptr(), dst[i].data_ptr(), n16,
-                                                            nt, 0, stream.cuda_stream)),
-                          stream, max(steps, sets))
-        out["nontemporal" if nt else "plain"] = round(2 * n16 * 16 / (ms * 1e-3) / 1e9, 1)
+        best = 0.0
+        for blocks in grids(n16):
+            ms = _time_launch(rotating(lambda i: L.probe_copy16(src[i].data_ptr(), dst[i].data_ptr(),
+                                                                n16, nt, blocks, stream.cuda_stream)),
+                              stream, max(steps, sets))
+            best = max(best, 2 * n16 * 16 / (ms * 1e-3) / 1e9)
+        out["nontemporal" if nt else "plain"] = round(best, 1)
     out["bytes"] = 2 * n16 * 16
     del src, dst
     n16 = max(1, nbytes // 48)
@@ -473,7 +479,7 @@ def copy_ceiling(nbytes, stream, steps=10):
     d = [torch.empty_like(x) for x in a]
     best = 0.0
     for nt in (0, 1):
-        for blocks in (1024, 2048):
+        for blocks in grids(n16):
             ms = _time_launch(rotating(lambda i: L.probe_read2_write1(
                 a[i].data_ptr(), b[i].data_ptr(), d[i].data_ptr(), n16, nt, blocks, stream.cuda_stream)),
                 stream, max(steps, sets))

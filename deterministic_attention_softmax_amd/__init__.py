@@ -62,7 +62,7 @@ class jas_launch_t(ctypes.Structure):
     _fields_ = [
         ("waves_per_row", ctypes.c_int32), ("chunks_per_lane", ctypes.c_int32),
         ("rows_per_block", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
-        ("streaming", ctypes.c_int32),
+        ("streaming", ctypes.c_int32), ("mask_in_registers", ctypes.c_int32),
     ]
 
 
@@ -209,8 +209,8 @@ def _launch(launch):
     if isinstance(launch, jas_launch_t):
         return launch
     L = jas_launch_t()
-    (L.waves_per_row, L.chunks_per_lane, L.rows_per_block, L.max_blocks,
-     L.streaming) = (int(v) for v in (tuple(launch) + (0, 0, 0, 0, 0))[:5])
+    (L.waves_per_row, L.chunks_per_lane, L.rows_per_block, L.max_blocks, L.streaming,
+     L.mask_in_registers) = (int(v) for v in (tuple(launch) + (0,) * 6)[:6])
     return L
 
 

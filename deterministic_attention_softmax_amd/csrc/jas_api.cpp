@@ -102,11 +102,26 @@ bool whole_chunk_rows(const jas_desc_t *d) {
   return d->keys % kpc == 0 && d->ld % kpc == 0;
 }
 
+// What the forward's mask allows: none, a mask, or a mask broadcast over
+// queries with no causal flag (consecutive rows of a batch entry and head
+// then share one mask row and one visible length).
+enum MaskKind { kNoMask = 0, kMask = 1, kSharedMask = 2 };
+
+MaskKind mask_kind(const jas_desc_t *d) {
+  if (!(d->flags & JAS_FLAG_MASK)) return kNoMask;
+  return (d->mask_stride_q == 0 && !(d->flags & JAS_FLAG_CAUSAL)) ? kSharedMask : kMask;
+}
+
+// Rows from which the forward keeps a shared mask row in registers by
+// default (then two rows per workgroup, and still 8,192 or more
+// workgroups).
+constexpr int64_t kMresMinRows = 16384;
+
 // Launch geometry: the override when given (checked), else the default.
 // tiles are covered by slots of TPS tiles; a row needs ceil(T/TPS) slots,
 // spread over wpr waves holding cpl slots each.
 jas_status_t choose_geometry(int dtype, int T, int64_t rows, bool backward, const jas_launch_t *ov,
-                             Geometry *g, bool whole_chunks = true) {
+                             Geometry *g, bool whole_chunks = true, MaskKind mk = kNoMask) {
   const int tps = jas::tiles_per_slot(dtype);
   const int nslots = (T + tps - 1) / tps;
   int ncpl = 0;
@@ -114,13 +129,19 @@ jas_status_t choose_geometry(int dtype, int T, int64_t rows, bool backward, cons
   int wpr = ov ? ov->waves_per_row : 0;
   int cpl = ov ? ov->chunks_per_lane : 0;
   int rpb = ov ? ov->rows_per_block : 0;
-  const int64_t cap = ov ? ov->max_blocks : 0;
+  int64_t cap = ov ? ov->max_blocks : 0;
+  int mres = ov ? ov->mask_in_registers : 0;
   if (wpr < 0 || cpl < 0 || rpb < 0 || cap < 0) return JAS_ERR_UNSUPPORTED;
   if (ov && ov->streaming != 0 && ov->streaming != 1) return JAS_ERR_UNSUPPORTED;
+  if (mres < 0 || mres > 2) return JAS_ERR_UNSUPPORTED;
+  // a field other than mask_in_registers set: the default does not turn it on
+  const bool geo_given = ov && (wpr || cpl || rpb || cap || ov->streaming);
   g->stream = 0;
+  g->mres = 0;
   if (T > jas::kMaxTiles || (ov && ov->streaming)) {
     // streaming: one row per workgroup of 4 or 16 waves, the row in segments
-    if ((wpr != 0 && wpr != jas::kBlockWaves && wpr != jas::kStreamWideWaves) || rpb > 1)
+    if ((wpr != 0 && wpr != jas::kBlockWaves && wpr != jas::kStreamWideWaves) || rpb > 1 ||
+        mres == 1)
       return JAS_ERR_UNSUPPORTED;
     // rows that cannot take 16-byte accesses run the 4-wave workgroup
     if (wpr == 0) wpr = whole_chunks ? jas::default_stream_wpr(dtype, nslots, backward) : jas::kBlockWaves;
@@ -139,6 +160,7 @@ jas_status_t choose_geometry(int dtype, int T, int64_t rows, bool backward, cons
     g->stream = 1;
     return JAS_OK;
   }
+  if (mres == 1 && wpr == 0) wpr = 2;  // the mask in registers is built for two waves per row
   if (wpr == 0) {
     if (cpl) {
       for (int w : {1, 2, 4})
@@ -161,6 +183,17 @@ jas_status_t choose_geometry(int dtype, int T, int64_t rows, bool backward, cons
     if (cpl == 0) return JAS_ERR_UNSUPPORTED;
   }
   if (!jas::cpl_compiled(dtype, wpr, cpl) || (int64_t)wpr * cpl < nslots) return JAS_ERR_UNSUPPORTED;
+  // the mask in registers: compiled for 16-bit rows of whole 16-byte chunks
+  // on two waves with at most 5 chunks per lane (more would cost a wave per
+  // SIMD); by default where consecutive rows share their mask row
+  const bool mres_ok = !backward && dtype != JAS_DTYPE_F32 && whole_chunks && mk != kNoMask &&
+                       wpr == 2 && cpl <= 5;
+  if (mres == 1 && !mres_ok) return JAS_ERR_UNSUPPORTED;
+  if (mres == 0) mres = (!geo_given && mres_ok && mk == kSharedMask && rows >= kMresMinRows) ? 1 : 2;
+  if (mres == 1) {  // one row per workgroup at a time, two rows per workgroup
+    if (rpb == 0) rpb = 1;
+    if (cap == 0) cap = (rows + 1) / 2;
+  }
   if (rpb == 0) rpb = jas::default_rpb(dtype, nslots, wpr, backward);
   if (rpb < 1 || wpr * rpb > jas::kBlockWaves) return JAS_ERR_UNSUPPORTED;
   int64_t blocks = (rows + rpb - 1) / rpb;
@@ -170,6 +203,7 @@ jas_status_t choose_geometry(int dtype, int T, int64_t rows, bool backward, cons
   g->cpl = cpl;
   g->rpb = rpb;
   g->blocks = blocks;
+  g->mres = mres == 1 ? 1 : 0;
   return JAS_OK;
 }
 
@@ -220,7 +254,7 @@ jas_status_t fwd_impl(const jas_desc_t *d, const void *scores, const float *mask
     return JAS_ERR_ALIASING;
 
   Geometry g;
-  st = choose_geometry(d->dtype, dm.T, dm.rows, false, launch, &g, whole_chunk_rows(d));
+  st = choose_geometry(d->dtype, dm.T, dm.rows, false, launch, &g, whole_chunk_rows(d), mask_kind(d));
   if (st != JAS_OK) return st;
   jas::FwdArgs a;
   a.stash = 0;  // the streaming launcher decides
@@ -518,7 +552,7 @@ jas_status_t jas_bwd_noalloc(const jas_desc_t *desc, const void *probs, const vo
 jas_status_t jas_launch_plan(const jas_desc_t *desc, int backward, const jas_launch_t *launch,
                              jas_launch_t *plan) {
   if (!plan) return JAS_ERR_NULL_POINTER;
-  *plan = jas_launch_t{0, 0, 0, 0, 0};
+  *plan = jas_launch_t{0, 0, 0, 0, 0, 0};
   if (backward != 0 && backward != 1) return JAS_ERR_BAD_FLAGS;
   Dims dm;
   const jas_status_t st = check_desc(desc, &dm);
@@ -526,13 +560,15 @@ jas_status_t jas_launch_plan(const jas_desc_t *desc, int backward, const jas_lau
   if (dm.rows == 0) return JAS_OK;  // no row kernel runs
   Geometry g;
   const jas_status_t sg =
-      choose_geometry(desc->dtype, dm.T, dm.rows, backward != 0, launch, &g, whole_chunk_rows(desc));
+      choose_geometry(desc->dtype, dm.T, dm.rows, backward != 0, launch, &g, whole_chunk_rows(desc),
+                      backward ? kNoMask : mask_kind(desc));
   if (sg != JAS_OK) return sg;
   plan->waves_per_row = g.wpr;
   plan->chunks_per_lane = g.cpl;
   plan->rows_per_block = g.rpb;
   plan->max_blocks = (int32_t)g.blocks;
   plan->streaming = g.stream;
+  plan->mask_in_registers = g.mres;
   return JAS_OK;
 }
 

@@ -70,6 +70,7 @@ struct Geometry {
   int rpb;         // rows per workgroup
   int64_t blocks;  // grid size
   int stream;      // 1: the streaming kernels (4 waves per row, rows in segments)
+  int mres;        // 1: forward with the mask kept in registers over runs of rows
 };
 
 // dtype codes: 0 fp32, 1 bf16, 2 fp16 (jas_dtype_t)

@@ -406,9 +406,16 @@ __device__ __forceinline__ int row_kend(const Exclusion &ex, int N, int64_t Sq, 
 // mask row, shared by the rows of a batch and L2-resident, is read one slot
 // ahead); the tile states meet in LDS; the merge runs in every wave of the
 // row; phase 3 rescales, converts once and stores.
+//
+// MRES (16-byte rows with a mask): each wave keeps its share of the mask row
+// in registers from one of its workgroup's row groups to the next (every
+// gridDim-th group, so the workgroups in flight read neighbouring rows), and
+// loads it again only when a row's mask row or visible length differs from
+// the previous row's: rows that share a mask row (a mask broadcast over
+// queries) load it once per workgroup.  The arithmetic is the same.
 // ---------------------------------------------------------------------------
 
-template <int DT, int WPR, int CPL, bool VEC, bool MASK, bool EXCL>
+template <int DT, int WPR, int CPL, bool VEC, bool MASK, bool EXCL, bool MRES = false>
 __global__ __launch_bounds__(kWave * kBlockWaves) void fwd_kernel(const FwdArgs a) {
   using C = Cfg<DT>;
   constexpr int KPL = C::KPL, TPS = C::TPS, ESZ = C::ESZ;
@@ -424,6 +431,11 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void fwd_kernel(const FwdArgs 
   const int nslots = (T + TPS - 1) / TPS;
   const int64_t ngroups = (a.s.rows + ix.rpb - 1) / ix.rpb;
   const bool has_sink = a.sink != nullptr;
+  constexpr bool kRes = MRES && MASK && VEC;
+  // the mask of the wave's slots (kRes), and the mask row and length it holds
+  float4 mres[kRes ? CPL : 1][KPL / 4];
+  const float *mheld = nullptr;
+  int kheld = -1;
 
   for (int64_t grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
     const int64_t r = grp * ix.rpb + ix.rib;
@@ -467,7 +479,7 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void fwd_kernel(const FwdArgs 
 
     // ---- phase 2: per tile max, exponentials, sum ----
     float e[CPL][KPL];
-    float4 mv[2][KPL / 4];  // mask of the current and the next slot
+    float4 mv[kRes ? 1 : 2][KPL / 4];  // mask of the current and the next slot (not kRes)
     auto load_mask = [&](int s, float4 (&dst)[KPL / 4]) {
       const uint32_t sb4 = (uint32_t)((s * WPR + ix.wir) * TPS * kTile * 4);
 #pragma unroll
@@ -476,14 +488,23 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void fwd_kernel(const FwdArgs 
         dst[k4] = make_float4(u2f(c.w[0]), u2f(c.w[1]), u2f(c.w[2]), u2f(c.w[3]));
       }
     };
-    if constexpr (MASK && VEC) load_mask(0, mv[0]);
+    if constexpr (kRes) {
+      if (mrow != mheld || kread != kheld) {  // uniform
+#pragma unroll
+        for (int s = 0; s < CPL; ++s) load_mask(s, mres[s]);
+        mheld = active ? mrow : nullptr;  // a spare row's buffer is empty
+        kheld = kread;
+      }
+    } else if constexpr (MASK && VEC) {
+      load_mask(0, mv[0]);
+    }
 #pragma unroll
     for (int s = 0; s < CPL; ++s) {
       const int gs = s * WPR + ix.wir;
       const int sb = gs * TPS * kTile;
       const int t = gs * TPS + ix.half;
       const int j0 = sb + ix.loff;
-      if constexpr (MASK && VEC) {
+      if constexpr (MASK && VEC && !kRes) {
         if (s + 1 < CPL) load_mask(s + 1, mv[(s + 1) & 1]);
       }
       float m = kNegInf, l = 0.0f;
@@ -497,7 +518,9 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void fwd_kernel(const FwdArgs 
         unpack<DT>(raw[s], x);
         if constexpr (MASK) {
           if constexpr (VEC) {
-            const float4 (&m4)[KPL / 4] = mv[s & 1];
+            const float4 *m4;
+            if constexpr (kRes) m4 = mres[s];
+            else m4 = mv[s & 1];
 #pragma unroll
             for (int k4 = 0; k4 < KPL / 4; ++k4) {
               x[4 * k4 + 0] = x[4 * k4 + 0] + m4[k4].x;
@@ -1280,8 +1303,14 @@ hipError_t launch_bwd_stream(const BwdArgs &a0, const Geometry &g, hipStream_t s
 // rows with an exclusion (causal or key lengths) run their own instances,
 // so the row-level cut costs the dense rows nothing
 template <int DT, int WPR, int CPL, bool EXCL>
-void launch_fwd_e(const FwdArgs &a, const dim3 grid, const dim3 block, hipStream_t st) {
+void launch_fwd_e(const FwdArgs &a, const dim3 grid, const dim3 block, bool mres, hipStream_t st) {
   const bool mask = a.mask != nullptr;
+  if constexpr (DT != 0 && WPR == 2 && CPL <= 5) {  // the mask-in-registers instances
+    if (mres && mask && a.vec_io) {
+      hipLaunchKernelGGL((fwd_kernel<DT, WPR, CPL, true, true, EXCL, true>), grid, block, 0, st, a);
+      return;
+    }
+  }
   if (a.vec_io) {
     if (mask) hipLaunchKernelGGL((fwd_kernel<DT, WPR, CPL, true, true, EXCL>), grid, block, 0, st, a);
     else hipLaunchKernelGGL((fwd_kernel<DT, WPR, CPL, true, false, EXCL>), grid, block, 0, st, a);
@@ -1294,8 +1323,8 @@ void launch_fwd_e(const FwdArgs &a, const dim3 grid, const dim3 block, hipStream
 template <int DT, int WPR, int CPL>
 hipError_t launch_fwd_t(const FwdArgs &a, const Geometry &g, hipStream_t st) {
   const dim3 grid((unsigned)g.blocks), block(kWave * WPR * g.rpb);
-  if (a.ex.causal || a.ex.key_len) launch_fwd_e<DT, WPR, CPL, true>(a, grid, block, st);
-  else launch_fwd_e<DT, WPR, CPL, false>(a, grid, block, st);
+  if (a.ex.causal || a.ex.key_len) launch_fwd_e<DT, WPR, CPL, true>(a, grid, block, g.mres != 0, st);
+  else launch_fwd_e<DT, WPR, CPL, false>(a, grid, block, g.mres != 0, st);
   return hipGetLastError();
 }
 

@@ -300,6 +300,60 @@ def test_default_geometry_exists_for_every_row_length(dtype):
     assert jas.STATUS.get(st) == "JAS_ERR_UNSUPPORTED"
 
 
+def test_mask_in_registers_choice():
+    # The forward keeps the mask row in registers by default only where
+    # consecutive rows share it: a mask broadcast over queries, no causal
+    # flag, 16-bit 16-byte rows on two waves with at most 5 chunks per lane,
+    # and at least 16,384 rows.  Then one row per workgroup and half as many
+    # workgroups as rows.
+    U = "JAS_ERR_UNSUPPORTED"
+    M, CAUSAL = jas.JAS_FLAG_MASK, jas.JAS_FLAG_CAUSAL
+    joint = dict(B=1, H=24, S=4352, N=4352, flags=M, ms=(4352, 0, 0))
+    rows = 24 * 4352
+    st, p = jas.jas_launch_plan(desc(**joint), 0)
+    assert st == 0 and p.mask_in_registers == 1
+    assert (p.waves_per_row, p.chunks_per_lane, p.rows_per_block) == (2, 5, 1)
+    assert p.max_blocks == rows // 2 and p.streaming == 0
+    # not by default: backward, a mask varying by query, the causal flag,
+    # fp32, no mask, too few rows, rows not whole chunks, a geometry given
+    for d, bw in [(desc(**joint), 1),
+                  (desc(**{**joint, "ms": (4352 * 4352, 0, 4352)}), 0),
+                  (desc(**{**joint, "flags": M | CAUSAL}), 0),
+                  (desc(**{**joint, "dtype": jas.JAS_DTYPE_F32}), 0),
+                  (desc(**{**joint, "flags": 0}), 0),
+                  (desc(**{**joint, "S": 600}), 0),
+                  (desc(**{**joint, "N": 4351, "ms": (4351, 0, 0)}), 0)]:
+        st, p = jas.jas_launch_plan(d, bw)
+        assert st == 0 and p.mask_in_registers == 0, (d.flags, d.keys, d.dtype, bw)
+    st, p = jas.jas_launch_plan(desc(**joint), 0, jas._launch((2, 5, 0, 0, 0)))
+    assert st == 0 and p.mask_in_registers == 0 and p.rows_per_block == 2
+    st, p = jas.jas_launch_plan(desc(**joint), 0, jas._launch((0, 0, 0, 0, 0, 2)))
+    assert st == 0 and p.mask_in_registers == 0 and p.max_blocks == rows // 2
+    # asked for: any mask, any row count; the geometry fields still apply
+    small = desc(B=2, H=3, S=5, N=4352, flags=M, ms=(4352, 0, 4352))
+    st, p = jas.jas_launch_plan(small, 0, jas._launch((0, 0, 0, 0, 0, 1)))
+    assert st == 0 and p.mask_in_registers == 1
+    assert (p.rows_per_block, p.max_blocks) == (1, 15)
+    st, p = jas.jas_launch_plan(small, 0, jas._launch((2, 5, 2, 7, 0, 1)))
+    assert st == 0 and p.mask_in_registers == 1 and (p.rows_per_block, p.max_blocks) == (2, 7)
+    # rows the default gives one wave: asked for, it takes two (5 slots: 3 chunks each)
+    st, p = jas.jas_launch_plan(desc(B=2, H=3, S=5, N=2560, flags=M, ms=(2560, 0, 0)), 0,
+                                jas._launch((0, 0, 0, 0, 0, 1)))
+    assert st == 0 and p.mask_in_registers == 1 and (p.waves_per_row, p.chunks_per_lane) == (2, 3)
+    # asked for where it is not built: an error, no plan
+    for d, bw, ov in [(small, 1, (0, 0, 0, 0, 0, 1)),
+                      (small, 0, (1, 9, 0, 0, 0, 1)),
+                      (small, 0, (4, 3, 0, 0, 0, 1)),
+                      (small, 0, (0, 0, 0, 0, 1, 1)),
+                      (desc(B=2, H=3, S=5, N=4352), 0, (0, 0, 0, 0, 0, 1)),
+                      (desc(B=2, H=3, S=5, N=4352, flags=M, dtype=jas.JAS_DTYPE_F32), 0,
+                       (0, 0, 0, 0, 0, 1)),
+                      (small, 0, (0, 0, 0, 0, 0, 3)),
+                      (small, 0, (0, 0, 0, 0, 0, -1))]:
+        st, p = jas.jas_launch_plan(d, bw, jas._launch(ov))
+        assert jas.STATUS.get(st) == U and p.max_blocks == 0, (bw, ov)
+
+
 def test_launch_plan_reports_overrides_and_errors():
     d = desc(B=2, H=3, S=5, N=1000, dtype=jas.JAS_DTYPE_BF16)
     st, p = jas.jas_launch_plan(d, 0, jas._launch((2, 1, 2, 0, 0)))
