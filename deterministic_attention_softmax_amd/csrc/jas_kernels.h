@@ -747,15 +747,17 @@ __global__ __launch_bounds__(kWave * kBlockWaves) void bwd_kernel(const BwdArgs 
 // ---------------------------------------------------------------------------
 // Streaming kernels, for rows longer than one pass keeps in registers (and
 // for any row when asked for).  A row belongs to one workgroup of 4 waves
-// and is cut into segments of 4 x CPL slots.  Pass 1 reduces each segment's
-// tiles exactly as the one-pass kernels do and keeps every tile state in
-// LDS; wave 0 then folds the states in tile order, 64 tiles at a time with
-// the running state carried from block to block (the same left fold);
-// pass 2 writes the outputs segment by segment, last segment first: that
-// one is still in registers, the ones just before it wait in an LDS stash
-// (one segment in the forward, P of two in the backward), the others are
-// read again (the forward loads the next segment while it writes the
-// current one).  The forward recomputes every segment's
+// (8 for the 16-bit backward of rows up to 65,536 keys) and is cut into
+// segments of WPR x CPL slots.  Pass 1 reduces each segment's tiles exactly
+// as the one-pass kernels do and keeps every tile state in LDS; wave 0 then
+// folds the states in tile order, 64 tiles at a time with the running state
+// carried from block to block (the same left fold); pass 2 writes the
+// outputs segment by segment, last segment first: the last one (the last two
+// in the forward) is still in registers, the ones just before wait in an
+// LDS stash (one segment in the forward, P of two in the 4-wave backward, P
+// of one in the 8-wave backward), the others are read again (the forward
+// loads the next segment while it writes the current one).  The forward
+// recomputes every segment's
 // exponentials from the raw chunks and the saved tile maxima -- the same
 // operations on the same inputs, so every output has the one-pass kernels'
 // bits.
