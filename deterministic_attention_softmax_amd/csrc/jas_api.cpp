@@ -183,13 +183,14 @@ jas_status_t choose_geometry(int dtype, int T, int64_t rows, bool backward, cons
     if (cpl == 0) return JAS_ERR_UNSUPPORTED;
   }
   if (!jas::cpl_compiled(dtype, wpr, cpl) || (int64_t)wpr * cpl < nslots) return JAS_ERR_UNSUPPORTED;
-  // the mask in registers: compiled for 16-bit rows of whole 16-byte chunks
-  // on two waves with at most 5 chunks per lane (more would cost a wave per
-  // SIMD); by default where consecutive rows share their mask row
-  const bool mres_ok = !backward && dtype != JAS_DTYPE_F32 && whole_chunks && mk != kNoMask &&
-                       wpr == 2 && cpl <= 5;
+  // the mask in registers: compiled for 16-bit rows on two waves with at
+  // most 5 chunks per lane (more would cost a wave per SIMD); rows that
+  // cannot take 16-byte accesses run the element-wise forward on the same
+  // grid.  By default where consecutive rows share their mask row.
+  const bool mres_ok = !backward && dtype != JAS_DTYPE_F32 && mk != kNoMask && wpr == 2 && cpl <= 5;
   if (mres == 1 && !mres_ok) return JAS_ERR_UNSUPPORTED;
-  if (mres == 0) mres = (!geo_given && mres_ok && mk == kSharedMask && rows >= kMresMinRows) ? 1 : 2;
+  if (mres == 0)
+    mres = (!geo_given && mres_ok && whole_chunks && mk == kSharedMask && rows >= kMresMinRows) ? 1 : 2;
   if (mres == 1) {  // one row per workgroup at a time, two rows per workgroup
     if (rpb == 0) rpb = 1;
     if (cap == 0) cap = (rows + 1) / 2;

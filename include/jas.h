@@ -160,14 +160,16 @@ typedef struct {
  * {4, 8} for 16-bit types, {8, 16} for fp32.  mask_in_registers (forward
  * only): 1 keeps each wave's share of the mask row in registers from one of
  * its workgroup's rows to the next, reloading it only when the row's mask
- * row (or visible length) changes; it needs a 16-bit dtype,
- * a mask, waves_per_row 2 (taken when waves_per_row is 0) and
- * chunks_per_lane at most 5, and defaults to rows_per_block 1 and half as
- * many workgroups as rows.  2 turns it off.
- * 0 takes the default: on when no other field is set, the mask is
- * broadcast over queries (mask_stride_q 0), there is no causal flag, the
- * default geometry qualifies and there are at least 16,384 rows.  In the
- * plan jas_launch_plan returns it reads 1 when used and 0 otherwise. */
+ * row (or visible length) changes; it needs a 16-bit dtype, a mask,
+ * waves_per_row 2 (taken when waves_per_row is 0) and chunks_per_lane at
+ * most 5 (rows that are not whole aligned 16-byte chunks then run the
+ * element-wise forward on the same grid), and defaults to rows_per_block 1
+ * and half as many workgroups as rows.  2 turns it off.  0 takes the
+ * default: on when no other field is set, the mask is broadcast over
+ * queries (mask_stride_q 0), there is no causal flag, the rows are whole
+ * 16-byte chunks, the default geometry qualifies and there are at least
+ * 16,384 rows.  In the plan jas_launch_plan returns it reads 1 when used
+ * and 0 otherwise. */
 typedef struct {
   int32_t waves_per_row;
   int32_t chunks_per_lane;

@@ -336,6 +336,10 @@ def test_mask_in_registers_choice():
     assert (p.rows_per_block, p.max_blocks) == (1, 15)
     st, p = jas.jas_launch_plan(small, 0, jas._launch((2, 5, 2, 7, 0, 1)))
     assert st == 0 and p.mask_in_registers == 1 and (p.rows_per_block, p.max_blocks) == (2, 7)
+    # rows that are not whole 16-byte chunks: asked for, it runs (the element-wise forward)
+    st, p = jas.jas_launch_plan(desc(B=2, H=3, S=5, N=4351, flags=M, ms=(4351, 0, 0)), 0,
+                                jas._launch((0, 0, 0, 0, 0, 1)))
+    assert st == 0 and p.mask_in_registers == 1
     # rows the default gives one wave: asked for, it takes two (5 slots: 3 chunks each)
     st, p = jas.jas_launch_plan(desc(B=2, H=3, S=5, N=2560, flags=M, ms=(2560, 0, 0)), 0,
                                 jas._launch((0, 0, 0, 0, 0, 1)))

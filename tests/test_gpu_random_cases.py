@@ -6,7 +6,9 @@ streaming rows, tails of every size), padded rows (ld > N, which also moves
 rows off 16-byte boundaries), a mask with broadcast or per-query strides and
 -inf entries, the sink, the causal flag and key lengths (including 0, past
 the row and negative), and checks every row: the forward within 1 ulp of
-the dtype (4e-6 relative for fp32) with the row log-sum-exp, and the
+the dtype (4e-6 relative for fp32) with the row log-sum-exp (and, for
+16-bit rows of 2 to 10 slots with a mask, byte-identical with the mask kept
+in registers on a random grid), and the
 backward stage-isolated (the oracle's P and p_sink, a synthetic dP) bit for
 bit, d_sink included.  RL-Kernel PR #453, Summary and Fixed-order backward;
 ROCm TransformerEngine PR #678 (sink); RL-Kernel PR #240, Path Status
@@ -90,6 +92,17 @@ def test_random_softmax_case(i):
     assert_lse_close(lse.cpu().numpy(), lse_o, f"case {i} lse")
     if sink is not None:
         assert_close(ps.cpu().numpy(), ps_o, f"case {i} p_sink")
+    # where it is built (16-bit rows of 2 to 10 slots with a mask), the
+    # forward with the mask kept in registers gives the same bytes
+    if mask is not None and dt != torch.float32 and 512 < N <= 5120:
+        grid = int(rng.integers(1, rows + 1))
+        P2, ps2, lse2 = jas.fwd(s, mask=mask.to(dev()), mask_strides=ms,
+                                sink=None if sink is None else sink.to(dev()), want_lse=True,
+                                launch=(0, 0, 0, grid, 0, 1), **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(P2, P) and torch.equal(lse2, lse), f"case {i} mask in registers"
+        if sink is not None:
+            assert torch.equal(ps2, ps)
     # backward, stage-isolated: the oracle's P and p_sink, a synthetic dP
     g_full = synth.normal((B, H, Sq, ld), 1.0, c["seed"] + 3, "cpu", dt)
     g_bits = synth.to_numpy_bits(g_full)
