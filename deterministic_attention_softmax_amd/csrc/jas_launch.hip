@@ -105,26 +105,33 @@ int default_stream_wpr(int dtype, int nslots, bool backward) {
 
 // Default waves per row for a row of `nslots` wave-wide chunks (the
 // chunks-per-lane size then is the smallest compiled one that covers the
-// row).  Measured on MI355X, bf16 (fp16 is laid out the same; an fp32 row
-// is twice as many slots for the same keys and registers): the 16-bit
-// forward runs fastest with one wavefront per row up to 5 slots (2,560
-// keys), two up to 18, four beyond (16,384 rows x N keys, with and without
-// a mask: at 6 to 9 slots two wavefronts take 3-12% less time than one, at
-// 2 and 3 slots 15-25% more); the fp32 forward with one wavefront up to 17
-// slots (4,352 keys), two up to 34; the backward, which keeps two inputs in
-// registers, with one wavefront up to 4 slots and four beyond.  Each
-// threshold is capped at what the compiled chunk sizes cover (17 per lane
-// for fp32), so every row up to 16,384 keys has a geometry.  Any choice
-// gives the same bits.
+// row), and rows per workgroup.  Measured on MI355X, 16,384 rows of N keys,
+// median of 5 x 20 calls over rotated copies; any choice gives the same
+// bits.
+//   16-bit forward (fp16 is laid out as bf16): one wavefront per row up to 5
+//   slots (2,560 keys), two up to 18, four beyond.  At 6 to 9 slots two
+//   wavefronts with two rows per workgroup take 3-12% less time than one
+//   (4,352 keys: 48.9 us against 51.4), at 2 and 3 slots 15-25% more; on the
+//   joint shape with its mask the two are level.
+//   16-bit backward, which keeps two inputs in registers: one wavefront up to
+//   4 slots, four beyond (two are within 1-2.5% from 5 to 8 slots).
+//   fp32 (a slot is 256 keys): one wavefront up to 3 slots (backward: 2),
+//   two up to 8, four beyond.  Against the earlier table (one wavefront per
+//   row up to 17 slots forward and 8 backward) the forward takes 5-7% less
+//   time from 4 slots up (1,024 keys: 23.5 us against 25.3; 4,352 keys: 92.7
+//   us against 98.4) and the backward 4-9% less from 3 to 8 slots (2,048
+//   keys: 63.0 us against 69.1, two rows per workgroup).
+// Each threshold is capped at what the compiled chunk sizes cover (17 per
+// lane for fp32), so every row up to 16,384 keys has a geometry.
 int default_wpr(int dtype, int nslots, bool backward) {
   int n = 0;
   const int *c = compiled_cpls(dtype, &n);
-  const int top = c[n - 1];                 // largest compiled chunks per lane
-  const int u = dtype == 0 ? 2 : 1;         // slots per 16-bit-type slot of keys
+  const int top = c[n - 1];  // largest compiled chunks per lane
   if (nslots > 4 * top) return 0;
-  if (backward) return nslots <= 4 * u ? 1 : 4;
-  if (nslots <= std::min(dtype == 0 ? 9 * u : 5, top)) return 1;
-  if (nslots <= std::min(18 * u, 2 * top)) return 2;
+  if (dtype == 0) return nslots <= (backward ? 2 : 3) ? 1 : nslots <= std::min(8, 2 * top) ? 2 : 4;
+  if (backward) return nslots <= 4 ? 1 : 4;
+  if (nslots <= std::min(5, top)) return 1;
+  if (nslots <= std::min(18, 2 * top)) return 2;
   return 4;
 }
 
@@ -132,12 +139,15 @@ int default_wpr(int dtype, int nslots, bool backward) {
 // per wavefront, 4 rows per workgroup; a 16-bit forward row of up to 9 slots
 // on two wavefronts, 2 rows (the 4,352-key rows: 48.4 us against 50.6 us
 // for one row per workgroup, and the joint shape with its mask unchanged);
-// any other row spread over several wavefronts, one row per workgroup
-// (measured faster: its barriers then couple only the row's own waves; 8,192
-// keys on two wavefronts: 1.38 ms against 1.51 ms with two rows).
+// an fp32 backward row on two wavefronts, 2 rows (2,048 keys: 63.0 us
+// against 66.4); any other row spread over several wavefronts, one row per
+// workgroup (measured faster: its barriers then couple only the row's own
+// waves; 8,192 keys on two wavefronts: 1.38 ms against 1.51 ms with two
+// rows).
 int default_rpb(int dtype, int nslots, int wpr, bool backward) {
   if (wpr == 1) return kBlockWaves;
   if (wpr == 2 && !backward && dtype != 0 && nslots <= 9) return 2;
+  if (wpr == 2 && backward && dtype == 0) return 2;
   return 1;
 }
 
