@@ -117,6 +117,11 @@ MaskKind mask_kind(const jas_desc_t *d) {
 // workgroups).
 constexpr int64_t kMresMinRows = 16384;
 
+// Rows from which the wide streaming backward takes two rows per workgroup
+// by default (then still 1,024 or more workgroups, two rounds of the 512
+// that fit).
+constexpr int64_t kStreamTwoRowsMin = 2048;
+
 // Launch geometry: the override when given (checked), else the default.
 // tiles are covered by slots of TPS tiles; a row needs ceil(T/TPS) slots,
 // spread over wpr waves holding cpl slots each.
@@ -151,6 +156,11 @@ jas_status_t choose_geometry(int dtype, int T, int64_t rows, bool backward, cons
     if (wpr == jas::kStreamWideWaves && (dtype == JAS_DTYPE_F32 || cpl != jas::default_stream_cpl(dtype)))
       return JAS_ERR_UNSUPPORTED;
     int64_t blocks = rows;
+    // the wide backward workgroup (66 KB of LDS, two per CU) runs faster
+    // taking two rows each than starting a new workgroup per row (65,536-key
+    // rows, 8,192 of them: 0.551-0.552 ms against 0.572-0.574)
+    if (backward && wpr == jas::kStreamWideWaves && !geo_given && rows >= kStreamTwoRowsMin)
+      blocks = (rows + 1) / 2;
     if (cap > 0 && blocks > cap) blocks = cap;
     if (blocks > 0x7fffffff) blocks = 0x7fffffff;
     g->wpr = wpr;

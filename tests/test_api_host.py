@@ -271,6 +271,19 @@ def test_streaming_workgroup_sizes():
     assert p.waves_per_row == 4                          # more than two wide segments
     st, p = jas.jas_launch_plan(desc(N=40001), 1)
     assert p.waves_per_row == 4                          # not whole 16-byte chunks
+    # the wide backward takes two rows per workgroup from 2,048 rows, unless
+    # a geometry is given; the forward and the 4-wave backward one each
+    big = desc(B=1, H=16, S=512, N=65536)
+    st, p = jas.jas_launch_plan(big, 1)
+    assert st == 0 and (p.waves_per_row, p.max_blocks) == (8, 4096)
+    st, p = jas.jas_launch_plan(big, 0)
+    assert st == 0 and (p.waves_per_row, p.max_blocks) == (4, 8192)
+    st, p = jas.jas_launch_plan(big, 1, jas._launch((8, 8, 1, 0, 1)))
+    assert st == 0 and p.max_blocks == 8192
+    st, p = jas.jas_launch_plan(desc(B=1, H=16, S=127, N=65536), 1)
+    assert st == 0 and p.max_blocks == 16 * 127          # fewer than 2,048 rows
+    st, p = jas.jas_launch_plan(desc(B=1, H=16, S=512, N=65544), 1)
+    assert st == 0 and (p.waves_per_row, p.max_blocks) == (4, 8192)
 
 
 def _plan_covers(d, backward):
